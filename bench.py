@@ -1,0 +1,263 @@
+"""Benchmark: one MoE layer forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole layer (routing metadata, permute, grouped
+SwiGLU GEMMs, combine, and every backward step) over one batch of seeded
+synthetic input already resident in HBM. The default workload is the large
+expert pool: T = 16384 tokens, d_model = 2048, 128 experts, top-4, d_ff = 1024,
+bf16, uniform random routing with Dirichlet(1) gate weights (the pages'
+headline system benchmarks are random-routed). Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+METRIC = "MoE layer fwd+bwd tokens/s at E=128 top-4 d=2048; grouped-GEMM % MFMA peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stage_work(name, wl, n_rows, R):
+    """(kind, algorithmic amount per launch): flops for GEMMs, bytes otherwise."""
+    T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.F
+    rows = n_rows
+    gemm = {"gg_fwd_gate_up": 4, "gg_fwd_down": 2, "gg_dgrad_down": 2, "gg_wgrad_down": 2,
+            "gg_dgrad_gate_up": 4, "gg_wgrad_gate_up": 4}
+    if name in gemm:
+        return "mfma", gemm[name] * rows * d * F
+    b = {
+        "permute": T * d * 2 + rows * d * 2 + R * 4,
+        "combine": R * d * 2 + T * d * 2 + R * 8,
+        "combine_bwd": T * d * 2 + 2 * R * d * 2 + R * 12,
+        "permute_bwd": R * d * 2 + T * d * 2 + R * 4,
+        "offsets": R * 4 * 3 + rows * 4,
+        "router_gemm": T * d * 2 + T * E * 4,
+        "route": T * E * 4 + T * k * 8,
+        "route_bwd": T * k * 12 + T * E * 4,
+        "router_gemm_bwd": T * d * 2 + T * E * 4 + d * E * 2,
+    }
+    return "hbm", b[name]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "routing_grouped_expert_router_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(stage, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        tab = json.load(open(path))
+    except ValueError:
+        return None
+    ent = tab.get(workload, {}).get(stage)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, budget_s):
+    """The oracle, as it stands, on the first T_s tokens of the same workload
+    (all experts, full weights), doubling T_s until one fwd+bwd takes at least
+    budget_s seconds of wall time."""
+    import numpy as np
+    import oracle.moe as om
+    from oracle.numerics import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = None
+    cores = len(os.sched_getaffinity(0))
+    p = {n: bf16_bits_to_f64(inp[n]) for n in ("w_gate", "w_up", "w_down")}
+    Ts = 128
+    while True:
+        q = dict(p)
+        q["x"] = bf16_bits_to_f64(inp["x"][:Ts])
+        dy = bf16_bits_to_f64(inp["dy"][:Ts])
+        if "topk_idx" in inp:
+            q["topk_idx"], q["topk_w"] = inp["topk_idx"][:Ts], inp["topk_w"][:Ts].astype(np.float64)
+        else:
+            q["w_r"] = bf16_bits_to_f64(inp["w_r"])
+        t0 = time.perf_counter()
+        fwd = om.layer_forward(q, wl.k, "bf16")
+        om.layer_backward(q, fwd, dy, wl.k, "bf16")
+        dt = time.perf_counter() - t0
+        log(f"cpu baseline: {Ts} tokens fwd+bwd in {dt:.1f} s")
+        if dt >= budget_s or Ts >= wl.T:
+            break
+        Ts = min(wl.T, Ts * 2)
+    return {"value": Ts / dt, "unit": "tokens/s", "cores": threads or cores, "kind": "oracle",
+            "sample": f"first {Ts} of {wl.T} tokens of the workload, all {wl.E} experts and full "
+                      f"weights, one float64 forward+backward ({dt:.1f} s wall, "
+                      f"{cores} host cores visible)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="e128_uniform_bf16")
+    ap.add_argument("--capacity-factor", type=float, default=0.0,
+                    help="> 0: run the padded-to-capacity path")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the layer "
+              "is built and timed on a single GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from moe_inputs import make_inputs, workload
+    from routing_grouped_expert_router_amd import _lib as L
+    from routing_grouped_expert_router_amd.layer import MoELayer
+
+    L.lib()   # fail loudly if the library is missing
+    wl = workload(args.workload)
+    cap = wl.scaled(capacity_factor=args.capacity_factor).capacity() if args.capacity_factor > 0 else 0
+    log(f"generating inputs for {wl.name} ...")
+    t0 = time.perf_counter()
+    inp = make_inputs(wl)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+    devc = torch.device("cuda:0")
+
+    def up(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(devc)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(devc)
+
+    t = {}
+    for n, a in inp.items():
+        t[n] = up(a, "raw" if n in ("topk_idx", "topk_w", "counts") else "bf16")
+    torch.cuda.synchronize()
+    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
+                     routing="learned" if wl.routing == "learned" else "given", capacity=cap)
+
+    def step():
+        layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
+                      topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
+        layer.backward(t["dy"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    # timed region: K steps, bracketed by synchronisation; per-stage events are
+    # recorded on the stream the kernels run on (torch's current stream)
+    stream = torch.cuda.current_stream()
+    marks = []
+
+    def hook(name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        marks.append((name, ev))
+
+    layer.hook = hook
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        hook("_step")
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    layer.hook = None
+    ms = start.elapsed_time(end) / args.steps
+
+    stage_ms = {}
+    for (a, ea), (b, eb) in zip(marks[:-1], marks[1:]):
+        if b == "_step":
+            continue
+        stage_ms.setdefault(b, []).append(ea.elapsed_time(eb))
+    stage_avg = {n: sum(v) / len(v) for n, v in stage_ms.items()}
+    n_rows = layer.n_rows
+    R = wl.T * wl.k
+    gemm_ms = sum(v for n, v in stage_avg.items() if n.startswith("gg_"))
+    gemm_flops = 18 * n_rows * wl.d * wl.F
+    dom = max(stage_avg, key=stage_avg.get)
+    kind, work = stage_work(dom, wl, n_rows, R)
+    dur_s = stage_avg[dom] / 1e3
+    if kind == "mfma":
+        achieved = work / dur_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = work / dur_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["kernel"] = dom
+    roof["avg_launch_us"] = round(stage_avg[dom] * 1e3, 1)
+    roof["traffic"] = measured_traffic(dom, wl.name)
+
+    stages = {}
+    for n, v in stage_avg.items():
+        kd, wk = stage_work(n, wl, n_rows, R)
+        s = v / 1e3
+        stages[n] = {"us": round(v * 1e3, 1),
+                     ("tflops" if kd == "mfma" else "gbs"): round(wk / s / (1e12 if kd == "mfma" else 1e9), 1)}
+    counts = layer.counts.cpu().numpy()
+    out = {
+        "metric": METRIC,
+        "value": round(wl.T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": wl.T, "d_model": wl.d, "experts": wl.E,
+                   "top_k": wl.k, "d_ff": wl.F, "routing": wl.routing,
+                   "capacity": cap, "parallelism": "single GPU"},
+        "roofline": roof,
+        "grouped_gemm": {"tflops": round(gemm_flops / (gemm_ms / 1e3) / 1e12, 1),
+                         "frac_mfma_peak": round(gemm_flops / (gemm_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "ms": round(gemm_ms, 4)},
+        "stages": stages,
+        "expert_load": {"min": int(counts.min()), "max": int(counts.max()),
+                        "mean": float(counts.mean()), "dropped": int(layer.n_dropped.cpu()[0])},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host for the CPU baseline ...")
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,237 @@
+/*
+ * moe.h -- C ABI of libmoe: one mixture-of-experts layer, forward and
+ * backward, on one AMD Instinct MI355X (gfx950).
+ *
+ * The layer follows the pages' description of Ai2's Olmo-core 3 MoE path:
+ *  - a router picks a few experts per token (deniz.in, "Hedeflediği kapasite
+ *    sorunu");
+ *  - routing metadata (group sizes, split sizes) stays on the GPU so the host
+ *    enqueues work without waiting for a copy back (deniz.in, "Yeni stack
+ *    nasıl çalışıyor"; unite.ai/hi, "पैरालेलिज़्म, प्रिसीजन, और मेमोरी तकनीकें");
+ *  - each selected token row is written straight into its expert's input
+ *    buffer (same sections; donmalab.com, "擴展與最佳化手段");
+ *  - device-scheduled grouped GEMMs run the uneven per-expert shapes, with a
+ *    padded-to-common-capacity alternative kept for comparison (deniz.in,
+ *    "Yeni stack nasıl çalışıyor");
+ *  - MXFP8 for the feed-forward GEMMs (bigchange.ai pt-BR, "Três números,
+ *    três denominadores").
+ *
+ * Conventions shared by every call:
+ *  - Pointers are device pointers unless a parameter says otherwise. The
+ *    caller allocates and owns every buffer, workspaces included; the library
+ *    never allocates, frees, synchronises or copies to the host.
+ *  - Every call only enqueues kernels on `stream` and returns at once.
+ *    Argument errors are detected on the host before anything is enqueued and
+ *    returned as a negative moe_status; a failed launch returns MOE_ERR_HIP.
+ *    Data-dependent errors (an expert id outside [0, E)) are reported through
+ *    a device-resident flag that the caller reads whenever it next syncs.
+ *  - Row-major storage. Element types: MOE_F32 (binary32) or MOE_BF16
+ *    (bfloat16, passed as raw 16-bit patterns). Logits, gate weights, their
+ *    gradients and dlogits are always binary32. Indices are int32.
+ *  - Tensors of 16-bit or 32-bit elements must start 16-byte aligned, and
+ *    row lengths (d, F) must be multiples of 8.
+ *  - Notation: T tokens, d model dim, E experts, k experts per token, F expert
+ *    hidden dim, R = T*k routed slots; slot s = t*k + j is token t's j-th
+ *    choice; n_rows is the row count of the permuted buffers (R dropless,
+ *    E*capacity padded).
+ *  - Results are bitwise reproducible run to run: no floating-point atomics.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or mode */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but outside the supported limits */
+  MOE_ERR_WORKSPACE = -3,    /* workspace missing or too small */
+  MOE_ERR_HIP = -4           /* a HIP launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Limits: 1 <= k <= min(E, 16), 1 <= E <= 1024, T*k < 2^31. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 16
+
+/* Text for a status code (static storage; never NULL). */
+const char* moe_status_string(int status);
+
+/* ABI version of this header: 1. */
+int moe_abi_version(void);
+
+/* ----------------------------------------------------------------- router
+ * moe_router_gemm: logits[t,e] = sum_i x[t,i] * w_r[i,e], binary32 out.
+ * The learned router of the pages' small configurations (bigchange.ai pt-BR,
+ * "O que um engenheiro pode realmente testar").
+ *   x [T,d] and w_r [d,E] of `dtype`; logits [T,E] binary32.
+ *   Accumulation is binary32 in a fixed order. */
+int moe_router_gemm(int dtype, const void* x, const void* w_r, int T, int d, int E,
+                    float* logits, hipStream_t stream);
+
+/* moe_route: top-k experts of each token and their gate weights.
+ * The pages say only that each token goes to a few experts; the reading is a
+ * softmax over all E logits, the k largest kept and renormalised to sum to 1,
+ * i.e. w_j = exp(l_j - l_max) / sum over the selected exp(l_i - l_max).
+ * Selection compares the binary32 logits (softmax is increasing); equal
+ * logits, +0 and -0 included, go to the lower expert id; slot j holds the
+ * j-th largest. NaN logits give unspecified (but in-range) results.
+ *   logits [T,E] binary32 -> topk_idx [T,k] int32, topk_w [T,k] binary32. */
+int moe_route(const float* logits, int T, int E, int k, int32_t* topk_idx, float* topk_w,
+              hipStream_t stream);
+
+/* ----------------------------------------------------------------- metadata
+ * moe_offsets: GPU-resident routing metadata (deniz.in, "Yeni stack nasıl
+ * çalışıyor": split and group sizes never leave the GPU).
+ * Rows are expert-major and, within an expert, in slot order (a stable
+ * counting sort of the flat expert ids):
+ *   counts[E]      slots routed to each expert (before any drop)
+ *   offsets[E+1]   exclusive prefix sum of counts; offsets[E] = R
+ *   row_of[R]      dropless (capacity == 0): offsets[e] + rank of the slot
+ *                  among e's slots; padded (capacity C > 0): e*C + rank if
+ *                  rank < C, else -1 (dropped: overflow goes in slot order)
+ *   src_slot[n]    inverse of row_of over n_rows = R (dropless) or E*C
+ *                  (padded) rows; -1 on pad rows
+ *   n_dropped[1]   number of dropped slots (0 when dropless)
+ *   err_flag[1]    set to 1 if any expert id is outside [0, E) (those slots
+ *                  get row_of = -1 and are not counted); left untouched
+ *                  otherwise, so the caller zeroes it once and may check it
+ *                  after any number of calls.
+ * ws: workspace of at least moe_offsets_workspace_bytes(T, k, E) bytes. */
+size_t moe_offsets_workspace_bytes(int T, int k, int E);
+int moe_offsets(const int32_t* topk_idx, int T, int k, int E, int capacity, int32_t* counts,
+                int32_t* offsets, int32_t* row_of, int32_t* src_slot, int32_t* n_dropped,
+                int32_t* err_flag, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------- row movement
+ * moe_permute: x_perm[row_of[s]] = x[s / k] for every kept slot s: each
+ * selected token row is written straight into its expert's rows (unite.ai/hi,
+ * "पैरालेलिज़्म, प्रिसीजन, और मेमोरी तकनीकें"). If src_slot is not NULL, every row r
+ * with src_slot[r] == -1 (a pad row of the padded layout) is zero-filled;
+ * src_slot may be NULL only when n_rows == T*k (dropless: all rows are hit).
+ *   x [T,d], x_perm [n_rows,d] of `dtype`. Row ids outside [0, n_rows) are
+ *   skipped. */
+int moe_permute(int dtype, const void* x, int T, int d, int k, const int32_t* row_of,
+                const int32_t* src_slot, int n_rows, void* x_perm, hipStream_t stream);
+
+/* moe_unpermute_combine: y[t] = sum_j w[t,j] * y_perm[row_of[t,j]], binary32
+ * accumulation in slot order j = 0..k-1; dropped slots (row -1) add nothing.
+ * Reading: the gate weight scales each expert's output after the down
+ * projection.
+ *   y_perm [n_rows,d], y [T,d] of `dtype`; topk_w [T,k] binary32. */
+int moe_unpermute_combine(int dtype, const void* y_perm, const int32_t* row_of,
+                          const float* topk_w, int T, int k, int d, int n_rows, void* y,
+                          hipStream_t stream);
+
+/* moe_unpermute_combine_bwd: adjoint of moe_unpermute_combine.
+ *   dy_perm[row_of[t,j]] = w[t,j] * dy[t]   (rounded once to `dtype`)
+ *   dtopk_w[t,j] = <dy[t], y_perm[row_of[t,j]]>  (binary32; 0 if dropped)
+ * If src_slot is not NULL, pad rows (src_slot == -1) of dy_perm are zeroed;
+ * src_slot may be NULL only when n_rows == T*k. */
+int moe_unpermute_combine_bwd(int dtype, const void* dy, const void* y_perm,
+                              const float* topk_w, const int32_t* row_of,
+                              const int32_t* src_slot, int T, int k, int d, int n_rows,
+                              void* dy_perm, float* dtopk_w, hipStream_t stream);
+
+/* moe_permute_bwd: adjoint of moe_permute,
+ *   dx[t] = sum_j dx_perm[row_of[t,j]]  (+ sum_e dlogits[t,e] * w_r[:,e])
+ * binary32 accumulation, one rounding to `dtype`. The router term is added
+ * when dlogits and w_r are not NULL (learned router); it is the router
+ * GEMM's share of dx, folded in so that dx is written once.
+ *   dx_perm [n_rows,d], dx [T,d], w_r [d,E] of `dtype`; dlogits [T,E] f32. */
+int moe_permute_bwd(int dtype, const void* dx_perm, const int32_t* row_of, int T, int k, int d,
+                    int n_rows, const float* dlogits, const void* w_r, int E, void* dx,
+                    hipStream_t stream);
+
+/* ----------------------------------------------------------------- router backward
+ * moe_route_bwd: dlogits through the renormalised top-k gate with the
+ * selection held fixed: for selected e_j, dl = w_j (dw_j - sum_i w_i dw_i);
+ * exactly 0 for unselected experts.
+ *   topk_idx, topk_w, dtopk_w [T,k] -> dlogits [T,E] binary32. */
+int moe_route_bwd(const int32_t* topk_idx, const float* topk_w, const float* dtopk_w, int T,
+                  int E, int k, float* dlogits, hipStream_t stream);
+
+/* moe_router_gemm_bwd: dw_r = x^T dlogits, binary32 accumulation over tokens
+ * in a fixed order, one rounding to `dtype`.
+ *   x [T,d], dw_r [d,E] of `dtype`; dlogits [T,E] binary32;
+ *   ws of at least moe_router_bwd_workspace_bytes(T, d, E) bytes. */
+size_t moe_router_bwd_workspace_bytes(int T, int d, int E);
+int moe_router_gemm_bwd(int dtype, const void* x, const float* dlogits, int T, int d, int E,
+                        void* dw_r, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ----------------------------------------------------------------- grouped GEMM
+ * moe_grouped_gemm: the expert GEMMs over the uneven per-expert row blocks
+ * ("device-scheduled grouped GEMM", deniz.in, "Yeni stack nasıl çalışıyor").
+ * Expert e owns rows [group_offsets[e], group_offsets[e+1]) of the permuted
+ * buffers (dropless), or rows [e*capacity, (e+1)*capacity) when capacity > 0
+ * (the padded comparison path). Group sizes are read on the device only.
+ * All products accumulate in binary32 and each output is rounded once to
+ * `dtype`. Expert FFN reading (the pages name no activation): SwiGLU without
+ * biases, H = silu(X Wg) * (X Wu), Y = H Wd.
+ *
+ *   op                     reads                        writes
+ *   MOE_GG_FWD_GATE_UP     x_perm, w_gate, w_up         g, u, h    (h from the
+ *                                                       rounded g and u)
+ *   MOE_GG_FWD_DOWN        h, w_down                    y_perm
+ *   MOE_GG_DGRAD_DOWN      dy_perm, w_down, g, u        dg, du:  dH = dY Wd^T,
+ *                          s = sigmoid(g), dg = dH*u*s*(1+g*(1-s)), du = dH*g*s
+ *   MOE_GG_DGRAD_GATE_UP   dg, du, w_gate, w_up         dx_perm = dg Wg^T + du Wu^T
+ *   MOE_GG_WGRAD_DOWN      h, dy_perm                   dw_down[e] = H_e^T dY_e
+ *   MOE_GG_WGRAD_GATE_UP   x_perm, dg, du               dw_gate[e] = X_e^T dG_e,
+ *                                                       dw_up[e] = X_e^T dU_e
+ * Shapes: x_perm, y_perm, dy_perm, dx_perm [n_rows,d]; g, u, h, dg, du
+ * [n_rows,F]; w_gate, w_up, dw_gate, dw_up [E,d,F]; w_down, dw_down [E,F,d].
+ * Weight gradients of experts with no rows are written as zeros. Rows outside
+ * every group are neither read nor written. The host cannot see the group
+ * sizes: offsets must be non-decreasing with group_offsets[E] <= n_rows
+ * (each group is clamped to [0, n_rows] on the device).
+ * ws: at least moe_grouped_gemm_workspace_bytes(desc) bytes (may be 0). */
+typedef enum {
+  MOE_GG_FWD_GATE_UP = 0,
+  MOE_GG_FWD_DOWN = 1,
+  MOE_GG_DGRAD_DOWN = 2,
+  MOE_GG_DGRAD_GATE_UP = 3,
+  MOE_GG_WGRAD_DOWN = 4,
+  MOE_GG_WGRAD_GATE_UP = 5
+} moe_gg_op;
+
+typedef struct moe_gg_desc {
+  int op;                        /* moe_gg_op */
+  int dtype;                     /* MOE_F32 or MOE_BF16 */
+  int E, d, F;                   /* experts, model dim, expert hidden dim */
+  int n_rows;                    /* rows of the permuted activations */
+  int capacity;                  /* 0: groups from group_offsets; > 0: uniform */
+  const int32_t* group_offsets;  /* [E+1], device; unused when capacity > 0 */
+  void* x_perm;
+  void* g;
+  void* u;
+  void* h;
+  void* y_perm;
+  void* dy_perm;
+  void* dg;
+  void* du;
+  void* dx_perm;
+  void* w_gate;
+  void* w_up;
+  void* w_down;
+  void* dw_gate;
+  void* dw_up;
+  void* dw_down;
+  void* ws;
+  size_t ws_bytes;
+} moe_gg_desc;
+
+size_t moe_grouped_gemm_workspace_bytes(const moe_gg_desc* desc);
+int moe_grouped_gemm(const moe_gg_desc* desc, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,158 @@
+// Grouped-GEMM plumbing shared by the MFMA and the plain FMA kernels: the
+// per-op operand mapping and the device-side group-tile scheduler.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+struct GGArgs {
+  int op, E, d, F, n_rows, capacity;
+  const int32_t* group_offsets;
+  void* x_perm;
+  void* g;
+  void* u;
+  void* h;
+  void* y_perm;
+  void* dy_perm;
+  void* dg;
+  void* du;
+  void* dx_perm;
+  void* w_gate;
+  void* w_up;
+  void* w_down;
+  void* dw_gate;
+  void* dw_up;
+  void* dw_down;
+};
+
+// Static shape of each op as C[M x N] = sum_k A[m, k] B[k, n] per expert.
+template <int OP> struct OpInfo;
+template <> struct OpInfo<MOE_GG_FWD_GATE_UP> {
+  static constexpr bool kDual = true, kKVar = false, kAKContig = true, kBKContig = false;
+};
+template <> struct OpInfo<MOE_GG_FWD_DOWN> {
+  static constexpr bool kDual = false, kKVar = false, kAKContig = true, kBKContig = false;
+};
+template <> struct OpInfo<MOE_GG_DGRAD_DOWN> {
+  static constexpr bool kDual = false, kKVar = false, kAKContig = true, kBKContig = true;
+};
+template <> struct OpInfo<MOE_GG_DGRAD_GATE_UP> {
+  static constexpr bool kDual = false, kKVar = false, kAKContig = true, kBKContig = true;
+};
+template <> struct OpInfo<MOE_GG_WGRAD_DOWN> {
+  static constexpr bool kDual = false, kKVar = true, kAKContig = false, kBKContig = false;
+};
+template <> struct OpInfo<MOE_GG_WGRAD_GATE_UP> {
+  static constexpr bool kDual = true, kKVar = true, kAKContig = false, kBKContig = false;
+};
+
+// Output columns N of an op (per matrix for the dual ops).
+inline __host__ __device__ int op_n(int op, int d, int F) {
+  switch (op) {
+    case MOE_GG_FWD_GATE_UP: return F;
+    case MOE_GG_FWD_DOWN: return d;
+    case MOE_GG_DGRAD_DOWN: return F;
+    case MOE_GG_DGRAD_GATE_UP: return d;
+    case MOE_GG_WGRAD_DOWN: return d;
+    default: return F;   // WGRAD_GATE_UP
+  }
+}
+// Output rows M of a weight-gradient op.
+inline __host__ __device__ int op_wgrad_m(int op, int d, int F) {
+  return op == MOE_GG_WGRAD_DOWN ? F : d;
+}
+// Contraction length of a row-varying op.
+inline __host__ __device__ int op_k(int op, int d, int F) {
+  switch (op) {
+    case MOE_GG_FWD_GATE_UP: return d;
+    case MOE_GG_FWD_DOWN: return F;
+    case MOE_GG_DGRAD_DOWN: return d;
+    default: return 2 * F;   // DGRAD_GATE_UP: [dG | dU] against [Wg ; Wu]
+  }
+}
+
+// Row range [r0, r0 + n) of expert e, clamped into [0, n_rows].
+MOE_DEV void group_rows(const GGArgs& a, int e, int& r0, int& n) {
+  if (a.capacity > 0) {
+    r0 = e * a.capacity;
+    n = a.capacity;
+  } else {
+    int lo = a.group_offsets[e], hi = a.group_offsets[e + 1];
+    lo = lo < 0 ? 0 : (lo > a.n_rows ? a.n_rows : lo);
+    hi = hi < lo ? lo : (hi > a.n_rows ? a.n_rows : hi);
+    r0 = lo;
+    n = hi - lo;
+  }
+  if (r0 + n > a.n_rows) n = a.n_rows - r0 > 0 ? a.n_rows - r0 : 0;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X; give
+// each XCD a contiguous range of tiles so that tiles sharing an expert's
+// weights and rows meet in the same L2.
+MOE_DEV int xcd_remap(int b, int nb) {
+  constexpr int kXcd = 8;
+  const int q = nb / kXcd, rmd = nb % kXcd;
+  const int x = b % kXcd, s = b / kXcd;
+  return x < rmd ? x * (q + 1) + s : rmd * (q + 1) + (x - rmd) * q + s;
+}
+
+// Row-varying ops: map a linear m-tile index to (expert, first row, rows).
+// tile_start[e] = number of BM-row tiles of experts < e, built once per
+// workgroup in LDS from the device-resident group offsets (E <= 1024).
+template <int BM, int NT>
+MOE_DEV bool find_m_tile(const GGArgs& a, int tm, int* tile_start, int& e, int& row0, int& mv) {
+  // per-thread partial sums over a contiguous run of experts
+  constexpr int kMaxPer = (MOE_MAX_EXPERTS + NT - 1) / NT;
+  const int per = (a.E + NT - 1) / NT;
+  const int e_lo = threadIdx.x * per;
+  int loc[kMaxPer];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    int t = 0;
+    if (i < per && e_lo + i < a.E) {
+      int r0, n;
+      group_rows(a, e_lo + i, r0, n);
+      t = (n + BM - 1) / BM;
+    }
+    loc[i] = t;
+    sum += t;
+  }
+  // exclusive scan of the per-thread sums (NT threads)
+  __shared__ int wtot[NT / 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wtot[w] = incl;
+  __syncthreads();
+  int before = incl - sum;
+  for (int i = 0; i < w; ++i) before += wtot[i];
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    if (i < per && e_lo + i < a.E) tile_start[e_lo + i] = before;
+    before += loc[i];
+  }
+  if (threadIdx.x == NT - 1) tile_start[a.E] = before;
+  __syncthreads();
+  if (tm >= tile_start[a.E]) return false;
+  int lo = 0, hi = a.E - 1;   // last e with tile_start[e] <= tm
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_start[mid] <= tm) lo = mid;
+    else hi = mid - 1;
+  }
+  e = lo;
+  int r0, n;
+  group_rows(a, e, r0, n);
+  const int mt = tm - tile_start[e];
+  row0 = r0 + mt * BM;
+  mv = n - mt * BM < BM ? n - mt * BM : BM;
+  return true;
+}
+
+}  // namespace moe

@@ -1,0 +1,296 @@
+// Row movement between token order and expert order (gfx950): permute,
+// weighted combine, and their adjoints. HBM-bound: one wave per token row,
+// 16-byte loads and stores, every token row read once and every routed row
+// written once. See include/moe.h for the contract of each entry point.
+#include "common.h"
+
+namespace moe {
+
+constexpr int kRowThreads = 256;   // 4 waves = 4 tokens per workgroup
+
+// Loads the token's row ids (k <= 16) into registers; ids outside [0, n_rows)
+// become -1 so that a bad id is skipped rather than dereferenced.
+MOE_DEV void load_rows(const int32_t* row_of, size_t t, int k, int n_rows, int (&rows)[MOE_MAX_TOPK]) {
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    int r = -1;
+    if (j < k) {
+      r = row_of[t * k + j];
+      if (r >= n_rows) r = -1;
+    }
+    rows[j] = r;
+  }
+}
+
+// x_perm[row_of[t, j]] = x[t]
+template <typename T>
+__global__ void __launch_bounds__(kRowThreads) permute_kernel(const T* __restrict__ x, int T_, int d,
+                                                              int k, const int32_t* __restrict__ row_of,
+                                                              int n_rows, T* __restrict__ x_perm) {
+  constexpr int V = kVec<T>;
+  const size_t t = ((size_t)blockIdx.x * kRowThreads + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (t >= (size_t)T_) return;
+  int rows[MOE_MAX_TOPK];
+  load_rows(row_of, t, k, n_rows, rows);
+  const int nvec = d / V;
+  const V16* src = reinterpret_cast<const V16*>(x + t * d);
+  for (int c = lane; c < nvec; c += 64) {
+    const V16 v = src[c];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j < k && rows[j] >= 0) reinterpret_cast<V16*>(x_perm + (size_t)rows[j] * d)[c] = v;
+  }
+}
+
+// Zero the rows r with src_slot[r] == -1 (pad rows of the padded layout).
+template <typename T>
+__global__ void __launch_bounds__(kRowThreads) zero_pad_rows_kernel(const int32_t* __restrict__ src_slot,
+                                                                    int n_rows, int d, T* __restrict__ buf) {
+  constexpr int V = kVec<T>;
+  const size_t r = ((size_t)blockIdx.x * kRowThreads + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (r >= (size_t)n_rows || src_slot[r] != -1) return;
+  V16 z;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z.w[i] = 0u;
+  V16* dst = reinterpret_cast<V16*>(buf + r * d);
+  for (int c = lane; c < d / V; c += 64) dst[c] = z;
+}
+
+// y[t] = sum_j w[t, j] y_perm[row_of[t, j]]  (binary32, slot order)
+template <typename T>
+__global__ void __launch_bounds__(kRowThreads) combine_kernel(const T* __restrict__ y_perm,
+                                                              const int32_t* __restrict__ row_of,
+                                                              const float* __restrict__ topk_w, int T_,
+                                                              int k, int d, int n_rows, T* __restrict__ y) {
+  constexpr int V = kVec<T>;
+  const size_t t = ((size_t)blockIdx.x * kRowThreads + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (t >= (size_t)T_) return;
+  int rows[MOE_MAX_TOPK];
+  float w[MOE_MAX_TOPK];
+  load_rows(row_of, t, k, n_rows, rows);
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) w[j] = j < k ? topk_w[t * k + j] : 0.f;
+  const int nvec = d / V;
+  for (int c = lane; c < nvec; c += 64) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k && rows[j] >= 0) {
+        float v[V];
+        unpack(reinterpret_cast<const V16*>(y_perm + (size_t)rows[j] * d)[c], v);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = fmaf(w[j], v[i], acc[i]);
+      }
+    }
+    reinterpret_cast<V16*>(y + t * d)[c] = pack(acc);
+  }
+}
+
+// dy_perm[row_of[t, j]] = w[t, j] dy[t];  dw[t, j] = <dy[t], y_perm[row_of[t, j]]>
+template <typename T>
+__global__ void __launch_bounds__(kRowThreads) combine_bwd_kernel(
+    const T* __restrict__ dy, const T* __restrict__ y_perm, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ row_of, int T_, int k, int d, int n_rows, T* __restrict__ dy_perm,
+    float* __restrict__ dtopk_w) {
+  constexpr int V = kVec<T>;
+  const size_t t = ((size_t)blockIdx.x * kRowThreads + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (t >= (size_t)T_) return;
+  int rows[MOE_MAX_TOPK];
+  float w[MOE_MAX_TOPK], dot[MOE_MAX_TOPK];
+  load_rows(row_of, t, k, n_rows, rows);
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    w[j] = j < k ? topk_w[t * k + j] : 0.f;
+    dot[j] = 0.f;
+  }
+  const int nvec = d / V;
+  for (int c = lane; c < nvec; c += 64) {
+    float g[V];
+    unpack(reinterpret_cast<const V16*>(dy + t * d)[c], g);
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k && rows[j] >= 0) {
+        float v[V], o[V];
+        unpack(reinterpret_cast<const V16*>(y_perm + (size_t)rows[j] * d)[c], v);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          dot[j] = fmaf(g[i], v[i], dot[j]);
+          o[i] = w[j] * g[i];
+        }
+        reinterpret_cast<V16*>(dy_perm + (size_t)rows[j] * d)[c] = pack(o);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j < k) {
+      const float s = wave_sum(dot[j]);
+      if (lane == j) dtopk_w[t * k + j] = rows[j] >= 0 ? s : 0.f;
+    }
+  }
+}
+
+// dx[t] = sum_j dx_perm[row_of[t, j]] (+ sum_e dlogits[t, e] w_r[:, e])
+template <typename T>
+__global__ void __launch_bounds__(kRowThreads) permute_bwd_kernel(
+    const T* __restrict__ dx_perm, const int32_t* __restrict__ row_of, int T_, int k, int d,
+    int n_rows, const float* __restrict__ dlogits, const T* __restrict__ w_r, int E,
+    T* __restrict__ dx) {
+  constexpr int V = kVec<T>;
+  const size_t t = ((size_t)blockIdx.x * kRowThreads + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (t >= (size_t)T_) return;
+  int rows[MOE_MAX_TOPK];
+  load_rows(row_of, t, k, n_rows, rows);
+  const int nvec = d / V;
+  const bool router = dlogits != nullptr;
+  const bool wide = router && (E % V == 0);
+  for (int c = lane; c < nvec; c += 64) {
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k && rows[j] >= 0) {
+        float v[V];
+        unpack(reinterpret_cast<const V16*>(dx_perm + (size_t)rows[j] * d)[c], v);
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] += v[i];
+      }
+    }
+    if (wide) {
+      // w_r rows c*V .. c*V+V-1 are contiguous runs of E values
+      for (int e0 = 0; e0 < E; e0 += V) {
+        float g[V];
+#pragma unroll
+        for (int ee = 0; ee < V; ++ee) g[ee] = dlogits[t * E + e0 + ee];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          float wv[V];
+          unpack(*reinterpret_cast<const V16*>(w_r + (size_t)(c * V + i) * E + e0), wv);
+#pragma unroll
+          for (int ee = 0; ee < V; ++ee) acc[i] = fmaf(g[ee], wv[ee], acc[i]);
+        }
+      }
+    } else if (router) {
+      for (int e = 0; e < E; ++e) {
+        const float g = dlogits[t * E + e];
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = fmaf(g, Elem<T>::load(w_r, (size_t)(c * V + i) * E + e), acc[i]);
+      }
+    }
+    reinterpret_cast<V16*>(dx + t * d)[c] = pack(acc);
+  }
+}
+
+}  // namespace moe
+
+// ============================================================== C ABI
+using namespace moe;
+
+namespace {
+
+int row_grid(long rows) { return static_cast<int>((rows * 64 + kRowThreads - 1) / kRowThreads); }
+
+int check_rows(int dtype, int T, int d, int k, int n_rows) {
+  MOE_CHECK_ARG(valid_dtype(dtype) && T >= 0 && d > 0 && k >= 1 && n_rows >= 0);
+  MOE_CHECK_ARG(d % 8 == 0);
+  MOE_CHECK_SUPPORTED(k <= MOE_MAX_TOPK && (long)T * k < (1L << 31));
+  return MOE_OK;
+}
+
+template <typename T>
+int zero_pads(const int32_t* src_slot, int n_rows, int d, void* buf, hipStream_t stream) {
+  if (n_rows == 0) return MOE_OK;
+  zero_pad_rows_kernel<T><<<row_grid(n_rows), kRowThreads, 0, stream>>>(src_slot, n_rows, d,
+                                                                         static_cast<T*>(buf));
+  return launch_status();
+}
+
+}  // namespace
+
+extern "C" int moe_permute(int dtype, const void* x, int T, int d, int k, const int32_t* row_of,
+                           const int32_t* src_slot, int n_rows, void* x_perm, hipStream_t stream) {
+  if (int st = check_rows(dtype, T, d, k, n_rows)) return st;
+  MOE_CHECK_ARG(src_slot || (long)n_rows == (long)T * k);
+  MOE_CHECK_ARG((T == 0 || (x && row_of && aligned16(x))) && (n_rows == 0 || (x_perm && aligned16(x_perm))));
+  if (src_slot) {
+    const int st = dtype == MOE_BF16 ? zero_pads<uint16_t>(src_slot, n_rows, d, x_perm, stream)
+                                     : zero_pads<float>(src_slot, n_rows, d, x_perm, stream);
+    if (st) return st;
+  }
+  if (T == 0) return MOE_OK;
+  if (dtype == MOE_BF16)
+    permute_kernel<uint16_t><<<row_grid(T), kRowThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(x), T, d, k, row_of, n_rows, static_cast<uint16_t*>(x_perm));
+  else
+    permute_kernel<float><<<row_grid(T), kRowThreads, 0, stream>>>(
+        static_cast<const float*>(x), T, d, k, row_of, n_rows, static_cast<float*>(x_perm));
+  return launch_status();
+}
+
+extern "C" int moe_unpermute_combine(int dtype, const void* y_perm, const int32_t* row_of,
+                                     const float* topk_w, int T, int k, int d, int n_rows, void* y,
+                                     hipStream_t stream) {
+  if (int st = check_rows(dtype, T, d, k, n_rows)) return st;
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(row_of && topk_w && y && aligned16(y) && (n_rows == 0 || (y_perm && aligned16(y_perm))));
+  if (dtype == MOE_BF16)
+    combine_kernel<uint16_t><<<row_grid(T), kRowThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(y_perm), row_of, topk_w, T, k, d, n_rows,
+        static_cast<uint16_t*>(y));
+  else
+    combine_kernel<float><<<row_grid(T), kRowThreads, 0, stream>>>(
+        static_cast<const float*>(y_perm), row_of, topk_w, T, k, d, n_rows, static_cast<float*>(y));
+  return launch_status();
+}
+
+extern "C" int moe_unpermute_combine_bwd(int dtype, const void* dy, const void* y_perm,
+                                         const float* topk_w, const int32_t* row_of,
+                                         const int32_t* src_slot, int T, int k, int d, int n_rows,
+                                         void* dy_perm, float* dtopk_w, hipStream_t stream) {
+  if (int st = check_rows(dtype, T, d, k, n_rows)) return st;
+  MOE_CHECK_ARG(src_slot || (long)n_rows == (long)T * k);
+  MOE_CHECK_ARG(T == 0 || (dy && aligned16(dy) && topk_w && row_of && dtopk_w));
+  MOE_CHECK_ARG(n_rows == 0 || (y_perm && dy_perm && aligned16(y_perm) && aligned16(dy_perm)));
+  if (src_slot) {
+    const int st = dtype == MOE_BF16 ? zero_pads<uint16_t>(src_slot, n_rows, d, dy_perm, stream)
+                                     : zero_pads<float>(src_slot, n_rows, d, dy_perm, stream);
+    if (st) return st;
+  }
+  if (T == 0) return MOE_OK;
+  if (dtype == MOE_BF16)
+    combine_bwd_kernel<uint16_t><<<row_grid(T), kRowThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(y_perm), topk_w, row_of, T,
+        k, d, n_rows, static_cast<uint16_t*>(dy_perm), dtopk_w);
+  else
+    combine_bwd_kernel<float><<<row_grid(T), kRowThreads, 0, stream>>>(
+        static_cast<const float*>(dy), static_cast<const float*>(y_perm), topk_w, row_of, T, k, d,
+        n_rows, static_cast<float*>(dy_perm), dtopk_w);
+  return launch_status();
+}
+
+extern "C" int moe_permute_bwd(int dtype, const void* dx_perm, const int32_t* row_of, int T, int k,
+                               int d, int n_rows, const float* dlogits, const void* w_r, int E,
+                               void* dx, hipStream_t stream) {
+  if (int st = check_rows(dtype, T, d, k, n_rows)) return st;
+  MOE_CHECK_ARG((dlogits == nullptr) == (w_r == nullptr));
+  MOE_CHECK_ARG(!dlogits || (E > 0 && E <= MOE_MAX_EXPERTS && aligned16(w_r)));
+  if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(row_of && dx && aligned16(dx) && (n_rows == 0 || (dx_perm && aligned16(dx_perm))));
+  if (dtype == MOE_BF16)
+    permute_bwd_kernel<uint16_t><<<row_grid(T), kRowThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(dx_perm), row_of, T, k, d, n_rows, dlogits,
+        static_cast<const uint16_t*>(w_r), E, static_cast<uint16_t*>(dx));
+  else
+    permute_bwd_kernel<float><<<row_grid(T), kRowThreads, 0, stream>>>(
+        static_cast<const float*>(dx_perm), row_of, T, k, d, n_rows, dlogits,
+        static_cast<const float*>(w_r), E, static_cast<float*>(dx));
+  return launch_status();
+}

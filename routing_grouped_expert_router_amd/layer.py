@@ -1,0 +1,161 @@
+"""One MoE layer on one GPU: buffers plus the call sequence of the C ABI.
+
+PyTorch only allocates device memory and supplies the stream; every step runs
+in libmoe's kernels, in this order (no device-to-host copy anywhere: group
+sizes and offsets are consumed on the device, as the pages' GPU-resident
+routing requires -- deniz.in, "Yeni stack nasıl çalışıyor"):
+
+  forward   router GEMM -> top-k gate -> offsets -> permute -> grouped GEMM
+            gate/up + SwiGLU -> grouped GEMM down -> weighted combine
+  backward  combine adjoint -> dgrad down + SwiGLU' -> wgrad down -> dgrad
+            gate/up -> wgrad gate/up -> (router: gate adjoint, router GEMM
+            adjoint) -> permute adjoint (+ router share of dx)
+
+With ``routing='given'`` the top-k ids and gate weights are inputs (the pages'
+random-routed system benchmarks) and the router steps are skipped.
+"""
+from __future__ import annotations
+
+from typing import Dict, Optional
+
+import torch
+
+from . import _lib as L
+
+
+class MoELayer:
+    def __init__(self, T: int, d: int, E: int, k: int, F: int, dtype=torch.bfloat16,
+                 routing: str = "learned", capacity: int = 0, backward: bool = True,
+                 device: str = "cuda"):
+        if routing not in ("learned", "given"):
+            raise ValueError(routing)
+        self.T, self.d, self.E, self.k, self.F = T, d, E, k, F
+        self.dtype, self.routing, self.capacity = dtype, routing, capacity
+        self.R = T * k
+        self.n_rows = E * capacity if capacity > 0 else self.R
+        dev = torch.device(device)
+        f32, i32 = torch.float32, torch.int32
+        e = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=dev)
+        nr = self.n_rows
+        if routing == "learned":
+            self.logits = e(T, E, dt=f32)
+            self.topk_idx = e(T, k, dt=i32)
+            self.topk_w = e(T, k, dt=f32)
+        self.counts = e(E, dt=i32)
+        self.offsets = e(E + 1, dt=i32)
+        self.row_of = e(self.R, dt=i32)
+        self.src_slot = e(nr, dt=i32)
+        self.n_dropped = e(1, dt=i32)
+        self.err_flag = torch.zeros(1, dtype=i32, device=dev)
+        ws = max(L.moe_offsets_workspace_bytes(T, k, E), 16)
+        self.ws_offsets = e((ws + 15) // 16 * 4, dt=i32)
+        self.x_perm = e(nr, d)
+        self.g, self.u, self.h = e(nr, F), e(nr, F), e(nr, F)
+        self.y_perm = e(nr, d)
+        self.y = e(T, d)
+        self.has_bwd = backward
+        if backward:
+            self.dy_perm = e(nr, d)
+            self.dtopk_w = e(T, k, dt=f32)
+            self.dg, self.du = e(nr, F), e(nr, F)
+            self.dx_perm = e(nr, d)
+            self.dx = e(T, d)
+            self.dw_gate, self.dw_up = e(E, d, F), e(E, d, F)
+            self.dw_down = e(E, F, d)
+            if routing == "learned":
+                self.dlogits = e(T, E, dt=f32)
+                self.dw_r = e(d, E)
+                wsr = max(L.moe_router_bwd_workspace_bytes(T, d, E), 16)
+                self.ws_router = e((wsr + 15) // 16 * 4, dt=f32)
+        self._dt = L.MOE_BF16 if dtype == torch.bfloat16 else L.MOE_F32
+        # optional callable(stage_name) run after each stage is enqueued (used
+        # by the benchmark to record per-stage events)
+        self.hook = None
+
+    def _mark(self, name: str):
+        if self.hook is not None:
+            self.hook(name)
+
+    # ------------------------------------------------------------------ helpers
+    def _gg(self, op, **tensors):
+        grp = None if self.capacity > 0 else self.offsets
+        desc = L.make_gg_desc(op, self._dt, self.E, self.d, self.F, self.n_rows, self.capacity,
+                              grp, **tensors)
+        L.moe_grouped_gemm(desc)
+
+    # ------------------------------------------------------------------ passes
+    def route(self, x, w_r):
+        L.moe_router_gemm(x, w_r, self.logits)
+        self._mark("router_gemm")
+        L.moe_route(self.logits, self.k, self.topk_idx, self.topk_w)
+        self._mark("route")
+
+    def forward(self, x, w_gate, w_up, w_down, w_r=None, topk_idx=None, topk_w=None):
+        self.x, self.w_gate, self.w_up, self.w_down, self.w_r = x, w_gate, w_up, w_down, w_r
+        if self.routing == "learned":
+            self.route(x, w_r)
+        else:
+            self.topk_idx, self.topk_w = topk_idx, topk_w
+        self.metadata()
+        self.permute()
+        self.experts_forward()
+        self.combine()
+        return self.y
+
+    def metadata(self):
+        L.moe_offsets(self.topk_idx, self.E, self.capacity, self.counts, self.offsets, self.row_of,
+                      self.src_slot, self.n_dropped, self.err_flag, self.ws_offsets)
+        self._mark("offsets")
+
+    def permute(self):
+        L.moe_permute(self.x, self.k, self.row_of, self.src_slot if self.capacity > 0 else None,
+                      self.x_perm)
+        self._mark("permute")
+
+    def experts_forward(self):
+        self._gg(L.MOE_GG_FWD_GATE_UP, x_perm=self.x_perm, w_gate=self.w_gate, w_up=self.w_up,
+                 g=self.g, u=self.u, h=self.h)
+        self._mark("gg_fwd_gate_up")
+        self._gg(L.MOE_GG_FWD_DOWN, h=self.h, w_down=self.w_down, y_perm=self.y_perm)
+        self._mark("gg_fwd_down")
+
+    def combine(self):
+        L.moe_unpermute_combine(self.y_perm, self.row_of, self.topk_w, self.y)
+        self._mark("combine")
+
+    def backward(self, dy):
+        L.moe_unpermute_combine_bwd(dy, self.y_perm, self.topk_w, self.row_of,
+                                    self.src_slot if self.capacity > 0 else None,
+                                    self.dy_perm, self.dtopk_w)
+        self._mark("combine_bwd")
+        self.experts_backward()
+        if self.routing == "learned":
+            L.moe_route_bwd(self.topk_idx, self.topk_w, self.dtopk_w, self.E, self.dlogits)
+            self._mark("route_bwd")
+            L.moe_router_gemm_bwd(self.x, self.dlogits, self.dw_r, self.ws_router)
+            self._mark("router_gemm_bwd")
+            L.moe_permute_bwd(self.dx_perm, self.row_of, self.k, self.dx, self.dlogits, self.w_r)
+        else:
+            L.moe_permute_bwd(self.dx_perm, self.row_of, self.k, self.dx)
+        self._mark("permute_bwd")
+        return self.dx
+
+    def experts_backward(self):
+        self._gg(L.MOE_GG_DGRAD_DOWN, dy_perm=self.dy_perm, w_down=self.w_down, g=self.g, u=self.u,
+                 dg=self.dg, du=self.du)
+        self._mark("gg_dgrad_down")
+        self._gg(L.MOE_GG_WGRAD_DOWN, h=self.h, dy_perm=self.dy_perm, dw_down=self.dw_down)
+        self._mark("gg_wgrad_down")
+        self._gg(L.MOE_GG_DGRAD_GATE_UP, dg=self.dg, du=self.du, w_gate=self.w_gate, w_up=self.w_up,
+                 dx_perm=self.dx_perm)
+        self._mark("gg_dgrad_gate_up")
+        self._gg(L.MOE_GG_WGRAD_GATE_UP, x_perm=self.x_perm, dg=self.dg, du=self.du,
+                 dw_gate=self.dw_gate, dw_up=self.dw_up)
+        self._mark("gg_wgrad_gate_up")
+
+    def grads(self) -> Dict[str, torch.Tensor]:
+        out = dict(dx=self.dx, dw_gate=self.dw_gate, dw_up=self.dw_up, dw_down=self.dw_down,
+                   dtopk_w=self.dtopk_w)
+        if self.routing == "learned":
+            out.update(dlogits=self.dlogits, dw_r=self.dw_r)
+        return out

@@ -1,0 +1,126 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point the header declares, the binding covers them all, and
+argument errors come back synchronously with the documented codes before
+anything is launched."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from routing_grouped_expert_router_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+INVALID, UNSUPPORTED, WORKSPACE = -1, -2, -3
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_north_star_calls():
+    names = declared()
+    for n in ("moe_route", "moe_offsets", "moe_permute", "moe_grouped_gemm",
+              "moe_unpermute_combine", "moe_unpermute_combine_bwd", "moe_permute_bwd",
+              "moe_route_bwd", "moe_router_gemm", "moe_router_gemm_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.CDLL(L.LIB_PATH)
+    missing = [n for n in declared() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_symbol():
+    assert sorted(L.SIGNATURES) == declared()
+    lib = L.lib()
+    assert lib.moe_abi_version() == 1
+    assert lib.moe_status_string(0) == b"ok"
+    assert lib.moe_status_string(-3) == b"workspace missing or too small"
+    assert lib.moe_status_string(12345) == b"unknown status"
+
+
+def test_desc_layout_matches_header():
+    # int op..capacity (7), pointer group_offsets, 15 tensor pointers, ws, ws_bytes
+    assert C.sizeof(L.moe_gg_desc) == 7 * 4 + 4 + 8 * 17 + 8
+
+
+FAKE = 0x1000   # 16-byte aligned, never dereferenced: every call below fails its checks first
+
+
+def test_route_argument_errors():
+    lib = L.lib()
+    assert lib.moe_route(FAKE, 4, 2, 3, FAKE, FAKE, None) == INVALID          # k > E
+    assert lib.moe_route(FAKE, 4, 8, 0, FAKE, FAKE, None) == INVALID          # k < 1
+    assert lib.moe_route(None, 4, 8, 2, FAKE, FAKE, None) == INVALID          # null logits
+    assert lib.moe_route(FAKE, -1, 8, 2, FAKE, FAKE, None) == INVALID
+    assert lib.moe_route(FAKE, 4, 2048, 2, FAKE, FAKE, None) == UNSUPPORTED   # E > 1024
+    assert lib.moe_route(FAKE, 4, 64, 17, FAKE, FAKE, None) == UNSUPPORTED    # k > 16
+
+
+def test_offsets_argument_errors():
+    lib = L.lib()
+    need = lib.moe_offsets_workspace_bytes(100, 4, 8)
+    assert need == 8 * 4
+    assert lib.moe_offsets_workspace_bytes(16384, 4, 128) == 64 * 128 * 4
+    args = lambda ws, nb, cap=0, k=4: (FAKE, 100, k, 8, cap, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, nb, None)
+    assert lib.moe_offsets(*args(None, 0)) == WORKSPACE
+    assert lib.moe_offsets(*args(FAKE, need - 1)) == WORKSPACE
+    assert lib.moe_offsets(*args(FAKE, need, cap=-1)) == INVALID
+    assert lib.moe_offsets(*args(FAKE, need, k=9)) == INVALID
+
+
+def test_row_calls_argument_errors():
+    lib = L.lib()
+    # d not a multiple of 8
+    assert lib.moe_permute(1, FAKE, 10, 12, 2, FAKE, None, 20, FAKE, None) == INVALID
+    # padded layout without src_slot
+    assert lib.moe_permute(1, FAKE, 10, 16, 2, FAKE, None, 25, FAKE, None) == INVALID
+    # misaligned tensor
+    assert lib.moe_permute(1, FAKE + 2, 10, 16, 2, FAKE, None, 20, FAKE, None) == INVALID
+    # bad dtype
+    assert lib.moe_unpermute_combine(7, FAKE, FAKE, FAKE, 10, 2, 16, 20, FAKE, None) == INVALID
+    assert lib.moe_unpermute_combine(1, FAKE, FAKE, FAKE, 10, 17, 16, 20, FAKE, None) == UNSUPPORTED
+    assert lib.moe_unpermute_combine_bwd(1, FAKE, FAKE, FAKE, FAKE, None, 10, 2, 16, 21, FAKE, FAKE, None) == INVALID
+    # router share needs both dlogits and w_r
+    assert lib.moe_permute_bwd(1, FAKE, FAKE, 10, 2, 16, 20, FAKE, None, 8, FAKE, None) == INVALID
+    assert lib.moe_route_bwd(FAKE, FAKE, FAKE, 10, 4, 5, FAKE, None) == INVALID
+
+
+def test_router_argument_errors():
+    lib = L.lib()
+    assert lib.moe_router_gemm(1, FAKE, FAKE, 10, 12, 8, FAKE, None) == INVALID
+    assert lib.moe_router_gemm(1, FAKE, FAKE, 10, 16, 4096, FAKE, None) == UNSUPPORTED
+    need = lib.moe_router_bwd_workspace_bytes(300, 16, 8)
+    assert need == 3 * 16 * 8 * 4
+    assert lib.moe_router_gemm_bwd(1, FAKE, FAKE, 300, 16, 8, FAKE, FAKE, need - 4, None) == WORKSPACE
+
+
+def test_grouped_gemm_argument_errors():
+    mk = lambda **kw: L.make_gg_desc(**{**dict(op=L.MOE_GG_FWD_DOWN, dtype=L.MOE_BF16, E=4, d=256,
+                                               F=256, n_rows=64, capacity=16), **kw})
+    lib = L.lib()
+    call = lambda d: lib.moe_grouped_gemm(C.byref(d), None)
+    assert call(mk()) == INVALID                         # operands missing
+    d = mk()
+    d.h, d.w_down, d.y_perm = FAKE, FAKE, FAKE
+    d.op = 17
+    assert call(d) == INVALID
+    d.op = L.MOE_GG_FWD_DOWN
+    d.capacity = 100                                     # E * capacity > n_rows
+    assert call(d) == INVALID
+    d.capacity, d.d = 16, 12                             # d % 8 != 0
+    assert call(d) == INVALID
+    d.d, d.E = 256, 5000
+    assert call(d) == UNSUPPORTED
+    d.E, d.capacity, d.group_offsets = 4, 0, None        # dropless needs offsets
+    assert call(d) == INVALID
+    d.h = FAKE + 4                                       # misaligned
+    d.capacity = 16
+    assert call(d) == INVALID
+    assert lib.moe_grouped_gemm(None, None) == INVALID

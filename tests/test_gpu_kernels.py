@@ -1,0 +1,294 @@
+"""GPU parity of each C-ABI entry point against the oracle, element by
+element, on seeded inputs that span several tiles with ragged tails, plus
+the edge cases: empty inputs, one expert, k = E, all tokens on one expert,
+experts with no rows, tied and signed-zero logits, capacity drops, and bad
+expert ids."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe as om
+from oracle.numerics import round_bf16, round_f32, storer
+from routing_grouped_expert_router_amd import _lib as L
+
+from parity import assert_close, dev, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _rng(*seed):
+    return np.random.default_rng(list(seed))
+
+
+def _bf16_bits(a):
+    from oracle.numerics import f64_to_bf16_bits
+    return f64_to_bf16_bits(a)
+
+
+def _to(a, kind):
+    """float64 values -> (device tensor of `kind`, the stored values)."""
+    if kind == "bf16":
+        v = round_bf16(a)
+        return dev(_bf16_bits(v), "bf16"), v
+    v = round_f32(a)
+    return dev(v.astype(np.float32), "f32"), v
+
+
+# ----------------------------------------------------------------------------- route
+@pytest.mark.parametrize("T,E,k", [(1, 1, 1), (37, 8, 2), (300, 8, 8), (513, 16, 4), (100, 33, 5),
+                                   (257, 64, 4), (1000, 128, 4), (129, 200, 16), (64, 1024, 16)])
+def test_route_parity(T, E, k):
+    rng = _rng(1, T, E, k)
+    lg = round_f32(rng.standard_normal((T, E)) * 3)
+    # inject exact ties and signed zeros
+    lg[::3, : E // 2] = np.round(lg[::3, : E // 2])
+    lg[::5, 0] = -0.0
+    lg[::7, -1] = 0.0
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    L.moe_route(dev(lg.astype(np.float32), "f32"), k, idx, w)
+    ridx, rw = om.route(lg, k)
+    assert np.array_equal(host(idx), ridx)
+    assert_close(host(w), rw, "f32", "topk_w")
+
+
+def test_route_all_equal_and_empty():
+    idx = torch.empty(5, 3, dtype=torch.int32, device="cuda")
+    w = torch.empty(5, 3, dtype=torch.float32, device="cuda")
+    L.moe_route(torch.zeros(5, 6, device="cuda"), 3, idx, w)
+    assert np.array_equal(host(idx), np.tile(np.arange(3), (5, 1)))
+    assert np.allclose(host(w), 1.0 / 3, rtol=0, atol=1e-7)
+    L.moe_route(torch.zeros(0, 6, device="cuda"), 3, idx[:0], w[:0])   # T = 0 is a no-op
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------- offsets
+def _run_offsets(idx_np, E, C):
+    T, k = idx_np.shape
+    R = T * k
+    n_rows = E * C if C else R
+    t = lambda n: torch.full((max(n, 1),), -7, dtype=torch.int32, device="cuda")
+    counts, offsets, row_of, src_slot = t(E), t(E + 1), t(R), t(n_rows)
+    nd, err = t(1), torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(L.moe_offsets_workspace_bytes(T, k, E) // 4 + 1, dtype=torch.int32, device="cuda")
+    L.moe_offsets(dev(idx_np.astype(np.int32), "i32"), E, C, counts, offsets, row_of, src_slot, nd, err, ws)
+    return (host(counts)[:E], host(offsets)[:E + 1], host(row_of)[:R], host(src_slot)[:n_rows],
+            int(host(nd)[0]), int(host(err)[0]))
+
+
+def _draw(rng, T, E, k, skew=0.0):
+    p = np.arange(1, E + 1, dtype=float) ** (-skew)
+    p /= p.sum()
+    g = rng.gumbel(size=(T, E)) + np.log(p)
+    return np.argsort(-g, axis=1)[:, :k].astype(np.int32)
+
+
+@pytest.mark.parametrize("T,E,k,C,skew", [
+    (1, 1, 1, 0, 0), (7, 4, 4, 0, 0), (1000, 8, 2, 0, 0), (3000, 128, 4, 0, 1.2),
+    (3000, 128, 4, 96, 1.2), (16384, 128, 4, 640, 1.2), (5000, 1024, 16, 0, 0.5),
+    (2049, 3, 1, 0, 0), (2000, 16, 4, 10, 0.0), (600, 8, 4, 400, 0.0)])
+def test_offsets_parity(T, E, k, C, skew):
+    rng = _rng(2, T, E, k, C)
+    idx = _draw(rng, T, E, k, skew)
+    counts, offsets, row_of, src_slot, nd, err = _run_offsets(idx, E, C)
+    ref = om.expert_offsets(idx, E, C)
+    assert err == 0
+    assert np.array_equal(counts, ref["counts"])
+    assert np.array_equal(offsets, ref["offsets"])
+    assert np.array_equal(row_of, ref["row_of"])
+    assert np.array_equal(src_slot, ref["src_slot"])
+    assert nd == ref["n_dropped"]
+
+
+def test_offsets_all_on_one_expert_and_empty_experts():
+    idx = np.full((2500, 1), 5, dtype=np.int32)
+    counts, offsets, row_of, src_slot, nd, err = _run_offsets(idx, 16, 0)
+    ref = om.expert_offsets(idx, 16)
+    assert np.array_equal(counts, ref["counts"]) and np.array_equal(row_of, ref["row_of"])
+    assert np.array_equal(offsets, ref["offsets"]) and np.array_equal(src_slot, ref["src_slot"])
+
+
+def test_offsets_bad_ids_raise_flag():
+    idx = np.array([[0, 1], [2, 9], [-1, 3]], dtype=np.int32)
+    counts, offsets, row_of, src_slot, nd, err = _run_offsets(idx, 4, 0)
+    assert err == 1
+    assert row_of[3] == -1 and row_of[4] == -1
+    assert counts.sum() == 4
+
+
+# ----------------------------------------------------------------------------- rows
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+@pytest.mark.parametrize("T,d,E,k,C", [(333, 264, 8, 2, 0), (1000, 2048, 128, 4, 0),
+                                       (700, 136, 16, 4, 150), (1, 8, 1, 1, 0)])
+def test_row_movement_parity(kind, T, d, E, k, C):
+    rng = _rng(3, T, d, E, k, C)
+    idx = _draw(rng, T, E, k, 1.0)
+    meta = om.expert_offsets(idx, E, C)
+    n_rows = meta["n_rows"]
+    st = storer(kind)
+    xt, x = _to(rng.standard_normal((T, d)), kind)
+    row_of = dev(meta["row_of"], "i32")
+    src = dev(meta["src_slot"], "i32")
+    padded = C > 0
+    dt = torch.bfloat16 if kind == "bf16" else torch.float32
+    # permute
+    xp = torch.full((n_rows, d), 7.0, dtype=dt, device="cuda")
+    L.moe_permute(xt, k, row_of, src if padded else None, xp)
+    assert np.array_equal(host(xp), om.permute(x, meta["src_slot"], k))
+    # combine
+    ypt, yp = _to(rng.standard_normal((n_rows, d)), kind)
+    wt = rng.dirichlet(np.ones(k), size=T).astype(np.float32)
+    w = wt.astype(np.float64)
+    y = torch.empty(T, d, dtype=dt, device="cuda")
+    L.moe_unpermute_combine(ypt, row_of, dev(wt, "f32"), y)
+    assert_close(host(y), om.combine(yp, meta["row_of"], w, T, k, st), kind, "y")
+    # combine backward
+    dyt, dy = _to(rng.standard_normal((T, d)), kind)
+    dyp = torch.full((n_rows, d), 7.0, dtype=dt, device="cuda")
+    dw = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    L.moe_unpermute_combine_bwd(dyt, ypt, dev(wt, "f32"), row_of, src if padded else None, dyp, dw)
+    rdyp, rdw = om.combine_bwd(dy, yp, w, meta["row_of"], n_rows, st)
+    assert_close(host(dyp), rdyp, kind, "dy_perm")
+    assert_close(host(dw), rdw, "f32" if kind == "f32" else "bf16", "dtopk_w")
+    # permute backward (with and without the router share)
+    dxpt, dxp = _to(rng.standard_normal((n_rows, d)), kind)
+    dx = torch.empty(T, d, dtype=dt, device="cuda")
+    L.moe_permute_bwd(dxpt, row_of, k, dx)
+    assert_close(host(dx), om.permute_bwd(dxp, meta["row_of"], T, k, st), kind, "dx")
+    wrt, wr = _to(rng.standard_normal((d, E)) / np.sqrt(d), kind)
+    dl = round_f32(rng.standard_normal((T, E)))
+    L.moe_permute_bwd(dxpt, row_of, k, dx, dev(dl.astype(np.float32), "f32"), wrt)
+    assert_close(host(dx), om.permute_bwd(dxp, meta["row_of"], T, k, st, dl @ wr.T), kind, "dx+router")
+
+
+# ----------------------------------------------------------------------------- router
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+@pytest.mark.parametrize("T,d,E,k", [(1000, 256, 8, 2), (129, 2048, 8, 4), (300, 136, 20, 3),
+                                     (64, 512, 128, 4)])
+def test_router_parity(kind, T, d, E, k):
+    rng = _rng(4, T, d, E)
+    xt, x = _to(rng.standard_normal((T, d)), kind)
+    wrt, wr = _to(rng.standard_normal((d, E)) / np.sqrt(d), kind)
+    lg = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    L.moe_router_gemm(xt, wrt, lg)
+    assert_close(host(lg), om.router_logits(x, wr), "f32", "logits")
+    # route backward and router GEMM backward from identical inputs
+    idx = _draw(rng, T, E, k)
+    w = rng.dirichlet(np.ones(k), size=T).astype(np.float32)
+    dw = rng.standard_normal((T, k)).astype(np.float32)
+    dl = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    L.moe_route_bwd(dev(idx, "i32"), dev(w, "f32"), dev(dw, "f32"), E, dl)
+    rdl = om.route_bwd(idx, w.astype(np.float64), dw.astype(np.float64), E)
+    assert_close(host(dl), rdl, "f32", "dlogits")
+    assert np.all(host(dl)[rdl == 0] == 0)
+    dt = torch.bfloat16 if kind == "bf16" else torch.float32
+    dwr = torch.empty(d, E, dtype=dt, device="cuda")
+    ws = torch.empty(L.moe_router_bwd_workspace_bytes(T, d, E) // 4 + 1, dtype=torch.float32, device="cuda")
+    L.moe_router_gemm_bwd(xt, dev(rdl.astype(np.float32), "f32"), dwr, ws)
+    rdwr, _ = om.router_bwd(x, wr, rdl, storer(kind))
+    assert_close(host(dwr), rdwr, kind, "dw_r")
+
+
+def test_router_backward_full_size():
+    """Router GEMM and its backward at the learned-router workload's full
+    size (16384 x 2048, 8 experts), from oracle-made dlogits."""
+    from moe_inputs import make_inputs, workload
+    from parity import values
+    wl = workload("e8_learned_bf16")
+    inp = make_inputs(wl, with_weights=False)
+    x, wr = values(inp["x"], "bf16"), values(inp["w_r"], "bf16")
+    xt, wrt = dev(inp["x"], "bf16"), dev(inp["w_r"], "bf16")
+    lg = torch.empty(wl.T, wl.E, dtype=torch.float32, device="cuda")
+    L.moe_router_gemm(xt, wrt, lg)
+    assert_close(host(lg), om.router_logits(x, wr), "f32", "logits")
+    rng = _rng(6)
+    dl = round_f32(rng.standard_normal((wl.T, wl.E)) * 0.1)
+    dwr = torch.empty(wl.d, wl.E, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(L.moe_router_bwd_workspace_bytes(wl.T, wl.d, wl.E) // 4 + 1, dtype=torch.float32, device="cuda")
+    L.moe_router_gemm_bwd(xt, dev(dl.astype(np.float32), "f32"), dwr, ws)
+    assert_close(host(dwr), om.router_bwd(x, wr, dl, storer("bf16"))[0], "bf16", "dw_r")
+
+
+# ----------------------------------------------------------------------------- grouped GEMM
+def _gg_case(kind, counts, d, F, seed, capacity=0):
+    rng = _rng(5, seed)
+    E = len(counts)
+    counts = np.asarray(counts)
+    st = storer(kind)
+    if capacity:
+        n_rows = E * capacity
+        groups = [(e * capacity, capacity) for e in range(E)]
+    else:
+        n_rows = int(counts.sum())
+        off = np.concatenate([[0], np.cumsum(counts)])
+        groups = [(int(off[e]), int(counts[e])) for e in range(E)]
+    mk = lambda *s, sc=1.0: _to(rng.standard_normal(s) * sc, kind)
+    T = dict(x_perm=mk(n_rows, d), dy_perm=mk(n_rows, d),
+             w_gate=mk(E, d, F, sc=d ** -0.5), w_up=mk(E, d, F, sc=d ** -0.5),
+             w_down=mk(E, F, d, sc=F ** -0.5))
+    if capacity:   # pad rows hold zeros, as the permute leaves them
+        for name in ("x_perm", "dy_perm"):
+            v = T[name][1].copy()
+            for e in range(E):
+                v[e * capacity + counts[e]:(e + 1) * capacity] = 0.0
+            T[name] = _to(v, kind)
+    grp = None if capacity else dev(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), "i32")
+    return rng, E, n_rows, groups, st, T, grp
+
+
+@pytest.mark.parametrize("kind,counts,d,F,capacity", [
+    ("bf16", [300, 0, 1, 129, 513, 64, 0, 257], 256, 512, 0),          # MFMA path, ragged
+    ("bf16", [700, 5, 1000, 0], 512, 256, 0),
+    ("bf16", [40, 100, 0, 7, 128, 3], 256, 256, 128),                 # padded (uniform groups)
+    ("bf16", [33, 0, 70], 136, 200, 0),                               # plain path, odd shapes
+    ("f32", [33, 0, 70, 1], 128, 256, 0),
+    ("f32", [20, 9], 72, 40, 24),
+    ("bf16", [0, 0, 0], 256, 256, 0),                                 # no rows at all
+])
+def test_grouped_gemm_parity(kind, counts, d, F, capacity):
+    rng, E, n_rows, groups, st, T, grp = _gg_case(kind, counts, d, F, hash((tuple(counts), d, F)) % 1000, capacity)
+    dt = torch.bfloat16 if kind == "bf16" else torch.float32
+    code = L.MOE_BF16 if kind == "bf16" else L.MOE_F32
+    e = lambda *s: torch.full(s, float("nan"), dtype=dt, device="cuda")
+    nr = max(n_rows, 1)
+    out = dict(g=e(nr, F), u=e(nr, F), h=e(nr, F), y_perm=e(nr, d), dg=e(nr, F), du=e(nr, F),
+               dx_perm=e(nr, d), dw_gate=e(E, d, F), dw_up=e(E, d, F), dw_down=e(E, F, d))
+    x, dyp = T["x_perm"], T["dy_perm"]
+    wg, wu, wd = T["w_gate"], T["w_up"], T["w_down"]
+
+    def run(op, **kw):
+        L.moe_grouped_gemm(L.make_gg_desc(op, code, E, d, F, n_rows, capacity, grp, **kw))
+
+    run(L.MOE_GG_FWD_GATE_UP, x_perm=x[0], w_gate=wg[0], w_up=wu[0], g=out["g"], u=out["u"], h=out["h"])
+    run(L.MOE_GG_FWD_DOWN, h=out["h"], w_down=wd[0], y_perm=out["y_perm"])
+    run(L.MOE_GG_DGRAD_DOWN, dy_perm=dyp[0], w_down=wd[0], g=out["g"], u=out["u"], dg=out["dg"], du=out["du"])
+    run(L.MOE_GG_WGRAD_DOWN, h=out["h"], dy_perm=dyp[0], dw_down=out["dw_down"])
+    run(L.MOE_GG_DGRAD_GATE_UP, dg=out["dg"], du=out["du"], w_gate=wg[0], w_up=wu[0], dx_perm=out["dx_perm"])
+    run(L.MOE_GG_WGRAD_GATE_UP, x_perm=x[0], dg=out["dg"], du=out["du"], dw_gate=out["dw_gate"], dw_up=out["dw_up"])
+    # the oracle runs its own chain from the same inputs
+    G, U, H = om.expert_fwd_gate_up(x[1], wg[1], wu[1], groups, st)
+    Y = om.expert_fwd_down(H, wd[1], groups, st)
+    dG, dU = om.expert_dgrad_down(dyp[1], wd[1], G, U, groups, st)
+    dWd = om.expert_wgrad_down(H, dyp[1], groups, F, d, st)
+    dX = om.expert_dgrad_gate_up(dG, dU, wg[1], wu[1], groups, st)
+    dWg, dWu = om.expert_wgrad_gate_up(x[1], dG, dU, groups, d, F, st)
+    if n_rows:
+        for name, ref in (("g", G), ("u", U), ("h", H), ("y_perm", Y), ("dg", dG), ("du", dU),
+                          ("dx_perm", dX)):
+            assert_close(host(out[name])[:n_rows], ref, kind, name)
+    assert_close(host(out["dw_down"]), dWd, kind, "dW_down")
+    assert_close(host(out["dw_gate"]), dWg, kind, "dW_gate")
+    assert_close(host(out["dw_up"]), dWu, kind, "dW_up")
+    # experts without rows get exact zeros
+    for e_ in range(E):
+        if groups[e_][1] == 0 or (capacity and counts[e_] == 0):
+            assert np.all(host(out["dw_down"][e_]) == 0) and np.all(host(out["dw_gate"][e_]) == 0)
+
+
+def test_grouped_gemm_rejects_bad_descriptors():
+    d = L.make_gg_desc(L.MOE_GG_FWD_DOWN, L.MOE_BF16, 4, 256, 256, 10, 0, None)
+    with pytest.raises(L.MoEError):
+        L.moe_grouped_gemm(d)           # no group offsets and no pointers
+    d = L.make_gg_desc(9, L.MOE_BF16, 4, 256, 256, 10, 2, None)
+    with pytest.raises(L.MoEError):
+        L.moe_grouped_gemm(d)
