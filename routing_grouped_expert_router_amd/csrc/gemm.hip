@@ -3,19 +3,16 @@
 // the device only ("device-scheduled grouped GEMM", deniz.in, "Yeni stack
 // nasıl çalışıyor").
 //
-// gg_mfma_kernel: bf16 operands, binary32 accumulation on the matrix cores
-// (v_mfma_f32_32x32x16_bf16). A 128 x 256 output tile per workgroup of four
-// waves (2 x 2, each wave 64 x 128), K staged through LDS in steps of 64 with
-// double buffering. Both operands reach the matrix cores K-contiguous:
-// operands that are contiguous along M or N in memory (weights in the
-// forward pass, every operand of the weight gradients) are transposed in
-// registers, four K-rows at a time, on their way into LDS. LDS rows are 128 B
-// with the 16-byte chunk index XOR-swizzled by the row so that both the
-// transposed writes and the fragment reads avoid bank conflicts.
+// gg_mfma_kernel (gemm_mfma.h): bf16 operands, binary32 accumulation on the
+// matrix cores, LDS-staged tiles, an on-device group-tile scheduler.
 //
 // gg_simple_kernel: any dtype and shape, binary32 FMA on 64 x 64 tiles; it
 // serves binary32 layers and shapes outside the MFMA kernel's limits.
-#include "gemm_common.h"
+#include "gemm_dma.h"
+#include "gemm_mfma.h"
+
+#include <cstdlib>
+#include <string>
 
 namespace moe {
 
@@ -174,284 +171,6 @@ __global__ void __launch_bounds__(256) gg_simple_kernel(GGArgs a) {
     }
 }
 
-// ======================================================================== MFMA kernel
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
-
-constexpr int kBM = 128;    // output rows per tile
-constexpr int kBN = 256;    // LDS n-rows per tile (128 + 128 for the dual ops)
-constexpr int kBK = 64;     // K step
-constexpr int kNT = 256;    // threads
-
-// 16-byte chunk swizzle of LDS row r (rows are kBK = 64 bf16 = 8 chunks).
-MOE_DEV int swz(int r) { return (r ^ (r >> 3)) & 7; }
-MOE_DEV int lds_off(int row, int chunk) { return row * kBK + ((chunk ^ swz(row)) << 3); }
-
-MOE_DEV V16 zero16() {
-  V16 z;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) z.w[i] = 0u;
-  return z;
-}
-
-// Store 4 K-rows x 8 MN-columns (one V16 per K-row) as 8 LDS rows (one per
-// MN column) of 4 K-values, at K-quad kq of the 64-wide row.
-MOE_DEV void store_transposed(uint16_t* s, int row0, int kq, const V16 (&r)[4]) {
-#pragma unroll
-  for (int mm = 0; mm < 8; ++mm) {
-    const int w = mm >> 1;
-    const bool hi = mm & 1;
-    auto pick = [&](const V16& v) -> uint32_t { return hi ? (v.w[w] >> 16) : (v.w[w] & 0xffffu); };
-    uint2 o;
-    o.x = pick(r[0]) | (pick(r[1]) << 16);
-    o.y = pick(r[2]) | (pick(r[3]) << 16);
-    const int row = row0 + mm;
-    *reinterpret_cast<uint2*>(s + row * kBK + ((((kq >> 1) ^ swz(row)) << 3) + (kq & 1) * 4)) = o;
-  }
-}
-
-template <int OP>
-__global__ void __launch_bounds__(kNT, 1) gg_mfma_kernel(GGArgs a) {
-  using I = OpInfo<OP>;
-  constexpr bool DUAL = I::kDual, KVAR = I::kKVar, AK = I::kAKContig, BKC = I::kBKContig;
-  constexpr int BNO = DUAL ? kBN / 2 : kBN;   // output columns per matrix per tile
-  __shared__ int tile_start[MOE_MAX_EXPERTS + 1];
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kBK];
-
-  const int d = a.d, F = a.F;
-  const int N = op_n(OP, d, F);
-  const int tilesN = N / BNO;
-  const int b = xcd_remap(blockIdx.x, gridDim.x);
-  int e, row0, mv, K, m0 = 0, tn;
-  if (!KVAR) {
-    tn = b % tilesN;
-    if (!find_m_tile<kBM, kNT>(a, b / tilesN, tile_start, e, row0, mv)) return;
-    K = op_k(OP, d, F);
-  } else {
-    const int M = op_wgrad_m(OP, d, F);
-    const int per = (M / kBM) * tilesN;
-    e = b / per;
-    m0 = ((b % per) / tilesN) * kBM;
-    tn = b % tilesN;
-    group_rows(a, e, row0, K);
-    mv = kBM;
-  }
-  const int n0 = tn * BNO;
-  const size_t dF = (size_t)d * F;
-  const uint16_t* Ab = nullptr;        // A base at (row 0 or m0, k 0)
-  const uint16_t* Bb[2] = {nullptr, nullptr};
-  int lda = 0, ldb = 0;
-  switch (OP) {
-    case MOE_GG_FWD_GATE_UP:
-      Ab = (const uint16_t*)a.x_perm + (size_t)row0 * d; lda = d;
-      Bb[0] = (const uint16_t*)a.w_gate + e * dF + n0;
-      Bb[1] = (const uint16_t*)a.w_up + e * dF + n0; ldb = F;
-      break;
-    case MOE_GG_FWD_DOWN:
-      Ab = (const uint16_t*)a.h + (size_t)row0 * F; lda = F;
-      Bb[0] = (const uint16_t*)a.w_down + e * dF + n0; ldb = d;
-      break;
-    case MOE_GG_DGRAD_DOWN:
-      Ab = (const uint16_t*)a.dy_perm + (size_t)row0 * d; lda = d;
-      Bb[0] = (const uint16_t*)a.w_down + e * dF + (size_t)n0 * d; ldb = d;
-      break;
-    case MOE_GG_DGRAD_GATE_UP:
-      Ab = (const uint16_t*)a.dg + (size_t)row0 * F; lda = F;
-      Bb[0] = (const uint16_t*)a.w_gate + e * dF + (size_t)n0 * F;
-      Bb[1] = (const uint16_t*)a.w_up + e * dF + (size_t)n0 * F; ldb = F;
-      break;
-    case MOE_GG_WGRAD_DOWN:
-      Ab = (const uint16_t*)a.h + (size_t)row0 * F + m0; lda = F;
-      Bb[0] = (const uint16_t*)a.dy_perm + (size_t)row0 * d + n0; ldb = d;
-      break;
-    default:   // WGRAD_GATE_UP
-      Ab = (const uint16_t*)a.x_perm + (size_t)row0 * d + m0; lda = d;
-      Bb[0] = (const uint16_t*)a.dg + (size_t)row0 * F + n0;
-      Bb[1] = (const uint16_t*)a.du + (size_t)row0 * F + n0; ldb = F;
-  }
-  const uint16_t* Ab2 = OP == MOE_GG_DGRAD_GATE_UP ? (const uint16_t*)a.du + (size_t)row0 * F : nullptr;
-
-  const int tid = threadIdx.x;
-  V16 ra[4], rb[8];
-
-  // ---- global -> registers
-  auto load = [&](int k0) {
-    if (AK) {
-      const uint16_t* A = Ab;
-      int kc0 = k0;
-      if (OP == MOE_GG_DGRAD_GATE_UP && k0 >= F) { A = Ab2; kc0 = k0 - F; }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = i * kNT + tid, m = q >> 3, kc = q & 7;
-        ra[i] = m < mv ? *reinterpret_cast<const V16*>(A + (size_t)m * lda + kc0 + kc * 8) : zero16();
-      }
-    } else {
-      const int o = tid & 15, kq = tid >> 4;
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        const int kk = k0 + 4 * kq + ii;
-        ra[ii] = kk < K ? *reinterpret_cast<const V16*>(Ab + (size_t)kk * lda + 8 * o) : zero16();
-      }
-    }
-    if (BKC) {
-      const uint16_t* B = Bb[0];
-      int kc0 = k0;
-      if (OP == MOE_GG_DGRAD_GATE_UP && k0 >= F) { B = Bb[1]; kc0 = k0 - F; }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = i * kNT + tid, n = q >> 3, kc = q & 7;
-        rb[i] = *reinterpret_cast<const V16*>(B + (size_t)n * ldb + kc0 + kc * 8);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int u = i * kNT + tid, o = u & 31, kq = u >> 5;
-        const int r = 8 * o;
-        int col = r, mat = 0;
-        if (DUAL) { mat = (r & 127) >> 6; col = (r >> 7) * 64 + (r & 63); }
-        const uint16_t* B = Bb[mat];
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int kk = k0 + 4 * kq + ii;
-          const bool ok = !KVAR || kk < K;
-          rb[i * 4 + ii] = ok ? *reinterpret_cast<const V16*>(B + (size_t)kk * ldb + col) : zero16();
-        }
-      }
-    }
-  };
-  // ---- registers -> LDS
-  auto store = [&](int buf) {
-    uint16_t* A = sA[buf];
-    uint16_t* B = sB[buf];
-    if (AK) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = i * kNT + tid, m = q >> 3, kc = q & 7;
-        *reinterpret_cast<V16*>(A + lds_off(m, kc)) = ra[i];
-      }
-    } else {
-      const int o = tid & 15, kq = tid >> 4;
-      store_transposed(A, 8 * o, kq, ra);
-    }
-    if (BKC) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = i * kNT + tid, n = q >> 3, kc = q & 7;
-        *reinterpret_cast<V16*>(B + lds_off(n, kc)) = rb[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int u = i * kNT + tid, o = u & 31, kq = u >> 5;
-        const V16 r4[4] = {rb[i * 4], rb[i * 4 + 1], rb[i * 4 + 2], rb[i * 4 + 3]};
-        store_transposed(B, 8 * o, kq, r4);
-      }
-    }
-  };
-
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 31, lk = lane >> 5;
-  f32x16_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int nk = (K + kBK - 1) / kBK;
-  if (nk > 0) {
-    load(0);
-    store(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * kBK);
-    const uint16_t* A = sA[cur];
-    const uint16_t* B = sB[cur];
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8_t af[2], bfr[4];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int row = wm * 64 + mi * 32 + lr;
-        af[mi] = *reinterpret_cast<const bf16x8_t*>(A + lds_off(row, 2 * kk + lk));
-      }
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int row = wn * 128 + ni * 32 + lr;
-        bfr[ni] = *reinterpret_cast<const bf16x8_t*>(B + lds_off(row, 2 * kk + lk));
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store(cur ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: lane holds row m = lr of each 32-row block and, per group g
-  // of 4 accumulators, 4 consecutive output columns 8g + 4lk .. +3.
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const int ml = wm * 64 + mi * 32 + lr;
-    if (ml >= mv) continue;
-    const size_t row = KVAR ? (size_t)(m0 + ml) : (size_t)(row0 + ml);
-#pragma unroll
-    for (int ni = 0; ni < (DUAL ? 2 : 4); ++ni) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int cl = ni * 32 + 8 * g + 4 * lk;
-        float v0[4], v1[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v0[r] = acc[mi][ni][4 * g + r];
-          v1[r] = DUAL ? acc[mi][ni + 2][4 * g + r] : 0.f;
-        }
-        if (OP == MOE_GG_FWD_GATE_UP) {
-          const size_t i = row * F + n0 + wn * 64 + cl;
-          float gg[4], uu[4], hh[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) swiglu_fwd<uint16_t>(v0[r], v1[r], gg[r], uu[r], hh[r]);
-          *reinterpret_cast<uint2*>((uint16_t*)a.g + i) = make_uint2(pack_bf16x2(gg[0], gg[1]), pack_bf16x2(gg[2], gg[3]));
-          *reinterpret_cast<uint2*>((uint16_t*)a.u + i) = make_uint2(pack_bf16x2(uu[0], uu[1]), pack_bf16x2(uu[2], uu[3]));
-          *reinterpret_cast<uint2*>((uint16_t*)a.h + i) = make_uint2(pack_bf16x2(hh[0], hh[1]), pack_bf16x2(hh[2], hh[3]));
-        } else if (OP == MOE_GG_WGRAD_GATE_UP) {
-          const size_t i = e * dF + row * F + n0 + wn * 64 + cl;
-          *reinterpret_cast<uint2*>((uint16_t*)a.dw_gate + i) = make_uint2(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]));
-          *reinterpret_cast<uint2*>((uint16_t*)a.dw_up + i) = make_uint2(pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3]));
-        } else if (OP == MOE_GG_DGRAD_DOWN) {
-          const size_t i = row * F + n0 + wn * 128 + cl;
-          const uint2 gv = *reinterpret_cast<const uint2*>((const uint16_t*)a.g + i);
-          const uint2 uv = *reinterpret_cast<const uint2*>((const uint16_t*)a.u + i);
-          const float gf[4] = {__uint_as_float(gv.x << 16), __uint_as_float(gv.x & 0xffff0000u),
-                               __uint_as_float(gv.y << 16), __uint_as_float(gv.y & 0xffff0000u)};
-          const float uf[4] = {__uint_as_float(uv.x << 16), __uint_as_float(uv.x & 0xffff0000u),
-                               __uint_as_float(uv.y << 16), __uint_as_float(uv.y & 0xffff0000u)};
-          float dg[4], du[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) swiglu_bwd(v0[r], gf[r], uf[r], dg[r], du[r]);
-          *reinterpret_cast<uint2*>((uint16_t*)a.dg + i) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-          *reinterpret_cast<uint2*>((uint16_t*)a.du + i) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-        } else {
-          uint16_t* out;
-          size_t i;
-          if (OP == MOE_GG_FWD_DOWN) { out = (uint16_t*)a.y_perm; i = row * d; }
-          else if (OP == MOE_GG_DGRAD_GATE_UP) { out = (uint16_t*)a.dx_perm; i = row * d; }
-          else { out = (uint16_t*)a.dw_down; i = e * dF + row * d; }
-          i += n0 + wn * 128 + cl;
-          *reinterpret_cast<uint2*>(out + i) = make_uint2(pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]));
-        }
-      }
-    }
-  }
-}
-
 }  // namespace moe
 
 // ======================================================================== C ABI
@@ -459,8 +178,26 @@ using namespace moe;
 
 namespace {
 
+// Tile shapes: register-staged kernel {BM, BN, WM, WN}; direct-load kernel
+// {BM, BN, WM, WN, BK, STAGES}.
+using Cfg128 = MfmaCfg<128, 256, 2, 2>;   // 4 waves, 64 x 128 each
+using Cfg256 = MfmaCfg<256, 256, 2, 4>;   // 8 waves, 128 x 64 each
+using CfgDma = DmaCfg<256, 256, 2, 4, 32, 4>;
+
+// Kernel choice; MOE_GG_TILE=128|256|dma overrides it (for tuning sweeps).
+int tile_choice() {
+  static int t = [] {
+    const char* s = std::getenv("MOE_GG_TILE");
+    if (!s) return 2;
+    if (std::string(s) == "128") return 0;
+    if (std::string(s) == "256") return 1;
+    return 2;
+  }();
+  return t;
+}
+
 bool mfma_ok(const moe_gg_desc* g) {
-  return g->dtype == MOE_BF16 && g->d % kBN == 0 && g->F % kBN == 0;
+  return g->dtype == MOE_BF16 && g->d % 256 == 0 && g->F % 256 == 0;
 }
 
 template <template <int> class Launch>
@@ -476,11 +213,43 @@ int dispatch_op(int op, const GGArgs& a, int grid, hipStream_t s) {
   return launch_status();
 }
 
-template <int OP> struct LaunchMfma {
-  static void go(const GGArgs& a, int grid, hipStream_t s) {
-    gg_mfma_kernel<OP><<<grid, kNT, 0, s>>>(a);
-  }
+template <class C> struct Mfma {
+  template <int OP> struct Launch {
+    static void go(const GGArgs& a, int grid, hipStream_t s) {
+      gg_mfma_kernel<OP, C><<<grid, C::NT, 0, s>>>(a);
+    }
+  };
 };
+
+template <class C> struct Dma {
+  template <int OP> struct Launch {
+    static void go(const GGArgs& a, int grid, hipStream_t s) {
+      gg_dma_kernel<OP, C><<<grid, C::NT, 0, s>>>(a);
+    }
+  };
+};
+
+template <class C>
+int launch_dma(const moe_gg_desc* g, const GGArgs& a, bool kvar, bool dual, int N, hipStream_t stream) {
+  const int bno = dual ? C::BN / 2 : C::BN;
+  long grid;
+  if (kvar) grid = (long)g->E * (op_wgrad_m(g->op, g->d, g->F) / C::BM) * (N / bno);
+  else grid = ((g->n_rows + C::BM - 1) / C::BM + g->E) * (long)(N / bno);
+  if (grid == 0) return MOE_OK;
+  MOE_CHECK_SUPPORTED(grid < (1L << 31));
+  return dispatch_op<Dma<C>::template Launch>(g->op, a, static_cast<int>(grid), stream);
+}
+
+template <class C>
+int launch_mfma(const moe_gg_desc* g, const GGArgs& a, bool kvar, bool dual, int N, hipStream_t stream) {
+  const int bno = dual ? C::BN / 2 : C::BN;
+  long grid;
+  if (kvar) grid = (long)g->E * (op_wgrad_m(g->op, g->d, g->F) / C::BM) * (N / bno);
+  else grid = ((g->n_rows + C::BM - 1) / C::BM + g->E) * (long)(N / bno);
+  if (grid == 0) return MOE_OK;
+  MOE_CHECK_SUPPORTED(grid < (1L << 31));
+  return dispatch_op<Mfma<C>::template Launch>(g->op, a, static_cast<int>(grid), stream);
+}
 template <int OP> struct LaunchSimpleBf16 {
   static void go(const GGArgs& a, int grid, hipStream_t s) {
     gg_simple_kernel<uint16_t, OP><<<grid, 256, 0, s>>>(a);
@@ -510,7 +279,13 @@ extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
   MOE_CHECK_SUPPORTED((long)g->n_rows * (g->d > g->F ? g->d : g->F) < (1L << 40));
   MOE_CHECK_ARG(g->capacity > 0 || g->group_offsets != nullptr);
   MOE_CHECK_ARG(g->capacity == 0 || (long)g->E * g->capacity <= g->n_rows);
+  const bool kvar = g->op == MOE_GG_WGRAD_DOWN || g->op == MOE_GG_WGRAD_GATE_UP;
+  // with no rows a row-varying op has nothing to do, and a weight gradient
+  // reads no activations (every expert's gradient is zero)
+  if (g->n_rows == 0 && !kvar) return MOE_OK;
+  const bool rows = g->n_rows > 0;
   auto need = [](const void* p) { return p != nullptr && aligned16(p); };
+  auto act = [&](const void* p) { return !rows || (p != nullptr && aligned16(p)); };
   switch (g->op) {
     case MOE_GG_FWD_GATE_UP:
       MOE_CHECK_ARG(need(g->x_perm) && need(g->w_gate) && need(g->w_up) && need(g->g) && need(g->u) && need(g->h));
@@ -525,25 +300,25 @@ extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
       MOE_CHECK_ARG(need(g->dg) && need(g->du) && need(g->w_gate) && need(g->w_up) && need(g->dx_perm));
       break;
     case MOE_GG_WGRAD_DOWN:
-      MOE_CHECK_ARG(need(g->h) && need(g->dy_perm) && need(g->dw_down));
+      MOE_CHECK_ARG(act(g->h) && act(g->dy_perm) && need(g->dw_down));
       break;
     default:
-      MOE_CHECK_ARG(need(g->x_perm) && need(g->dg) && need(g->du) && need(g->dw_gate) && need(g->dw_up));
+      MOE_CHECK_ARG(act(g->x_perm) && act(g->dg) && act(g->du) && need(g->dw_gate) && need(g->dw_up));
   }
   GGArgs a{g->op, g->E, g->d, g->F, g->n_rows, g->capacity, g->group_offsets,
            g->x_perm, g->g, g->u, g->h, g->y_perm, g->dy_perm, g->dg, g->du, g->dx_perm,
            g->w_gate, g->w_up, g->w_down, g->dw_gate, g->dw_up, g->dw_down};
-  const bool kvar = g->op == MOE_GG_WGRAD_DOWN || g->op == MOE_GG_WGRAD_GATE_UP;
   const bool dual = g->op == MOE_GG_FWD_GATE_UP || g->op == MOE_GG_WGRAD_GATE_UP;
   const int N = op_n(g->op, g->d, g->F);
   if (mfma_ok(g)) {
-    const int bno = dual ? kBN / 2 : kBN;
-    long grid;
-    if (kvar) grid = (long)g->E * (op_wgrad_m(g->op, g->d, g->F) / kBM) * (N / bno);
-    else grid = (cdiv(g->n_rows, kBM) + g->E) * (N / bno);
-    if (grid == 0) return MOE_OK;
-    MOE_CHECK_SUPPORTED(grid < (1L << 31));
-    return dispatch_op<LaunchMfma>(g->op, a, static_cast<int>(grid), stream);
+    // buffer-resource offsets are 32-bit: every expert's rows and weights
+    // must span less than 2 GiB
+    const long span = (long)g->n_rows * (g->d > g->F ? g->d : g->F) * 2;
+    const bool dma_fits = span < (1L << 31) && (long)g->d * g->F * 2 < (1L << 31);
+    const int choice = tile_choice();
+    if (choice == 2 && dma_fits) return launch_dma<CfgDma>(g, a, kvar, dual, N, stream);
+    if (choice == 0) return launch_mfma<Cfg128>(g, a, kvar, dual, N, stream);
+    return launch_mfma<Cfg256>(g, a, kvar, dual, N, stream);
   }
   long grid;
   if (kvar) grid = (long)g->E * cdiv(op_wgrad_m(g->op, g->d, g->F), kSBM) * cdiv(N, kSBN);

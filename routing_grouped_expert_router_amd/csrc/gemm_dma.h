@@ -1,0 +1,401 @@
+// bf16 grouped expert GEMM, matrix cores fed by direct global->LDS loads.
+//
+// One workgroup computes a BM x BN tile of one expert (BN counts LDS n-rows;
+// for the dual ops half are gate columns and half are up columns). WM x WN
+// wave64s each own a (BM/WM) x (BN/WN) sub-tile of 32 x 32 blocks of
+// v_mfma_f32_32x32x16_bf16. K advances BK at a time through a ring of STAGES
+// LDS buffers filled by buffer_load ... lds (16 bytes per lane, no register
+// staging), so the loads of step k + STAGES - 1 are in flight while step k
+// computes.
+//
+// Operand layouts in LDS:
+//  * K-contiguous operands (rows of activations in the forward pass, weights
+//    in dgrad) keep their rows: [rows][BK], 16-byte chunks XOR-swizzled by
+//    (row >> 2) & 3 so that 16 consecutive rows of one chunk hit 16 distinct
+//    bank groups; fragments are read with ds_read_b128.
+//  * MN-contiguous operands (weights in the forward pass, everything in the
+//    weight gradients) are copied as they are in memory: [BK][MN], 16-byte
+//    chunks XOR-swizzled by 4 * (k & 3); fragments are read with two
+//    ds_read_b64_tr_b16, whose 16-lane transpose turns four k-rows of four
+//    columns into the k-contiguous fragment each lane needs.
+// Tail rows (past an expert's rows, in M for the row-varying ops and in K for
+// the weight gradients) read as zeros: every load goes through a buffer
+// resource whose range ends at the expert's last row.
+#pragma once
+
+#include "gemm_common.h"
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 dbf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float df32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short ds4_t;
+
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int ST_> struct DmaCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = ST_;
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int NW = WM * WN;
+  static constexpr int WMR = BM / WM, WNR = BN / WN;
+  static constexpr int MI = WMR / 32, NI = WNR / 32;
+  static constexpr int CPR = BK / 8;                       // 16-byte chunks per K-contig row
+  static constexpr int A_INSTR = BM * BK * 2 / 1024;       // 1 KB wave-loads per stage
+  static constexpr int B_INSTR = BN * BK * 2 / 1024;
+  static constexpr int A_PER_WAVE = A_INSTR / NW, B_PER_WAVE = B_INSTR / NW;
+  static constexpr int STAGE_ELEMS = (BM + BN) * BK;
+  static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0, "loads per wave");
+  static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(WMR % 32 == 0 && WNR % 64 == 0, "wave tile");
+  static_assert((BK * BN / 16) % 64 == 0, "dual sub-tiles hold whole wave-loads");
+};
+
+// ------------------------------------------------------------------ primitives
+// Raw buffer resource (4 SGPRs): 48-bit base, stride 0, range in bytes; loads
+// past the range return zeros.
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int rsrc_t;
+MOE_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  rsrc_t r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(p & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((p >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+// One 1 KB wave-load: lane l's 16 bytes from byte offset voff of the resource
+// land at LDS byte address lds_addr + 16 l. Issued from inline assembly so
+// that the compiler, which cannot tell the ring slots apart, does not wait
+// for every outstanding load before each LDS read; completion is tracked with
+// explicit vmcnt waits instead (the instruction has no register result).
+MOE_DEV void dma16(rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(r), "{m0}"(lds_addr)
+      : "memory");
+}
+
+MOE_DEV uint32_t lds_addr_of(const void* p) {
+  typedef const __attribute__((address_space(3))) char* lds_ptr_t;
+  return static_cast<uint32_t>((uintptr_t)(lds_ptr_t)p);
+}
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left alone).
+template <int N> MOE_DEV void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// chunk swizzles (16-byte chunk index within an LDS row)
+MOE_DEV int swz_k(int row) { return (row >> 2) & 3; }      // K-contiguous rows
+MOE_DEV int swz_t(int krow) { return (krow & 3) << 2; }     // MN-contiguous rows
+
+MOE_DEV dbf16x8_t read_tr8(const uint16_t* p0, const uint16_t* p1) {
+  const ds4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) ds4_t*)p0);
+  const ds4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) ds4_t*)p1);
+  typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s8_t;
+  const s8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(dbf16x8_t, v);
+}
+
+MOE_DEV uint2 dpack4(const float* v) { return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])); }
+MOE_DEV void dunpack4(uint2 p, float* v) {
+  v[0] = __uint_as_float(p.x << 16);
+  v[1] = __uint_as_float(p.x & 0xffff0000u);
+  v[2] = __uint_as_float(p.y << 16);
+  v[3] = __uint_as_float(p.y & 0xffff0000u);
+}
+
+// ------------------------------------------------------------------ kernel
+template <int OP, class C>
+__global__ void __launch_bounds__(C::NT, 1) gg_dma_kernel(GGArgs a) {
+  using I = OpInfo<OP>;
+  constexpr bool DUAL = I::kDual, KVAR = I::kKVar, AK = I::kAKContig, BKC = I::kBKContig;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::STAGES, NT = C::NT;
+  constexpr int MI = C::MI, NI = C::NI, CPR = C::CPR;
+  constexpr int BNO = DUAL ? BN / 2 : BN;          // output columns per matrix per tile
+  constexpr int A_ELEMS = BM * BK;
+  __shared__ int tile_start[MOE_MAX_EXPERTS + 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[S * C::STAGE_ELEMS];
+
+  const int d = a.d, F = a.F;
+  const int N = op_n(OP, d, F);
+  const int tilesN = N / BNO;
+  const int b = xcd_remap(blockIdx.x, gridDim.x);
+  int e, row0, mv, K, m0 = 0, tn;
+  if (!KVAR) {
+    tn = b % tilesN;
+    if (!find_m_tile<BM, NT>(a, b / tilesN, tile_start, e, row0, mv)) return;
+    K = op_k(OP, d, F);
+  } else {
+    const int M = op_wgrad_m(OP, d, F);
+    const int per = (M / BM) * tilesN;
+    e = b / per;
+    m0 = ((b % per) / tilesN) * BM;
+    tn = b % tilesN;
+    group_rows(a, e, row0, K);
+    mv = BM;
+  }
+  const int n0 = tn * BNO;
+  const size_t dF = (size_t)d * F;
+
+  // ---- buffer resources (byte ranges end at the last valid row)
+  // A0/A1: the two K phases of DGRAD_GATE_UP (otherwise A1 = A0)
+  // B0/B1: gate/up matrices (dual ops), or the two K phases (DGRAD_GATE_UP)
+  rsrc_t rA0, rA1, rB0, rB1;
+  int lda = 0, ldb = 0;
+  {
+    const uint16_t *pa0, *pa1, *pb0, *pb1;
+    uint32_t na, nb;
+    switch (OP) {
+      case MOE_GG_FWD_GATE_UP:
+        lda = d; ldb = F;
+        pa0 = pa1 = (const uint16_t*)a.x_perm + (size_t)row0 * d; na = (uint32_t)mv * d * 2;
+        pb0 = (const uint16_t*)a.w_gate + e * dF; pb1 = (const uint16_t*)a.w_up + e * dF; nb = (uint32_t)(dF * 2);
+        break;
+      case MOE_GG_FWD_DOWN:
+        lda = F; ldb = d;
+        pa0 = pa1 = (const uint16_t*)a.h + (size_t)row0 * F; na = (uint32_t)mv * F * 2;
+        pb0 = pb1 = (const uint16_t*)a.w_down + e * dF; nb = (uint32_t)(dF * 2);
+        break;
+      case MOE_GG_DGRAD_DOWN:
+        lda = d; ldb = d;
+        pa0 = pa1 = (const uint16_t*)a.dy_perm + (size_t)row0 * d; na = (uint32_t)mv * d * 2;
+        pb0 = pb1 = (const uint16_t*)a.w_down + e * dF; nb = (uint32_t)(dF * 2);
+        break;
+      case MOE_GG_DGRAD_GATE_UP:
+        lda = F; ldb = F;
+        pa0 = (const uint16_t*)a.dg + (size_t)row0 * F; pa1 = (const uint16_t*)a.du + (size_t)row0 * F;
+        na = (uint32_t)mv * F * 2;
+        pb0 = (const uint16_t*)a.w_gate + e * dF; pb1 = (const uint16_t*)a.w_up + e * dF; nb = (uint32_t)(dF * 2);
+        break;
+      case MOE_GG_WGRAD_DOWN:
+        lda = F; ldb = d;
+        pa0 = pa1 = (const uint16_t*)a.h + (size_t)row0 * F; na = (uint32_t)K * F * 2;
+        pb0 = pb1 = (const uint16_t*)a.dy_perm + (size_t)row0 * d; nb = (uint32_t)K * d * 2;
+        break;
+      default:   // WGRAD_GATE_UP
+        lda = d; ldb = F;
+        pa0 = pa1 = (const uint16_t*)a.x_perm + (size_t)row0 * d; na = (uint32_t)K * d * 2;
+        pb0 = (const uint16_t*)a.dg + (size_t)row0 * F; pb1 = (const uint16_t*)a.du + (size_t)row0 * F;
+        nb = (uint32_t)K * F * 2;
+    }
+    rA0 = make_rsrc(pa0, na); rA1 = make_rsrc(pa1, na);
+    rB0 = make_rsrc(pb0, nb); rB1 = make_rsrc(pb1, nb);
+  }
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+
+  // ---- per-lane byte offsets of this wave's loads at k = 0 (and their
+  // increment per K step). A K-contiguous operand moves along its row; an
+  // MN-contiguous one moves down BK rows.
+  uint32_t a_off[C::A_PER_WAVE], b_off[C::B_PER_WAVE];
+  int b_mat[C::B_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::A_PER_WAVE; ++i) {
+    const int q = (wave * C::A_PER_WAVE + i) * 64 + lane;           // 16-byte chunk of the stage tile
+    if (AK) {
+      const int row = q / CPR, c = (q % CPR) ^ swz_k(row);
+      a_off[i] = (uint32_t)(row * lda + c * 8) * 2;
+    } else {   // [BK][BM]: BM/8 chunks per k-row
+      const int kr = q / (BM / 8), c = (q % (BM / 8)) ^ swz_t(kr);
+      a_off[i] = (uint32_t)(kr * lda + c * 8) * 2;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C::B_PER_WAVE; ++i) {
+    const int q = (wave * C::B_PER_WAVE + i) * 64 + lane;
+    b_mat[i] = 0;
+    if (BKC) {
+      const int row = q / CPR, c = (q % CPR) ^ swz_k(row);
+      b_off[i] = (uint32_t)((n0 + row) * ldb + c * 8) * 2;
+    } else if (DUAL) {   // two [BK][BN/2] sub-tiles, gate then up
+      // a 1 KB wave-load never straddles the sub-tiles, so the matrix is
+      // wave-uniform and comes from the wave-load index alone
+      const int sub = (wave * C::B_PER_WAVE + i) * 64 / (BK * BN / 16);
+      const int qq = q % (BK * BN / 16);
+      const int kr = qq / (BN / 16), c = (qq % (BN / 16)) ^ swz_t(kr);
+      b_mat[i] = sub;
+      b_off[i] = (uint32_t)(kr * ldb + n0 + c * 8) * 2;
+    } else {
+      const int kr = q / (BN / 8), c = (q % (BN / 8)) ^ swz_t(kr);
+      b_off[i] = (uint32_t)(kr * ldb + n0 + c * 8) * 2;
+    }
+  }
+  // wgrad A starts at column m0 of the token rows
+  if (!AK) {
+#pragma unroll
+    for (int i = 0; i < C::A_PER_WAVE; ++i) a_off[i] += (uint32_t)m0 * 2;
+  }
+  const uint32_t a_step = AK ? BK * 2 : (uint32_t)BK * lda * 2;
+  const uint32_t b_step = BKC ? BK * 2 : (uint32_t)BK * ldb * 2;
+
+  // issue the loads of K step kt into ring slot `slot`
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr_of(lds));
+  auto issue = [&](int kt, int slot) {
+    const uint32_t sa = lds_base + (uint32_t)slot * C::STAGE_ELEMS * 2;
+    const uint32_t sb = sa + A_ELEMS * 2;
+    int ks = kt;
+    bool second = false;
+    if (OP == MOE_GG_DGRAD_GATE_UP) {
+      const int half = F / BK;
+      second = kt >= half;
+      ks = second ? kt - half : kt;
+    }
+#pragma unroll
+    for (int i = 0; i < C::A_PER_WAVE; ++i)
+      dma16(second ? rA1 : rA0, sa + (wave * C::A_PER_WAVE + i) * 1024, a_off[i] + (uint32_t)ks * a_step);
+#pragma unroll
+    for (int i = 0; i < C::B_PER_WAVE; ++i) {
+      const bool use1 = DUAL ? (b_mat[i] != 0) : second;
+      dma16(use1 ? rB1 : rB0, sb + (wave * C::B_PER_WAVE + i) * 1024, b_off[i] + (uint32_t)ks * b_step);
+    }
+  };
+
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int lr = lane & 31, lk = lane >> 5;
+  // ds_read_b64_tr_b16 lane roles: 16-lane group g, source lane (j, q)
+  const int tg = lane >> 4, tj = (lane & 15) >> 2, tq = lane & 3;
+  const bool active = wm * C::WMR < mv;
+
+  df32x16_t acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto compute = [&](int slot) {
+    const uint16_t* sa = lds + slot * C::STAGE_ELEMS;
+    const uint16_t* sb = sa + A_ELEMS;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      dbf16x8_t af[MI], bfr[NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int m = wm * C::WMR + mi * 32;
+        if (AK) {
+          const int row = m + lr;
+          af[mi] = *reinterpret_cast<const dbf16x8_t*>(sa + row * BK + (((2 * ks + lk) ^ swz_k(row)) << 3));
+        } else {
+          const int col = m + 16 * (tg & 1) + 4 * tq;
+          const int k0 = 16 * ks + 8 * (tg >> 1) + tj;
+          const int k1 = k0 + 4;
+          af[mi] = read_tr8(sa + k0 * BM + ((((col >> 3) ^ swz_t(k0)) << 3) | (col & 7)),
+                            sa + k1 * BM + ((((col >> 3) ^ swz_t(k1)) << 3) | (col & 7)));
+        }
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        if (BKC) {
+          const int row = wn * C::WNR + ni * 32 + lr;
+          bfr[ni] = *reinterpret_cast<const dbf16x8_t*>(sb + row * BK + (((2 * ks + lk) ^ swz_k(row)) << 3));
+        } else {
+          const uint16_t* base = sb;
+          int col, width;
+          if (DUAL) {   // block ni < NI/2: gate sub-tile, else up sub-tile, same columns
+            width = BN / 2;
+            base = sb + (ni >= NI / 2 ? BK * (BN / 2) : 0);
+            col = wn * (C::WNR / 2) + (ni % (NI / 2)) * 32;
+          } else {
+            width = BN;
+            col = wn * C::WNR + ni * 32;
+          }
+          col += 16 * (tg & 1) + 4 * tq;
+          const int k0 = 16 * ks + 8 * (tg >> 1) + tj;
+          const int k1 = k0 + 4;
+          bfr[ni] = read_tr8(base + k0 * width + ((((col >> 3) ^ swz_t(k0)) << 3) | (col & 7)),
+                             base + k1 * width + ((((col >> 3) ^ swz_t(k1)) << 3) | (col & 7)));
+        }
+      }
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+    }
+  };
+
+  // ---- K loop over a ring of S slots
+  constexpr int PER_STAGE = C::A_PER_WAVE + C::B_PER_WAVE;   // wave-loads per stage
+  const int nk = (K + BK - 1) / BK;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt is complete once at most (stages issued after it) loads remain
+    const int after = min(S - 2, nk - 1 - kt);
+    if (after >= S - 2) wait_vm<PER_STAGE * (S - 2)>();
+    else if (after == 1) wait_vm<PER_STAGE>();
+    else wait_vm<0>();
+    __syncthreads();
+    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+    if (active) compute(kt % S);
+  }
+
+  // ---- epilogue: each 32x32 block holds C^T (B fragment first): lane
+  // (lr, lk) has output row lr and, for accumulator group g, the 4
+  // consecutive output columns 8g + 4lk .. 8g + 4lk + 3.
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int ml = wm * C::WMR + mi * 32 + lr;
+    if (ml >= mv) continue;
+    const size_t row = KVAR ? (size_t)(m0 + ml) : (size_t)(row0 + ml);
+#pragma unroll
+    for (int ni = 0; ni < (DUAL ? NI / 2 : NI); ++ni) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int cl = ni * 32 + 8 * g + 4 * lk;
+        float v0[4], v1[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v0[r] = acc[mi][ni][4 * g + r];
+          v1[r] = DUAL ? acc[mi][ni + NI / 2][4 * g + r] : 0.f;
+        }
+        if (OP == MOE_GG_FWD_GATE_UP) {
+          const size_t i = row * F + n0 + wn * (C::WNR / 2) + cl;
+          float gg[4], uu[4], hh[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            gg[r] = bf16_to_f32(f32_to_bf16(v0[r]));
+            uu[r] = bf16_to_f32(f32_to_bf16(v1[r]));
+            hh[r] = gg[r] * uu[r] / (1.0f + expf(-gg[r]));
+          }
+          *reinterpret_cast<uint2*>((uint16_t*)a.g + i) = dpack4(gg);
+          *reinterpret_cast<uint2*>((uint16_t*)a.u + i) = dpack4(uu);
+          *reinterpret_cast<uint2*>((uint16_t*)a.h + i) = dpack4(hh);
+        } else if (OP == MOE_GG_WGRAD_GATE_UP) {
+          const size_t i = e * dF + row * F + n0 + wn * (C::WNR / 2) + cl;
+          *reinterpret_cast<uint2*>((uint16_t*)a.dw_gate + i) = dpack4(v0);
+          *reinterpret_cast<uint2*>((uint16_t*)a.dw_up + i) = dpack4(v1);
+        } else if (OP == MOE_GG_DGRAD_DOWN) {
+          const size_t i = row * F + n0 + wn * C::WNR + cl;
+          float gf[4], uf[4], dg[4], du[4];
+          dunpack4(*reinterpret_cast<const uint2*>((const uint16_t*)a.g + i), gf);
+          dunpack4(*reinterpret_cast<const uint2*>((const uint16_t*)a.u + i), uf);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float s = 1.0f / (1.0f + expf(-gf[r]));
+            dg[r] = v0[r] * uf[r] * s * (1.0f + gf[r] * (1.0f - s));
+            du[r] = v0[r] * gf[r] * s;
+          }
+          *reinterpret_cast<uint2*>((uint16_t*)a.dg + i) = dpack4(dg);
+          *reinterpret_cast<uint2*>((uint16_t*)a.du + i) = dpack4(du);
+        } else {
+          uint16_t* out;
+          size_t i;
+          if (OP == MOE_GG_FWD_DOWN) { out = (uint16_t*)a.y_perm; i = row * d; }
+          else if (OP == MOE_GG_DGRAD_GATE_UP) { out = (uint16_t*)a.dx_perm; i = row * d; }
+          else { out = (uint16_t*)a.dw_down; i = e * dF + row * d; }
+          i += n0 + wn * C::WNR + cl;
+          *reinterpret_cast<uint2*>(out + i) = dpack4(v0);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace moe

@@ -197,29 +197,64 @@ __device__ int block_exclusive_scan_1024(int v, int* total) {
   return before;
 }
 
+// G threads (a power of two, G <= 64, within one wave) share expert e: each
+// sums a run of blocks with independent loads, the group scans those sums,
+// and each thread then writes the exclusive per-block bases of its run.
 __global__ void __launch_bounds__(1024) scan_kernel(int32_t* __restrict__ hist, int nblk, int E,
                                                     int capacity, int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets,
                                                     int32_t* __restrict__ n_dropped) {
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      const int v = hist[(size_t)b * E + e];
-      hist[(size_t)b * E + e] = run;
-      run += v;
+  int G = 1;
+  while (G * 2 * E <= 1024 && G * 2 <= 64) G *= 2;
+  const int e = threadIdx.x / G, g = threadIdx.x % G;
+  const bool live = e < E;
+  const int per = (nblk + G - 1) / G;
+  const int b0 = min(nblk, g * per), b1 = min(nblk, b0 + per);
+  constexpr int kBurst = 16;
+  int part = 0;
+  if (live) {
+    for (int b = b0; b < b1; b += kBurst) {
+      int v[kBurst];
+#pragma unroll
+      for (int i = 0; i < kBurst; ++i) v[i] = b + i < b1 ? hist[(size_t)(b + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBurst; ++i) part += v[i];
     }
-    counts[e] = run;
   }
-  int total;
-  const int off = block_exclusive_scan_1024(e < E ? run : 0, &total);
-  if (e < E) offsets[e] = off;
-  if (e == 0) offsets[E] = total;
-  int drop = (capacity > 0 && e < E && run > capacity) ? run - capacity : 0;
+  // inclusive scan of the partial sums over the G lanes of this expert
+  const int lane = threadIdx.x & 63;
+  int incl = part;
+  for (int o = 1; o < G; o <<= 1) {
+    const int n = __shfl_up(incl, o, 64);
+    if ((lane % G) >= o) incl += n;
+  }
+  const int total = __shfl(incl, (lane / G) * G + G - 1, 64);
+  if (live) {
+    int run = incl - part;
+    for (int b = b0; b < b1; b += kBurst) {
+      int v[kBurst];
+#pragma unroll
+      for (int i = 0; i < kBurst; ++i) v[i] = b + i < b1 ? hist[(size_t)(b + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBurst; ++i) {
+        if (b + i < b1) hist[(size_t)(b + i) * E + e] = run;
+        run += v[i];
+      }
+    }
+    if (g == 0) counts[e] = total;
+  }
+  __syncthreads();
+  // exclusive scan of counts over experts: one thread per expert
+  const int ce = threadIdx.x < E ? counts[threadIdx.x] : 0;
+  int tot;
+  const int off = block_exclusive_scan_1024(ce, &tot);
+  if (threadIdx.x < E) offsets[threadIdx.x] = off;
+  if (threadIdx.x == 0) offsets[E] = tot;
+  const int drop = (capacity > 0 && threadIdx.x < E && ce > capacity) ? ce - capacity : 0;
   int dtotal;
   __syncthreads();
   (void)block_exclusive_scan_1024(drop, &dtotal);
-  if (e == 0) *n_dropped = dtotal;
+  if (threadIdx.x == 0) *n_dropped = dtotal;
 }
 
 __global__ void __launch_bounds__(kMetaThreads) rank_kernel(
@@ -364,10 +399,10 @@ using namespace moe;
 
 extern "C" int moe_router_gemm(int dtype, const void* x, const void* w_r, int T, int d, int E,
                                float* logits, hipStream_t stream) {
-  MOE_CHECK_ARG(valid_dtype(dtype) && x && w_r && logits && T >= 0 && d > 0 && E > 0);
-  MOE_CHECK_ARG(d % 8 == 0 && aligned16(x));
+  MOE_CHECK_ARG(valid_dtype(dtype) && T >= 0 && d > 0 && E > 0 && d % 8 == 0);
   MOE_CHECK_SUPPORTED(E <= MOE_MAX_EXPERTS);
   if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(x && w_r && logits && aligned16(x));
   const int waves = (T + kRouterTok - 1) / kRouterTok;
   const int blocks = (waves + 3) / 4;
   if (dtype == MOE_BF16)
@@ -390,9 +425,10 @@ static void launch_route(const float* logits, int T, int E, int k, int32_t* idx,
 
 extern "C" int moe_route(const float* logits, int T, int E, int k, int32_t* topk_idx,
                          float* topk_w, hipStream_t stream) {
-  MOE_CHECK_ARG(logits && topk_idx && topk_w && T >= 0 && E > 0 && k >= 1 && k <= E);
+  MOE_CHECK_ARG(T >= 0 && E > 0 && k >= 1 && k <= E);
   MOE_CHECK_SUPPORTED(E <= MOE_MAX_EXPERTS && k <= MOE_MAX_TOPK);
   if (T == 0) return MOE_OK;
+  MOE_CHECK_ARG(logits && topk_idx && topk_w);
   if (E <= 1) launch_route<1, 1>(logits, T, E, k, topk_idx, topk_w, stream);
   else if (E <= 2) launch_route<2, 1>(logits, T, E, k, topk_idx, topk_w, stream);
   else if (E <= 4) launch_route<4, 1>(logits, T, E, k, topk_idx, topk_w, stream);
@@ -441,10 +477,11 @@ extern "C" int moe_offsets(const int32_t* topk_idx, int T, int k, int E, int cap
 
 extern "C" int moe_route_bwd(const int32_t* topk_idx, const float* topk_w, const float* dtopk_w,
                              int T, int E, int k, float* dlogits, hipStream_t stream) {
-  MOE_CHECK_ARG(topk_idx && topk_w && dtopk_w && dlogits && T >= 0 && E > 0 && k >= 1 && k <= E);
+  MOE_CHECK_ARG(T >= 0 && E > 0 && k >= 1 && k <= E);
   MOE_CHECK_SUPPORTED(E <= MOE_MAX_EXPERTS && k <= MOE_MAX_TOPK);
   const size_t n = (size_t)T * E;
   if (n == 0) return MOE_OK;
+  MOE_CHECK_ARG(topk_idx && topk_w && dtopk_w && dlogits);
   route_bwd_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, stream>>>(
       topk_idx, topk_w, dtopk_w, T, E, k, dlogits);
   return launch_status();

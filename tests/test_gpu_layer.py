@@ -44,9 +44,37 @@ def _run_gpu(wl, inp, capacity=0, backward=True):
     return layer, t
 
 
-def _margin_ok(logits, k, rel=1e-4):
+def _margin_ok(logits, k, err):
+    """Tokens whose k-th and (k+1)-th logits are further apart than twice the
+    measured logit error (plus a little): no rounding can flip their top-k."""
+    if k >= logits.shape[1]:
+        return np.ones(len(logits), bool)
     s = -np.sort(-logits, axis=1)
-    return (s[:, k - 1] - s[:, k]) > rel * np.abs(logits).max() if k < logits.shape[1] else np.ones(len(logits), bool)
+    return (s[:, k - 1] - s[:, k]) > 2 * err + 1e-7 * np.abs(logits).max()
+
+
+def _check_routing(layer, lg_ref, k):
+    """Logits within binary32 tolerance; top-k identical except where the
+    oracle's own logits are a near-tie within the measured logit error.
+    Returns the oracle's routing and the per-token agreement mask."""
+    lg_gpu = host(layer.logits)
+    assert_close(lg_gpu, lg_ref, "f32", "logits")
+    err = np.abs(lg_gpu - lg_ref).max()
+    idx, w = om.route(lg_ref, k)
+    agree = np.all(host(layer.topk_idx) == idx, axis=1)
+    assert np.all(agree | ~_margin_ok(lg_ref, k, err)), "routing differs away from a near-tie"
+    assert_close(host(layer.topk_w)[agree], w[agree], "f32", "topk_w")
+    return idx, w, agree
+
+
+def _check_meta_valid(layer, T, k):
+    """Row maps are a stable expert-major bijection of the GPU's own top-k."""
+    R = T * k
+    ro, src = host(layer.row_of), host(layer.src_slot)
+    assert np.array_equal(np.sort(ro), np.arange(R)) and np.array_equal(src[ro], np.arange(R))
+    flat = host(layer.topk_idx).reshape(-1)
+    assert np.all(np.diff(flat[src]) >= 0)
+    assert np.all(np.diff(src)[np.diff(flat[src]) == 0] > 0)
 
 
 def _full_oracle_check(wl, capacity=0, backward=True):
@@ -58,27 +86,37 @@ def _full_oracle_check(wl, capacity=0, backward=True):
     if "topk_idx" in inp:
         p["topk_idx"], p["topk_w"] = inp["topk_idx"], inp["topk_w"].astype(np.float64)
     fwd = om.layer_forward(p, wl.k, kind, capacity)
+    agree = np.ones(wl.T, bool)
     if "w_r" in p:
-        assert_close(host(layer.logits), fwd["logits"], "f32", "logits")
-        assert np.all(_margin_ok(fwd["logits"], wl.k)), "near-tie in a small case: pick another seed"
-        assert np.array_equal(host(layer.topk_idx), fwd["topk_idx"])
-        assert_close(host(layer.topk_w), fwd["topk_w"], "f32", "topk_w")
-    for n in ("counts", "offsets", "row_of", "src_slot"):
-        assert np.array_equal(host(getattr(layer, n)), fwd[n]), n
-    assert int(host(layer.n_dropped)[0]) == fwd["n_dropped"]
+        _, _, agree = _check_routing(layer, fwd["logits"], wl.k)
+    if agree.all():
+        for n in ("counts", "offsets", "row_of", "src_slot"):
+            assert np.array_equal(host(getattr(layer, n)), fwd[n]), n
+        assert int(host(layer.n_dropped)[0]) == fwd["n_dropped"]
+        assert np.array_equal(host(layer.x_perm), fwd["x_perm"])
+        for n, ref in (("g", "G"), ("u", "U"), ("h", "H"), ("y_perm", "y_perm")):
+            assert_close(host(getattr(layer, n)), fwd[ref], kind, n)
+    else:
+        # a near-tie flip moves single rows: compare token-order outputs of the
+        # agreeing tokens and check the GPU's own maps are valid
+        assert capacity == 0
+        _check_meta_valid(layer, wl.T, wl.k)
     assert int(host(layer.err_flag)[0]) == 0
-    assert np.array_equal(host(layer.x_perm), fwd["x_perm"])
-    for n, ref in (("g", "G"), ("u", "U"), ("h", "H"), ("y_perm", "y_perm"), ("y", "y")):
-        assert_close(host(getattr(layer, n)), fwd[ref], kind, n)
+    assert_close(host(layer.y)[agree], fwd["y"][agree], kind, "y")
     if not backward:
         return
     dy = values(inp["dy"], kind)
     bwd = om.layer_backward(p, fwd, dy, wl.k, kind, capacity)
-    for n in ("dy_perm", "dtopk_w", "dg", "du", "dx_perm", "dw_gate", "dw_up", "dw_down", "dx"):
-        ref = {"dg": "dG", "du": "dU"}.get(n, n)
-        assert_close(host(getattr(layer, n)), bwd[ref], kind, n)
+    if agree.all():
+        for n in ("dy_perm", "dg", "du", "dx_perm"):
+            ref = {"dg": "dG", "du": "dU"}.get(n, n)
+            assert_close(host(getattr(layer, n)), bwd[ref], kind, n)
+    for n in ("dtopk_w", "dx"):
+        assert_close(host(getattr(layer, n))[agree], bwd[n][agree], kind, n)
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        assert_close(host(getattr(layer, n)), bwd[n], kind, n)
     if "w_r" in p:
-        assert_close(host(layer.dlogits), bwd["dlogits"], kind, "dlogits")
+        assert_close(host(layer.dlogits)[agree], bwd["dlogits"][agree], kind, "dlogits")
         assert_close(host(layer.dw_r), bwd["dw_r"], kind, "dw_r")
 
 
@@ -131,14 +169,7 @@ def _sampled_check(wl, capacity=0, n_tok=48, seed=0):
     dy = values(inp["dy"], kind)
     W = Weights({n: inp[n] for n in ("w_gate", "w_up", "w_down")}, kind)
     if wl.routing == "learned":
-        lg_ref = round_f32(x @ values(inp["w_r"], kind))
-        assert_close(host(layer.logits), lg_ref, "f32", "logits")
-        idx, w = om.route(lg_ref, wl.k)
-        idx_gpu = host(layer.topk_idx)
-        agree = np.all(idx_gpu == idx, axis=1)
-        # a disagreement is allowed only at a near-tie of the oracle's logits
-        assert np.all(agree | ~_margin_ok(lg_ref, wl.k)), "routing differs away from a near-tie"
-        assert_close(host(layer.topk_w)[agree], w[agree], "f32", "topk_w")
+        idx, w, agree = _check_routing(layer, round_f32(x @ values(inp["w_r"], kind)), wl.k)
     else:
         idx, w = inp["topk_idx"], inp["topk_w"].astype(np.float64)
         agree = np.ones(wl.T, bool)
@@ -148,14 +179,8 @@ def _sampled_check(wl, capacity=0, n_tok=48, seed=0):
             assert np.array_equal(host(getattr(layer, n)), meta[n]), n
         assert int(host(layer.n_dropped)[0]) == meta["n_dropped"]
     else:
-        # near-tie flips move single rows: the maps must still be a stable
-        # expert-major bijection of the GPU's own choices
-        ro, src = host(layer.row_of), host(layer.src_slot)
-        assert np.array_equal(np.sort(ro), np.arange(wl.R)) and np.array_equal(src[ro], np.arange(wl.R))
-        flat = host(layer.topk_idx).reshape(-1)
-        assert np.all(np.diff(flat[src]) >= 0)
-        assert np.all(np.diff(src)[np.diff(flat[src]) == 0] > 0)
-        assert (~agree).sum() <= 4
+        assert capacity == 0
+        _check_meta_valid(layer, wl.T, wl.k)
     rng = np.random.default_rng(seed)
     tokens = [int(v) for v in rng.choice(np.nonzero(agree)[0], n_tok, replace=False)]
     keep = (meta["row_of"] >= 0).reshape(wl.T, wl.k)
