@@ -92,7 +92,7 @@ def cpu_baseline(wl, inp, budget_s):
         threads = None
     cores = len(os.sched_getaffinity(0))
     p = {n: bf16_bits_to_f64(inp[n]) for n in ("w_gate", "w_up", "w_down")}
-    Ts = 128
+    Ts = 1024
     while True:
         q = dict(p)
         q["x"] = bf16_bits_to_f64(inp["x"][:Ts])

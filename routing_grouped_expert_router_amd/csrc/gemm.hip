@@ -182,16 +182,34 @@ namespace {
 // {BM, BN, WM, WN, BK, STAGES}.
 using Cfg128 = MfmaCfg<128, 256, 2, 2>;   // 4 waves, 64 x 128 each
 using Cfg256 = MfmaCfg<256, 256, 2, 4>;   // 8 waves, 128 x 64 each
-using CfgDma = DmaCfg<256, 256, 2, 4, 32, 4>;
+using CfgDma256 = DmaCfg<256, 256, 2, 4, 32, 4>;      // 8 waves, 128 x 64 each, 1 workgroup per CU
+using CfgDma128 = DmaCfg<128, 256, 2, 2, 32, 3, 2>;   // 4 waves, 64 x 128 each, 2 workgroups per CU
+using CfgDma4w = DmaCfg<256, 256, 2, 2, 32, 4>;       // 4 waves, 128 x 128 each
 
-// Kernel choice; MOE_GG_TILE=128|256|dma overrides it (for tuning sweeps).
+// Kernel choice. The default is the direct-load kernel on 128 x 256 tiles
+// with two workgroups per CU (so one workgroup's barrier and epilogue overlap
+// the other's matrix work); MOE_GG_TILE overrides it for tuning sweeps:
+// dma128 | dma256 | dma4w (direct loads) | 128 | 256 (register-staged).
 int tile_choice() {
   static int t = [] {
     const char* s = std::getenv("MOE_GG_TILE");
-    if (!s) return 2;
-    if (std::string(s) == "128") return 0;
-    if (std::string(s) == "256") return 1;
-    return 2;
+    if (!s) return 3;
+    const std::string v(s);
+    if (v == "128") return 0;
+    if (v == "256") return 1;
+    if (v == "dma256") return 2;
+    if (v == "dma4w") return 4;
+    return 3;
+  }();
+  return t;
+}
+
+// Row-varying tile order; MOE_GG_ORDER=m puts the m-tiles of one expert's
+// n-tile next to each other (for tuning sweeps).
+int tile_order() {
+  static int t = [] {
+    const char* s = std::getenv("MOE_GG_ORDER");
+    return (s && std::string(s) == "m") ? 1 : 0;
   }();
   return t;
 }
@@ -305,7 +323,7 @@ extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
     default:
       MOE_CHECK_ARG(act(g->x_perm) && act(g->dg) && act(g->du) && need(g->dw_gate) && need(g->dw_up));
   }
-  GGArgs a{g->op, g->E, g->d, g->F, g->n_rows, g->capacity, g->group_offsets,
+  GGArgs a{g->op, g->E, g->d, g->F, g->n_rows, g->capacity, tile_order(), g->group_offsets,
            g->x_perm, g->g, g->u, g->h, g->y_perm, g->dy_perm, g->dg, g->du, g->dx_perm,
            g->w_gate, g->w_up, g->w_down, g->dw_gate, g->dw_up, g->dw_down};
   const bool dual = g->op == MOE_GG_FWD_GATE_UP || g->op == MOE_GG_WGRAD_GATE_UP;
@@ -316,7 +334,14 @@ extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
     const long span = (long)g->n_rows * (g->d > g->F ? g->d : g->F) * 2;
     const bool dma_fits = span < (1L << 31) && (long)g->d * g->F * 2 < (1L << 31);
     const int choice = tile_choice();
-    if (choice == 2 && dma_fits) return launch_dma<CfgDma>(g, a, kvar, dual, N, stream);
+    if (dma_fits) {
+      switch (choice) {
+        case 2: return launch_dma<CfgDma256>(g, a, kvar, dual, N, stream);
+        case 3: return launch_dma<CfgDma128>(g, a, kvar, dual, N, stream);
+        case 4: return launch_dma<CfgDma4w>(g, a, kvar, dual, N, stream);
+        default: break;
+      }
+    }
     if (choice == 0) return launch_mfma<Cfg128>(g, a, kvar, dual, N, stream);
     return launch_mfma<Cfg256>(g, a, kvar, dual, N, stream);
   }

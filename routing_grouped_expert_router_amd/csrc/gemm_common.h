@@ -8,6 +8,7 @@ namespace moe {
 
 struct GGArgs {
   int op, E, d, F, n_rows, capacity;
+  int order;   // row-varying tile order: 0 = n-tiles of one m-tile adjacent, 1 = m-tiles adjacent
   const int32_t* group_offsets;
   void* x_perm;
   void* g;
@@ -150,6 +151,37 @@ MOE_DEV bool find_m_tile(const GGArgs& a, int tm, int* tile_start, int& e, int& 
   int r0, n;
   group_rows(a, e, r0, n);
   const int mt = tm - tile_start[e];
+  row0 = r0 + mt * BM;
+  mv = n - mt * BM < BM ? n - mt * BM : BM;
+  return true;
+}
+
+// Row-varying ops, expert-grouped order: linear tile b runs over experts in
+// order; inside expert e (with mt_e m-tiles) the tiles are ordered n-tile
+// major, m-tile minor, so all m-tiles reading one weight slice are adjacent.
+template <int BM, int NT>
+MOE_DEV bool find_m_tile_grouped(const GGArgs& a, int b, int tilesN, int* tile_start, int& e,
+                                 int& row0, int& mv, int& tn) {
+  int dummy_r0, dummy_mv, dummy_e;
+  // builds tile_start[] (m-tile prefix over experts) as a side effect
+  (void)find_m_tile<BM, NT>(a, 0, tile_start, dummy_e, dummy_r0, dummy_mv);
+  const int tm_lin = b / tilesN;   // only used to bound the search
+  if (tm_lin >= tile_start[a.E]) return false;
+  // the tiles of experts < e are tile_start[e] * tilesN
+  const int tt = b;
+  int lo = 0, hi = a.E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_start[mid] * tilesN <= tt) lo = mid;
+    else hi = mid - 1;
+  }
+  e = lo;
+  const int mt_e = tile_start[e + 1] - tile_start[e];
+  const int rel = tt - tile_start[e] * tilesN;
+  tn = rel / mt_e;
+  const int mt = rel % mt_e;
+  int r0, n;
+  group_rows(a, e, r0, n);
   row0 = r0 + mt * BM;
   mv = n - mt * BM < BM ? n - mt * BM : BM;
   return true;

@@ -31,8 +31,9 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 dbf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float df32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short ds4_t;
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int ST_> struct DmaCfg {
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int ST_, int OCC_ = 1> struct DmaCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = ST_;
+  static constexpr int OCC = OCC_;                         // workgroups per CU
   static constexpr int NT = WM * WN * 64;
   static constexpr int NW = WM * WN;
   static constexpr int WMR = BM / WM, WNR = BN / WN;
@@ -42,10 +43,19 @@ template <int BM_, int BN_, int WM_, int WN_, int BK_, int ST_> struct DmaCfg {
   static constexpr int B_INSTR = BN * BK * 2 / 1024;
   static constexpr int A_PER_WAVE = A_INSTR / NW, B_PER_WAVE = B_INSTR / NW;
   static constexpr int STAGE_ELEMS = (BM + BN) * BK;
+  // epilogue staging: two planes of BM rows x 128 columns (+8 padding)
+  static constexpr int CW = 128, LDW = CW + 8;
+  static constexpr int STAGING_ELEMS = 2 * BM * LDW;
+  static constexpr int LDS_ELEMS = STAGE_ELEMS * STAGES > STAGING_ELEMS ? STAGE_ELEMS * STAGES : STAGING_ELEMS;
   static_assert(A_INSTR % NW == 0 && B_INSTR % NW == 0, "loads per wave");
   static_assert(BK == 32 || BK == 64, "K step");
   static_assert(WMR % 32 == 0 && WNR % 64 == 0, "wave tile");
   static_assert((BK * BN / 16) % 64 == 0, "dual sub-tiles hold whole wave-loads");
+  // the MN-contiguous swizzle XORs chunk indices with up to 12: rows of an
+  // MN-contiguous tile (A: BM, B: BN or BN/2 for the dual ops) need >= 16 chunks
+  static_assert(BM >= 128 && BN / 2 >= 128, "MN-contiguous rows of >= 16 chunks");
+  static_assert(OCC * (LDS_ELEMS * 2 + 4 * (MOE_MAX_EXPERTS + 1)) <= 160 * 1024, "LDS");
+  static_assert(WNR <= CW && (BN <= CW || BN % CW == 0), "wave columns within one staging chunk");
 };
 
 // ------------------------------------------------------------------ primitives
@@ -109,7 +119,7 @@ MOE_DEV void dunpack4(uint2 p, float* v) {
 
 // ------------------------------------------------------------------ kernel
 template <int OP, class C>
-__global__ void __launch_bounds__(C::NT, 1) gg_dma_kernel(GGArgs a) {
+__global__ void __launch_bounds__(C::NT, C::OCC) gg_dma_kernel(GGArgs a) {
   using I = OpInfo<OP>;
   constexpr bool DUAL = I::kDual, KVAR = I::kKVar, AK = I::kAKContig, BKC = I::kBKContig;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::STAGES, NT = C::NT;
@@ -117,7 +127,7 @@ __global__ void __launch_bounds__(C::NT, 1) gg_dma_kernel(GGArgs a) {
   constexpr int BNO = DUAL ? BN / 2 : BN;          // output columns per matrix per tile
   constexpr int A_ELEMS = BM * BK;
   __shared__ int tile_start[MOE_MAX_EXPERTS + 1];
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[S * C::STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[C::LDS_ELEMS];
 
   const int d = a.d, F = a.F;
   const int N = op_n(OP, d, F);
@@ -125,8 +135,14 @@ __global__ void __launch_bounds__(C::NT, 1) gg_dma_kernel(GGArgs a) {
   const int b = xcd_remap(blockIdx.x, gridDim.x);
   int e, row0, mv, K, m0 = 0, tn;
   if (!KVAR) {
-    tn = b % tilesN;
-    if (!find_m_tile<BM, NT>(a, b / tilesN, tile_start, e, row0, mv)) return;
+    if (a.order == 0) {
+      tn = b % tilesN;
+      if (!find_m_tile<BM, NT>(a, b / tilesN, tile_start, e, row0, mv)) return;
+    } else {
+      // blocks of (expert's m-tiles) x (one n-tile): the m-tiles sharing a
+      // weight slice run side by side; experts are visited in order
+      if (!find_m_tile_grouped<BM, NT>(a, b, tilesN, tile_start, e, row0, mv, tn)) return;
+    }
     K = op_k(OP, d, F);
   } else {
     const int M = op_wgrad_m(OP, d, F);
@@ -268,133 +284,244 @@ __global__ void __launch_bounds__(C::NT, 1) gg_dma_kernel(GGArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](int slot) {
+  // fragments of K sub-step ks (16 deep) of ring slot `slot`
+  auto read_frags = [&](int slot, int ks, dbf16x8_t (&af)[MI], dbf16x8_t (&bfr)[NI]) {
     const uint16_t* sa = lds + slot * C::STAGE_ELEMS;
     const uint16_t* sb = sa + A_ELEMS;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      dbf16x8_t af[MI], bfr[NI];
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int m = wm * C::WMR + mi * 32;
-        if (AK) {
-          const int row = m + lr;
-          af[mi] = *reinterpret_cast<const dbf16x8_t*>(sa + row * BK + (((2 * ks + lk) ^ swz_k(row)) << 3));
-        } else {
-          const int col = m + 16 * (tg & 1) + 4 * tq;
-          const int k0 = 16 * ks + 8 * (tg >> 1) + tj;
-          const int k1 = k0 + 4;
-          af[mi] = read_tr8(sa + k0 * BM + ((((col >> 3) ^ swz_t(k0)) << 3) | (col & 7)),
-                            sa + k1 * BM + ((((col >> 3) ^ swz_t(k1)) << 3) | (col & 7)));
-        }
+    for (int mi = 0; mi < MI; ++mi) {
+      const int m = wm * C::WMR + mi * 32;
+      if (AK) {
+        const int row = m + lr;
+        af[mi] = *reinterpret_cast<const dbf16x8_t*>(sa + row * BK + (((2 * ks + lk) ^ swz_k(row)) << 3));
+      } else {
+        const int col = m + 16 * (tg & 1) + 4 * tq;
+        const int k0 = 16 * ks + 8 * (tg >> 1) + tj;
+        const int k1 = k0 + 4;
+        af[mi] = read_tr8(sa + k0 * BM + ((((col >> 3) ^ swz_t(k0)) << 3) | (col & 7)),
+                          sa + k1 * BM + ((((col >> 3) ^ swz_t(k1)) << 3) | (col & 7)));
       }
+    }
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        if (BKC) {
-          const int row = wn * C::WNR + ni * 32 + lr;
-          bfr[ni] = *reinterpret_cast<const dbf16x8_t*>(sb + row * BK + (((2 * ks + lk) ^ swz_k(row)) << 3));
+    for (int ni = 0; ni < NI; ++ni) {
+      if (BKC) {
+        const int row = wn * C::WNR + ni * 32 + lr;
+        bfr[ni] = *reinterpret_cast<const dbf16x8_t*>(sb + row * BK + (((2 * ks + lk) ^ swz_k(row)) << 3));
+      } else {
+        const uint16_t* base = sb;
+        int col, width;
+        if (DUAL) {   // block ni < NI/2: gate sub-tile, else up sub-tile, same columns
+          width = BN / 2;
+          base = sb + (ni >= NI / 2 ? BK * (BN / 2) : 0);
+          col = wn * (C::WNR / 2) + (ni % (NI / 2)) * 32;
         } else {
-          const uint16_t* base = sb;
-          int col, width;
-          if (DUAL) {   // block ni < NI/2: gate sub-tile, else up sub-tile, same columns
-            width = BN / 2;
-            base = sb + (ni >= NI / 2 ? BK * (BN / 2) : 0);
-            col = wn * (C::WNR / 2) + (ni % (NI / 2)) * 32;
-          } else {
-            width = BN;
-            col = wn * C::WNR + ni * 32;
-          }
-          col += 16 * (tg & 1) + 4 * tq;
-          const int k0 = 16 * ks + 8 * (tg >> 1) + tj;
-          const int k1 = k0 + 4;
-          bfr[ni] = read_tr8(base + k0 * width + ((((col >> 3) ^ swz_t(k0)) << 3) | (col & 7)),
-                             base + k1 * width + ((((col >> 3) ^ swz_t(k1)) << 3) | (col & 7)));
+          width = BN;
+          col = wn * C::WNR + ni * 32;
         }
+        col += 16 * (tg & 1) + 4 * tq;
+        const int k0 = 16 * ks + 8 * (tg >> 1) + tj;
+        const int k1 = k0 + 4;
+        bfr[ni] = read_tr8(base + k0 * width + ((((col >> 3) ^ swz_t(k0)) << 3) | (col & 7)),
+                           base + k1 * width + ((((col >> 3) ^ swz_t(k1)) << 3) | (col & 7)));
       }
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
     }
   };
+  auto mfmas = [&](const dbf16x8_t (&af)[MI], const dbf16x8_t (&bfr)[NI]) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+  };
 
-  // ---- K loop over a ring of S slots
+  // ---- K loop over a ring of S slots. Step kt has KS sub-steps of 16. The
+  // fragments of each sub-step are read while the previous sub-step's MFMAs
+  // run; before the last sub-step of step kt every wave waits for stage kt+1
+  // and meets the others at one barrier, so the first fragments of step kt+1
+  // are read under the last MFMAs of step kt. A slot is refilled only after
+  // the barrier that follows the last read of it.
+  constexpr int KS = BK / 16;
   constexpr int PER_STAGE = C::A_PER_WAVE + C::B_PER_WAVE;   // wave-loads per stage
+  static_assert(S >= 3, "ring depth");
   const int nk = (K + BK - 1) / BK;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < nk) issue(s, s);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt is complete once at most (stages issued after it) loads remain
-    const int after = min(S - 2, nk - 1 - kt);
-    if (after >= S - 2) wait_vm<PER_STAGE * (S - 2)>();
-    else if (after == 1) wait_vm<PER_STAGE>();
+  dbf16x8_t af[2][MI], bfr[2][NI];
+  if (nk > 0) {
+    // stage 0 complete: at most S-2 later stages outstanding
+    if (nk - 1 >= S - 2) wait_vm<PER_STAGE * (S - 2)>();
+    else if (nk - 1 == 1) wait_vm<PER_STAGE>();
     else wait_vm<0>();
     __syncthreads();
-    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
-    if (active) compute(kt % S);
+    if (active) read_frags(0, 0, af[0], bfr[0]);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int slot = kt % S;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks + 1 < KS) {
+        if (active) read_frags(slot, ks + 1, af[nxt], bfr[nxt]);
+      } else {
+        // stage kt+1 complete: stages issued so far end at min(kt+S-2, nk-1)
+        const int after = min(kt + S - 2, nk - 1) - (kt + 1);
+        if (after >= S - 3 && S - 3 > 0) wait_vm<PER_STAGE * (S - 3 > 0 ? S - 3 : 0)>();
+        else wait_vm<0>();
+        __syncthreads();
+        if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+        if (kt + 1 < nk && active) read_frags((kt + 1) % S, 0, af[nxt], bfr[nxt]);
+      }
+      if (active) mfmas(af[cur], bfr[cur]);
+    }
   }
 
-  // ---- epilogue: each 32x32 block holds C^T (B fragment first): lane
-  // (lr, lk) has output row lr and, for accumulator group g, the 4
-  // consecutive output columns 8g + 4lk .. 8g + 4lk + 3.
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi) {
-    const int ml = wm * C::WMR + mi * 32 + lr;
-    if (ml >= mv) continue;
-    const size_t row = KVAR ? (size_t)(m0 + ml) : (size_t)(row0 + ml);
-#pragma unroll
-    for (int ni = 0; ni < (DUAL ? NI / 2 : NI); ++ni) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int cl = ni * 32 + 8 * g + 4 * lk;
-        float v0[4], v1[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v0[r] = acc[mi][ni][4 * g + r];
-          v1[r] = DUAL ? acc[mi][ni + NI / 2][4 * g + r] : 0.f;
-        }
-        if (OP == MOE_GG_FWD_GATE_UP) {
-          const size_t i = row * F + n0 + wn * (C::WNR / 2) + cl;
-          float gg[4], uu[4], hh[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            gg[r] = bf16_to_f32(f32_to_bf16(v0[r]));
-            uu[r] = bf16_to_f32(f32_to_bf16(v1[r]));
-            hh[r] = gg[r] * uu[r] / (1.0f + expf(-gg[r]));
-          }
-          *reinterpret_cast<uint2*>((uint16_t*)a.g + i) = dpack4(gg);
-          *reinterpret_cast<uint2*>((uint16_t*)a.u + i) = dpack4(uu);
-          *reinterpret_cast<uint2*>((uint16_t*)a.h + i) = dpack4(hh);
-        } else if (OP == MOE_GG_WGRAD_GATE_UP) {
-          const size_t i = e * dF + row * F + n0 + wn * (C::WNR / 2) + cl;
-          *reinterpret_cast<uint2*>((uint16_t*)a.dw_gate + i) = dpack4(v0);
-          *reinterpret_cast<uint2*>((uint16_t*)a.dw_up + i) = dpack4(v1);
-        } else if (OP == MOE_GG_DGRAD_DOWN) {
-          const size_t i = row * F + n0 + wn * C::WNR + cl;
-          float gf[4], uf[4], dg[4], du[4];
-          dunpack4(*reinterpret_cast<const uint2*>((const uint16_t*)a.g + i), gf);
-          dunpack4(*reinterpret_cast<const uint2*>((const uint16_t*)a.u + i), uf);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float s = 1.0f / (1.0f + expf(-gf[r]));
-            dg[r] = v0[r] * uf[r] * s * (1.0f + gf[r] * (1.0f - s));
-            du[r] = v0[r] * gf[r] * s;
-          }
-          *reinterpret_cast<uint2*>((uint16_t*)a.dg + i) = dpack4(dg);
-          *reinterpret_cast<uint2*>((uint16_t*)a.du + i) = dpack4(du);
-        } else {
-          uint16_t* out;
-          size_t i;
-          if (OP == MOE_GG_FWD_DOWN) { out = (uint16_t*)a.y_perm; i = row * d; }
-          else if (OP == MOE_GG_DGRAD_GATE_UP) { out = (uint16_t*)a.dx_perm; i = row * d; }
-          else { out = (uint16_t*)a.dw_down; i = e * dF + row * d; }
-          i += n0 + wn * C::WNR + cl;
-          *reinterpret_cast<uint2*>(out + i) = dpack4(v0);
-        }
-      }
+  // ---- epilogue, staged through LDS so that global traffic is whole
+  // 16-byte row segments. Each 32x32 block holds C^T (B fragment first):
+  // lane (lr, lk) has tile row wm*WMR + mi*32 + lr and, for accumulator group
+  // g, the 4 consecutive columns 8g + 4lk .. +3 of block ni. Output columns
+  // are handled in chunks of CW = 128 (one chunk per matrix for the dual
+  // ops, BN/128 chunks otherwise); a wave's columns lie in one chunk.
+  constexpr int CW = C::CW, LDW = C::LDW;
+  constexpr int NCH = BNO / CW > 0 ? BNO / CW : 1;          // column chunks per matrix
+  constexpr int WCOLS = DUAL ? C::WNR / 2 : C::WNR;          // output columns per wave
+  const int wcol0 = wn * WCOLS;                              // first output column of the wave
+  const int wchunk = wcol0 / CW;
+  uint16_t* stg0 = lds;
+  uint16_t* stg1 = lds + BM * LDW;
+  const int rows_valid = mv;
+
+  // value of accumulator element (mi, ni, g, r): tile row, chunk column
+  auto row_of_acc = [&](int mi) { return wm * C::WMR + mi * 32 + lr; };
+  auto col_of_acc = [&](int ni, int g) { return (wcol0 % CW) + ni * 32 + 8 * g + 4 * lk; };
+
+  // cooperative copy of plane `src` (rows_valid x CW, columns chunk*CW..) to
+  // global rows out + r * ld (+ chunk column offset)
+  auto store_plane = [&](const uint16_t* src, uint16_t* out, size_t ld, int chunk) {
+    constexpr int CPRW = CW / 8;                             // 16-byte chunks per row
+    for (int q = tid; q < rows_valid * CPRW; q += NT) {
+      const int r = q / CPRW, c = q % CPRW;
+      *reinterpret_cast<V16*>(out + (size_t)r * ld + chunk * CW + c * 8) =
+          *reinterpret_cast<const V16*>(src + r * LDW + c * 8);
     }
+  };
+  auto load_plane = [&](uint16_t* dst, const uint16_t* in, size_t ld, int chunk) {
+    constexpr int CPRW = CW / 8;
+    for (int q = tid; q < rows_valid * CPRW; q += NT) {
+      const int r = q / CPRW, c = q % CPRW;
+      *reinterpret_cast<V16*>(dst + r * LDW + c * 8) =
+          *reinterpret_cast<const V16*>(in + (size_t)r * ld + chunk * CW + c * 8);
+    }
+  };
+  // write 4 values as bf16 at (tile row, chunk column) of a staging plane
+  auto put4 = [&](uint16_t* stg, int row, int col, const float* v) {
+    *reinterpret_cast<uint2*>(stg + row * LDW + col) = dpack4(v);
+  };
+
+  __syncthreads();   // every wave is done with the ring
+
+  // global destinations (row 0 of the tile, column n0)
+  const size_t rbase = KVAR ? (size_t)m0 : (size_t)row0;
+  if (OP == MOE_GG_FWD_GATE_UP || OP == MOE_GG_WGRAD_GATE_UP) {
+    // planes: G|dW_gate -> stg0, U|dW_up -> stg1, then H -> stg0
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI / 2; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v0[4], v1[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            v0[r] = acc[mi][ni][4 * g + r];
+            v1[r] = acc[mi][ni + NI / 2][4 * g + r];
+          }
+          put4(stg0, row_of_acc(mi), col_of_acc(ni, g), v0);
+          put4(stg1, row_of_acc(mi), col_of_acc(ni, g), v1);
+        }
+    __syncthreads();
+    if (OP == MOE_GG_FWD_GATE_UP) {
+      store_plane(stg0, (uint16_t*)a.g + rbase * F + n0, F, 0);
+      store_plane(stg1, (uint16_t*)a.u + rbase * F + n0, F, 0);
+      __syncthreads();
+      // H from the stored (bf16-rounded) g and u
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI / 2; ++ni)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float hh[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float gg = bf16_to_f32(f32_to_bf16(acc[mi][ni][4 * g + r]));
+              const float uu = bf16_to_f32(f32_to_bf16(acc[mi][ni + NI / 2][4 * g + r]));
+              hh[r] = gg * uu / (1.0f + expf(-gg));
+            }
+            put4(stg0, row_of_acc(mi), col_of_acc(ni, g), hh);
+          }
+      __syncthreads();
+      store_plane(stg0, (uint16_t*)a.h + rbase * F + n0, F, 0);
+    } else {
+      store_plane(stg0, (uint16_t*)a.dw_gate + e * dF + rbase * F + n0, F, 0);
+      store_plane(stg1, (uint16_t*)a.dw_up + e * dF + rbase * F + n0, F, 0);
+    }
+  } else if (OP == MOE_GG_DGRAD_DOWN) {
+    // per column chunk: stage G and U, turn them into dG and dU in place
+    for (int ch = 0; ch < NCH; ++ch) {
+      load_plane(stg0, (const uint16_t*)a.g + rbase * F + n0, F, ch);
+      load_plane(stg1, (const uint16_t*)a.u + rbase * F + n0, F, ch);
+      __syncthreads();
+      if (wchunk == ch) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int row = row_of_acc(mi), col = col_of_acc(ni, g);
+              float gf[4], uf[4], dg[4], du[4];
+              dunpack4(*reinterpret_cast<const uint2*>(stg0 + row * LDW + col), gf);
+              dunpack4(*reinterpret_cast<const uint2*>(stg1 + row * LDW + col), uf);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float dh = acc[mi][ni][4 * g + r];
+                const float sg = 1.0f / (1.0f + expf(-gf[r]));
+                dg[r] = dh * uf[r] * sg * (1.0f + gf[r] * (1.0f - sg));
+                du[r] = dh * gf[r] * sg;
+              }
+              put4(stg0, row, col, dg);
+              put4(stg1, row, col, du);
+            }
+      }
+      __syncthreads();
+      store_plane(stg0, (uint16_t*)a.dg + rbase * F + n0, F, ch);
+      store_plane(stg1, (uint16_t*)a.du + rbase * F + n0, F, ch);
+      __syncthreads();
+    }
+  } else {
+    // single output: chunk 0 -> stg0, chunk 1 -> stg1 (at most two chunks)
+    static_assert(NCH <= 2, "two staging planes");
+    uint16_t* out;
+    size_t ld;
+    if (OP == MOE_GG_FWD_DOWN) { out = (uint16_t*)a.y_perm + rbase * d + n0; ld = d; }
+    else if (OP == MOE_GG_DGRAD_GATE_UP) { out = (uint16_t*)a.dx_perm + rbase * d + n0; ld = d; }
+    else { out = (uint16_t*)a.dw_down + e * dF + rbase * d + n0; ld = d; }
+    uint16_t* mine = wchunk == 0 ? stg0 : stg1;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = acc[mi][ni][4 * g + r];
+          put4(mine, row_of_acc(mi), col_of_acc(ni, g), v);
+        }
+    __syncthreads();
+    store_plane(stg0, out, ld, 0);
+    if (NCH > 1) store_plane(stg1, out, ld, 1);
   }
 }
 
