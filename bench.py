@@ -53,6 +53,19 @@ def stage_work(name, wl, n_rows, R):
     return "hbm", b[name]
 
 
+def stage_algorithmic_bytes(name, wl, n_rows, R):
+    """Bytes a stage must move at least once (inputs read, outputs written)."""
+    d, F = wl.d, wl.F
+    W = wl.E * d * F * 2            # one bf16 expert weight tensor, all experts
+    x, f = n_rows * d * 2, n_rows * F * 2
+    gemm = {"gg_fwd_gate_up": x + 2 * W + 3 * f, "gg_fwd_down": f + W + x,
+            "gg_dgrad_down": x + W + 4 * f, "gg_dgrad_gate_up": 2 * f + 2 * W + x,
+            "gg_wgrad_down": f + x + W, "gg_wgrad_gate_up": x + 2 * f + 2 * W}
+    if name in gemm:
+        return gemm[name]
+    return stage_work(name, wl, n_rows, R)[1]
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "routing_grouped_expert_router_amd", "csrc")
@@ -63,13 +76,14 @@ def kernel_source_hash():
 
 
 def measured_traffic(stage, workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, if it was taken on the current kernel sources; else None."""
+    from profile_summary import read_traffic_table
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     try:
-        tab = json.load(open(path))
+        tab = read_traffic_table(path)
     except ValueError:
         return None
     ent = tab.get(workload, {}).get(stage)
@@ -263,6 +277,7 @@ def main():
         "expert_load": {"min": int(counts.min()), "max": int(counts.max()),
                         "mean": float(counts.mean()), "dropped": int(layer.n_dropped.cpu()[0])},
         "wall_s_timed": round(wall, 3),
+        "kernel_sources": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
         log("timing the oracle on the host for the CPU baseline ...")

@@ -1,0 +1,180 @@
+"""Turn rocprofv3 CSV output of bench.py runs into the text summaries kept
+under profiles/.
+
+    python profile_summary.py kernels  OUT.md KT_DIR  [--command CMD]
+    python profile_summary.py traffic  OUT.md FETCH_CSV WRITE_CSV CAL_FETCH_CSV CAL_WRITE_CSV
+                                       [--workload NAME] [--command CMD ...]
+
+`kernels` summarises a `--kernel-trace --stats` run (the *_kernel_stats.csv
+file in KT_DIR). `traffic` takes one `--pmc FETCH_SIZE` and one
+`--pmc WRITE_SIZE` run of the same bench command, plus the same two counters
+over `bench.py --copy-calibration MIB` (plain copies of a known size), and
+writes per-stage HBM bytes per launch: each counter is scaled by
+(bytes the copy moves) / (what the counter reads for it). The traffic file
+ends with a JSON block that bench.py reads for `roofline.traffic`; each entry
+carries the hash of the kernel sources it was measured on, so a later kernel
+change turns the figure back into null.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import json
+import os
+import re
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+GG_OPS = ["gg_fwd_gate_up", "gg_fwd_down", "gg_dgrad_down", "gg_dgrad_gate_up",
+          "gg_wgrad_down", "gg_wgrad_gate_up"]
+ROW_KERNELS = [
+    ("combine_bwd_kernel", "combine_bwd"), ("permute_bwd_kernel", "permute_bwd"),
+    ("combine_kernel", "combine"), ("permute_kernel", "permute"),
+    ("zero_pad_rows_kernel", "permute"),
+    ("hist_kernel", "offsets"), ("scan_kernel", "offsets"), ("rank_kernel", "offsets"),
+    ("router_gemm_kernel", "router_gemm"), ("route_bwd_kernel", "route_bwd"),
+    ("route_kernel", "route"), ("router_bwd_partial", "router_gemm_bwd"),
+    ("router_bwd_reduce", "router_gemm_bwd"),
+]
+TRAFFIC_BEGIN = "<!-- traffic-json -->"
+
+
+def stage_of(kernel):
+    """Pipeline stage a kernel belongs to, or None for library kernels."""
+    m = re.search(r"moe::gg_\w+_kernel<(\d+),", kernel)
+    if m:
+        return GG_OPS[int(m.group(1))]
+    for pat, st in ROW_KERNELS:
+        if re.search(r"moe::" + pat + r"\b", kernel):
+            return st
+    return None
+
+
+def short(kernel):
+    m = re.search(r"moe::(\w+)(<[^()]*>)?", kernel)
+    if not m:
+        return kernel[:60]
+    return m.group(1) + (m.group(2) or "")
+
+
+def kernels(args):
+    path = glob.glob(os.path.join(args.dir, "*kernel_stats.csv"))
+    if len(path) != 1:
+        sys.exit(f"expected one *kernel_stats.csv under {args.dir}, found {path}")
+    rows = list(csv.DictReader(open(path[0])))
+    out = ["# Kernel durations", ""]
+    if args.command:
+        out += ["Command (from the repository root):", "", "```", args.command, "```", ""]
+    out += ["Source: rocprofv3 `--kernel-trace --stats` (kernel_stats.csv). Averages include "
+            "the warm-up launches.", "",
+            "| stage | kernel | calls | avg us | min us | max us | % of GPU time |",
+            "|---|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append("| {} | `{}` | {} | {:.1f} | {:.1f} | {:.1f} | {:.2f} |".format(
+            stage_of(r["Name"]) or "-", short(r["Name"]), r["Calls"],
+            float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["Percentage"])))
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print(args.out)
+
+
+def _counter(path, name):
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == name]
+    if not rows:
+        sys.exit(f"no {name} rows in {path}")
+    return rows
+
+
+def _calibration(path, name, copy_bytes):
+    """Counter KiB reported for the plain copies -> bytes per counted KiB."""
+    rows = [r for r in _counter(path, name) if "copyBuffer" in r["Kernel_Name"]]
+    if not rows:
+        sys.exit(f"no copy kernels in {path}")
+    kib = sum(float(r["Counter_Value"]) for r in rows) / len(rows)
+    direction = copy_bytes  # a copy reads and writes copy_bytes each
+    return direction / kib, kib
+
+
+def _per_stage(path, name):
+    """Mean counter KiB per launch of each stage (kernels of one stage summed
+    within a step: a stage's kernels run once per step)."""
+    tot, calls = {}, {}
+    for r in _counter(path, name):
+        st = stage_of(r["Kernel_Name"])
+        if st is None:
+            continue
+        tot[st] = tot.get(st, 0.0) + float(r["Counter_Value"])
+        k = short(r["Kernel_Name"])
+        calls.setdefault(st, {}).setdefault(k, 0)
+        calls[st][k] += 1
+    return {st: tot[st] / max(calls[st].values()) for st in tot}
+
+
+def traffic(args):
+    from bench import kernel_source_hash, stage_algorithmic_bytes
+    from moe_inputs import workload
+    wl = workload(args.workload)
+    copy_bytes = args.copy_mib * (1 << 20)
+    f_scale, f_kib = _calibration(args.cal_fetch, "FETCH_SIZE", copy_bytes)
+    w_scale, w_kib = _calibration(args.cal_write, "WRITE_SIZE", copy_bytes)
+    fetch = _per_stage(args.fetch, "FETCH_SIZE")
+    write = _per_stage(args.write, "WRITE_SIZE")
+    h = kernel_source_hash()
+    out = ["# HBM traffic per launch: " + args.workload, ""]
+    if args.command:
+        out += ["Commands (from the repository root):", "", "```"] + args.command + ["```", ""]
+    out += [f"Calibration: a plain copy of {args.copy_mib} MiB reads {f_kib:.0f} KiB on "
+            f"FETCH_SIZE and writes {w_kib:.0f} KiB on WRITE_SIZE, so FETCH_SIZE is scaled by "
+            f"{f_scale / 1024:.3f} and WRITE_SIZE by {w_scale / 1024:.3f} (bytes per counted "
+            "byte). FETCH_SIZE counts L2 misses, some of which the MALL may serve.", "",
+            f"Kernel sources hash: `{h}`", "",
+            "| stage | FETCH KiB | WRITE KiB | traffic MB | algorithmic MB | traffic / algorithmic |",
+            "|---|---:|---:|---:|---:|---:|"]
+    tab = {}
+    R = wl.T * wl.k
+    for st in sorted(fetch, key=lambda s: -(fetch[s] * f_scale + write.get(s, 0) * w_scale)):
+        b = fetch[st] * f_scale + write.get(st, 0.0) * w_scale
+        alg = stage_algorithmic_bytes(st, wl, R, R)
+        out.append("| {} | {:.0f} | {:.0f} | {:.1f} | {:.1f} | {:.2f} |".format(
+            st, fetch[st], write.get(st, 0.0), b / 1e6, alg / 1e6, b / alg))
+        tab[st] = {"bytes_per_launch": round(b), "source_hash": h}
+    out += ["", TRAFFIC_BEGIN, "```json", json.dumps({args.workload: tab}, indent=1), "```"]
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print(args.out)
+
+
+def read_traffic_table(path):
+    """The JSON block of a traffic summary (bench.py reads it)."""
+    txt = open(path).read()
+    i = txt.find(TRAFFIC_BEGIN)
+    if i < 0:
+        return {}
+    body = txt[i:].split("```json", 1)[1].split("```", 1)[0]
+    return json.loads(body)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    k = sub.add_parser("kernels")
+    k.add_argument("out")
+    k.add_argument("dir")
+    k.add_argument("--command")
+    t = sub.add_parser("traffic")
+    t.add_argument("out")
+    t.add_argument("fetch")
+    t.add_argument("write")
+    t.add_argument("cal_fetch")
+    t.add_argument("cal_write")
+    t.add_argument("--workload", default="e128_uniform_bf16")
+    t.add_argument("--copy-mib", type=int, default=1024)
+    t.add_argument("--command", action="append")
+    a = ap.parse_args()
+    (kernels if a.mode == "kernels" else traffic)(a)
+
+
+if __name__ == "__main__":
+    main()
