@@ -64,7 +64,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Text for a status code (static storage; never NULL). */
 const char* moe_status_string(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int moe_abi_version(void);
 
 /* ----------------------------------------------------------------- router
@@ -230,6 +230,81 @@ typedef struct moe_gg_desc {
 
 size_t moe_grouped_gemm_workspace_bytes(const moe_gg_desc* desc);
 int moe_grouped_gemm(const moe_gg_desc* desc, hipStream_t stream);
+
+/* ----------------------------------------------------------------- MXFP8
+ * The pages credit MXFP8 for most of the feed-forward speed-up (bigchange.ai
+ * pt-BR, "Três números, três denominadores"; unite.ai/hi, "पैरालेलिज़्म,
+ * प्रिसीजन, और मेमोरी तकनीकें") but fix no format. Reading, per the public OCP
+ * Microscaling Formats v1.0 specification: blocks of 32 consecutive values
+ * along each GEMM's contraction axis share one E8M0 scale byte (value
+ * 2^(code-127)); elements are E4M3 bytes (bias 7, largest 448, subnormals
+ * m*2^-9, no infinities). For a block with largest magnitude amax the scale
+ * exponent is X = clamp(floor(log2 amax) - 8, -127, 127) (X = -127 for an
+ * all-zero block) and each element is v * 2^-X rounded to nearest-even and
+ * saturated to +-448, keeping the sign bit (also when it rounds to zero).
+ * Code 0xFF (NaN) is never written.
+ *
+ * moe_mx_quantize: bf16 src [rows, cols] -> E4M3 codes + E8M0 scales.
+ *   axis 0: blocks along each row. q [rows, cols], s [rows, cols/32];
+ *           cols % 32 == 0; group_offsets must be NULL and col_stride 0.
+ *   axis 1: blocks along the rows of each group, written transposed: group g
+ *           (rows [group_offsets[g], group_offsets[g+1]) of src; when
+ *           group_offsets is NULL, n_groups equal groups of rows/n_groups
+ *           rows) becomes columns [p_g, p_g + ceil(n_g/128)*128) of
+ *           q [cols, col_stride] and of s [cols, col_stride/32], with
+ *           p_g = 128 * sum_{h<g} ceil(n_h/128). Blocks restart at each
+ *           group's first row; the columns past a group's last row are
+ *           written as zero codes with scale code 0. Columns past the last
+ *           group's segment are not written. col_stride must be a multiple of
+ *           128 and at least moe_mx_col_stride(rows, n_groups) when the
+ *           offsets are on the device (a bound that holds whatever the group
+ *           sizes), or n_groups * ceil(rows/n_groups/128)*128 for equal
+ *           groups (rows % n_groups == 0).
+ *   src 16-byte aligned, cols % 64 == 0 for axis 1. rows may be 0. */
+int moe_mx_col_stride(int rows, int n_groups);
+int moe_mx_quantize(const void* src, int rows, int cols, int axis, const int32_t* group_offsets,
+                    int n_groups, int col_stride, void* q, void* s, hipStream_t stream);
+
+/* moe_grouped_gemm_mx: the six expert GEMMs of moe_grouped_gemm with every
+ * operand MXFP8 (blocks of 32 along that GEMM's contraction), binary32
+ * accumulation of the exact block products on the matrix cores, and bf16
+ * outputs rounded once, with the same SwiGLU epilogues. Dropless groups only
+ * (group_offsets [E+1] on the device). Each operand is a (codes, scales)
+ * pair from moe_mx_quantize; "rows" means axis 0, "cols" axis 1 with the
+ * experts as groups and token stride col_stride:
+ *
+ *   op                    a0            a1        b0                    b1            out0, out1, out2
+ *   FWD_GATE_UP  K=d      x_perm rows   -         w_gate as [E*d,F] cols w_up likewise g, u, h
+ *                                                  (groups of d rows; col_stride E*d)
+ *   FWD_DOWN     K=F      h rows        -         w_down as [E*F,d] cols -             y_perm
+ *                                                  (groups of F rows; col_stride E*F)
+ *   DGRAD_DOWN   K=d      dy_perm rows  -         w_down as [E*F,d] rows -             dg, du (reads bf16 g, u)
+ *   DGRAD_GATE_UP K=2F    dg rows       du rows   w_gate as [E*d,F] rows w_up likewise dx_perm
+ *   WGRAD_DOWN   K=n_e    h cols        -         dy_perm cols           -             dw_down
+ *   WGRAD_GATE_UP K=n_e   x_perm cols   -         dg cols                du cols       dw_gate, dw_up
+ *
+ * Shapes of the bf16 tensors are those of moe_grouped_gemm. d % 256 == 0 and
+ * F % 256 == 0. Weight gradients of experts with no rows are zeros. */
+typedef struct moe_mx_tensor {
+  const void* q;   /* E4M3 codes */
+  const void* s;   /* E8M0 scales */
+} moe_mx_tensor;
+
+typedef struct moe_mx_gg_desc {
+  int op;                        /* moe_gg_op */
+  int E, d, F;
+  int n_rows;                    /* rows of the permuted activations */
+  int col_stride;                /* token stride of the "cols" operands (weight gradients) */
+  const int32_t* group_offsets;  /* [E+1], device */
+  moe_mx_tensor a0, a1, b0, b1;
+  const void* g;                 /* bf16 [n_rows,F], read by DGRAD_DOWN */
+  const void* u;
+  void* out0;
+  void* out1;
+  void* out2;
+} moe_mx_gg_desc;
+
+int moe_grouped_gemm_mx(const moe_mx_gg_desc* desc, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -35,6 +35,19 @@ class moe_gg_desc(C.Structure):
     ]
 
 
+class moe_mx_tensor(C.Structure):
+    _fields_ = [("q", _vp), ("s", _vp)]
+
+
+class moe_mx_gg_desc(C.Structure):
+    _fields_ = [
+        ("op", _i), ("E", _i), ("d", _i), ("F", _i), ("n_rows", _i), ("col_stride", _i),
+        ("group_offsets", _vp),
+        ("a0", moe_mx_tensor), ("a1", moe_mx_tensor), ("b0", moe_mx_tensor), ("b1", moe_mx_tensor),
+        ("g", _vp), ("u", _vp), ("out0", _vp), ("out1", _vp), ("out2", _vp),
+    ]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "moe_status_string": (C.c_char_p, [_i]),
@@ -52,6 +65,9 @@ SIGNATURES = {
     "moe_router_gemm_bwd": (_i, [_i, _vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
     "moe_grouped_gemm_workspace_bytes": (_sz, [C.POINTER(moe_gg_desc)]),
     "moe_grouped_gemm": (_i, [C.POINTER(moe_gg_desc), _vp]),
+    "moe_mx_col_stride": (_i, [_i, _i]),
+    "moe_mx_quantize": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp]),
+    "moe_grouped_gemm_mx": (_i, [C.POINTER(moe_mx_gg_desc), _vp]),
 }
 
 _lib: Optional[C.CDLL] = None
@@ -204,3 +220,38 @@ def moe_grouped_gemm_workspace_bytes(desc: moe_gg_desc) -> int:
 
 def moe_grouped_gemm(desc: moe_gg_desc, stream=None):
     _check(lib().moe_grouped_gemm(C.byref(desc), _stream(stream)), "moe_grouped_gemm")
+
+
+# ----------------------------------------------------------------- MXFP8
+class MxTensor:
+    """E4M3 codes and E8M0 scales of one quantised operand (uint8 tensors)."""
+
+    def __init__(self, q: torch.Tensor, s: torch.Tensor):
+        self.q, self.s = q, s
+
+
+def moe_mx_col_stride(rows: int, n_groups: int) -> int:
+    return lib().moe_mx_col_stride(rows, n_groups)
+
+
+def moe_mx_quantize(src, axis, q, s, group_offsets=None, n_groups=1, col_stride=0, stream=None):
+    rows, cols = src.shape
+    _check(lib().moe_mx_quantize(_p(src), rows, cols, axis, _p(group_offsets), n_groups, col_stride,
+                                 _p(q), _p(s), _stream(stream)), "moe_mx_quantize")
+
+
+def make_mx_gg_desc(op, E, d, F, n_rows, group_offsets, col_stride=0, a0=None, a1=None, b0=None,
+                    b1=None, g=None, u=None, out0=None, out1=None, out2=None) -> moe_mx_gg_desc:
+    desc = moe_mx_gg_desc()
+    desc.op, desc.E, desc.d, desc.F, desc.n_rows, desc.col_stride = op, E, d, F, n_rows, col_stride
+    desc.group_offsets = _p(group_offsets)
+    for name, t in (("a0", a0), ("a1", a1), ("b0", b0), ("b1", b1)):
+        if t is not None:
+            getattr(desc, name).q, getattr(desc, name).s = _p(t.q), _p(t.s)
+    for name, t in (("g", g), ("u", u), ("out0", out0), ("out1", out1), ("out2", out2)):
+        setattr(desc, name, _p(t))
+    return desc
+
+
+def moe_grouped_gemm_mx(desc: moe_mx_gg_desc, stream=None):
+    _check(lib().moe_grouped_gemm_mx(C.byref(desc), _stream(stream)), "moe_grouped_gemm_mx")

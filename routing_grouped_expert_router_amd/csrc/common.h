@@ -85,6 +85,7 @@ MOE_DEV float wave_sum(float v) {
 namespace moe {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 inline bool valid_dtype(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
 inline size_t dtype_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 

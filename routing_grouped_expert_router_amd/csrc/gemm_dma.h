@@ -23,12 +23,11 @@
 // resource whose range ends at the expert's last row.
 #pragma once
 
-#include "gemm_common.h"
+#include "gemm_epilogue.h"
 
 namespace moe {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 dbf16x8_t;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float df32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short ds4_t;
 
 template <int BM_, int BN_, int WM_, int WN_, int BK_, int ST_, int OCC_ = 1> struct DmaCfg {
@@ -107,14 +106,6 @@ MOE_DEV dbf16x8_t read_tr8(const uint16_t* p0, const uint16_t* p1) {
   typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s8_t;
   const s8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(dbf16x8_t, v);
-}
-
-MOE_DEV uint2 dpack4(const float* v) { return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])); }
-MOE_DEV void dunpack4(uint2 p, float* v) {
-  v[0] = __uint_as_float(p.x << 16);
-  v[1] = __uint_as_float(p.x & 0xffff0000u);
-  v[2] = __uint_as_float(p.y << 16);
-  v[3] = __uint_as_float(p.y & 0xffff0000u);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -376,153 +367,7 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_dma_kernel(GGArgs a) {
     }
   }
 
-  // ---- epilogue, staged through LDS so that global traffic is whole
-  // 16-byte row segments. Each 32x32 block holds C^T (B fragment first):
-  // lane (lr, lk) has tile row wm*WMR + mi*32 + lr and, for accumulator group
-  // g, the 4 consecutive columns 8g + 4lk .. +3 of block ni. Output columns
-  // are handled in chunks of CW = 128 (one chunk per matrix for the dual
-  // ops, BN/128 chunks otherwise); a wave's columns lie in one chunk.
-  constexpr int CW = C::CW, LDW = C::LDW;
-  constexpr int NCH = BNO / CW > 0 ? BNO / CW : 1;          // column chunks per matrix
-  constexpr int WCOLS = DUAL ? C::WNR / 2 : C::WNR;          // output columns per wave
-  const int wcol0 = wn * WCOLS;                              // first output column of the wave
-  const int wchunk = wcol0 / CW;
-  uint16_t* stg0 = lds;
-  uint16_t* stg1 = lds + BM * LDW;
-  const int rows_valid = mv;
-
-  // value of accumulator element (mi, ni, g, r): tile row, chunk column
-  auto row_of_acc = [&](int mi) { return wm * C::WMR + mi * 32 + lr; };
-  auto col_of_acc = [&](int ni, int g) { return (wcol0 % CW) + ni * 32 + 8 * g + 4 * lk; };
-
-  // cooperative copy of plane `src` (rows_valid x CW, columns chunk*CW..) to
-  // global rows out + r * ld (+ chunk column offset)
-  auto store_plane = [&](const uint16_t* src, uint16_t* out, size_t ld, int chunk) {
-    constexpr int CPRW = CW / 8;                             // 16-byte chunks per row
-    for (int q = tid; q < rows_valid * CPRW; q += NT) {
-      const int r = q / CPRW, c = q % CPRW;
-      *reinterpret_cast<V16*>(out + (size_t)r * ld + chunk * CW + c * 8) =
-          *reinterpret_cast<const V16*>(src + r * LDW + c * 8);
-    }
-  };
-  auto load_plane = [&](uint16_t* dst, const uint16_t* in, size_t ld, int chunk) {
-    constexpr int CPRW = CW / 8;
-    for (int q = tid; q < rows_valid * CPRW; q += NT) {
-      const int r = q / CPRW, c = q % CPRW;
-      *reinterpret_cast<V16*>(dst + r * LDW + c * 8) =
-          *reinterpret_cast<const V16*>(in + (size_t)r * ld + chunk * CW + c * 8);
-    }
-  };
-  // write 4 values as bf16 at (tile row, chunk column) of a staging plane
-  auto put4 = [&](uint16_t* stg, int row, int col, const float* v) {
-    *reinterpret_cast<uint2*>(stg + row * LDW + col) = dpack4(v);
-  };
-
-  __syncthreads();   // every wave is done with the ring
-
-  // global destinations (row 0 of the tile, column n0)
-  const size_t rbase = KVAR ? (size_t)m0 : (size_t)row0;
-  if (OP == MOE_GG_FWD_GATE_UP || OP == MOE_GG_WGRAD_GATE_UP) {
-    // planes: G|dW_gate -> stg0, U|dW_up -> stg1, then H -> stg0
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NI / 2; ++ni)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float v0[4], v1[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            v0[r] = acc[mi][ni][4 * g + r];
-            v1[r] = acc[mi][ni + NI / 2][4 * g + r];
-          }
-          put4(stg0, row_of_acc(mi), col_of_acc(ni, g), v0);
-          put4(stg1, row_of_acc(mi), col_of_acc(ni, g), v1);
-        }
-    __syncthreads();
-    if (OP == MOE_GG_FWD_GATE_UP) {
-      store_plane(stg0, (uint16_t*)a.g + rbase * F + n0, F, 0);
-      store_plane(stg1, (uint16_t*)a.u + rbase * F + n0, F, 0);
-      __syncthreads();
-      // H from the stored (bf16-rounded) g and u
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI / 2; ++ni)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float hh[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float gg = bf16_to_f32(f32_to_bf16(acc[mi][ni][4 * g + r]));
-              const float uu = bf16_to_f32(f32_to_bf16(acc[mi][ni + NI / 2][4 * g + r]));
-              hh[r] = gg * uu / (1.0f + expf(-gg));
-            }
-            put4(stg0, row_of_acc(mi), col_of_acc(ni, g), hh);
-          }
-      __syncthreads();
-      store_plane(stg0, (uint16_t*)a.h + rbase * F + n0, F, 0);
-    } else {
-      store_plane(stg0, (uint16_t*)a.dw_gate + e * dF + rbase * F + n0, F, 0);
-      store_plane(stg1, (uint16_t*)a.dw_up + e * dF + rbase * F + n0, F, 0);
-    }
-  } else if (OP == MOE_GG_DGRAD_DOWN) {
-    // per column chunk: stage G and U, turn them into dG and dU in place
-    for (int ch = 0; ch < NCH; ++ch) {
-      load_plane(stg0, (const uint16_t*)a.g + rbase * F + n0, F, ch);
-      load_plane(stg1, (const uint16_t*)a.u + rbase * F + n0, F, ch);
-      __syncthreads();
-      if (wchunk == ch) {
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int row = row_of_acc(mi), col = col_of_acc(ni, g);
-              float gf[4], uf[4], dg[4], du[4];
-              dunpack4(*reinterpret_cast<const uint2*>(stg0 + row * LDW + col), gf);
-              dunpack4(*reinterpret_cast<const uint2*>(stg1 + row * LDW + col), uf);
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float dh = acc[mi][ni][4 * g + r];
-                const float sg = 1.0f / (1.0f + expf(-gf[r]));
-                dg[r] = dh * uf[r] * sg * (1.0f + gf[r] * (1.0f - sg));
-                du[r] = dh * gf[r] * sg;
-              }
-              put4(stg0, row, col, dg);
-              put4(stg1, row, col, du);
-            }
-      }
-      __syncthreads();
-      store_plane(stg0, (uint16_t*)a.dg + rbase * F + n0, F, ch);
-      store_plane(stg1, (uint16_t*)a.du + rbase * F + n0, F, ch);
-      __syncthreads();
-    }
-  } else {
-    // single output: chunk 0 -> stg0, chunk 1 -> stg1 (at most two chunks)
-    static_assert(NCH <= 2, "two staging planes");
-    uint16_t* out;
-    size_t ld;
-    if (OP == MOE_GG_FWD_DOWN) { out = (uint16_t*)a.y_perm + rbase * d + n0; ld = d; }
-    else if (OP == MOE_GG_DGRAD_GATE_UP) { out = (uint16_t*)a.dx_perm + rbase * d + n0; ld = d; }
-    else { out = (uint16_t*)a.dw_down + e * dF + rbase * d + n0; ld = d; }
-    uint16_t* mine = wchunk == 0 ? stg0 : stg1;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[mi][ni][4 * g + r];
-          put4(mine, row_of_acc(mi), col_of_acc(ni, g), v);
-        }
-    __syncthreads();
-    store_plane(stg0, out, ld, 0);
-    if (NCH > 1) store_plane(stg1, out, ld, 1);
-  }
+  gg_store_tile<OP, C>(a, acc, lds, e, KVAR ? (size_t)m0 : (size_t)row0, n0, mv, wm, wn, lane, tid);
 }
 
 }  // namespace moe

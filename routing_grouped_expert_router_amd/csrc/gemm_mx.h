@@ -1,0 +1,339 @@
+// MXFP8 grouped expert GEMM on the gfx950 scaled matrix cores.
+//
+// Every operand is E4M3 bytes plus one E8M0 scale byte per 32 values along the
+// GEMM's contraction (K), stored with K contiguous, so each per-expert
+// product is C[m][n] = sum_k A[m][k] B[n][k]. One v_mfma_scale_f32_32x32x64
+// _f8f6f4 takes 64 K values of a 32-row block of each operand together with
+// their scales and accumulates the exact scaled products in binary32.
+//
+// Operand layout of that instruction, for lane l of the wave (row l % 32 of
+// the block, half h = l / 32): bytes 0..15 of its 32-byte operand are K values
+// 16h..16h+15 of the first 32-block and bytes 16..31 are K values
+// 32+16h..32+16h+15 of the second; the scale operand of lane l is the scale
+// of row l % 32 in block h. Both operands use the same layout, so a row's 64
+// bytes of one K step are read from LDS as two 16-byte chunks (h and 2 + h).
+//
+// The load path is the one of the bf16 kernel (gemm_dma.h): a ring of LDS
+// stages filled with buffer_load ... lds. A stage holds 64 K values of the
+// BM A-rows and BN B-rows (rows of 64 bytes, 16-byte chunks XOR-swizzled by
+// (row >> 2) & 3) and one 4-byte word of scales per row: the scales of four
+// 32-blocks, i.e. of this stage and the next (each word is loaded twice, by
+// the two stages that use it, so every stage issues the same loads).
+#pragma once
+
+#include "gemm_dma.h"
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int di32x8_t;
+
+struct MxArgs {
+  GGArgs o;                 // shapes, group offsets, bf16 g/u inputs and the outputs
+  const uint8_t* aq[2];     // A codes / scales (two K phases for DGRAD_GATE_UP)
+  const uint8_t* as[2];
+  const uint8_t* bq[2];     // B codes / scales (gate/up, or the two K phases)
+  const uint8_t* bs[2];
+  int P;                    // token stride of the column-quantised operands
+};
+
+template <int BM_, int BN_, int WM_, int WN_, int ST_, int OCC_> struct MxCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = ST_, OCC = OCC_;
+  static constexpr int BK = 64;                             // K values (bytes) per row per stage
+  static constexpr int NT = WM * WN * 64, NW = WM * WN;
+  static constexpr int WMR = BM / WM, WNR = BN / WN;
+  static constexpr int MI = WMR / 32, NI = WNR / 32;
+  static constexpr int A_PER_WAVE = BM * BK / 1024 / NW;    // 1 KB code wave-loads
+  static constexpr int B_PER_WAVE = BN * BK / 1024 / NW;
+  static constexpr int S_INSTR = (BM + BN) / 64;            // 256-byte scale wave-loads
+  static constexpr int S_PER_WAVE = (S_INSTR + NW - 1) / NW;
+  static constexpr int CODE_BYTES = (BM + BN) * BK;
+  static constexpr int STAGE_BYTES = CODE_BYTES + (BM + BN) * 4;
+  static constexpr int CW = 128, LDW = CW + 8;              // epilogue staging (bf16)
+  static constexpr int STAGING_BYTES = 2 * BM * LDW * 2;
+  static constexpr int RING_BYTES = STAGE_BYTES * STAGES;
+  static constexpr int LDS_BYTES0 = RING_BYTES > STAGING_BYTES ? RING_BYTES : STAGING_BYTES;
+  static constexpr int TS_BYTES = 4 * (MOE_MAX_EXPERTS + 1);
+  static constexpr int LDS_BYTES = LDS_BYTES0 > TS_BYTES ? LDS_BYTES0 : TS_BYTES;
+  static_assert(BM * BK % (1024 * NW) == 0 && BN * BK % (1024 * NW) == 0, "code loads per wave");
+  static_assert(BM % 64 == 0 && BN % 128 == 0, "scale wave-loads stay within one operand and matrix");
+  static_assert(WMR % 32 == 0 && WNR % 64 == 0, "wave tile");
+  static_assert(STAGE_BYTES % 256 == 0, "stage alignment");
+  static_assert(OCC * LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(WNR <= CW && (BN <= CW || BN % CW == 0), "wave columns within one staging chunk");
+  static_assert(STAGES >= 3, "ring depth");
+};
+
+// One 256-byte wave-load: lane l's 4 bytes land at LDS lds_addr + 4 l.
+MOE_DEV void dma4(rsrc_t r, uint32_t lds_addr, uint32_t voff) {
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(r), "{m0}"(lds_addr)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(PER * n) for a runtime n in [0, MAXN].
+template <int PER, int MAXN> MOE_DEV void wait_stages(int n) {
+  if constexpr (MAXN >= 2) {
+    if (n >= 2) { wait_vm<PER * 2>(); return; }
+  }
+  if constexpr (MAXN >= 1) {
+    if (n >= 1) { wait_vm<PER>(); return; }
+  }
+  wait_vm<0>();
+}
+
+template <int OP, class C>
+__global__ void __launch_bounds__(C::NT, C::OCC) gg_mx_kernel(MxArgs x) {
+  using I = OpInfo<OP>;
+  constexpr bool DUAL = I::kDual, KVAR = I::kKVar;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::STAGES, NT = C::NT, NW = C::NW;
+  constexpr int MI = C::MI, NI = C::NI;
+  constexpr int BNO = DUAL ? BN / 2 : BN;          // output columns per matrix per tile
+  static_assert(S - 2 <= 2, "wait_stages covers up to two stages in flight");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
+  int* tile_start = reinterpret_cast<int*>(lds);    // used before the ring, then overwritten
+
+  const GGArgs& a = x.o;
+  const int d = a.d, F = a.F, E = a.E;
+  const int N = op_n(OP, d, F);
+  const int tilesN = N / BNO;
+  const int b = xcd_remap(blockIdx.x, gridDim.x);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int e, row0, mv, K, m0 = 0, tn, p_e = 0;
+  if (!KVAR) {
+    tn = b % tilesN;
+    if (!find_m_tile<BM, NT>(a, b / tilesN, tile_start, e, row0, mv)) return;
+    K = op_k(OP, d, F);
+  } else {
+    const int M = op_wgrad_m(OP, d, F);
+    const int per = (M / BM) * tilesN;
+    e = b / per;
+    m0 = ((b % per) / tilesN) * BM;
+    tn = b % tilesN;
+    group_rows(a, e, row0, K);
+    mv = BM;
+    // first padded token column of expert e: 128 * sum_{h<e} ceil(n_h / 128)
+    int part = 0;
+    for (int h = tid; h < e; h += NT) {
+      int r0, n;
+      group_rows(a, h, r0, n);
+      part += (n + 127) >> 7;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    if (lane == 0) tile_start[wave] = part;
+    __syncthreads();
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += tile_start[w];
+    p_e = 128 * tot;
+  }
+  __syncthreads();   // every wave is past its reads of tile_start before the ring is filled
+  const int n0 = tn * BNO;
+
+  // ---- operands: base pointers (bytes), row strides, ranges
+  const int P = x.P;
+  const uint8_t *qa0, *qa1, *qb0, *qb1, *sa0, *sa1, *sb0, *sb1;
+  uint32_t lda, ldb, na, nb;
+  switch (OP) {
+    case MOE_GG_FWD_GATE_UP:
+      lda = d; ldb = (uint32_t)E * d;
+      qa0 = qa1 = x.aq[0] + (size_t)row0 * d; sa0 = sa1 = x.as[0] + (size_t)row0 * (d / 32);
+      na = (uint32_t)mv * d;
+      qb0 = x.bq[0] + (size_t)e * d; qb1 = x.bq[1] + (size_t)e * d;
+      sb0 = x.bs[0] + (size_t)e * (d / 32); sb1 = x.bs[1] + (size_t)e * (d / 32);
+      nb = (uint32_t)((size_t)F * E * d - (size_t)e * d);
+      break;
+    case MOE_GG_FWD_DOWN:
+      lda = F; ldb = (uint32_t)E * F;
+      qa0 = qa1 = x.aq[0] + (size_t)row0 * F; sa0 = sa1 = x.as[0] + (size_t)row0 * (F / 32);
+      na = (uint32_t)mv * F;
+      qb0 = qb1 = x.bq[0] + (size_t)e * F; sb0 = sb1 = x.bs[0] + (size_t)e * (F / 32);
+      nb = (uint32_t)((size_t)d * E * F - (size_t)e * F);
+      break;
+    case MOE_GG_DGRAD_DOWN:
+      lda = d; ldb = d;
+      qa0 = qa1 = x.aq[0] + (size_t)row0 * d; sa0 = sa1 = x.as[0] + (size_t)row0 * (d / 32);
+      na = (uint32_t)mv * d;
+      qb0 = qb1 = x.bq[0] + (size_t)e * F * d; sb0 = sb1 = x.bs[0] + (size_t)e * F * (d / 32);
+      nb = (uint32_t)F * d;
+      break;
+    case MOE_GG_DGRAD_GATE_UP:
+      lda = F; ldb = F;
+      qa0 = x.aq[0] + (size_t)row0 * F; qa1 = x.aq[1] + (size_t)row0 * F;
+      sa0 = x.as[0] + (size_t)row0 * (F / 32); sa1 = x.as[1] + (size_t)row0 * (F / 32);
+      na = (uint32_t)mv * F;
+      qb0 = x.bq[0] + (size_t)e * d * F; qb1 = x.bq[1] + (size_t)e * d * F;
+      sb0 = x.bs[0] + (size_t)e * d * (F / 32); sb1 = x.bs[1] + (size_t)e * d * (F / 32);
+      nb = (uint32_t)d * F;
+      break;
+    case MOE_GG_WGRAD_DOWN:   // A = H^T [F][P], B = dY^T [d][P]
+      lda = P; ldb = P;
+      qa0 = qa1 = x.aq[0] + p_e; sa0 = sa1 = x.as[0] + p_e / 32;
+      na = p_e < P ? (uint32_t)((size_t)F * P - p_e) : 0;
+      qb0 = qb1 = x.bq[0] + p_e; sb0 = sb1 = x.bs[0] + p_e / 32;
+      nb = p_e < P ? (uint32_t)((size_t)d * P - p_e) : 0;
+      break;
+    default:                  // WGRAD_GATE_UP: A = X^T [d][P], B = dG^T, dU^T [F][P]
+      lda = P; ldb = P;
+      qa0 = qa1 = x.aq[0] + p_e; sa0 = sa1 = x.as[0] + p_e / 32;
+      na = p_e < P ? (uint32_t)((size_t)d * P - p_e) : 0;
+      qb0 = x.bq[0] + p_e; qb1 = x.bq[1] + p_e; sb0 = x.bs[0] + p_e / 32; sb1 = x.bs[1] + p_e / 32;
+      nb = p_e < P ? (uint32_t)((size_t)F * P - p_e) : 0;
+  }
+  const rsrc_t rA0 = make_rsrc(qa0, na), rA1 = make_rsrc(qa1, na);
+  const rsrc_t rB0 = make_rsrc(qb0, nb), rB1 = make_rsrc(qb1, nb);
+  const rsrc_t rSA0 = make_rsrc(sa0, na / 32), rSA1 = make_rsrc(sa1, na / 32);
+  const rsrc_t rSB0 = make_rsrc(sb0, nb / 32), rSB1 = make_rsrc(sb1, nb / 32);
+
+  // ---- per-lane byte offsets at k = 0
+  uint32_t a_off[C::A_PER_WAVE], b_off[C::B_PER_WAVE], s_off[C::S_PER_WAVE];
+  int b_mat[C::B_PER_WAVE], s_kind[C::S_PER_WAVE], s_slot[C::S_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::A_PER_WAVE; ++i) {
+    const int q = (wave * C::A_PER_WAVE + i) * 64 + lane;      // 16-byte chunk of the A stage tile
+    const int row = q >> 2, c = (q & 3) ^ swz_k(row);
+    a_off[i] = (uint32_t)(m0 + row) * lda + c * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < C::B_PER_WAVE; ++i) {
+    const int q = (wave * C::B_PER_WAVE + i) * 64 + lane;
+    const int row = q >> 2, c = (q & 3) ^ swz_k(row);
+    // a 1 KB wave-load covers 16 rows, so the matrix is wave-uniform
+    const int sub = DUAL ? ((wave * C::B_PER_WAVE + i) * 16) / (BN / 2) : 0;
+    b_mat[i] = sub;
+    b_off[i] = (uint32_t)(n0 + row - sub * (BN / 2)) * ldb + c * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < C::S_PER_WAVE; ++i) {
+    int j = wave * C::S_PER_WAVE + i;
+    if (j >= C::S_INSTR) j -= C::S_INSTR;   // spare loads repeat one of the others (same bytes, same place)
+    s_slot[i] = j;
+    const int srow = 64 * j + lane;         // rows: A 0..BM-1, then B
+    if (64 * j < BM) {
+      s_kind[i] = 0;
+      s_off[i] = (uint32_t)(m0 + srow) * (lda / 32);
+    } else {
+      const int rb = srow - BM;
+      const int sub = DUAL ? (64 * j - BM) / (BN / 2) : 0;
+      s_kind[i] = 1 + sub;
+      s_off[i] = (uint32_t)(n0 + rb - sub * (BN / 2)) * (ldb / 32);
+    }
+  }
+
+  const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr_of(lds));
+  // Resources are picked by branching on wave-uniform conditions rather than
+  // by selecting between them, so that each load names one SGPR quad.
+  auto issue_phase = [&](uint32_t sa, int ks, const rsrc_t& ra, const rsrc_t& rb, const rsrc_t& rsa,
+                         const rsrc_t& rsb) {
+    const uint32_t sb = sa + BM * BK;
+    const uint32_t ss = sa + C::CODE_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::A_PER_WAVE; ++i)
+      dma16(ra, sa + (wave * C::A_PER_WAVE + i) * 1024, a_off[i] + (uint32_t)ks * BK);
+#pragma unroll
+    for (int i = 0; i < C::B_PER_WAVE; ++i) {
+      const uint32_t dst = sb + (wave * C::B_PER_WAVE + i) * 1024, off = b_off[i] + (uint32_t)ks * BK;
+      if (DUAL && b_mat[i] != 0) dma16(rB1, dst, off);
+      else dma16(rb, dst, off);
+    }
+#pragma unroll
+    for (int i = 0; i < C::S_PER_WAVE; ++i) {
+      const uint32_t dst = ss + s_slot[i] * 256, off = s_off[i] + (uint32_t)(ks >> 1) * 4;
+      if (s_kind[i] == 0) dma4(rsa, dst, off);
+      else if (DUAL && s_kind[i] == 2) dma4(rSB1, dst, off);
+      else dma4(rsb, dst, off);
+    }
+  };
+  auto issue = [&](int kt, int slot) {
+    const uint32_t sa = lds_base + (uint32_t)slot * C::STAGE_BYTES;
+    if (OP == MOE_GG_DGRAD_GATE_UP) {
+      const int half = F / BK;
+      if (kt >= half) issue_phase(sa, kt - half, rA1, rB1, rSA1, rSB1);
+      else issue_phase(sa, kt, rA0, rB0, rSA0, rSB0);
+    } else {
+      issue_phase(sa, kt, rA0, rB0, rSA0, rSB0);
+    }
+  };
+
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int lr = lane & 31, lk = lane >> 5;
+  const bool active = wm * C::WMR < mv;
+
+  df32x16_t acc[MI][NI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // fragments and scale words of stage kt (ring slot `slot`)
+  auto read_frags = [&](int slot, int kt, di32x8_t (&af)[MI], di32x8_t (&bfr)[NI], int (&sa)[MI], int (&sb)[NI]) {
+    const uint8_t* st = lds + slot * C::STAGE_BYTES;
+    const uint32_t* sw = reinterpret_cast<const uint32_t*>(st + C::CODE_BYTES);
+    const int sh = 8 * (2 * (kt & 1) + lk);
+    auto frag = [&](const uint8_t* base, int row) {
+      const uint4 lo = *reinterpret_cast<const uint4*>(base + row * BK + ((lk ^ swz_k(row)) << 4));
+      const uint4 hi = *reinterpret_cast<const uint4*>(base + row * BK + (((2 + lk) ^ swz_k(row)) << 4));
+      const di32x8_t v = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      return v;
+    };
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = wm * C::WMR + mi * 32 + lr;
+      af[mi] = frag(st, row);
+      sa[mi] = (int)(sw[row] >> sh);
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      int row;
+      if (DUAL) row = (ni >= NI / 2 ? BN / 2 : 0) + wn * (C::WNR / 2) + (ni % (NI / 2)) * 32 + lr;
+      else row = wn * C::WNR + ni * 32 + lr;
+      bfr[ni] = frag(st + BM * BK, row);
+      sb[ni] = (int)(sw[BM + row] >> sh);
+    }
+  };
+  auto mfmas = [&](const di32x8_t (&af)[MI], const di32x8_t (&bfr)[NI], const int (&sa)[MI], const int (&sb)[NI]) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0,
+                                                                     sb[ni], 0, sa[mi]);
+  };
+
+  // ---- K loop: one MFMA depth per stage. At step kt every wave waits for
+  // stage kt, meets the others at one barrier, refills the slot of stage
+  // kt-1 (read and consumed by every wave before this barrier) with stage
+  // kt+S-1, then reads stage kt's fragments and runs its MFMAs; the other
+  // workgroup on the CU covers the fragment reads. Loads get S-1 steps to land.
+  constexpr int PER_STAGE = C::A_PER_WAVE + C::B_PER_WAVE + C::S_PER_WAVE;
+  int nk = (K + BK - 1) / BK;
+  // an expert's token columns end inside the col_stride P (always so for
+  // group offsets that keep the documented contract)
+  if (KVAR) nk = p_e >= P ? 0 : min(nk, (P - p_e) / BK);
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // stages issued so far end at min(kt + S - 2, nk - 1); stage kt must be complete
+    wait_stages<PER_STAGE, S - 2>(min(kt + S - 2, nk - 1) - kt);
+    __syncthreads();
+    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+    if (active) {
+      di32x8_t af[MI], bfr[NI];
+      int saw[MI], sbw[NI];
+      read_frags(kt % S, kt, af, bfr, saw, sbw);
+      mfmas(af, bfr, saw, sbw);
+    }
+  }
+
+  gg_store_tile<OP, C>(a, acc, reinterpret_cast<uint16_t*>(lds), e, KVAR ? (size_t)m0 : (size_t)row0, n0, mv,
+                       wm, wn, lane, tid);
+}
+
+}  // namespace moe

@@ -1,0 +1,131 @@
+"""The experts of one MoE layer in MXFP8 on one GPU: buffers plus the call
+sequence of the C ABI (quantise, then the scaled-MFMA grouped GEMM).
+
+The pages credit MXFP8 for most of the feed-forward speed-up (bigchange.ai
+pt-BR, "Três números, três denominadores"). Every GEMM operand is quantised
+along that GEMM's contraction: token rows along d or F for the forward and
+data-gradient GEMMs, token columns (blocks restarting at each expert's first
+row) for the weight gradients, and each weight in the orientation its GEMM
+reads. Outputs, and the SwiGLU in between, stay bf16.
+
+The rows arrive grouped by expert (x_perm with group offsets on the device),
+as in the pages' expert-parallel microbenchmark; routing, permute and combine
+are the bf16 layer's and are not repeated here.
+"""
+from __future__ import annotations
+
+from typing import Dict
+
+import torch
+
+from . import _lib as L
+
+
+class _Q:
+    """Codes and scales of one quantised operand."""
+
+    def __init__(self, rows: int, cols: int, dev):
+        self.q = torch.empty(rows, cols, dtype=torch.uint8, device=dev)
+        self.s = torch.empty(rows, cols // 32, dtype=torch.uint8, device=dev)
+        self.t = L.MxTensor(self.q, self.s)
+
+
+class MxExperts:
+    def __init__(self, n_rows: int, d: int, E: int, F: int, device: str = "cuda"):
+        if d % 256 or F % 256:
+            raise ValueError("d and F must be multiples of 256")
+        self.n, self.d, self.E, self.F = n_rows, d, E, F
+        dev = torch.device(device)
+        bf = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device=dev)
+        n = n_rows
+        self.P = L.moe_mx_col_stride(n, E)
+        # forward operands
+        self.xq = _Q(n, d, dev)              # x_perm rows, blocks along d
+        self.wg_c = _Q(F, E * d, dev)        # W_gate columns: [F][E*d], blocks along d
+        self.wu_c = _Q(F, E * d, dev)
+        self.hq = _Q(n, F, dev)              # H rows
+        self.wd_c = _Q(d, E * F, dev)        # W_down columns: [d][E*F], blocks along F
+        # data-gradient operands
+        self.dyq = _Q(n, d, dev)
+        self.wd_r = _Q(E * F, d, dev)        # W_down rows, blocks along d
+        self.dgq, self.duq = _Q(n, F, dev), _Q(n, F, dev)
+        self.wg_r, self.wu_r = _Q(E * d, F, dev), _Q(E * d, F, dev)
+        # weight-gradient operands: token columns, blocks along each expert's rows
+        self.x_c = _Q(d, self.P, dev)
+        self.h_c = _Q(F, self.P, dev)
+        self.dy_c = _Q(d, self.P, dev)
+        self.dg_c, self.du_c = _Q(F, self.P, dev), _Q(F, self.P, dev)
+        # bf16 results
+        self.g, self.u, self.h = bf(n, F), bf(n, F), bf(n, F)
+        self.y_perm = bf(n, d)
+        self.dg, self.du = bf(n, F), bf(n, F)
+        self.dx_perm = bf(n, d)
+        self.dw_gate, self.dw_up, self.dw_down = bf(E, d, F), bf(E, d, F), bf(E, F, d)
+        self.hook = None
+
+    def _mark(self, name: str):
+        if self.hook is not None:
+            self.hook(name)
+
+    def _gg(self, op, **kw):
+        desc = L.make_mx_gg_desc(op, self.E, self.d, self.F, self.n, self.offsets, self.P, **kw)
+        L.moe_grouped_gemm_mx(desc)
+
+    # ------------------------------------------------------------------ steps
+    def quantize_weights(self, w_gate, w_up, w_down):
+        """Both orientations of each weight (they change every optimiser step)."""
+        E, d, F = self.E, self.d, self.F
+        wg, wu, wd = w_gate.view(E * d, F), w_up.view(E * d, F), w_down.view(E * F, d)
+        L.moe_mx_quantize(wg, 1, self.wg_c.q, self.wg_c.s, None, E, E * d)
+        L.moe_mx_quantize(wu, 1, self.wu_c.q, self.wu_c.s, None, E, E * d)
+        L.moe_mx_quantize(wd, 1, self.wd_c.q, self.wd_c.s, None, E, E * F)
+        L.moe_mx_quantize(wd, 0, self.wd_r.q, self.wd_r.s)
+        L.moe_mx_quantize(wg, 0, self.wg_r.q, self.wg_r.s)
+        L.moe_mx_quantize(wu, 0, self.wu_r.q, self.wu_r.s)
+        self._mark("mx_quantize_weights")
+
+    def forward(self, x_perm, offsets, w_gate, w_up, w_down):
+        self.x_perm, self.offsets = x_perm, offsets
+        self.quantize_weights(w_gate, w_up, w_down)
+        L.moe_mx_quantize(x_perm, 0, self.xq.q, self.xq.s)
+        self._mark("mx_quantize_x")
+        self._gg(L.MOE_GG_FWD_GATE_UP, a0=self.xq.t, b0=self.wg_c.t, b1=self.wu_c.t,
+                 out0=self.g, out1=self.u, out2=self.h)
+        self._mark("mx_fwd_gate_up")
+        L.moe_mx_quantize(self.h, 0, self.hq.q, self.hq.s)
+        self._mark("mx_quantize_h")
+        self._gg(L.MOE_GG_FWD_DOWN, a0=self.hq.t, b0=self.wd_c.t, out0=self.y_perm)
+        self._mark("mx_fwd_down")
+        return self.y_perm
+
+    def backward(self, dy_perm):
+        E, off, P = self.E, self.offsets, self.P
+        L.moe_mx_quantize(dy_perm, 0, self.dyq.q, self.dyq.s)
+        L.moe_mx_quantize(dy_perm, 1, self.dy_c.q, self.dy_c.s, off, E, P)
+        self._mark("mx_quantize_dy")
+        self._gg(L.MOE_GG_DGRAD_DOWN, a0=self.dyq.t, b0=self.wd_r.t, g=self.g, u=self.u,
+                 out0=self.dg, out1=self.du)
+        self._mark("mx_dgrad_down")
+        L.moe_mx_quantize(self.h, 1, self.h_c.q, self.h_c.s, off, E, P)
+        self._mark("mx_quantize_h_cols")
+        self._gg(L.MOE_GG_WGRAD_DOWN, a0=self.h_c.t, b0=self.dy_c.t, out0=self.dw_down)
+        self._mark("mx_wgrad_down")
+        L.moe_mx_quantize(self.dg, 0, self.dgq.q, self.dgq.s)
+        L.moe_mx_quantize(self.du, 0, self.duq.q, self.duq.s)
+        L.moe_mx_quantize(self.dg, 1, self.dg_c.q, self.dg_c.s, off, E, P)
+        L.moe_mx_quantize(self.du, 1, self.du_c.q, self.du_c.s, off, E, P)
+        self._mark("mx_quantize_dg_du")
+        self._gg(L.MOE_GG_DGRAD_GATE_UP, a0=self.dgq.t, a1=self.duq.t, b0=self.wg_r.t, b1=self.wu_r.t,
+                 out0=self.dx_perm)
+        self._mark("mx_dgrad_gate_up")
+        L.moe_mx_quantize(self.x_perm, 1, self.x_c.q, self.x_c.s, off, E, P)
+        self._mark("mx_quantize_x_cols")
+        self._gg(L.MOE_GG_WGRAD_GATE_UP, a0=self.x_c.t, b0=self.dg_c.t, b1=self.du_c.t,
+                 out0=self.dw_gate, out1=self.dw_up)
+        self._mark("mx_wgrad_gate_up")
+        return self.dx_perm
+
+    def outputs(self) -> Dict[str, torch.Tensor]:
+        return dict(G=self.g, U=self.u, H=self.h, y_perm=self.y_perm, dG=self.dg, dU=self.du,
+                    dx_perm=self.dx_perm, dw_gate=self.dw_gate, dw_up=self.dw_up,
+                    dw_down=self.dw_down)

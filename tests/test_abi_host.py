@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 def test_binding_covers_every_declared_symbol():
     assert sorted(L.SIGNATURES) == declared()
     lib = L.lib()
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(-3) == b"workspace missing or too small"
     assert lib.moe_status_string(12345) == b"unknown status"
@@ -48,6 +48,10 @@ def test_binding_covers_every_declared_symbol():
 def test_desc_layout_matches_header():
     # int op..capacity (7), pointer group_offsets, 15 tensor pointers, ws, ws_bytes
     assert C.sizeof(L.moe_gg_desc) == 7 * 4 + 4 + 8 * 17 + 8
+    # int op..col_stride (6), group_offsets, 4 (codes, scales) pairs, g, u, 3 outputs
+    assert C.sizeof(L.moe_mx_tensor) == 16
+    assert C.sizeof(L.moe_mx_gg_desc) == 6 * 4 + 8 + 4 * 16 + 5 * 8
+    assert L.moe_mx_gg_desc.a0.offset == 32 and L.moe_mx_gg_desc.g.offset == 96
 
 
 FAKE = 0x1000   # 16-byte aligned, never dereferenced: every call below fails its checks first
@@ -124,3 +128,52 @@ def test_grouped_gemm_argument_errors():
     d.capacity = 16
     assert call(d) == INVALID
     assert lib.moe_grouped_gemm(None, None) == INVALID
+
+
+def test_mx_quantize_argument_errors():
+    lib = L.lib()
+    q = lambda *a: lib.moe_mx_quantize(*a, None)
+    # axis 0: cols % 32, no groups, no stride
+    assert q(FAKE, 8, 48, 0, None, 1, 0, FAKE, FAKE) == INVALID
+    assert q(FAKE, 8, 64, 0, FAKE, 1, 0, FAKE, FAKE) == INVALID
+    assert q(FAKE, 8, 64, 0, None, 1, 128, FAKE, FAKE) == INVALID
+    assert q(FAKE, 8, 64, 2, None, 1, 0, FAKE, FAKE) == INVALID
+    assert q(FAKE + 2, 8, 64, 0, None, 1, 0, FAKE, FAKE) == INVALID
+    assert q(FAKE, 0, 64, 0, None, 1, 0, None, None) == 0            # nothing to do
+    # axis 1: stride bound with device offsets, equal groups
+    assert lib.moe_mx_col_stride(1000, 4) == 128 * (8 + 4)
+    assert q(FAKE, 1000, 64, 1, FAKE, 4, 128 * 11, FAKE, FAKE) == INVALID
+    assert q(FAKE, 1000, 64, 1, FAKE, 4, 128 * 12 + 64, FAKE, FAKE) == INVALID
+    assert q(FAKE, 1000, 96, 1, FAKE, 4, 128 * 12, FAKE, FAKE) == INVALID   # cols % 64
+    assert q(FAKE, 1024, 64, 1, None, 4, 896, FAKE, FAKE) == INVALID         # 4 groups of 256 need 1024
+    assert q(FAKE, 1000, 64, 1, None, 3, 1152, FAKE, FAKE) == INVALID        # rows % groups
+    assert q(FAKE, 1000, 64, 1, FAKE, 2000, 128 * 2010, FAKE, FAKE) == UNSUPPORTED
+
+
+def test_mx_gemm_argument_errors():
+    lib = L.lib()
+    call = lambda d: lib.moe_grouped_gemm_mx(C.byref(d), None)
+    t = L.MxTensor(None, None)
+
+    def mk(**kw):
+        d = L.make_mx_gg_desc(**{**dict(op=L.MOE_GG_FWD_DOWN, E=4, d=256, F=256, n_rows=64,
+                                        group_offsets=None), **kw})
+        return d
+    d = mk()
+    assert call(d) == INVALID                            # no offsets
+    d.group_offsets = FAKE
+    assert call(d) == INVALID                            # operands missing
+    d.a0.q, d.a0.s, d.b0.q, d.b0.s, d.out0 = FAKE, FAKE, FAKE, FAKE, FAKE
+    d.a0.s = FAKE + 2                                    # scales must be 4-byte aligned
+    assert call(d) == INVALID
+    d.a0.s = FAKE
+    d.d = 384                                            # d % 256
+    assert call(d) == UNSUPPORTED
+    d.d, d.op = 256, L.MOE_GG_WGRAD_DOWN
+    d.col_stride = 128 * 4                               # below 128 * (ceil(64/128) + E)
+    assert call(d) == INVALID
+    d.col_stride = 128 * 5 + 64
+    assert call(d) == INVALID
+    d.op = 9
+    assert call(d) == INVALID
+    assert lib.moe_grouped_gemm_mx(None, None) == INVALID
