@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_MXFP8_TFLOPS = 5033.2   # MI355X dense fp8 / MXFP8 MFMA
 
 METRIC = "MoE layer fwd+bwd tokens/s at E=128 top-4 d=2048; grouped-GEMM % MFMA peak"
 
@@ -129,6 +130,116 @@ def cpu_baseline(wl, inp, budget_s):
                       f"{cores} host cores visible)"}
 
 
+def timed(obj, step, steps, warmup):
+    """Run `warmup` untimed steps, then time exactly `steps` steps between two
+    events on the stream the kernels run on (torch's current stream), with a
+    synchronisation on both sides. obj.hook records one event after each
+    stage, so stage times come from the same run. Returns (ms per step,
+    {stage: mean ms}, wall seconds of the timed region)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    marks = []
+
+    def hook(name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        marks.append((name, ev))
+
+    obj.hook = hook
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        hook("_step")
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    obj.hook = None
+    stage_ms = {}
+    for (_, ea), (b, eb) in zip(marks[:-1], marks[1:]):
+        if b == "_step":
+            continue
+        stage_ms.setdefault(b, []).append(ea.elapsed_time(eb))
+    return (start.elapsed_time(end) / steps, {n: sum(v) / len(v) for n, v in stage_ms.items()}, wall)
+
+
+def experts_leg(steps, warmup):
+    """The MXFP8 expert layer on its own workload (32 experts, d = 4096,
+    d_ff = 2048, 32768 rows arriving grouped by expert with Zipf(0.8) counts:
+    the pages' expert-parallel microbenchmark shape), timed next to the bf16
+    grouped GEMMs on the same rows. A step is every weight quantised in both
+    orientations, the forward and the backward of the experts. Inputs are drawn
+    on the device from a seeded generator (normal rows, weights scaled by
+    fan-in) so that the leg adds seconds, not minutes, to a run."""
+    import numpy as np
+    import torch
+    from moe_inputs import workload
+    from moe_inputs.generators import pregrouped_counts
+    from routing_grouped_expert_router_amd.layer import MoELayer
+    from routing_grouped_expert_router_amd.mx_layer import MxExperts
+
+    wl = workload("e32_mxfp8_share")
+    n, d, E, F = wl.T, wl.d, wl.E, wl.F
+    counts = pregrouped_counts(wl.seed, n, E, wl.zipf_s)
+    off = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).cuda()
+    gen = torch.Generator(device="cuda").manual_seed(wl.seed)
+    rnd = lambda *shape, scale=1.0: (torch.randn(*shape, generator=gen, device="cuda") * scale).to(torch.bfloat16)
+    x, dy = rnd(n, d), rnd(n, d)
+    wg, wu, wd = rnd(E, d, F, scale=d ** -0.5), rnd(E, d, F, scale=d ** -0.5), rnd(E, F, d, scale=F ** -0.5)
+    flops = 18.0 * n * d * F
+
+    mx = MxExperts(n, d, E, F)
+
+    def mx_step():
+        mx.forward(x, off, wg, wu, wd)
+        mx.backward(dy)
+
+    ms_mx, st_mx, _ = timed(mx, mx_step, steps, warmup)
+    gemm_mx = sum(v for k, v in st_mx.items() if not k.startswith("mx_quantize"))
+    del mx
+    torch.cuda.empty_cache()
+
+    bf = MoELayer(n, d, E, 1, F, torch.bfloat16, routing="given")
+    bf.x_perm, bf.offsets, bf.dy_perm = x, off, dy
+    bf.w_gate, bf.w_up, bf.w_down = wg, wu, wd
+
+    def bf_step():
+        bf.experts_forward()
+        bf.experts_backward()
+
+    ms_bf, st_bf, _ = timed(bf, bf_step, steps, warmup)
+    del bf
+    torch.cuda.empty_cache()
+    dom = max((k for k in st_mx if not k.startswith("mx_quantize")), key=st_mx.get)
+    dom_flops = {"mx_fwd_gate_up": 4, "mx_fwd_down": 2, "mx_dgrad_down": 2, "mx_dgrad_gate_up": 4,
+                 "mx_wgrad_down": 2, "mx_wgrad_gate_up": 4}[dom] * n * d * F
+    return {
+        "workload": wl.name,
+        "config": {"rows": n, "d_model": d, "experts": E, "d_ff": F, "counts_min": int(counts.min()),
+                   "counts_max": int(counts.max())},
+        "mxfp8_tokens_per_s": round(n / (ms_mx / 1e3), 1),
+        "mxfp8_ms_per_step": round(ms_mx, 4),
+        "bf16_tokens_per_s": round(n / (ms_bf / 1e3), 1),
+        "bf16_ms_per_step": round(ms_bf, 4),
+        "mxfp8_speedup": round(ms_bf / ms_mx, 3),
+        "mxfp8_gemm_tflops": round(flops / (gemm_mx / 1e3) / 1e12, 1),
+        "mxfp8_gemm_frac_peak": round(flops / (gemm_mx / 1e3) / 1e12 / PEAK_MXFP8_TFLOPS, 4),
+        "mxfp8_quantize_ms": round(ms_mx - gemm_mx, 4),
+        "roofline": {"bound": "mfma", "kernel": dom, "avg_launch_us": round(st_mx[dom] * 1e3, 1),
+                     "achieved": round(dom_flops / (st_mx[dom] / 1e3) / 1e12, 1),
+                     "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom_flops / (st_mx[dom] / 1e3) / 1e12 / PEAK_MXFP8_TFLOPS, 4)},
+        "stages_mxfp8_us": {k: round(v * 1e3, 1) for k, v in st_mx.items()},
+        "stages_bf16_us": {k: round(v * 1e3, 1) for k, v in st_bf.items()},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +249,7 @@ def main():
     ap.add_argument("--capacity-factor", type=float, default=0.0,
                     help="> 0: run the padded-to-capacity path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mxfp8", action="store_true", help="skip the MXFP8 expert-layer leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the reference "
@@ -191,42 +303,7 @@ def main():
                       topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
         layer.backward(t["dy"])
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log("warmup done")
-
-    # timed region: K steps, bracketed by synchronisation; per-stage events are
-    # recorded on the stream the kernels run on (torch's current stream)
-    stream = torch.cuda.current_stream()
-    marks = []
-
-    def hook(name):
-        ev = torch.cuda.Event(enable_timing=True)
-        ev.record(stream)
-        marks.append((name, ev))
-
-    layer.hook = hook
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        hook("_step")
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    layer.hook = None
-    ms = start.elapsed_time(end) / args.steps
-
-    stage_ms = {}
-    for (a, ea), (b, eb) in zip(marks[:-1], marks[1:]):
-        if b == "_step":
-            continue
-        stage_ms.setdefault(b, []).append(ea.elapsed_time(eb))
-    stage_avg = {n: sum(v) / len(v) for n, v in stage_ms.items()}
+    ms, stage_avg, wall = timed(layer, step, args.steps, args.warmup)
     n_rows = layer.n_rows
     R = wl.T * wl.k
     gemm_ms = sum(v for n, v in stage_avg.items() if n.startswith("gg_"))
@@ -279,6 +356,9 @@ def main():
         "wall_s_timed": round(wall, 3),
         "kernel_sources": kernel_source_hash(),
     }
+    if not args.no_mxfp8:
+        log("MXFP8 expert-layer leg ...")
+        out["mxfp8_experts"] = experts_leg(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host for the CPU baseline ...")
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)

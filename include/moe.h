@@ -245,22 +245,29 @@ int moe_grouped_gemm(const moe_gg_desc* desc, hipStream_t stream);
  * Code 0xFF (NaN) is never written.
  *
  * moe_mx_quantize: bf16 src [rows, cols] -> E4M3 codes + E8M0 scales.
- *   axis 0: blocks along each row. q [rows, cols], s [rows, cols/32];
- *           cols % 32 == 0; group_offsets must be NULL and col_stride 0.
- *   axis 1: blocks along the rows of each group, written transposed: group g
- *           (rows [group_offsets[g], group_offsets[g+1]) of src; when
- *           group_offsets is NULL, n_groups equal groups of rows/n_groups
- *           rows) becomes columns [p_g, p_g + ceil(n_g/128)*128) of
- *           q [cols, col_stride] and of s [cols, col_stride/32], with
- *           p_g = 128 * sum_{h<g} ceil(n_h/128). Blocks restart at each
- *           group's first row; the columns past a group's last row are
- *           written as zero codes with scale code 0. Columns past the last
- *           group's segment are not written. col_stride must be a multiple of
- *           128 and at least moe_mx_col_stride(rows, n_groups) when the
- *           offsets are on the device (a bound that holds whatever the group
- *           sizes), or n_groups * ceil(rows/n_groups/128)*128 for equal
- *           groups (rows % n_groups == 0).
- *   src 16-byte aligned, cols % 64 == 0 for axis 1. rows may be 0. */
+ * The quantised operand is a matrix of R rows whose K values (the GEMM's
+ * contraction) run along each row: codes q [R, K], one byte per value, and
+ * scales in groups of four: the scale of block b (values 32b..32b+31) of
+ * row r is byte 4 * (R * (b / 4) + r) + b % 4 of s (R * K / 32 bytes). So
+ * the four scales of 128 consecutive values of a row share one 4-byte word,
+ * and the words of one 128-value column group are contiguous over the rows,
+ * which lets a GEMM fetch the scales of many rows with one contiguous load.
+ *   axis 0: blocks along each row: R = rows, K = cols; cols % 128 == 0;
+ *           group_offsets must be NULL and col_stride 0.
+ *   axis 1: blocks along the rows of each group, written transposed:
+ *           R = cols, K = col_stride. Group g (rows [group_offsets[g],
+ *           group_offsets[g+1]) of src; when group_offsets is NULL, n_groups
+ *           equal groups of rows/n_groups rows) becomes K columns
+ *           [p_g, p_g + ceil(n_g/128)*128) with p_g = 128 * sum_{h<g}
+ *           ceil(n_h/128). Blocks restart at each group's first row; the
+ *           columns past a group's last row are written as zero codes with
+ *           scale code 0. Columns past the last group's segment are not
+ *           written. col_stride must be a multiple of 128 and at least
+ *           moe_mx_col_stride(rows, n_groups) when the offsets are on the
+ *           device (a bound that holds whatever the group sizes), or
+ *           n_groups * ceil(rows/n_groups/128)*128 for equal groups
+ *           (rows % n_groups == 0); cols % 64 == 0.
+ *   src and q 16-byte aligned, s 4-byte aligned. rows may be 0. */
 int moe_mx_col_stride(int rows, int n_groups);
 int moe_mx_quantize(const void* src, int rows, int cols, int axis, const int32_t* group_offsets,
                     int n_groups, int col_stride, void* q, void* s, hipStream_t stream);

@@ -18,7 +18,9 @@
 // BM A-rows and BN B-rows (rows of 64 bytes, 16-byte chunks XOR-swizzled by
 // (row >> 2) & 3) and one 4-byte word of scales per row: the scales of four
 // 32-blocks, i.e. of this stage and the next (each word is loaded twice, by
-// the two stages that use it, so every stage issues the same loads).
+// the two stages that use it, so every stage issues the same loads). The
+// quantiser stores scale words of one 128-value column group contiguously
+// over rows, so the words of 64 consecutive rows are one 256-byte load.
 #pragma once
 
 #include "gemm_dma.h"
@@ -134,64 +136,68 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_mx_kernel(MxArgs x) {
   __syncthreads();   // every wave is past its reads of tile_start before the ring is filled
   const int n0 = tn * BNO;
 
-  // ---- operands: base pointers (bytes), row strides, ranges
+  // ---- operands. Codes: base pointer of this expert's block (bytes), row
+  // stride, range. Scales (grouped layout: the word of rows r, 128-value
+  // column group c is at 4 * (R * c + r)): the whole buffer, its row count R,
+  // the first column group g0 of this expert's K range, and the row of tile
+  // row 0 (A: m, B: n before the dual split).
   const int P = x.P;
-  const uint8_t *qa0, *qa1, *qb0, *qb1, *sa0, *sa1, *sb0, *sb1;
+  const uint8_t *qa0, *qa1, *qb0, *qb1;
   uint32_t lda, ldb, na, nb;
+  int sRa, sRb, g0a = 0, g0b = 0, rba, rbb;
+  uint32_t sna, snb;
   switch (OP) {
     case MOE_GG_FWD_GATE_UP:
       lda = d; ldb = (uint32_t)E * d;
-      qa0 = qa1 = x.aq[0] + (size_t)row0 * d; sa0 = sa1 = x.as[0] + (size_t)row0 * (d / 32);
-      na = (uint32_t)mv * d;
+      qa0 = qa1 = x.aq[0] + (size_t)row0 * d; na = (uint32_t)mv * d;
       qb0 = x.bq[0] + (size_t)e * d; qb1 = x.bq[1] + (size_t)e * d;
-      sb0 = x.bs[0] + (size_t)e * (d / 32); sb1 = x.bs[1] + (size_t)e * (d / 32);
       nb = (uint32_t)((size_t)F * E * d - (size_t)e * d);
+      sRa = a.n_rows; rba = row0; sna = (uint32_t)a.n_rows * (d / 32);
+      sRb = F; g0b = e * d / 128; rbb = n0; snb = (uint32_t)F * (E * d / 32);
       break;
     case MOE_GG_FWD_DOWN:
       lda = F; ldb = (uint32_t)E * F;
-      qa0 = qa1 = x.aq[0] + (size_t)row0 * F; sa0 = sa1 = x.as[0] + (size_t)row0 * (F / 32);
-      na = (uint32_t)mv * F;
-      qb0 = qb1 = x.bq[0] + (size_t)e * F; sb0 = sb1 = x.bs[0] + (size_t)e * (F / 32);
-      nb = (uint32_t)((size_t)d * E * F - (size_t)e * F);
+      qa0 = qa1 = x.aq[0] + (size_t)row0 * F; na = (uint32_t)mv * F;
+      qb0 = qb1 = x.bq[0] + (size_t)e * F; nb = (uint32_t)((size_t)d * E * F - (size_t)e * F);
+      sRa = a.n_rows; rba = row0; sna = (uint32_t)a.n_rows * (F / 32);
+      sRb = d; g0b = e * F / 128; rbb = n0; snb = (uint32_t)d * (E * F / 32);
       break;
     case MOE_GG_DGRAD_DOWN:
       lda = d; ldb = d;
-      qa0 = qa1 = x.aq[0] + (size_t)row0 * d; sa0 = sa1 = x.as[0] + (size_t)row0 * (d / 32);
-      na = (uint32_t)mv * d;
-      qb0 = qb1 = x.bq[0] + (size_t)e * F * d; sb0 = sb1 = x.bs[0] + (size_t)e * F * (d / 32);
-      nb = (uint32_t)F * d;
+      qa0 = qa1 = x.aq[0] + (size_t)row0 * d; na = (uint32_t)mv * d;
+      qb0 = qb1 = x.bq[0] + (size_t)e * F * d; nb = (uint32_t)F * d;
+      sRa = a.n_rows; rba = row0; sna = (uint32_t)a.n_rows * (d / 32);
+      sRb = E * F; rbb = e * F + n0; snb = (uint32_t)E * F * (d / 32);
       break;
     case MOE_GG_DGRAD_GATE_UP:
       lda = F; ldb = F;
-      qa0 = x.aq[0] + (size_t)row0 * F; qa1 = x.aq[1] + (size_t)row0 * F;
-      sa0 = x.as[0] + (size_t)row0 * (F / 32); sa1 = x.as[1] + (size_t)row0 * (F / 32);
-      na = (uint32_t)mv * F;
-      qb0 = x.bq[0] + (size_t)e * d * F; qb1 = x.bq[1] + (size_t)e * d * F;
-      sb0 = x.bs[0] + (size_t)e * d * (F / 32); sb1 = x.bs[1] + (size_t)e * d * (F / 32);
-      nb = (uint32_t)d * F;
+      qa0 = x.aq[0] + (size_t)row0 * F; qa1 = x.aq[1] + (size_t)row0 * F; na = (uint32_t)mv * F;
+      qb0 = x.bq[0] + (size_t)e * d * F; qb1 = x.bq[1] + (size_t)e * d * F; nb = (uint32_t)d * F;
+      sRa = a.n_rows; rba = row0; sna = (uint32_t)a.n_rows * (F / 32);
+      sRb = E * d; rbb = e * d + n0; snb = (uint32_t)E * d * (F / 32);
       break;
     case MOE_GG_WGRAD_DOWN:   // A = H^T [F][P], B = dY^T [d][P]
       lda = P; ldb = P;
-      qa0 = qa1 = x.aq[0] + p_e; sa0 = sa1 = x.as[0] + p_e / 32;
-      na = p_e < P ? (uint32_t)((size_t)F * P - p_e) : 0;
-      qb0 = qb1 = x.bq[0] + p_e; sb0 = sb1 = x.bs[0] + p_e / 32;
-      nb = p_e < P ? (uint32_t)((size_t)d * P - p_e) : 0;
+      qa0 = qa1 = x.aq[0] + p_e; na = p_e < P ? (uint32_t)((size_t)F * P - p_e) : 0;
+      qb0 = qb1 = x.bq[0] + p_e; nb = p_e < P ? (uint32_t)((size_t)d * P - p_e) : 0;
+      sRa = F; g0a = p_e / 128; rba = m0; sna = (uint32_t)F * (P / 32);
+      sRb = d; g0b = p_e / 128; rbb = n0; snb = (uint32_t)d * (P / 32);
       break;
     default:                  // WGRAD_GATE_UP: A = X^T [d][P], B = dG^T, dU^T [F][P]
       lda = P; ldb = P;
-      qa0 = qa1 = x.aq[0] + p_e; sa0 = sa1 = x.as[0] + p_e / 32;
-      na = p_e < P ? (uint32_t)((size_t)d * P - p_e) : 0;
-      qb0 = x.bq[0] + p_e; qb1 = x.bq[1] + p_e; sb0 = x.bs[0] + p_e / 32; sb1 = x.bs[1] + p_e / 32;
-      nb = p_e < P ? (uint32_t)((size_t)F * P - p_e) : 0;
+      qa0 = qa1 = x.aq[0] + p_e; na = p_e < P ? (uint32_t)((size_t)d * P - p_e) : 0;
+      qb0 = x.bq[0] + p_e; qb1 = x.bq[1] + p_e; nb = p_e < P ? (uint32_t)((size_t)F * P - p_e) : 0;
+      sRa = d; g0a = p_e / 128; rba = m0; sna = (uint32_t)d * (P / 32);
+      sRb = F; g0b = p_e / 128; rbb = n0; snb = (uint32_t)F * (P / 32);
   }
   const rsrc_t rA0 = make_rsrc(qa0, na), rA1 = make_rsrc(qa1, na);
   const rsrc_t rB0 = make_rsrc(qb0, nb), rB1 = make_rsrc(qb1, nb);
-  const rsrc_t rSA0 = make_rsrc(sa0, na / 32), rSA1 = make_rsrc(sa1, na / 32);
-  const rsrc_t rSB0 = make_rsrc(sb0, nb / 32), rSB1 = make_rsrc(sb1, nb / 32);
+  const rsrc_t rSA0 = make_rsrc(x.as[0], sna), rSA1 = make_rsrc(x.as[1] ? x.as[1] : x.as[0], sna);
+  const rsrc_t rSB0 = make_rsrc(x.bs[0], snb), rSB1 = make_rsrc(x.bs[1] ? x.bs[1] : x.bs[0], snb);
 
   // ---- per-lane byte offsets at k = 0
   uint32_t a_off[C::A_PER_WAVE], b_off[C::B_PER_WAVE], s_off[C::S_PER_WAVE];
-  int b_mat[C::B_PER_WAVE], s_kind[C::S_PER_WAVE], s_slot[C::S_PER_WAVE];
+  int b_mat[C::B_PER_WAVE], s_kind[C::S_PER_WAVE], s_slot[C::S_PER_WAVE], s_R[C::S_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::A_PER_WAVE; ++i) {
     const int q = (wave * C::A_PER_WAVE + i) * 64 + lane;      // 16-byte chunk of the A stage tile
@@ -215,12 +221,14 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_mx_kernel(MxArgs x) {
     const int srow = 64 * j + lane;         // rows: A 0..BM-1, then B
     if (64 * j < BM) {
       s_kind[i] = 0;
-      s_off[i] = (uint32_t)(m0 + srow) * (lda / 32);
+      s_R[i] = sRa;
+      s_off[i] = 4u * ((uint32_t)g0a * sRa + rba + srow);
     } else {
       const int rb = srow - BM;
       const int sub = DUAL ? (64 * j - BM) / (BN / 2) : 0;
       s_kind[i] = 1 + sub;
-      s_off[i] = (uint32_t)(n0 + rb - sub * (BN / 2)) * (ldb / 32);
+      s_R[i] = sRb;
+      s_off[i] = 4u * ((uint32_t)g0b * sRb + rbb + rb - sub * (BN / 2));
     }
   }
 
@@ -242,7 +250,7 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_mx_kernel(MxArgs x) {
     }
 #pragma unroll
     for (int i = 0; i < C::S_PER_WAVE; ++i) {
-      const uint32_t dst = ss + s_slot[i] * 256, off = s_off[i] + (uint32_t)(ks >> 1) * 4;
+      const uint32_t dst = ss + s_slot[i] * 256, off = s_off[i] + 4u * (uint32_t)(ks >> 1) * s_R[i];
       if (s_kind[i] == 0) dma4(rsa, dst, off);
       else if (DUAL && s_kind[i] == 2) dma4(rSB1, dst, off);
       else dma4(rsb, dst, off);

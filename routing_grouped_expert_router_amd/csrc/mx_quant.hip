@@ -49,12 +49,17 @@ MOE_DEV uint32_t e4m3_byte(float v, float inv) {
   return code | sign;
 }
 
+// Scales are stored in groups of four: the word of row r and 128-value column
+// group c (the scales of blocks 4c..4c+3) is at byte 4 * (R * c + r).
+
 // ------------------------------------------------------------------ axis 0
 // One thread per 16 values (half a block); the two halves of a block are
-// neighbouring lanes. Codes go out as one 16-byte store per thread.
-__global__ void __launch_bounds__(256) mx_rows_kernel(const uint16_t* __restrict__ src, long n_half,
-                                                      uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
-  const long stride = static_cast<long>(gridDim.x) * 256;   // even: pairs stay together
+// neighbouring lanes and the eight lanes of a 128-value group share one scale
+// word, written by the group's first lane. Codes go out as one 16-byte store
+// per thread.
+__global__ void __launch_bounds__(256) mx_rows_kernel(const uint16_t* __restrict__ src, long n_half, int rows,
+                                                      int nb, uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const long stride = static_cast<long>(gridDim.x) * 256;   // a multiple of 8: groups stay together
   for (long h = static_cast<long>(blockIdx.x) * 256 + threadIdx.x; h < n_half; h += stride) {
     const V16* p = reinterpret_cast<const V16*>(src + h * 16);
     float v[16];
@@ -80,7 +85,14 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(const uint16_t* __restrict
       out.w[w] = word;
     }
     *reinterpret_cast<V16*>(q + h * 16) = out;
-    if ((h & 1) == 0) s[h >> 1] = static_cast<uint8_t>(x + 127);
+    const uint32_t code = static_cast<uint32_t>(x + 127);
+    const uint32_t c1 = __shfl_down(code, 2, 64), c2 = __shfl_down(code, 4, 64), c3 = __shfl_down(code, 6, 64);
+    if ((h & 7) == 0) {
+      const long bl = h >> 1;
+      const long r = bl / nb, b = bl % nb;
+      *reinterpret_cast<uint32_t*>(s + 4 * (static_cast<size_t>(rows) * (b >> 2) + r)) =
+          code | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    }
   }
 }
 
@@ -215,7 +227,14 @@ __global__ void __launch_bounds__(256) mx_cols_kernel(const uint16_t* __restrict
   uint8_t* qp = q + static_cast<size_t>(c0 + c) * col_stride + col;
   reinterpret_cast<V16*>(qp)[0] = out[0];
   reinterpret_cast<V16*>(qp)[1] = out[1];
-  s[static_cast<size_t>(c0 + c) * (col_stride / 32) + col / 32] = static_cast<uint8_t>(x + 127);
+  // the tile's 128 output columns are one column group: the four block
+  // scales of output row c0 + c form one word
+  __shared__ uint32_t words[kQCols];
+  reinterpret_cast<uint8_t*>(words)[4 * c + b] = static_cast<uint8_t>(x + 127);
+  __syncthreads();
+  if (tid < kQCols)
+    *reinterpret_cast<uint32_t*>(s + 4 * (static_cast<size_t>(cols) * ((p_g + row_in) / kQRows) + c0 + tid)) =
+        words[tid];
 }
 
 }  // namespace
@@ -233,15 +252,16 @@ extern "C" int moe_mx_quantize(const void* src, int rows, int cols, int axis, co
                                int n_groups, int col_stride, void* q, void* s, hipStream_t stream) {
   MOE_CHECK_ARG(rows >= 0 && cols > 0 && (axis == 0 || axis == 1));
   if (axis == 0) {
-    MOE_CHECK_ARG(cols % 32 == 0 && group_offsets == nullptr && col_stride == 0);
+    MOE_CHECK_ARG(cols % 128 == 0 && group_offsets == nullptr && col_stride == 0);
     if (rows == 0) return MOE_OK;
-    MOE_CHECK_ARG(src && q && s && aligned16(src) && aligned16(q));
+    MOE_CHECK_ARG(src && q && s && aligned16(src) && aligned16(q) && aligned4(s));
     const long n_half = static_cast<long>(rows) * (cols / 16);
     MOE_CHECK_SUPPORTED(n_half < (1L << 40));
     long blocks = (n_half + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     mx_rows_kernel<<<static_cast<int>(blocks), 256, 0, stream>>>(
-        static_cast<const uint16_t*>(src), n_half, static_cast<uint8_t*>(q), static_cast<uint8_t*>(s));
+        static_cast<const uint16_t*>(src), n_half, rows, cols / 32, static_cast<uint8_t*>(q),
+        static_cast<uint8_t*>(s));
     return launch_status();
   }
   MOE_CHECK_ARG(cols % kQCols == 0 && n_groups >= 1 && col_stride > 0 && col_stride % 128 == 0);
@@ -258,7 +278,7 @@ extern "C" int moe_mx_quantize(const void* src, int rows, int cols, int axis, co
   MOE_CHECK_ARG(col_stride >= need);
   MOE_CHECK_SUPPORTED(static_cast<long>(cols) * col_stride < (1L << 40));
   if (rows == 0) return MOE_OK;
-  MOE_CHECK_ARG(src && q && s && aligned16(src) && aligned16(q));
+  MOE_CHECK_ARG(src && q && s && aligned16(src) && aligned16(q) && aligned4(s));
   const long row_tiles = group_offsets ? (rows + kQRows - 1) / kQRows + n_groups
                                        : static_cast<long>(n_groups) * ((gr.per + kQRows - 1) / kQRows);
   const long grid = row_tiles * (cols / kQCols);

@@ -22,11 +22,12 @@ from . import _lib as L
 
 
 class _Q:
-    """Codes and scales of one quantised operand."""
+    """Codes [rows, cols] and scales (rows * cols / 32 bytes, in the library's
+    grouped layout) of one quantised operand."""
 
     def __init__(self, rows: int, cols: int, dev):
         self.q = torch.empty(rows, cols, dtype=torch.uint8, device=dev)
-        self.s = torch.empty(rows, cols // 32, dtype=torch.uint8, device=dev)
+        self.s = torch.empty(rows * cols // 32, dtype=torch.uint8, device=dev)
         self.t = L.MxTensor(self.q, self.s)
 
 

@@ -139,7 +139,9 @@ def test_mx_quantize_argument_errors():
     assert q(FAKE, 8, 64, 0, None, 1, 128, FAKE, FAKE) == INVALID
     assert q(FAKE, 8, 64, 2, None, 1, 0, FAKE, FAKE) == INVALID
     assert q(FAKE + 2, 8, 64, 0, None, 1, 0, FAKE, FAKE) == INVALID
-    assert q(FAKE, 0, 64, 0, None, 1, 0, None, None) == 0            # nothing to do
+    assert q(FAKE, 0, 128, 0, None, 1, 0, None, None) == 0           # nothing to do
+    assert q(FAKE, 8, 96, 0, None, 1, 0, FAKE, FAKE) == INVALID       # cols % 128 (scale words)
+    assert q(FAKE, 8, 128, 0, None, 1, 0, FAKE, FAKE + 2) == INVALID   # scales 4-byte aligned
     # axis 1: stride bound with device offsets, equal groups
     assert lib.moe_mx_col_stride(1000, 4) == 128 * (8 + 4)
     assert q(FAKE, 1000, 64, 1, FAKE, 4, 128 * 11, FAKE, FAKE) == INVALID

@@ -21,6 +21,14 @@ def _rng(*seed):
     return np.random.default_rng(list(seed))
 
 
+def grouped_scales(s):
+    """Scales [R, K/32] in the library's layout: the four scales of 128
+    consecutive values of a row form one word, words of one 128-value column
+    group are contiguous over the rows (byte 4 * (R * (b // 4) + r) + b % 4)."""
+    R, nb = s.shape
+    return np.ascontiguousarray(s.reshape(R, nb // 4, 4).transpose(1, 0, 2)).reshape(-1)
+
+
 def _values(rng, rows, cols):
     """bf16 values whose 32-blocks cover many binades and the format's edge
     cases (rows of blocks run along the last axis)."""
@@ -44,14 +52,14 @@ def _values(rng, rows, cols):
 
 
 # ----------------------------------------------------------------------------- quantiser
-@pytest.mark.parametrize("rows,cols", [(1, 32), (37, 96), (129, 256), (5, 4096), (2000, 64)])
+@pytest.mark.parametrize("rows,cols", [(1, 128), (37, 384), (129, 256), (5, 4096), (2000, 128)])
 def test_mx_quantize_rows_bitwise(rows, cols):
     v = _values(_rng(7, rows, cols), rows, cols)
     q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
-    s = torch.empty(rows, cols // 32, dtype=torch.uint8, device="cuda")
+    s = torch.empty(rows * cols // 32, dtype=torch.uint8, device="cuda")
     L.moe_mx_quantize(dev(f64_to_bf16_bits(v), "bf16"), 0, q, s)
     rq, rs = mx_quantize(v)
-    assert np.array_equal(host(s), rs)
+    assert np.array_equal(host(s), grouped_scales(rs))
     assert np.array_equal(host(q), rq)
 
 
@@ -85,11 +93,11 @@ def test_mx_quantize_cols_ragged_groups_bitwise(counts, cols):
     P = L.moe_mx_col_stride(n, len(counts))
     sentinel = 0xA5
     q = torch.full((cols, P), sentinel, dtype=torch.uint8, device="cuda")
-    s = torch.full((cols, P // 32), sentinel, dtype=torch.uint8, device="cuda")
+    s = torch.full((cols * P // 32,), sentinel, dtype=torch.uint8, device="cuda")
     src = dev(f64_to_bf16_bits(v), "bf16") if n else torch.empty(0, cols, dtype=torch.bfloat16, device="cuda")
     L.moe_mx_quantize(src, 1, q, s, dev(off, "i32"), len(counts), P)
     eq, es = _expected_cols(v, off[:-1], counts, P, sentinel)
-    assert np.array_equal(host(s), es)
+    assert np.array_equal(host(s), grouped_scales(es))
     assert np.array_equal(host(q), eq)
 
 
@@ -97,10 +105,10 @@ def test_mx_quantize_cols_equal_groups_bitwise():
     E, d, F = 3, 256, 128            # a weight [E, d, F] viewed as [E*d, F], blocks along d
     v = _values(_rng(9), E * d, F)
     q = torch.empty(F, E * d, dtype=torch.uint8, device="cuda")
-    s = torch.empty(F, E * d // 32, dtype=torch.uint8, device="cuda")
+    s = torch.empty(F * E * d // 32, dtype=torch.uint8, device="cuda")
     L.moe_mx_quantize(dev(f64_to_bf16_bits(v), "bf16"), 1, q, s, None, E, E * d)
     eq, es = _expected_cols(v, [e * d for e in range(E)], [d] * E, E * d, 0)
-    assert np.array_equal(host(s), es)
+    assert np.array_equal(host(s), grouped_scales(es))
     assert np.array_equal(host(q), eq)
 
 
