@@ -269,6 +269,15 @@ int moe_grouped_gemm(const moe_gg_desc* desc, hipStream_t stream);
  *           (rows % n_groups == 0); cols % 64 == 0.
  *   src and q 16-byte aligned, s 4-byte aligned. rows may be 0. */
 int moe_mx_col_stride(int rows, int n_groups);
+
+/* moe_mx_quantize_both: both orientations of moe_mx_quantize from one read of
+ * src: q_rows/s_rows as axis 0 and q_cols/s_cols as axis 1 with the same
+ * groups and col_stride (each GEMM operand of the expert layer is needed in
+ * both: by rows for one GEMM, by token columns for a weight gradient).
+ * cols % 128 == 0. Rows outside every group are written in neither. */
+int moe_mx_quantize_both(const void* src, int rows, int cols, const int32_t* group_offsets, int n_groups,
+                         int col_stride, void* q_rows, void* s_rows, void* q_cols, void* s_cols,
+                         hipStream_t stream);
 int moe_mx_quantize(const void* src, int rows, int cols, int axis, const int32_t* group_offsets,
                     int n_groups, int col_stride, void* q, void* s, hipStream_t stream);
 

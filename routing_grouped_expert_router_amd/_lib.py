@@ -67,6 +67,7 @@ SIGNATURES = {
     "moe_grouped_gemm": (_i, [C.POINTER(moe_gg_desc), _vp]),
     "moe_mx_col_stride": (_i, [_i, _i]),
     "moe_mx_quantize": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp]),
+    "moe_mx_quantize_both": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "moe_grouped_gemm_mx": (_i, [C.POINTER(moe_mx_gg_desc), _vp]),
 }
 
@@ -238,6 +239,14 @@ def moe_mx_quantize(src, axis, q, s, group_offsets=None, n_groups=1, col_stride=
     rows, cols = src.shape
     _check(lib().moe_mx_quantize(_p(src), rows, cols, axis, _p(group_offsets), n_groups, col_stride,
                                  _p(q), _p(s), _stream(stream)), "moe_mx_quantize")
+
+
+def moe_mx_quantize_both(src, rows_out: MxTensor, cols_out: MxTensor, group_offsets=None, n_groups=1,
+                         col_stride=0, stream=None):
+    rows, cols = src.shape
+    _check(lib().moe_mx_quantize_both(_p(src), rows, cols, _p(group_offsets), n_groups, col_stride,
+                                      _p(rows_out.q), _p(rows_out.s), _p(cols_out.q), _p(cols_out.s),
+                                      _stream(stream)), "moe_mx_quantize_both")
 
 
 def make_mx_gg_desc(op, E, d, F, n_rows, group_offsets, col_stride=0, a0=None, a1=None, b0=None,

@@ -28,29 +28,17 @@ MOE_DEV int mx_exponent(float amax) {
 // 2^n as binary32 for -126 <= n <= 127.
 MOE_DEV float pow2(int n) { return __uint_as_float(static_cast<uint32_t>(n + 127) << 23); }
 
-// E4M3 byte of v * 2^-X; inv = 2^-X. v * inv is exact (a power-of-two scaling
-// of a bf16 value) unless it falls below binary32's normal range, where it
-// rounds to zero in E4M3 anyway.
-MOE_DEV uint32_t e4m3_byte(float v, float inv) {
-  const float sv = v * inv;
-  const uint32_t sign = (__float_as_uint(sv) >> 24) & 0x80u;
-  const float a = fminf(fabsf(sv), kE4M3Max);
-  // quantum of a's binade: 2^(e - 3) with e = floor(log2 a), or the
-  // subnormal quantum 2^-9 below 2^-6
-  const int e = a >= 0x1p-6f ? static_cast<int>(__float_as_uint(a) >> 23) - 127 : -6;
-  const float r = fminf(rintf(a * pow2(3 - e)) * pow2(e - 3), kE4M3Max);
-  uint32_t code;
-  if (r >= 0x1p-6f) {
-    const uint32_t rb = __float_as_uint(r);
-    code = ((((rb >> 23) & 0xffu) - 127u + 7u) << 3) | ((rb >> 20) & 7u);
-  } else {
-    code = static_cast<uint32_t>(r * 512.0f);   // m * 2^-9, m = 0..7
-  }
-  return code | sign;
+// Four E4M3 bytes (v0 lowest) of v * 2^-X, inv = 2^-X. v * inv is exact (a
+// power-of-two scaling of a bf16 value) unless it falls below binary32's
+// normal range, where it rounds to zero in E4M3 anyway. The clamp to +-448
+// is the format's saturation (values from 448 up round to 448, never to
+// NaN); the conversion itself is gfx950's v_cvt_pk_fp8_f32 (OCP E4M3,
+// round to nearest even, subnormals, sign of zero kept).
+MOE_DEV uint32_t e4m3_word(float v0, float v1, float v2, float v3, float inv) {
+  auto sat = [&](float v) { return __builtin_amdgcn_fmed3f(v * inv, -kE4M3Max, kE4M3Max); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat(v0), sat(v1), 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(sat(v2), sat(v3), lo, true));
 }
-
-// Scales are stored in groups of four: the word of row r and 128-value column
-// group c (the scales of blocks 4c..4c+3) is at byte 4 * (R * c + r).
 
 // ------------------------------------------------------------------ axis 0
 // One thread per 16 values (half a block); the two halves of a block are
@@ -78,12 +66,7 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(const uint16_t* __restrict
     const float inv = pow2(-x);
     V16 out;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) word |= e4m3_byte(v[4 * w + b], inv) << (8 * b);
-      out.w[w] = word;
-    }
+    for (int w = 0; w < 4; ++w) out.w[w] = e4m3_word(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], inv);
     *reinterpret_cast<V16*>(q + h * 16) = out;
     const uint32_t code = static_cast<uint32_t>(x + 127);
     const uint32_t c1 = __shfl_down(code, 2, 64), c2 = __shfl_down(code, 4, 64), c3 = __shfl_down(code, 6, 64);
@@ -120,121 +103,205 @@ MOE_DEV void group_range(const Groups1& g, int i, int& r0, int& n) {
   n = hi - lo;
 }
 
+// Group and 128-row tile of row-tile index rt (tiles of every group in group
+// order, ceil(n_g/128) per group), and the group's first padded column p_g =
+// 128 * sum_{h<g} ceil(n_h/128). Every thread of the 256-thread workgroup
+// calls it (it synchronises); false: rt is past the last tile.
+MOE_DEV bool find_group_tile(const Groups1& gr, int rt, int* tile_start, int& g, int& i, long& p_g) {
+  const int tid = threadIdx.x;
+  if (!gr.offsets) {
+    const int per_tiles = (gr.per + kQRows - 1) / kQRows;
+    if (per_tiles == 0 || rt >= per_tiles * gr.G) return false;
+    g = rt / per_tiles;
+    i = rt % per_tiles;
+    p_g = static_cast<long>(g) * per_tiles * kQRows;
+    return true;
+  }
+  constexpr int kMaxPer = (MOE_MAX_EXPERTS + 255) / 256;
+  const int per = (gr.G + 255) / 256;
+  const int g_lo = tid * per;
+  int loc[kMaxPer];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    int t = 0;
+    if (j < per && g_lo + j < gr.G) {
+      int r0, n;
+      group_range(gr, g_lo + j, r0, n);
+      t = (n + kQRows - 1) / kQRows;
+    }
+    loc[j] = t;
+    sum += t;
+  }
+  __shared__ int wtot[4];
+  const int lane = tid & 63, w = tid >> 6;
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wtot[w] = incl;
+  __syncthreads();
+  int before = incl - sum;
+  for (int j = 0; j < w; ++j) before += wtot[j];
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    if (j < per && g_lo + j < gr.G) tile_start[g_lo + j] = before;
+    before += loc[j];
+  }
+  if (tid == 255) tile_start[gr.G] = before;
+  __syncthreads();
+  if (rt >= tile_start[gr.G]) return false;
+  int lo = 0, hi = gr.G - 1;   // last g with tile_start[g] <= rt
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_start[mid] <= rt) lo = mid;
+    else hi = mid - 1;
+  }
+  g = lo;
+  i = rt - tile_start[g];
+  p_g = 128L * tile_start[g];
+  return true;
+}
+
+// Codes of one 32-value block (bytes of two 16-byte words) and its scale code.
+MOE_DEV uint32_t quantize_block(const float (&v)[32], V16 (&out)[2]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) amax = fmaxf(amax, fabsf(v[r]));
+  const int x = mx_exponent(amax);
+  const float inv = pow2(-x);
+#pragma unroll
+  for (int w = 0; w < 8; ++w)
+    out[w >> 2].w[w & 3] = e4m3_word(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], inv);
+  return static_cast<uint32_t>(x + 127);
+}
+
+// Stage a tile of TC columns and 128 rows of one group into LDS (rows past the
+// group's end read as zeros).
+template <int TC, int LDW>
+MOE_DEV void stage_tile(const uint16_t* __restrict__ src, int cols, int r0, int n, int row_in, int c0,
+                        uint16_t* tile) {
+  constexpr int CH = TC / 8;   // 16-byte chunks per row
+#pragma unroll
+  for (int j = 0; j < kQRows * CH / 256; ++j) {
+    const int qd = threadIdx.x + 256 * j;
+    const int r = qd / CH, c = qd % CH;
+    V16 v = {{0u, 0u, 0u, 0u}};
+    if (row_in + r < n)
+      v = *reinterpret_cast<const V16*>(src + static_cast<size_t>(r0 + row_in + r) * cols + c0 + c * 8);
+    *reinterpret_cast<V16*>(tile + r * LDW + c * 8) = v;
+  }
+}
+
+// Column (transposed) quantisation of the tile's columns [c_lo, c_lo + 64):
+// thread (c, b) turns rows 32b..32b+31 of column c into 32 code bytes of output
+// row c0 + c and one scale byte; the four scales of a column form one word.
+template <int LDW>
+MOE_DEV void cols_part(const uint16_t* tile, int c_lo, int c0, int cols, long p_g, int row_in, int col_stride,
+                       uint8_t* __restrict__ q, uint8_t* __restrict__ s, uint32_t* words) {
+  const int tid = threadIdx.x;
+  const int c = c_lo + (tid & 63), b = tid >> 6;
+  float v[32];
+#pragma unroll
+  for (int r = 0; r < 32; ++r) v[r] = bf16_to_f32(tile[(32 * b + r) * LDW + c]);
+  V16 out[2];
+  const uint32_t code = quantize_block(v, out);
+  const size_t col = static_cast<size_t>(p_g) + row_in + 32 * b;   // output column of the block
+  uint8_t* qp = q + static_cast<size_t>(c0 + c) * col_stride + col;
+  reinterpret_cast<V16*>(qp)[0] = out[0];
+  reinterpret_cast<V16*>(qp)[1] = out[1];
+  reinterpret_cast<uint8_t*>(words)[4 * (c - c_lo) + b] = static_cast<uint8_t>(code);
+  __syncthreads();
+  if (tid < 64)
+    *reinterpret_cast<uint32_t*>(s + 4 * (static_cast<size_t>(cols) * ((p_g + row_in) / kQRows) + c0 + c_lo + tid)) =
+        words[tid];
+  __syncthreads();
+}
+
 __global__ void __launch_bounds__(256) mx_cols_kernel(const uint16_t* __restrict__ src, int cols, Groups1 gr,
                                                       int col_stride, uint8_t* __restrict__ q,
                                                       uint8_t* __restrict__ s) {
   __shared__ int tile_start[MOE_MAX_EXPERTS + 1];
   __shared__ __attribute__((aligned(16))) uint16_t tile[kQRows * kQLdw];
-  const int tid = threadIdx.x;
+  __shared__ uint32_t words[64];
   const int tiles_c = cols / kQCols;
   const int rt = blockIdx.x / tiles_c, ct = blockIdx.x % tiles_c;
-
-  // group of row-tile rt: tile_start[g] = sum_{h<g} ceil(n_h / 128)
   int g, i;
-  if (!gr.offsets) {
-    const int per_tiles = (gr.per + kQRows - 1) / kQRows;
-    if (per_tiles == 0 || rt >= per_tiles * gr.G) return;
-    g = rt / per_tiles;
-    i = rt % per_tiles;
-  } else {
-    constexpr int kMaxPer = (MOE_MAX_EXPERTS + 255) / 256;
-    const int per = (gr.G + 255) / 256;
-    const int g_lo = tid * per;
-    int loc[kMaxPer];
-    int sum = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      int t = 0;
-      if (j < per && g_lo + j < gr.G) {
-        int r0, n;
-        group_range(gr, g_lo + j, r0, n);
-        t = (n + kQRows - 1) / kQRows;
-      }
-      loc[j] = t;
-      sum += t;
-    }
-    __shared__ int wtot[4];
-    const int lane = tid & 63, w = tid >> 6;
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    if (lane == 63) wtot[w] = incl;
-    __syncthreads();
-    int before = incl - sum;
-    for (int j = 0; j < w; ++j) before += wtot[j];
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      if (j < per && g_lo + j < gr.G) tile_start[g_lo + j] = before;
-      before += loc[j];
-    }
-    if (tid == 255) tile_start[gr.G] = before;
-    __syncthreads();
-    if (rt >= tile_start[gr.G]) return;
-    int lo = 0, hi = gr.G - 1;   // last g with tile_start[g] <= rt
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (tile_start[mid] <= rt) lo = mid;
-      else hi = mid - 1;
-    }
-    g = lo;
-    i = rt - tile_start[g];
-  }
+  long p_g;
+  if (!find_group_tile(gr, rt, tile_start, g, i, p_g)) return;
   int r0, n;
   group_range(gr, g, r0, n);
-  // padded column of the group's first row
-  const long p_g = gr.offsets ? 128L * tile_start[g]
-                              : static_cast<long>(g) * ((gr.per + kQRows - 1) / kQRows) * kQRows;
   const int row_in = i * kQRows;            // first row of the tile within the group
   const int c0 = ct * kQCols;
   // offsets that break the documented contract (decreasing ones) could ask for
   // more padded columns than col_stride holds: such tiles write nothing
   if (p_g + row_in + kQRows > col_stride) return;
+  stage_tile<kQCols, kQLdw>(src, cols, r0, n, row_in, c0, tile);
+  __syncthreads();
+  cols_part<kQLdw>(tile, 0, c0, cols, p_g, row_in, col_stride, q, s, words);
+}
 
-  // stage the tile (rows past the group's end read as zeros)
-#pragma unroll
-  for (int j = 0; j < kQRows * kQCols / 8 / 256; ++j) {
-    const int qd = tid + 256 * j;
-    const int r = qd / (kQCols / 8), c = qd % (kQCols / 8);
-    V16 v = {{0u, 0u, 0u, 0u}};
-    if (row_in + r < n)
-      v = *reinterpret_cast<const V16*>(src + static_cast<size_t>(r0 + row_in + r) * cols + c0 + c * 8);
-    *reinterpret_cast<V16*>(tile + r * kQLdw + c * 8) = v;
-  }
+// ------------------------------------------------------------------ both
+// One pass, both orientations: a 128-row x 128-column tile of one group is
+// staged once; the column part writes the transposed codes as above, and the
+// row part quantises each valid row's 128 values (four blocks, one scale word)
+// into the row-oriented output.
+constexpr int kBCols = 128, kBLdw = kBCols + 8;
+
+__global__ void __launch_bounds__(256) mx_both_kernel(const uint16_t* __restrict__ src, int rows, int cols,
+                                                      Groups1 gr, int col_stride, uint8_t* __restrict__ q_rows,
+                                                      uint8_t* __restrict__ s_rows, uint8_t* __restrict__ q_cols,
+                                                      uint8_t* __restrict__ s_cols) {
+  __shared__ int tile_start[MOE_MAX_EXPERTS + 1];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kQRows * kBLdw];
+  __shared__ uint32_t words[64];
+  const int tid = threadIdx.x;
+  const int tiles_c = cols / kBCols;
+  const int rt = blockIdx.x / tiles_c, ct = blockIdx.x % tiles_c;
+  int g, i;
+  long p_g;
+  if (!find_group_tile(gr, rt, tile_start, g, i, p_g)) return;
+  int r0, n;
+  group_range(gr, g, r0, n);
+  const int row_in = i * kQRows;
+  const int c0 = ct * kBCols;
+  if (p_g + row_in + kQRows > col_stride) return;
+  stage_tile<kBCols, kBLdw>(src, cols, r0, n, row_in, c0, tile);
   __syncthreads();
 
-  const int c = tid & 63, b = tid >> 6;    // column, block of 32 rows
-  float v[32];
-  float amax = 0.f;
+  // rows: thread (r, h) quantises blocks 2h, 2h+1 (64 values) of tile row r
+  {
+    const int r = tid >> 1, h = tid & 1;
+    float v[2][32];
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    v[r] = bf16_to_f32(tile[(32 * b + r) * kQLdw + c]);
-    amax = fmaxf(amax, fabsf(v[r]));
+    for (int k = 0; k < 8; ++k) {
+      float f[8];
+      unpack(*reinterpret_cast<const V16*>(tile + r * kBLdw + 64 * h + 8 * k), f);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) v[k >> 2][8 * (k & 3) + m] = f[m];
+    }
+    V16 out[2][2];
+    const uint32_t c_lo = quantize_block(v[0], out[0]);
+    const uint32_t c_hi = quantize_block(v[1], out[1]);
+    const uint32_t pair = c_lo | (c_hi << 8);
+    const uint32_t other = __shfl_xor(pair, 1, 64);
+    if (row_in + r < n) {
+      const size_t grow = static_cast<size_t>(r0) + row_in + r;
+      V16* qp = reinterpret_cast<V16*>(q_rows + grow * cols + c0 + 64 * h);
+      qp[0] = out[0][0];
+      qp[1] = out[0][1];
+      qp[2] = out[1][0];
+      qp[3] = out[1][1];
+      if (h == 0)
+        *reinterpret_cast<uint32_t*>(s_rows + 4 * (static_cast<size_t>(rows) * (c0 / kBCols) + grow)) =
+            pair | (other << 16);
+    }
   }
-  const int x = mx_exponent(amax);
-  const float inv = pow2(-x);
-  V16 out[2];
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) word |= e4m3_byte(v[4 * w + k], inv) << (8 * k);
-    out[w >> 2].w[w & 3] = word;
-  }
-  const size_t col = static_cast<size_t>(p_g) + row_in + 32 * b;   // output column of the block
-  uint8_t* qp = q + static_cast<size_t>(c0 + c) * col_stride + col;
-  reinterpret_cast<V16*>(qp)[0] = out[0];
-  reinterpret_cast<V16*>(qp)[1] = out[1];
-  // the tile's 128 output columns are one column group: the four block
-  // scales of output row c0 + c form one word
-  __shared__ uint32_t words[kQCols];
-  reinterpret_cast<uint8_t*>(words)[4 * c + b] = static_cast<uint8_t>(x + 127);
-  __syncthreads();
-  if (tid < kQCols)
-    *reinterpret_cast<uint32_t*>(s + 4 * (static_cast<size_t>(cols) * ((p_g + row_in) / kQRows) + c0 + tid)) =
-        words[tid];
+  // columns, 64 at a time
+  cols_part<kBLdw>(tile, 0, c0, cols, p_g, row_in, col_stride, q_cols, s_cols, words);
+  cols_part<kBLdw>(tile, 64, c0, cols, p_g, row_in, col_stride, q_cols, s_cols, words);
 }
 
 }  // namespace
@@ -286,5 +353,35 @@ extern "C" int moe_mx_quantize(const void* src, int rows, int cols, int axis, co
   mx_cols_kernel<<<static_cast<int>(grid), 256, 0, stream>>>(static_cast<const uint16_t*>(src), cols, gr,
                                                              col_stride, static_cast<uint8_t*>(q),
                                                              static_cast<uint8_t*>(s));
+  return launch_status();
+}
+
+extern "C" int moe_mx_quantize_both(const void* src, int rows, int cols, const int32_t* group_offsets,
+                                    int n_groups, int col_stride, void* q_rows, void* s_rows, void* q_cols,
+                                    void* s_cols, hipStream_t stream) {
+  MOE_CHECK_ARG(rows >= 0 && cols > 0 && cols % 128 == 0);
+  MOE_CHECK_ARG(n_groups >= 1 && col_stride > 0 && col_stride % 128 == 0);
+  MOE_CHECK_SUPPORTED(n_groups <= MOE_MAX_EXPERTS);
+  Groups1 gr{group_offsets, n_groups, rows, 0};
+  long need;
+  if (group_offsets) {
+    need = 128L * ((rows + 127L) / 128 + n_groups);
+  } else {
+    MOE_CHECK_ARG(rows % n_groups == 0);
+    gr.per = rows / n_groups;
+    need = static_cast<long>(n_groups) * ((gr.per + 127L) / 128) * 128;
+  }
+  MOE_CHECK_ARG(col_stride >= need);
+  MOE_CHECK_SUPPORTED(static_cast<long>(cols) * col_stride < (1L << 40) && static_cast<long>(rows) * cols < (1L << 40));
+  if (rows == 0) return MOE_OK;
+  MOE_CHECK_ARG(src && q_rows && s_rows && q_cols && s_cols && aligned16(src) && aligned16(q_rows) &&
+                aligned16(q_cols) && aligned4(s_rows) && aligned4(s_cols));
+  const long row_tiles = group_offsets ? (rows + kQRows - 1) / kQRows + n_groups
+                                       : static_cast<long>(n_groups) * ((gr.per + kQRows - 1) / kQRows);
+  const long grid = row_tiles * (cols / kBCols);
+  MOE_CHECK_SUPPORTED(grid < (1L << 31));
+  mx_both_kernel<<<static_cast<int>(grid), 256, 0, stream>>>(
+      static_cast<const uint16_t*>(src), rows, cols, gr, col_stride, static_cast<uint8_t*>(q_rows),
+      static_cast<uint8_t*>(s_rows), static_cast<uint8_t*>(q_cols), static_cast<uint8_t*>(s_cols));
   return launch_status();
 }

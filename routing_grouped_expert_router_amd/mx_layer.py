@@ -74,53 +74,46 @@ class MxExperts:
 
     # ------------------------------------------------------------------ steps
     def quantize_weights(self, w_gate, w_up, w_down):
-        """Both orientations of each weight (they change every optimiser step)."""
+        """Both orientations of each weight in one pass (they change every
+        optimiser step)."""
         E, d, F = self.E, self.d, self.F
         wg, wu, wd = w_gate.view(E * d, F), w_up.view(E * d, F), w_down.view(E * F, d)
-        L.moe_mx_quantize(wg, 1, self.wg_c.q, self.wg_c.s, None, E, E * d)
-        L.moe_mx_quantize(wu, 1, self.wu_c.q, self.wu_c.s, None, E, E * d)
-        L.moe_mx_quantize(wd, 1, self.wd_c.q, self.wd_c.s, None, E, E * F)
-        L.moe_mx_quantize(wd, 0, self.wd_r.q, self.wd_r.s)
-        L.moe_mx_quantize(wg, 0, self.wg_r.q, self.wg_r.s)
-        L.moe_mx_quantize(wu, 0, self.wu_r.q, self.wu_r.s)
+        L.moe_mx_quantize_both(wg, self.wg_r.t, self.wg_c.t, None, E, E * d)
+        L.moe_mx_quantize_both(wu, self.wu_r.t, self.wu_c.t, None, E, E * d)
+        L.moe_mx_quantize_both(wd, self.wd_r.t, self.wd_c.t, None, E, E * F)
         self._mark("mx_quantize_weights")
+
+    def _both(self, src, rows_out, cols_out):
+        L.moe_mx_quantize_both(src, rows_out.t, cols_out.t, self.offsets, self.E, self.P)
 
     def forward(self, x_perm, offsets, w_gate, w_up, w_down):
         self.x_perm, self.offsets = x_perm, offsets
         self.quantize_weights(w_gate, w_up, w_down)
-        L.moe_mx_quantize(x_perm, 0, self.xq.q, self.xq.s)
+        self._both(x_perm, self.xq, self.x_c)
         self._mark("mx_quantize_x")
         self._gg(L.MOE_GG_FWD_GATE_UP, a0=self.xq.t, b0=self.wg_c.t, b1=self.wu_c.t,
                  out0=self.g, out1=self.u, out2=self.h)
         self._mark("mx_fwd_gate_up")
-        L.moe_mx_quantize(self.h, 0, self.hq.q, self.hq.s)
+        self._both(self.h, self.hq, self.h_c)
         self._mark("mx_quantize_h")
         self._gg(L.MOE_GG_FWD_DOWN, a0=self.hq.t, b0=self.wd_c.t, out0=self.y_perm)
         self._mark("mx_fwd_down")
         return self.y_perm
 
     def backward(self, dy_perm):
-        E, off, P = self.E, self.offsets, self.P
-        L.moe_mx_quantize(dy_perm, 0, self.dyq.q, self.dyq.s)
-        L.moe_mx_quantize(dy_perm, 1, self.dy_c.q, self.dy_c.s, off, E, P)
+        self._both(dy_perm, self.dyq, self.dy_c)
         self._mark("mx_quantize_dy")
         self._gg(L.MOE_GG_DGRAD_DOWN, a0=self.dyq.t, b0=self.wd_r.t, g=self.g, u=self.u,
                  out0=self.dg, out1=self.du)
         self._mark("mx_dgrad_down")
-        L.moe_mx_quantize(self.h, 1, self.h_c.q, self.h_c.s, off, E, P)
-        self._mark("mx_quantize_h_cols")
         self._gg(L.MOE_GG_WGRAD_DOWN, a0=self.h_c.t, b0=self.dy_c.t, out0=self.dw_down)
         self._mark("mx_wgrad_down")
-        L.moe_mx_quantize(self.dg, 0, self.dgq.q, self.dgq.s)
-        L.moe_mx_quantize(self.du, 0, self.duq.q, self.duq.s)
-        L.moe_mx_quantize(self.dg, 1, self.dg_c.q, self.dg_c.s, off, E, P)
-        L.moe_mx_quantize(self.du, 1, self.du_c.q, self.du_c.s, off, E, P)
+        self._both(self.dg, self.dgq, self.dg_c)
+        self._both(self.du, self.duq, self.du_c)
         self._mark("mx_quantize_dg_du")
         self._gg(L.MOE_GG_DGRAD_GATE_UP, a0=self.dgq.t, a1=self.duq.t, b0=self.wg_r.t, b1=self.wu_r.t,
                  out0=self.dx_perm)
         self._mark("mx_dgrad_gate_up")
-        L.moe_mx_quantize(self.x_perm, 1, self.x_c.q, self.x_c.s, off, E, P)
-        self._mark("mx_quantize_x_cols")
         self._gg(L.MOE_GG_WGRAD_GATE_UP, a0=self.x_c.t, b0=self.dg_c.t, b1=self.du_c.t,
                  out0=self.dw_gate, out1=self.dw_up)
         self._mark("mx_wgrad_gate_up")

@@ -179,3 +179,14 @@ def test_mx_gemm_argument_errors():
     d.op = 9
     assert call(d) == INVALID
     assert lib.moe_grouped_gemm_mx(None, None) == INVALID
+
+
+def test_mx_quantize_both_argument_errors():
+    lib = L.lib()
+    q = lambda *a: lib.moe_mx_quantize_both(*a, None)
+    assert q(FAKE, 100, 64, FAKE, 2, 128 * 3, FAKE, FAKE, FAKE, FAKE) == INVALID     # cols % 128
+    assert q(FAKE, 100, 128, FAKE, 2, 128 * 2, FAKE, FAKE, FAKE, FAKE) == INVALID    # stride bound
+    assert q(FAKE, 100, 128, None, 3, 128 * 3, FAKE, FAKE, FAKE, FAKE) == INVALID    # rows % groups
+    assert q(FAKE, 100, 128, FAKE, 2, 128 * 3, FAKE, FAKE, None, FAKE) == INVALID    # missing output
+    assert q(FAKE, 100, 128, FAKE, 2, 128 * 3, FAKE, FAKE + 1, FAKE, FAKE) == INVALID
+    assert q(FAKE, 0, 128, FAKE, 2, 128 * 2, None, None, None, None) == 0

@@ -112,6 +112,108 @@ def test_mx_quantize_cols_equal_groups_bitwise():
     assert np.array_equal(host(q), eq)
 
 
+@pytest.mark.parametrize("counts,cols", [([0, 5, 128, 129, 300, 0, 33], 128), ([700, 64, 31, 257], 384),
+                                         ([1], 256)])
+def test_mx_quantize_both_bitwise(counts, cols):
+    # one pass, both orientations: each equals the oracle's quantiser
+    counts = np.array(counts, dtype=np.int64)
+    n = int(counts.sum())
+    v = _values(_rng(10, n, cols), n, cols)
+    off = np.zeros(len(counts) + 1, dtype=np.int32)
+    off[1:] = np.cumsum(counts)
+    P = L.moe_mx_col_stride(n, len(counts))
+    sentinel = 0x5A
+    rows_out = L.MxTensor(torch.full((n, cols), sentinel, dtype=torch.uint8, device="cuda"),
+                          torch.full((n * cols // 32,), sentinel, dtype=torch.uint8, device="cuda"))
+    cols_out = L.MxTensor(torch.full((cols, P), sentinel, dtype=torch.uint8, device="cuda"),
+                          torch.full((cols * P // 32,), sentinel, dtype=torch.uint8, device="cuda"))
+    L.moe_mx_quantize_both(dev(f64_to_bf16_bits(v), "bf16"), rows_out, cols_out, dev(off, "i32"),
+                           len(counts), P)
+    rq, rs = mx_quantize(v)
+    assert np.array_equal(host(rows_out.s), grouped_scales(rs))
+    assert np.array_equal(host(rows_out.q), rq)
+    eq, es = _expected_cols(v, off[:-1], counts, P, sentinel)
+    assert np.array_equal(host(cols_out.s), grouped_scales(es))
+    assert np.array_equal(host(cols_out.q), eq)
+
+
+def test_mx_quantize_both_equal_groups_bitwise():
+    E, d, F = 2, 256, 384            # a weight [E, d, F] as [E*d, F]: rows along F, columns along d
+    v = _values(_rng(13), E * d, F)
+    rows_out = L.MxTensor(torch.empty(E * d, F, dtype=torch.uint8, device="cuda"),
+                          torch.empty(E * d * F // 32, dtype=torch.uint8, device="cuda"))
+    cols_out = L.MxTensor(torch.empty(F, E * d, dtype=torch.uint8, device="cuda"),
+                          torch.empty(F * E * d // 32, dtype=torch.uint8, device="cuda"))
+    L.moe_mx_quantize_both(dev(f64_to_bf16_bits(v), "bf16"), rows_out, cols_out, None, E, E * d)
+    rq, rs = mx_quantize(v)
+    assert np.array_equal(host(rows_out.s), grouped_scales(rs))
+    assert np.array_equal(host(rows_out.q), rq)
+    eq, es = _expected_cols(v, [e * d for e in range(E)], [d] * E, E * d, 0)
+    assert np.array_equal(host(cols_out.s), grouped_scales(es))
+    assert np.array_equal(host(cols_out.q), eq)
+
+
+def _exhaustive_blocks():
+    """Every finite bf16 value inside 32-blocks whose scale it does not set,
+    plus blocks of each binade's values under a few anchors: rows of 128
+    values (four blocks). Covers every mantissa at every exponent relative to
+    the block scale, E4M3 subnormals, rounding ties, saturation, +-0."""
+    from oracle.numerics import bf16_bits_to_f64
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = bf16_bits_to_f64(bits)
+    vals = vals[np.isfinite(vals)]
+    blocks = []
+    # (1) all values sorted by magnitude: each block's largest element sets its scale
+    srt = vals[np.argsort(np.abs(vals), kind="stable")]
+    blocks += [srt[i:i + 32] for i in range(0, len(srt), 32)]
+    # (2) for anchors 2^A * 1.9921875, the 18 binades below A in full (both signs)
+    exps = np.floor(np.log2(np.abs(np.where(vals == 0, 1, vals))))
+    for A in (-126, -100, -20, 0, 7, 60, 119):
+        sel = vals[(exps <= A) & (exps >= A - 17) & (vals != 0)]
+        anchor = np.ldexp(1.9921875, A)
+        for i in range(0, len(sel), 31):
+            blocks.append(np.concatenate([[anchor], sel[i:i + 31]]))
+    out = np.zeros((len(blocks), 32))
+    for i, b in enumerate(blocks):
+        out[i, :len(b)] = b
+    nb = -(-len(blocks) // 4) * 4
+    full = np.zeros((nb, 32))
+    full[:len(blocks)] = out
+    return full.reshape(nb // 4, 128)
+
+
+def test_mx_quantize_exhaustive_bf16():
+    A = _exhaustive_blocks()                      # rows of four blocks
+    R = A.shape[0]
+    q = torch.empty(R, 128, dtype=torch.uint8, device="cuda")
+    s = torch.empty(R * 4, dtype=torch.uint8, device="cuda")
+    L.moe_mx_quantize(dev(f64_to_bf16_bits(A), "bf16"), 0, q, s)
+    rq, rs = mx_quantize(A)
+    assert np.array_equal(host(s), grouped_scales(rs))
+    assert np.array_equal(host(q), rq)
+    # the same blocks down the columns: transposed quantiser and the fused one
+    Rp = -(-R // 128) * 128
+    At = np.zeros((128, Rp))
+    At[:, :R] = A.T
+    src = dev(f64_to_bf16_bits(At), "bf16")
+    cq = torch.empty(Rp, 128, dtype=torch.uint8, device="cuda")
+    cs = torch.empty(Rp * 4, dtype=torch.uint8, device="cuda")
+    L.moe_mx_quantize(src, 1, cq, cs, None, 1, 128)
+    eq, es = mx_quantize(At.T)
+    assert np.array_equal(host(cs), grouped_scales(es))
+    assert np.array_equal(host(cq), eq)
+    rows_out = L.MxTensor(torch.empty(128, Rp, dtype=torch.uint8, device="cuda"),
+                          torch.empty(128 * Rp // 32, dtype=torch.uint8, device="cuda"))
+    cols_out = L.MxTensor(torch.empty(Rp, 128, dtype=torch.uint8, device="cuda"),
+                          torch.empty(Rp * 4, dtype=torch.uint8, device="cuda"))
+    L.moe_mx_quantize_both(src, rows_out, cols_out, None, 1, 128)
+    assert np.array_equal(host(cols_out.s), grouped_scales(es))
+    assert np.array_equal(host(cols_out.q), eq)
+    bq, bs = mx_quantize(At)
+    assert np.array_equal(host(rows_out.s), grouped_scales(bs))
+    assert np.array_equal(host(rows_out.q), bq)
+
+
 # ----------------------------------------------------------------------------- expert layer
 def _layer_inputs(seed, counts, d, F):
     rng = _rng(seed, d, F, len(counts))
@@ -207,4 +309,86 @@ def test_mx_each_gemm_on_oracle_inputs(counts, d, F):
         report[name] = (f"{e:.2e}", f"{same:.4f}")
         assert e <= 8e-3, (name, report)
         assert same > 0.95, (name, report)
+    print("rel err, exact fraction", report)
+
+
+# ----------------------------------------------------------------------------- full size
+def test_mx_full_size_sampled_experts():
+    """The expert layer at full size (32768 rows grouped by Zipf(0.8) counts,
+    d = 4096, d_ff = 2048, 32 experts) in the launch configuration the
+    benchmark times. The oracle recomputes two experts (the smallest and a
+    median one) on their own: experts are independent, and weight-gradient
+    blocks restart at each expert's first row. Each GEMM is checked on the
+    oracle's inputs (the sampled experts' rows of G, U, H, dG, dU are replaced
+    by the oracle's before the op runs), the tight check of the op itself."""
+    from moe_inputs import make_inputs, workload
+    from oracle.numerics import bf16_bits_to_f64
+
+    wl = workload("e32_mxfp8_share")
+    inp = make_inputs(wl)
+    counts = inp["counts"].astype(np.int64)
+    n, d, E, F = wl.T, wl.d, wl.E, wl.F
+    off = np.zeros(E + 1, dtype=np.int32)
+    off[1:] = np.cumsum(counts)
+    order = np.argsort(counts, kind="stable")
+    experts = [int(order[0]), int(order[E // 2])]
+    print("sampled experts", experts, "rows", [int(counts[e]) for e in experts], flush=True)
+
+    up = lambda a: dev(a, "bf16")
+    x, dy = up(inp["x_perm"]), up(inp["dy_perm"])
+    wg, wu, wd = up(inp["w_gate"]), up(inp["w_up"]), up(inp["w_down"])
+    lay = MxExperts(n, d, E, F)
+    offs = dev(off, "i32")
+    lay.forward(x, offs, wg, wu, wd)
+    lay.backward(dy)
+    torch.cuda.synchronize()
+
+    refs = {}
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        sub = lambda name, a, b: bf16_bits_to_f64(inp[name][a:b])
+        refs[e] = om.mx_expert_layer(sub("x_perm", r0, r1), sub("dy_perm", r0, r1), np.array([r1 - r0]),
+                                     sub("w_gate", e, e + 1), sub("w_up", e, e + 1), sub("w_down", e, e + 1))
+    # forward gate/up saw the oracle's inputs already (x and the weights)
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        for name, t in (("G", lay.g), ("U", lay.u), ("H", lay.h)):
+            got = host(t[r0:r1])
+            assert_close(got, refs[e][name], "mxfp8", f"{name}[{e}]")
+            assert np.mean(got == refs[e][name]) > 0.95, (name, e)
+    # the other ops on the oracle's intermediates for the sampled experts
+    b = lambda a: dev(f64_to_bf16_bits(a), "bf16")
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        for name, t in (("G", lay.g), ("U", lay.u), ("H", lay.h), ("dG", lay.dg), ("dU", lay.du)):
+            t[r0:r1] = b(refs[e][name])
+    G, U, H = lay.g.clone(), lay.u.clone(), lay.h.clone()
+    dG, dU = lay.dg.clone(), lay.du.clone()
+    P = lay.P
+    q = lambda src, t, axis=0: (L.moe_mx_quantize(src, 0, t.q, t.s) if axis == 0 else
+                                L.moe_mx_quantize(src, 1, t.q, t.s, offs, E, P))
+    q(H, lay.hq)
+    lay._gg(L.MOE_GG_FWD_DOWN, a0=lay.hq.t, b0=lay.wd_c.t, out0=lay.y_perm)
+    lay._gg(L.MOE_GG_DGRAD_DOWN, a0=lay.dyq.t, b0=lay.wd_r.t, g=G, u=U, out0=lay.dg, out1=lay.du)
+    q(dG, lay.dgq)
+    q(dU, lay.duq)
+    lay._gg(L.MOE_GG_DGRAD_GATE_UP, a0=lay.dgq.t, a1=lay.duq.t, b0=lay.wg_r.t, b1=lay.wu_r.t, out0=lay.dx_perm)
+    q(H, lay.h_c, 1)
+    lay._gg(L.MOE_GG_WGRAD_DOWN, a0=lay.h_c.t, b0=lay.dy_c.t, out0=lay.dw_down)
+    q(dG, lay.dg_c, 1)
+    q(dU, lay.du_c, 1)
+    lay._gg(L.MOE_GG_WGRAD_GATE_UP, a0=lay.x_c.t, b0=lay.dg_c.t, b1=lay.du_c.t, out0=lay.dw_gate, out1=lay.dw_up)
+    torch.cuda.synchronize()
+    report = {}
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        for name, got in (("y_perm", host(lay.y_perm[r0:r1])), ("dG", host(lay.dg[r0:r1])),
+                          ("dU", host(lay.du[r0:r1])), ("dx_perm", host(lay.dx_perm[r0:r1])),
+                          ("dw_gate", host(lay.dw_gate[e])), ("dw_up", host(lay.dw_up[e])),
+                          ("dw_down", host(lay.dw_down[e]))):
+            ref = refs[e][name] if not name.startswith("dw") else refs[e][name][0]
+            err = assert_close(got, ref, "mxfp8", f"{name}[{e}]")
+            same = float(np.mean(got == ref))
+            report[f"{name}[{e}]"] = (f"{err:.2e}", f"{same:.4f}")
+            assert err <= 8e-3 and same > 0.95, report
     print("rel err, exact fraction", report)
