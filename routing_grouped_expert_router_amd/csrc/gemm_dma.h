@@ -30,9 +30,13 @@ namespace moe {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 dbf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short ds4_t;
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int ST_, int OCC_ = 1> struct DmaCfg {
+// VAR_ bit 0: issue the next stage's loads one at a time between the last
+// sub-step's MFMAs instead of in one burst after the barrier; bit 1: raise
+// the wave's issue priority while it issues MFMAs.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int ST_, int OCC_ = 1, int VAR_ = 0> struct DmaCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = ST_;
   static constexpr int OCC = OCC_;                         // workgroups per CU
+  static constexpr bool INTERLEAVE = (VAR_ & 1) != 0, PRIO = (VAR_ & 2) != 0;
   static constexpr int NT = WM * WN * 64;
   static constexpr int NW = WM * WN;
   static constexpr int WMR = BM / WM, WNR = BN / WN;
@@ -144,6 +148,13 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_dma_kernel(GGArgs a) {
     group_rows(a, e, row0, K);
     mv = BM;
   }
+  // the tile decode read LDS; its results are the same in every lane
+  e = __builtin_amdgcn_readfirstlane(e);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  mv = __builtin_amdgcn_readfirstlane(mv);
+  K = __builtin_amdgcn_readfirstlane(K);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  tn = __builtin_amdgcn_readfirstlane(tn);
   const int n0 = tn * BNO;
   const size_t dF = (size_t)d * F;
 
@@ -241,7 +252,10 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_dma_kernel(GGArgs a) {
 
   // issue the loads of K step kt into ring slot `slot`
   const uint32_t lds_base = __builtin_amdgcn_readfirstlane(lds_addr_of(lds));
-  auto issue = [&](int kt, int slot) {
+  // load i (A loads first, then B) of this wave's share of K step kt into
+  // ring slot `slot`
+  constexpr int PER_STAGE = C::A_PER_WAVE + C::B_PER_WAVE;   // wave-loads per stage
+  auto issue_one = [&](int kt, int slot, int i) {
     const uint32_t sa = lds_base + (uint32_t)slot * C::STAGE_ELEMS * 2;
     const uint32_t sb = sa + A_ELEMS * 2;
     int ks = kt;
@@ -251,14 +265,17 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_dma_kernel(GGArgs a) {
       second = kt >= half;
       ks = second ? kt - half : kt;
     }
-#pragma unroll
-    for (int i = 0; i < C::A_PER_WAVE; ++i)
+    if (i < C::A_PER_WAVE) {
       dma16(second ? rA1 : rA0, sa + (wave * C::A_PER_WAVE + i) * 1024, a_off[i] + (uint32_t)ks * a_step);
-#pragma unroll
-    for (int i = 0; i < C::B_PER_WAVE; ++i) {
-      const bool use1 = DUAL ? (b_mat[i] != 0) : second;
-      dma16(use1 ? rB1 : rB0, sb + (wave * C::B_PER_WAVE + i) * 1024, b_off[i] + (uint32_t)ks * b_step);
+    } else {
+      const int j = i - C::A_PER_WAVE;
+      const bool use1 = DUAL ? (b_mat[j] != 0) : second;
+      dma16(use1 ? rB1 : rB0, sb + (wave * C::B_PER_WAVE + j) * 1024, b_off[j] + (uint32_t)ks * b_step);
     }
+  };
+  auto issue = [&](int kt, int slot) {
+#pragma unroll
+    for (int i = 0; i < PER_STAGE; ++i) issue_one(kt, slot, i);
   };
 
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -318,32 +335,56 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_dma_kernel(GGArgs a) {
     }
   };
   auto mfmas = [&](const dbf16x8_t (&af)[MI], const dbf16x8_t (&bfr)[NI]) {
+    if (C::PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+    if (C::PRIO) __builtin_amdgcn_s_setprio(0);
+  };
+  // the same MFMAs (when the wave has rows) with load i of K step kt issued
+  // after MFMA i (when `refill`): one instruction sequence for every case
+  auto mfmas_loading = [&](const dbf16x8_t (&af)[MI], const dbf16x8_t (&bfr)[NI], int kt, int slot, bool refill,
+                           bool act) {
+    static_assert(MI * NI >= PER_STAGE, "one load per MFMA at most");
+    if (C::PRIO) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        if (act) acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+        const int i = mi * NI + ni;
+        if (i < PER_STAGE && refill) issue_one(kt, slot, i);
+      }
+    if (C::PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- K loop over a ring of S slots. Step kt has KS sub-steps of 16. The
   // fragments of each sub-step are read while the previous sub-step's MFMAs
-  // run; before the last sub-step of step kt every wave waits for stage kt+1
-  // and meets the others at one barrier, so the first fragments of step kt+1
-  // are read under the last MFMAs of step kt. A slot is refilled only after
-  // the barrier that follows the last read of it.
+  // run, so all of step kt's fragments are in registers before the barrier
+  // that precedes its last sub-step (the barrier's fence drains LDS reads).
+  // At that barrier every wave has waited for step kt+1; right after it the
+  // slot of step kt is refilled with step kt+S, and step kt+1's first
+  // fragments are read under step kt's last MFMAs. A step's loads thus have
+  // S-1 steps to land.
   constexpr int KS = BK / 16;
-  constexpr int PER_STAGE = C::A_PER_WAVE + C::B_PER_WAVE;   // wave-loads per stage
-  static_assert(S >= 3, "ring depth");
+  static_assert(S >= 2, "ring depth");
   const int nk = (K + BK - 1) / BK;
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s)
+  for (int s = 0; s < S; ++s)
     if (s < nk) issue(s, s);
   dbf16x8_t af[2][MI], bfr[2][NI];
-  if (nk > 0) {
-    // stage 0 complete: at most S-2 later stages outstanding
-    if (nk - 1 >= S - 2) wait_vm<PER_STAGE * (S - 2)>();
-    else if (nk - 1 == 1) wait_vm<PER_STAGE>();
+  // s_waitcnt vmcnt(PER_STAGE * n), n = stages allowed in flight (< S)
+  auto wait_stages = [&](int n) {
+    if (S > 3 && n >= 3) wait_vm<PER_STAGE * (S > 3 ? 3 : 0)>();
+    else if (S > 2 && n == 2) wait_vm<PER_STAGE * (S > 2 ? 2 : 0)>();
+    else if (n == 1) wait_vm<PER_STAGE>();
     else wait_vm<0>();
+  };
+  static_assert(S <= 4, "wait_stages covers up to three stages in flight");
+  if (nk > 0) {
+    wait_stages(min(S, nk) - 1);   // step 0 complete
     __syncthreads();
     if (active) read_frags(0, 0, af[0], bfr[0]);
   }
@@ -354,16 +395,20 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_dma_kernel(GGArgs a) {
       const int cur = ks & 1, nxt = cur ^ 1;
       if (ks + 1 < KS) {
         if (active) read_frags(slot, ks + 1, af[nxt], bfr[nxt]);
+        if (active) mfmas(af[cur], bfr[cur]);
       } else {
-        // stage kt+1 complete: stages issued so far end at min(kt+S-2, nk-1)
-        const int after = min(kt + S - 2, nk - 1) - (kt + 1);
-        if (after >= S - 3 && S - 3 > 0) wait_vm<PER_STAGE * (S - 3 > 0 ? S - 3 : 0)>();
-        else wait_vm<0>();
+        // steps issued so far end at min(kt + S - 1, nk - 1); step kt+1 must be complete
+        if (kt + 1 < nk) wait_stages(min(kt + S - 1, nk - 1) - (kt + 1));
         __syncthreads();
-        if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+        const bool refill = kt + S < nk;
         if (kt + 1 < nk && active) read_frags((kt + 1) % S, 0, af[nxt], bfr[nxt]);
+        if (C::INTERLEAVE) {
+          mfmas_loading(af[cur], bfr[cur], kt + S, slot, refill, active);
+        } else {
+          if (refill) issue(kt + S, slot);
+          if (active) mfmas(af[cur], bfr[cur]);
+        }
       }
-      if (active) mfmas(af[cur], bfr[cur]);
     }
   }
 

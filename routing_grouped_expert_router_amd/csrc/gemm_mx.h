@@ -134,6 +134,13 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_mx_kernel(MxArgs x) {
     p_e = 128 * tot;
   }
   __syncthreads();   // every wave is past its reads of tile_start before the ring is filled
+  // the tile decode read LDS; its results are the same in every lane
+  e = __builtin_amdgcn_readfirstlane(e);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  mv = __builtin_amdgcn_readfirstlane(mv);
+  K = __builtin_amdgcn_readfirstlane(K);
+  m0 = __builtin_amdgcn_readfirstlane(m0);
+  tn = __builtin_amdgcn_readfirstlane(tn);
   const int n0 = tn * BNO;
 
   // ---- operands. Codes: base pointer of this expert's block (bytes), row
@@ -141,6 +148,7 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_mx_kernel(MxArgs x) {
   // column group c is at 4 * (R * c + r)): the whole buffer, its row count R,
   // the first column group g0 of this expert's K range, and the row of tile
   // row 0 (A: m, B: n before the dual split).
+  p_e = __builtin_amdgcn_readfirstlane(p_e);
   const int P = x.P;
   const uint8_t *qa0, *qa1, *qb0, *qb1;
   uint32_t lda, ldb, na, nb;

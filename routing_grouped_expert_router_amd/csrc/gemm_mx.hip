@@ -3,14 +3,29 @@
 // "Três números, três denominadores"); the kernel is in gemm_mx.h.
 #include "gemm_mx.h"
 
+#include <cstdlib>
+#include <string>
+
 namespace moe {
 namespace {
 
-// 128 x 256 tiles, 4 waves of 64 x 128, a 3-deep ring, two workgroups per CU.
-using CfgMx = MxCfg<128, 256, 2, 2, 3, 2>;
+// 128 x 256 tiles, a 3-deep ring, two workgroups per CU; 8 waves of 64 x 64
+// (default) or 4 waves of 64 x 128 (MOE_MX_TILE=w4, for tuning sweeps).
+using CfgMx = MxCfg<128, 256, 2, 4, 3, 2>;
+using CfgMx4 = MxCfg<128, 256, 2, 2, 3, 2>;
+static_assert(CfgMx::BM == CfgMx4::BM && CfgMx::BN == CfgMx4::BN, "same grid for both shapes");
+
+bool mx_four_waves() {
+  static const bool v = [] {
+    const char* s = std::getenv("MOE_MX_TILE");
+    return s && std::string(s) == "w4";
+  }();
+  return v;
+}
 
 template <int OP> void launch_mx_op(const MxArgs& x, int grid, hipStream_t s) {
-  gg_mx_kernel<OP, CfgMx><<<grid, CfgMx::NT, 0, s>>>(x);
+  if (mx_four_waves()) gg_mx_kernel<OP, CfgMx4><<<grid, CfgMx4::NT, 0, s>>>(x);
+  else gg_mx_kernel<OP, CfgMx><<<grid, CfgMx::NT, 0, s>>>(x);
 }
 
 int launch_mx(int op, const MxArgs& x, int grid, hipStream_t s) {
