@@ -164,12 +164,13 @@ def permute_bwd(dx_perm: np.ndarray, row_of: np.ndarray, T: int, k: int, store,
 
 
 def combine(y_perm: np.ndarray, row_of: np.ndarray, topk_w: np.ndarray, T: int,
-            k: int, store) -> np.ndarray:
+            k: int, store, extra: Optional[np.ndarray] = None) -> np.ndarray:
     """Weighted unpermute: y[t] = sum_j w[t,j] Y_perm[row_of[t,j]], dropped
-    slots contribute nothing. Reading: the gate weight multiplies the expert
-    output after the down projection."""
+    slots contribute nothing, plus ``extra`` (the shared expert's output)
+    before storing. Reading: the gate weight multiplies the expert output
+    after the down projection."""
     d = y_perm.shape[1]
-    acc = np.zeros((T, d))
+    acc = np.zeros((T, d)) if extra is None else np.array(extra, dtype=np.float64)
     ro = row_of.reshape(T, k)
     for j in range(k):
         live = ro[:, j] >= 0
@@ -299,9 +300,45 @@ def layer_forward(p: Dict[str, np.ndarray], k: int, dtype: str, capacity: int = 
     xp = permute(x, meta["src_slot"], k)
     G, U, H = expert_fwd_gate_up(xp, p["w_gate"], p["w_up"], groups, store)
     Y = expert_fwd_down(H, p["w_down"], groups, store)
-    y = combine(Y, meta["row_of"], w, T, k, store)
+    ys = None
+    if "w_gate_s" in p:
+        out.update(shared_forward(p, store))
+        ys = out["y_s"]
+    y = combine(Y, meta["row_of"], w, T, k, store, ys)
     out.update(x_perm=xp, G=G, U=U, H=H, y_perm=Y, y=y)
     return out
+
+
+def _shared_groups(T: int) -> Groups:
+    return [(0, T)]
+
+
+def shared_forward(p: Dict[str, np.ndarray], store) -> Dict[str, np.ndarray]:
+    """The shared expert: one SwiGLU FFN (w_gate_s, w_up_s [d,F_s], w_down_s
+    [F_s,d]) applied to every token, its stored output added to the routed
+    combine. The pages' production configurations use one shared expert next
+    to top-four routing (bigchange.ai pt-BR, "O que um engenheiro pode
+    realmente testar"; bigchange.ai id, "Apa yang benar-benar dapat dicoba
+    insinyur"); its size and placement are a reading: the same SwiGLU form as
+    a routed expert, added before y is stored."""
+    x = p["x"]
+    grp = _shared_groups(x.shape[0])
+    Gs, Us, Hs = expert_fwd_gate_up(x, p["w_gate_s"][None], p["w_up_s"][None], grp, store)
+    Ys = expert_fwd_down(Hs, p["w_down_s"][None], grp, store)
+    return dict(G_s=Gs, U_s=Us, H_s=Hs, y_s=Ys)
+
+
+def shared_backward(p: Dict[str, np.ndarray], fwd: Dict[str, np.ndarray], dy: np.ndarray,
+                    store) -> Dict[str, np.ndarray]:
+    """Chain rule of ``shared_forward``: its output gradient is dy itself."""
+    x = p["x"]
+    d, F = p["w_gate_s"].shape
+    grp = _shared_groups(x.shape[0])
+    dGs, dUs = expert_dgrad_down(dy, p["w_down_s"][None], fwd["G_s"], fwd["U_s"], grp, store)
+    dWds = expert_wgrad_down(fwd["H_s"], dy, grp, F, d, store)[0]
+    dXs = expert_dgrad_gate_up(dGs, dUs, p["w_gate_s"][None], p["w_up_s"][None], grp, store)
+    dWgs, dWus = expert_wgrad_gate_up(x, dGs, dUs, grp, d, F, store)
+    return dict(dG_s=dGs, dU_s=dUs, dx_s=dXs, dw_gate_s=dWgs[0], dw_up_s=dWus[0], dw_down_s=dWds)
 
 
 def layer_backward(p: Dict[str, np.ndarray], fwd: Dict[str, np.ndarray], dy: np.ndarray,
@@ -326,6 +363,9 @@ def layer_backward(p: Dict[str, np.ndarray], fwd: Dict[str, np.ndarray], dy: np.
         dl = route_bwd(fwd["topk_idx"], fwd["topk_w"], dw, E, r32)
         dWr, extra = router_bwd(p["x"], p["w_r"], dl, store)
         out.update(dlogits=dl, dw_r=dWr)
+    if "w_gate_s" in p:
+        out.update(shared_backward(p, fwd, dy, store))
+        extra = out["dx_s"] if extra is None else extra + out["dx_s"]
     out["dx"] = permute_bwd(dXp, fwd["row_of"], T, k, store, extra)
     return out
 

@@ -139,7 +139,8 @@ def _fd_check(p, k, capacity, names, seed):
     fwd = layer_forward(p, k, "f64", capacity=capacity,
                         logits=(p["x"] @ p["w_r"]) if "w_r" in p else None)
     g = layer_backward(p, fwd, dy, k, "f64", capacity=capacity)
-    gmap = {"x": "dx", "w_gate": "dw_gate", "w_up": "dw_up", "w_down": "dw_down", "w_r": "dw_r"}
+    gmap = {"x": "dx", "w_gate": "dw_gate", "w_up": "dw_up", "w_down": "dw_down", "w_r": "dw_r",
+            "w_gate_s": "dw_gate_s", "w_up_s": "dw_up_s", "w_down_s": "dw_down_s"}
 
     def loss(q):
         f = layer_forward(q, k, "f64", capacity=capacity,
@@ -180,6 +181,41 @@ def test_backward_finite_differences_padded_with_drops():
     m = expert_offsets(p["topk_idx"], E, 3)
     assert m["n_dropped"] > 0
     _fd_check(p, k, 3, ["x", "w_gate", "w_up", "w_down"], 18)
+
+
+def _with_shared(rng, p, F_s):
+    d = p["x"].shape[1]
+    p["w_gate_s"] = rng.standard_normal((d, F_s)) / np.sqrt(d)
+    p["w_up_s"] = rng.standard_normal((d, F_s)) / np.sqrt(d)
+    p["w_down_s"] = rng.standard_normal((F_s, d)) / np.sqrt(F_s)
+    return p
+
+
+def test_shared_expert_finite_differences():
+    rng = np.random.default_rng(19)
+    T, d, E, F, k = 8, 12, 4, 16, 2
+    p = _with_shared(rng, _params(rng, T, d, E, F, learned=False, k=k), 20)
+    _fd_check(p, k, 0, ["x", "w_gate_s", "w_up_s", "w_down_s"], 20)
+
+
+def test_shared_expert_equals_a_routed_expert_every_token_takes():
+    # one routed expert taken by every token with gate weight 1 and no shared
+    # expert, against a routed expert that outputs zero plus a shared expert
+    # with the same weights: forward and every gradient agree exactly
+    rng = np.random.default_rng(21)
+    T, d, F = 24, 16, 20
+    a = _params(rng, T, d, 1, F, learned=False, k=1)
+    a["topk_w"] = np.ones((T, 1))
+    b = {n: v.copy() for n, v in a.items()}
+    b["w_gate_s"], b["w_up_s"], b["w_down_s"] = a["w_gate"][0], a["w_up"][0], a["w_down"][0]
+    b["w_down"] = np.zeros_like(a["w_down"])
+    dy = rng.standard_normal((T, d))
+    fa, fb = layer_forward(a, 1, "f64"), layer_forward(b, 1, "f64")
+    assert np.array_equal(fa["y"], fb["y"])
+    ga, gb = layer_backward(a, fa, dy, 1, "f64"), layer_backward(b, fb, dy, 1, "f64")
+    assert np.array_equal(ga["dx"], gb["dx"])
+    for n in ("w_gate", "w_up", "w_down"):
+        assert np.array_equal(ga["d" + n][0], gb["d" + n + "_s"]), n
 
 
 def test_fp32_storage_is_close_to_f64():
