@@ -169,6 +169,64 @@ def timed(obj, step, steps, warmup):
     return (start.elapsed_time(end) / steps, {n: sum(v) / len(v) for n, v in stage_ms.items()}, wall)
 
 
+def shared_leg(wl, t, cap, steps, warmup, ms_base):
+    """The same workload with one shared expert (d_ff as a routed expert's)
+    beside the routed ones: a dense SwiGLU on every token whose output joins
+    y in the combine. Inputs of the shared weights are drawn on the device
+    from a seeded generator (normal, scaled by fan-in)."""
+    import torch
+    from routing_grouped_expert_router_amd.layer import MoELayer
+    Fs = wl.F
+    gen = torch.Generator(device="cuda").manual_seed(wl.seed + 1000)
+    rnd = lambda *shape, scale: (torch.randn(*shape, generator=gen, device="cuda") * scale).to(torch.bfloat16)
+    ws = dict(w_gate_s=rnd(wl.d, Fs, scale=wl.d ** -0.5), w_up_s=rnd(wl.d, Fs, scale=wl.d ** -0.5),
+              w_down_s=rnd(Fs, wl.d, scale=Fs ** -0.5))
+    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
+                     routing="learned" if wl.routing == "learned" else "given", capacity=cap, shared_ff=Fs)
+
+    def step():
+        layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
+                      topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"), **ws)
+        layer.backward(t["dy"])
+
+    ms, st, _ = timed(layer, step, steps, warmup)
+    del layer
+    torch.cuda.empty_cache()
+    sh_us = st.get("gg_shared_fwd", 0.0) + st.get("gg_shared_bwd", 0.0)
+    flops = 18.0 * wl.T * wl.d * Fs
+    return {"d_ff_shared": Fs, "tokens_per_s": round(wl.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+            "shared_gemm_us": round(sh_us * 1e3, 1),
+            "shared_gemm_tflops": round(flops / (sh_us / 1e3) / 1e12, 1) if sh_us > 0 else None,
+            "step_time_added": round(ms / ms_base - 1.0, 4)}
+
+
+def recompute_leg(wl, t, cap, steps, warmup, ms_base, base_layer):
+    """The same workload with per-layer recompute (the backward recomputes G,
+    U and H from x_perm): step time, the throughput given up, and the expert
+    activations no longer kept from the forward for the backward."""
+    import torch
+    from routing_grouped_expert_router_amd.layer import MoELayer
+    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
+                     routing="learned" if wl.routing == "learned" else "given", capacity=cap, recompute=True)
+
+    def step():
+        layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
+                      topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
+        layer.backward(t["dy"])
+
+    ms, _, _ = timed(layer, step, steps, warmup)
+    el = base_layer.x_perm.element_size()
+    kept_base = (base_layer.x_perm.numel() + base_layer.y_perm.numel()) * el \
+        + base_layer.activation_bytes_between_passes()
+    saved = base_layer.activation_bytes_between_passes() - layer.activation_bytes_between_passes()
+    del layer
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": round(wl.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+            "throughput_cost": round(1.0 - ms_base / ms, 4),
+            "expert_activation_bytes_saved": int(saved),
+            "fraction_of_kept_activations_saved": round(saved / kept_base, 4)}
+
+
 def experts_leg(steps, warmup):
     """The MXFP8 expert layer on its own workload (32 experts, d = 4096,
     d_ff = 2048, 32768 rows arriving grouped by expert with Zipf(0.8) counts:
@@ -250,6 +308,8 @@ def main():
                     help="> 0: run the padded-to-capacity path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mxfp8", action="store_true", help="skip the MXFP8 expert-layer leg")
+    ap.add_argument("--no-recompute", action="store_true", help="skip the per-layer recompute leg")
+    ap.add_argument("--no-shared", action="store_true", help="skip the shared-expert leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the reference "
@@ -356,6 +416,12 @@ def main():
         "wall_s_timed": round(wall, 3),
         "kernel_sources": kernel_source_hash(),
     }
+    if not args.no_recompute:
+        log("recompute leg ...")
+        out["recompute"] = recompute_leg(wl, t, cap, args.steps, args.warmup, ms, layer)
+    if not args.no_shared:
+        log("shared-expert leg ...")
+        out["shared_expert"] = shared_leg(wl, t, cap, args.steps, args.warmup, ms)
     if not args.no_mxfp8:
         log("MXFP8 expert-layer leg ...")
         out["mxfp8_experts"] = experts_leg(args.steps, args.warmup)

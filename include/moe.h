@@ -64,7 +64,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Text for a status code (static storage; never NULL). */
 const char* moe_status_string(int status);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 3. */
 int moe_abi_version(void);
 
 /* ----------------------------------------------------------------- router
@@ -121,14 +121,17 @@ int moe_offsets(const int32_t* topk_idx, int T, int k, int E, int capacity, int3
 int moe_permute(int dtype, const void* x, int T, int d, int k, const int32_t* row_of,
                 const int32_t* src_slot, int n_rows, void* x_perm, hipStream_t stream);
 
-/* moe_unpermute_combine: y[t] = sum_j w[t,j] * y_perm[row_of[t,j]], binary32
- * accumulation in slot order j = 0..k-1; dropped slots (row -1) add nothing.
- * Reading: the gate weight scales each expert's output after the down
- * projection.
- *   y_perm [n_rows,d], y [T,d] of `dtype`; topk_w [T,k] binary32. */
+/* moe_unpermute_combine: y[t] = y_add[t] + sum_j w[t,j] * y_perm[row_of[t,j]],
+ * binary32 accumulation in slot order j = 0..k-1, one rounding to `dtype`;
+ * dropped slots (row -1) add nothing. Reading: the gate weight scales each
+ * expert's output after the down projection. y_add (may be NULL) is the
+ * shared expert's output, which the pages' production configurations add to
+ * the routed experts' (bigchange.ai pt-BR, "O que um engenheiro pode
+ * realmente testar").
+ *   y_perm [n_rows,d], y_add and y [T,d] of `dtype`; topk_w [T,k] binary32. */
 int moe_unpermute_combine(int dtype, const void* y_perm, const int32_t* row_of,
-                          const float* topk_w, int T, int k, int d, int n_rows, void* y,
-                          hipStream_t stream);
+                          const float* topk_w, int T, int k, int d, int n_rows,
+                          const void* y_add, void* y, hipStream_t stream);
 
 /* moe_unpermute_combine_bwd: adjoint of moe_unpermute_combine.
  *   dy_perm[row_of[t,j]] = w[t,j] * dy[t]   (rounded once to `dtype`)
@@ -141,14 +144,16 @@ int moe_unpermute_combine_bwd(int dtype, const void* dy, const void* y_perm,
                               void* dy_perm, float* dtopk_w, hipStream_t stream);
 
 /* moe_permute_bwd: adjoint of moe_permute,
- *   dx[t] = sum_j dx_perm[row_of[t,j]]  (+ sum_e dlogits[t,e] * w_r[:,e])
+ *   dx[t] = dx_add[t] + sum_j dx_perm[row_of[t,j]]  (+ sum_e dlogits[t,e] * w_r[:,e])
  * binary32 accumulation, one rounding to `dtype`. The router term is added
  * when dlogits and w_r are not NULL (learned router); it is the router
- * GEMM's share of dx, folded in so that dx is written once.
- *   dx_perm [n_rows,d], dx [T,d], w_r [d,E] of `dtype`; dlogits [T,E] f32. */
+ * GEMM's share of dx, folded in so that dx is written once. dx_add (may be
+ * NULL) is the shared expert's share of dx.
+ *   dx_perm [n_rows,d], dx_add and dx [T,d], w_r [d,E] of `dtype`;
+ *   dlogits [T,E] f32. */
 int moe_permute_bwd(int dtype, const void* dx_perm, const int32_t* row_of, int T, int k, int d,
-                    int n_rows, const float* dlogits, const void* w_r, int E, void* dx,
-                    hipStream_t stream);
+                    int n_rows, const float* dlogits, const void* w_r, int E, const void* dx_add,
+                    void* dx, hipStream_t stream);
 
 /* ----------------------------------------------------------------- router backward
  * moe_route_bwd: dlogits through the renormalised top-k gate with the

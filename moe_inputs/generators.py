@@ -40,6 +40,7 @@ _TAGS = {
     "x": 1, "w_r": 2, "w_gate": 3, "w_up": 4, "w_down": 5, "dy": 6,
     "route_perm": 7, "route_w": 8, "zipf_perm": 9, "gumbel": 10,
     "x_perm": 11, "dy_perm": 12, "group_perm": 13,
+    "w_gate_s": 14, "w_up_s": 15, "w_down_s": 16,
 }
 
 
@@ -58,6 +59,7 @@ class Workload:
     zipf_s: float = 0.0
     zero_cold: int = 0
     capacity_factor: float = 0.0   # > 0: padded-to-capacity comparison path
+    shared_ff: int = 0             # > 0: one shared expert of this hidden size
 
     @property
     def R(self) -> int:
@@ -176,7 +178,8 @@ def make_inputs(wl: Workload, with_weights: bool = True) -> Dict[str, np.ndarray
     """Inputs of one workload. Keys present depend on the routing mode:
     x [T,d] (or x_perm [R,d] and counts [E] when pregrouped), w_r [d,E]
     (learned), topk_idx [T,k] int32 and topk_w [T,k] float32 (uniform, zipf),
-    w_gate, w_up [E,d,F], w_down [E,F,d], dy [T,d] (or dy_perm [R,d])."""
+    w_gate, w_up [E,d,F], w_down [E,F,d], dy [T,d] (or dy_perm [R,d]); with a
+    shared expert also w_gate_s, w_up_s [d,F_s] and w_down_s [F_s,d]."""
     T, d, E, k, F, s = wl.T, wl.d, wl.E, wl.k, wl.F, wl.seed
     st = "f32" if wl.dtype == "f32" else "bf16"
     out: Dict[str, np.ndarray] = {}
@@ -201,4 +204,9 @@ def make_inputs(wl: Workload, with_weights: bool = True) -> Dict[str, np.ndarray
         out["w_gate"] = _store(_normal(s, "w_gate", (E, d, F), d ** -0.5), st)
         out["w_up"] = _store(_normal(s, "w_up", (E, d, F), d ** -0.5), st)
         out["w_down"] = _store(_normal(s, "w_down", (E, F, d), F ** -0.5), st)
+        if wl.shared_ff > 0:
+            Fs = wl.shared_ff
+            out["w_gate_s"] = _store(_normal(s, "w_gate_s", (d, Fs), d ** -0.5), st)
+            out["w_up_s"] = _store(_normal(s, "w_up_s", (d, Fs), d ** -0.5), st)
+            out["w_down_s"] = _store(_normal(s, "w_down_s", (Fs, d), Fs ** -0.5), st)
     return out

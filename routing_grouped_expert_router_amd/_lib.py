@@ -57,9 +57,9 @@ SIGNATURES = {
     "moe_offsets_workspace_bytes": (_sz, [_i, _i, _i]),
     "moe_offsets": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_permute": (_i, [_i, _vp, _i, _i, _i, _vp, _vp, _i, _vp, _vp]),
-    "moe_unpermute_combine": (_i, [_i, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
+    "moe_unpermute_combine": (_i, [_i, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]),
     "moe_unpermute_combine_bwd": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]),
-    "moe_permute_bwd": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp]),
+    "moe_permute_bwd": (_i, [_i, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _vp, _vp, _vp]),
     "moe_route_bwd": (_i, [_vp, _vp, _vp, _i, _i, _i, _vp, _vp]),
     "moe_router_bwd_workspace_bytes": (_sz, [_i, _i, _i]),
     "moe_router_gemm_bwd": (_i, [_i, _vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp]),
@@ -161,10 +161,10 @@ def moe_permute(x, k, row_of, src_slot, x_perm, stream=None):
                              _p(x_perm), _stream(stream)), "moe_permute")
 
 
-def moe_unpermute_combine(y_perm, row_of, topk_w, y, stream=None):
+def moe_unpermute_combine(y_perm, row_of, topk_w, y, y_add=None, stream=None):
     T, k = topk_w.shape
     _check(lib().moe_unpermute_combine(_dt(y), _p(y_perm), _p(row_of), _p(topk_w), T, k, y.shape[1],
-                                       y_perm.shape[0], _p(y), _stream(stream)),
+                                       y_perm.shape[0], _p(y_add), _p(y), _stream(stream)),
            "moe_unpermute_combine")
 
 
@@ -176,11 +176,11 @@ def moe_unpermute_combine_bwd(dy, y_perm, topk_w, row_of, src_slot, dy_perm, dto
            "moe_unpermute_combine_bwd")
 
 
-def moe_permute_bwd(dx_perm, row_of, k, dx, dlogits=None, w_r=None, stream=None):
+def moe_permute_bwd(dx_perm, row_of, k, dx, dlogits=None, w_r=None, dx_add=None, stream=None):
     T, d = dx.shape
     E = 0 if w_r is None else w_r.shape[1]
     _check(lib().moe_permute_bwd(_dt(dx), _p(dx_perm), _p(row_of), T, k, d, dx_perm.shape[0],
-                                 _p(dlogits), _p(w_r), E, _p(dx), _stream(stream)),
+                                 _p(dlogits), _p(w_r), E, _p(dx_add), _p(dx), _stream(stream)),
            "moe_permute_bwd")
 
 

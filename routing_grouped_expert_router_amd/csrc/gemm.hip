@@ -353,6 +353,7 @@ extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
         case 6: return launch_dma<CfgDma128p>(g, a, kvar, dual, N, stream);
         case 7: return launch_dma<CfgDma128ip>(g, a, kvar, dual, N, stream);
         case 8: return launch_dma<CfgDma128w8>(g, a, kvar, dual, N, stream);
+
         default: break;
       }
     }

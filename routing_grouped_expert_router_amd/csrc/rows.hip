@@ -58,12 +58,15 @@ __global__ void __launch_bounds__(kRowThreads) zero_pad_rows_kernel(const int32_
   for (int c = lane; c < d / V; c += 64) dst[c] = z;
 }
 
-// y[t] = sum_j w[t, j] y_perm[row_of[t, j]]  (binary32, slot order)
+// y[t] = y_add[t] + sum_j w[t, j] y_perm[row_of[t, j]]  (binary32, slot order;
+// y_add optional)
 template <typename T>
 __global__ void __launch_bounds__(kRowThreads) combine_kernel(const T* __restrict__ y_perm,
                                                               const int32_t* __restrict__ row_of,
                                                               const float* __restrict__ topk_w, int T_,
-                                                              int k, int d, int n_rows, T* __restrict__ y) {
+                                                              int k, int d, int n_rows,
+                                                              const T* __restrict__ y_add,
+                                                              T* __restrict__ y) {
   constexpr int V = kVec<T>;
   const size_t t = ((size_t)blockIdx.x * kRowThreads + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
@@ -76,8 +79,12 @@ __global__ void __launch_bounds__(kRowThreads) combine_kernel(const T* __restric
   const int nvec = d / V;
   for (int c = lane; c < nvec; c += 64) {
     float acc[V];
+    if (y_add) {
+      unpack(reinterpret_cast<const V16*>(y_add + t * d)[c], acc);
+    } else {
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
       if (j < k && rows[j] >= 0) {
@@ -136,12 +143,13 @@ __global__ void __launch_bounds__(kRowThreads) combine_bwd_kernel(
   }
 }
 
-// dx[t] = sum_j dx_perm[row_of[t, j]] (+ sum_e dlogits[t, e] w_r[:, e])
+// dx[t] = dx_add[t] + sum_j dx_perm[row_of[t, j]] (+ sum_e dlogits[t, e] w_r[:, e]);
+// dx_add and the router term optional
 template <typename T>
 __global__ void __launch_bounds__(kRowThreads) permute_bwd_kernel(
     const T* __restrict__ dx_perm, const int32_t* __restrict__ row_of, int T_, int k, int d,
     int n_rows, const float* __restrict__ dlogits, const T* __restrict__ w_r, int E,
-    T* __restrict__ dx) {
+    const T* __restrict__ dx_add, T* __restrict__ dx) {
   constexpr int V = kVec<T>;
   const size_t t = ((size_t)blockIdx.x * kRowThreads + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
@@ -153,8 +161,12 @@ __global__ void __launch_bounds__(kRowThreads) permute_bwd_kernel(
   const bool wide = router && (E % V == 0);
   for (int c = lane; c < nvec; c += 64) {
     float acc[V];
+    if (dx_add) {
+      unpack(reinterpret_cast<const V16*>(dx_add + t * d)[c], acc);
+    } else {
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
       if (j < k && rows[j] >= 0) {
@@ -236,18 +248,20 @@ extern "C" int moe_permute(int dtype, const void* x, int T, int d, int k, const 
 }
 
 extern "C" int moe_unpermute_combine(int dtype, const void* y_perm, const int32_t* row_of,
-                                     const float* topk_w, int T, int k, int d, int n_rows, void* y,
-                                     hipStream_t stream) {
+                                     const float* topk_w, int T, int k, int d, int n_rows,
+                                     const void* y_add, void* y, hipStream_t stream) {
   if (int st = check_rows(dtype, T, d, k, n_rows)) return st;
   if (T == 0) return MOE_OK;
   MOE_CHECK_ARG(row_of && topk_w && y && aligned16(y) && (n_rows == 0 || (y_perm && aligned16(y_perm))));
+  MOE_CHECK_ARG(!y_add || aligned16(y_add));
   if (dtype == MOE_BF16)
     combine_kernel<uint16_t><<<row_grid(T), kRowThreads, 0, stream>>>(
         static_cast<const uint16_t*>(y_perm), row_of, topk_w, T, k, d, n_rows,
-        static_cast<uint16_t*>(y));
+        static_cast<const uint16_t*>(y_add), static_cast<uint16_t*>(y));
   else
     combine_kernel<float><<<row_grid(T), kRowThreads, 0, stream>>>(
-        static_cast<const float*>(y_perm), row_of, topk_w, T, k, d, n_rows, static_cast<float*>(y));
+        static_cast<const float*>(y_perm), row_of, topk_w, T, k, d, n_rows,
+        static_cast<const float*>(y_add), static_cast<float*>(y));
   return launch_status();
 }
 
@@ -278,19 +292,20 @@ extern "C" int moe_unpermute_combine_bwd(int dtype, const void* dy, const void* 
 
 extern "C" int moe_permute_bwd(int dtype, const void* dx_perm, const int32_t* row_of, int T, int k,
                                int d, int n_rows, const float* dlogits, const void* w_r, int E,
-                               void* dx, hipStream_t stream) {
+                               const void* dx_add, void* dx, hipStream_t stream) {
   if (int st = check_rows(dtype, T, d, k, n_rows)) return st;
   MOE_CHECK_ARG((dlogits == nullptr) == (w_r == nullptr));
   MOE_CHECK_ARG(!dlogits || (E > 0 && E <= MOE_MAX_EXPERTS && aligned16(w_r)));
   if (T == 0) return MOE_OK;
   MOE_CHECK_ARG(row_of && dx && aligned16(dx) && (n_rows == 0 || (dx_perm && aligned16(dx_perm))));
+  MOE_CHECK_ARG(!dx_add || aligned16(dx_add));
   if (dtype == MOE_BF16)
     permute_bwd_kernel<uint16_t><<<row_grid(T), kRowThreads, 0, stream>>>(
         static_cast<const uint16_t*>(dx_perm), row_of, T, k, d, n_rows, dlogits,
-        static_cast<const uint16_t*>(w_r), E, static_cast<uint16_t*>(dx));
+        static_cast<const uint16_t*>(w_r), E, static_cast<const uint16_t*>(dx_add), static_cast<uint16_t*>(dx));
   else
     permute_bwd_kernel<float><<<row_grid(T), kRowThreads, 0, stream>>>(
         static_cast<const float*>(dx_perm), row_of, T, k, d, n_rows, dlogits,
-        static_cast<const float*>(w_r), E, static_cast<float*>(dx));
+        static_cast<const float*>(w_r), E, static_cast<const float*>(dx_add), static_cast<float*>(dx));
   return launch_status();
 }

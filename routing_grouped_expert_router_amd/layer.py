@@ -13,6 +13,21 @@ routing requires -- deniz.in, "Yeni stack nasıl çalışıyor"):
 
 With ``routing='given'`` the top-k ids and gate weights are inputs (the pages'
 random-routed system benchmarks) and the router steps are skipped.
+
+With ``shared_ff > 0`` the layer also has one shared expert: a SwiGLU FFN of
+hidden size shared_ff applied to every token, run as a one-group grouped GEMM
+over the token rows; its output is added inside the combine and its share of
+dx inside the permute adjoint, so y and dx are still written once (the pages'
+production configurations pair top-four routing with one shared expert:
+bigchange.ai pt-BR, "O que um engenheiro pode realmente testar").
+
+With ``recompute=True`` the expert activations G, U and H are treated as
+scratch that need not survive from the forward to the backward: the backward
+runs the gate/up grouped GEMM again from x_perm before its first expert
+GEMM. This is the pages' per-layer recompute, which trades activation memory
+for throughput (p1 deniz.in, "Ai2'nin raporladığı sayılar"; unite.ai/hi,
+"पैरालेलिज़्म, प्रिसीजन, और मेमोरी तकनीकें"). The recomputed values are
+bitwise those of the forward (the kernels are deterministic).
 """
 from __future__ import annotations
 
@@ -26,11 +41,12 @@ from . import _lib as L
 class MoELayer:
     def __init__(self, T: int, d: int, E: int, k: int, F: int, dtype=torch.bfloat16,
                  routing: str = "learned", capacity: int = 0, backward: bool = True,
-                 device: str = "cuda"):
+                 device: str = "cuda", recompute: bool = False, shared_ff: int = 0):
         if routing not in ("learned", "given"):
             raise ValueError(routing)
         self.T, self.d, self.E, self.k, self.F = T, d, E, k, F
         self.dtype, self.routing, self.capacity = dtype, routing, capacity
+        self.recompute = recompute
         self.R = T * k
         self.n_rows = E * capacity if capacity > 0 else self.R
         dev = torch.device(device)
@@ -67,6 +83,16 @@ class MoELayer:
                 self.dw_r = e(d, E)
                 wsr = max(L.moe_router_bwd_workspace_bytes(T, d, E), 16)
                 self.ws_router = e((wsr + 15) // 16 * 4, dt=f32)
+        self.shared_ff = shared_ff
+        if shared_ff > 0:
+            Fs = shared_ff
+            self.offsets_s = torch.tensor([0, T], dtype=i32, device=dev)
+            self.g_s, self.u_s, self.h_s = e(T, Fs), e(T, Fs), e(T, Fs)
+            self.y_s = e(T, d)
+            if backward:
+                self.dg_s, self.du_s = e(T, Fs), e(T, Fs)
+                self.dx_s = e(T, d)
+                self.dw_gate_s, self.dw_up_s, self.dw_down_s = e(d, Fs), e(d, Fs), e(Fs, d)
         self._dt = L.MOE_BF16 if dtype == torch.bfloat16 else L.MOE_F32
         # optional callable(stage_name) run after each stage is enqueued (used
         # by the benchmark to record per-stage events)
@@ -90,8 +116,33 @@ class MoELayer:
         L.moe_route(self.logits, self.k, self.topk_idx, self.topk_w)
         self._mark("route")
 
-    def forward(self, x, w_gate, w_up, w_down, w_r=None, topk_idx=None, topk_w=None):
+    def _gg_shared(self, op, **tensors):
+        desc = L.make_gg_desc(op, self._dt, 1, self.d, self.shared_ff, self.T, 0, self.offsets_s, **tensors)
+        L.moe_grouped_gemm(desc)
+
+    def shared_forward(self):
+        self._gg_shared(L.MOE_GG_FWD_GATE_UP, x_perm=self.x, w_gate=self.w_gate_s, w_up=self.w_up_s,
+                        g=self.g_s, u=self.u_s, h=self.h_s)
+        self._gg_shared(L.MOE_GG_FWD_DOWN, h=self.h_s, w_down=self.w_down_s, y_perm=self.y_s)
+        self._mark("gg_shared_fwd")
+
+    def shared_backward(self, dy):
+        self._gg_shared(L.MOE_GG_DGRAD_DOWN, dy_perm=dy, w_down=self.w_down_s, g=self.g_s, u=self.u_s,
+                        dg=self.dg_s, du=self.du_s)
+        self._gg_shared(L.MOE_GG_WGRAD_DOWN, h=self.h_s, dy_perm=dy, dw_down=self.dw_down_s)
+        self._gg_shared(L.MOE_GG_DGRAD_GATE_UP, dg=self.dg_s, du=self.du_s, w_gate=self.w_gate_s,
+                        w_up=self.w_up_s, dx_perm=self.dx_s)
+        self._gg_shared(L.MOE_GG_WGRAD_GATE_UP, x_perm=self.x, dg=self.dg_s, du=self.du_s,
+                        dw_gate=self.dw_gate_s, dw_up=self.dw_up_s)
+        self._mark("gg_shared_bwd")
+
+    def forward(self, x, w_gate, w_up, w_down, w_r=None, topk_idx=None, topk_w=None,
+                w_gate_s=None, w_up_s=None, w_down_s=None):
         self.x, self.w_gate, self.w_up, self.w_down, self.w_r = x, w_gate, w_up, w_down, w_r
+        if self.shared_ff > 0:
+            if w_gate_s is None or w_up_s is None or w_down_s is None:
+                raise ValueError("a layer with a shared expert needs its weights")
+            self.w_gate_s, self.w_up_s, self.w_down_s = w_gate_s, w_up_s, w_down_s
         if self.routing == "learned":
             self.route(x, w_r)
         else:
@@ -99,6 +150,8 @@ class MoELayer:
         self.metadata()
         self.permute()
         self.experts_forward()
+        if self.shared_ff > 0:
+            self.shared_forward()
         self.combine()
         return self.y
 
@@ -120,7 +173,8 @@ class MoELayer:
         self._mark("gg_fwd_down")
 
     def combine(self):
-        L.moe_unpermute_combine(self.y_perm, self.row_of, self.topk_w, self.y)
+        L.moe_unpermute_combine(self.y_perm, self.row_of, self.topk_w, self.y,
+                                y_add=self.y_s if self.shared_ff > 0 else None)
         self._mark("combine")
 
     def backward(self, dy):
@@ -129,18 +183,33 @@ class MoELayer:
                                     self.dy_perm, self.dtopk_w)
         self._mark("combine_bwd")
         self.experts_backward()
+        dx_add = None
+        if self.shared_ff > 0:
+            self.shared_backward(dy)
+            dx_add = self.dx_s
         if self.routing == "learned":
             L.moe_route_bwd(self.topk_idx, self.topk_w, self.dtopk_w, self.E, self.dlogits)
             self._mark("route_bwd")
             L.moe_router_gemm_bwd(self.x, self.dlogits, self.dw_r, self.ws_router)
             self._mark("router_gemm_bwd")
-            L.moe_permute_bwd(self.dx_perm, self.row_of, self.k, self.dx, self.dlogits, self.w_r)
+            L.moe_permute_bwd(self.dx_perm, self.row_of, self.k, self.dx, self.dlogits, self.w_r,
+                              dx_add=dx_add)
         else:
-            L.moe_permute_bwd(self.dx_perm, self.row_of, self.k, self.dx)
+            L.moe_permute_bwd(self.dx_perm, self.row_of, self.k, self.dx, dx_add=dx_add)
         self._mark("permute_bwd")
         return self.dx
 
+    def activation_bytes_between_passes(self) -> int:
+        """Bytes of expert activations the forward must leave for the backward
+        (besides x_perm, which both modes keep): G, U and H, or none when
+        recomputing."""
+        return 0 if self.recompute else 3 * self.n_rows * self.F * self.g.element_size()
+
     def experts_backward(self):
+        if self.recompute:
+            self._gg(L.MOE_GG_FWD_GATE_UP, x_perm=self.x_perm, w_gate=self.w_gate, w_up=self.w_up,
+                     g=self.g, u=self.u, h=self.h)
+            self._mark("gg_recompute_gate_up")
         self._gg(L.MOE_GG_DGRAD_DOWN, dy_perm=self.dy_perm, w_down=self.w_down, g=self.g, u=self.u,
                  dg=self.dg, du=self.du)
         self._mark("gg_dgrad_down")
@@ -156,6 +225,8 @@ class MoELayer:
     def grads(self) -> Dict[str, torch.Tensor]:
         out = dict(dx=self.dx, dw_gate=self.dw_gate, dw_up=self.dw_up, dw_down=self.dw_down,
                    dtopk_w=self.dtopk_w)
+        if self.shared_ff > 0:
+            out.update(dw_gate_s=self.dw_gate_s, dw_up_s=self.dw_up_s, dw_down_s=self.dw_down_s)
         if self.routing == "learned":
             out.update(dlogits=self.dlogits, dw_r=self.dw_r)
         return out

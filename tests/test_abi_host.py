@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 def test_binding_covers_every_declared_symbol():
     assert sorted(L.SIGNATURES) == declared()
     lib = L.lib()
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(-3) == b"workspace missing or too small"
     assert lib.moe_status_string(12345) == b"unknown status"
@@ -88,11 +88,13 @@ def test_row_calls_argument_errors():
     # misaligned tensor
     assert lib.moe_permute(1, FAKE + 2, 10, 16, 2, FAKE, None, 20, FAKE, None) == INVALID
     # bad dtype
-    assert lib.moe_unpermute_combine(7, FAKE, FAKE, FAKE, 10, 2, 16, 20, FAKE, None) == INVALID
-    assert lib.moe_unpermute_combine(1, FAKE, FAKE, FAKE, 10, 17, 16, 20, FAKE, None) == UNSUPPORTED
+    assert lib.moe_unpermute_combine(7, FAKE, FAKE, FAKE, 10, 2, 16, 20, None, FAKE, None) == INVALID
+    assert lib.moe_unpermute_combine(1, FAKE, FAKE, FAKE, 10, 17, 16, 20, None, FAKE, None) == UNSUPPORTED
+    assert lib.moe_unpermute_combine(1, FAKE, FAKE, FAKE, 10, 2, 16, 20, FAKE + 4, FAKE, None) == INVALID
     assert lib.moe_unpermute_combine_bwd(1, FAKE, FAKE, FAKE, FAKE, None, 10, 2, 16, 21, FAKE, FAKE, None) == INVALID
     # router share needs both dlogits and w_r
-    assert lib.moe_permute_bwd(1, FAKE, FAKE, 10, 2, 16, 20, FAKE, None, 8, FAKE, None) == INVALID
+    assert lib.moe_permute_bwd(1, FAKE, FAKE, 10, 2, 16, 20, FAKE, None, 8, None, FAKE, None) == INVALID
+    assert lib.moe_permute_bwd(1, FAKE, FAKE, 10, 2, 16, 20, None, None, 0, FAKE + 2, FAKE, None) == INVALID
     assert lib.moe_route_bwd(FAKE, FAKE, FAKE, 10, 4, 5, FAKE, None) == INVALID
 
 

@@ -159,6 +159,13 @@ def test_row_movement_parity(kind, T, d, E, k, C):
     dl = round_f32(rng.standard_normal((T, E)))
     L.moe_permute_bwd(dxpt, row_of, k, dx, dev(dl.astype(np.float32), "f32"), wrt)
     assert_close(host(dx), om.permute_bwd(dxp, meta["row_of"], T, k, st, dl @ wr.T), kind, "dx+router")
+    # the shared expert's shares: added to y and to dx before rounding
+    yat, ya = _to(rng.standard_normal((T, d)), kind)
+    L.moe_unpermute_combine(ypt, row_of, dev(wt, "f32"), y, y_add=yat)
+    assert_close(host(y), om.combine(yp, meta["row_of"], w, T, k, st, ya), kind, "y+shared")
+    L.moe_permute_bwd(dxpt, row_of, k, dx, dev(dl.astype(np.float32), "f32"), wrt, dx_add=yat)
+    assert_close(host(dx), om.permute_bwd(dxp, meta["row_of"], T, k, st, dl @ wr.T + ya), kind,
+                 "dx+router+shared")
 
 
 # ----------------------------------------------------------------------------- router

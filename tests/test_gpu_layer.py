@@ -244,3 +244,66 @@ def test_deterministic_bitwise():
     b, _ = _run_gpu(wl, inp)
     for n, v in snap.items():
         assert np.array_equal(host(getattr(b, n)), v), n
+
+
+@pytest.mark.parametrize("name,over", [("e128_uniform_bf16", dict(T=2048, E=16, d=512, F=256)),
+                                       ("e8_learned_bf16", dict(T=1024, d=256, F=512))])
+def test_recompute_backward_matches_bitwise(name, over):
+    # per-layer recompute: the backward recomputes G, U, H from x_perm, so the
+    # forward's copies may be overwritten in between (they are filled with NaN
+    # here) and every gradient must still equal the stored-activation run's
+    wl = workload(name).scaled(**over)
+    inp = make_inputs(wl)
+    ref, _ = _run_gpu(wl, inp)
+    snap = {n: host(getattr(ref, n)).copy() for n in ("y", "dx", "dw_gate", "dw_up", "dw_down", "dtopk_w",
+                                                      "dg", "du")}
+    if wl.routing == "learned":
+        snap.update(dlogits=host(ref.dlogits).copy(), dw_r=host(ref.dw_r).copy())
+    del ref
+    t = _upload(inp, "bf16")
+    lay = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
+                   routing="learned" if wl.routing == "learned" else "given", recompute=True)
+    lay.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
+                topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
+    for buf in (lay.g, lay.u, lay.h):
+        buf.fill_(float("nan"))
+    lay.backward(t["dy"])
+    torch.cuda.synchronize()
+    assert lay.activation_bytes_between_passes() == 0
+    for n, v in snap.items():
+        assert np.array_equal(host(getattr(lay, n)), v, equal_nan=False), n
+
+
+@pytest.mark.parametrize("name,over", [("e128_uniform_bf16", dict(T=1024, E=16, d=256, F=256, shared_ff=256)),
+                                       ("e8_learned_bf16", dict(T=512, d=256, F=512, shared_ff=768))])
+def test_shared_expert_layer_full(name, over):
+    # one shared expert beside the routed ones: its output joins y inside the
+    # combine and its share of dx joins the permute adjoint
+    wl = workload(name).scaled(**over)
+    inp = make_inputs(wl)
+    t = _upload(inp, "bf16")
+    lay = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
+                   routing="learned" if wl.routing == "learned" else "given", shared_ff=wl.shared_ff)
+    lay.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
+                topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"),
+                w_gate_s=t["w_gate_s"], w_up_s=t["w_up_s"], w_down_s=t["w_down_s"])
+    lay.backward(t["dy"])
+    torch.cuda.synchronize()
+    names = ("x", "w_gate", "w_up", "w_down", "w_r", "w_gate_s", "w_up_s", "w_down_s")
+    p = {n: values(inp[n], "bf16") for n in names if n in inp}
+    if "topk_idx" in inp:
+        p["topk_idx"], p["topk_w"] = inp["topk_idx"], inp["topk_w"].astype(np.float64)
+    fwd = om.layer_forward(p, wl.k, "bf16")
+    agree = np.ones(wl.T, bool)
+    if "w_r" in p:
+        _, _, agree = _check_routing(lay, fwd["logits"], wl.k)
+    for n, ref in (("g_s", "G_s"), ("u_s", "U_s"), ("h_s", "H_s"), ("y_s", "y_s")):
+        assert_close(host(getattr(lay, n)), fwd[ref], "bf16", n)
+    assert_close(host(lay.y)[agree], fwd["y"][agree], "bf16", "y")
+    bwd = om.layer_backward(p, fwd, values(inp["dy"], "bf16"), wl.k, "bf16")
+    for n, ref in (("dg_s", "dG_s"), ("du_s", "dU_s"), ("dx_s", "dx_s"), ("dw_gate_s", "dw_gate_s"),
+                   ("dw_up_s", "dw_up_s"), ("dw_down_s", "dw_down_s")):
+        assert_close(host(getattr(lay, n)), bwd[ref], "bf16", n)
+    assert_close(host(lay.dx)[agree], bwd["dx"][agree], "bf16", "dx")
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        assert_close(host(getattr(lay, n)), bwd[n], "bf16", n)
