@@ -421,3 +421,44 @@ def mx_expert_layer(x_perm, dy_perm, counts, w_gate, w_up, w_down) -> Dict[str, 
         dWu[e] = st(Xt @ _mx_rows(dU[r0:r1].T).T)
     return dict(G=G, U=U, H=H, y_perm=Y, dG=dG, dU=dU, dx_perm=dX,
                 dw_gate=dWg, dw_up=dWu, dw_down=dWd)
+
+
+# ----------------------------------------------------------------------------- MXFP8 routed layer
+def mx_layer(p: Dict[str, np.ndarray], k: int, dy: np.ndarray,
+             logits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Forward and backward of the whole routed layer with every expert GEMM
+    in MXFP8 (``mx_expert_layer`` on the permuted rows) and everything else as
+    in the bf16 layer: routing, offsets, permute, combine and their adjoints,
+    bf16 storage. Dropless. The pages report MXFP8 against BF16 on the
+    feed-forward of a routed model (bigchange.ai pt-BR, "Três números, três
+    denominadores"); the routed rows are what the expert layer receives."""
+    st, r32 = storer("bf16"), _f32("bf16")
+    x = p["x"]
+    T = x.shape[0]
+    E = p["w_gate"].shape[0]
+    out: Dict[str, np.ndarray] = {}
+    if "w_r" in p:
+        out["logits"] = r32(x @ p["w_r"]) if logits is None else logits
+        idx, w = route(out["logits"], k, r32)
+    else:
+        idx, w = p["topk_idx"].astype(np.int32), r32(p["topk_w"])
+    out["topk_idx"], out["topk_w"] = idx, w
+    meta = expert_offsets(idx, E)
+    out.update(meta)
+    xp = permute(x, meta["src_slot"], k)
+    # dY_perm rows are w * dy of their token: they do not depend on the forward
+    dyp = np.zeros((meta["n_rows"], x.shape[1]))
+    ro = meta["row_of"].reshape(T, k)
+    for j in range(k):
+        dyp[ro[:, j]] = st(w[:, j:j + 1] * dy)
+    ex = mx_expert_layer(xp, dyp, meta["counts"], p["w_gate"], p["w_up"], p["w_down"])
+    out.update(x_perm=xp, dy_perm=dyp, **ex)
+    out["y"] = combine(ex["y_perm"], meta["row_of"], w, T, k, st)
+    _, out["dtopk_w"] = combine_bwd(dy, ex["y_perm"], w, meta["row_of"], meta["n_rows"], st, r32)
+    extra = None
+    if "w_r" in p:
+        dl = route_bwd(idx, w, out["dtopk_w"], E, r32)
+        out["dw_r"], extra = router_bwd(x, p["w_r"], dl, st)
+        out["dlogits"] = dl
+    out["dx"] = permute_bwd(ex["dx_perm"], meta["row_of"], T, k, st, extra)
+    return out

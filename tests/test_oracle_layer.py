@@ -296,3 +296,29 @@ def test_mx_layer_error_against_bf16_layer():
     Y = om.expert_fwd_down(H, wd, groups, st)
     rel = np.abs(mx["y_perm"] - Y).max() / np.abs(Y).max()
     assert 1e-4 < rel < 0.1
+
+
+def test_mx_routed_layer_without_quantisation_is_the_bf16_layer(monkeypatch):
+    # with the quantiser replaced by the identity, the MXFP8 routed layer must
+    # be the bf16 layer exactly (routing, permute, combine and adjoints are
+    # shared; only the expert GEMM operands are quantised)
+    rng = np.random.default_rng(22)
+    T, d, E, F, k = 40, 64, 6, 96, 2
+    for learned in (False, True):
+        p = _params(rng, T, d, E, F, learned=learned, k=k)
+        for n in list(p):
+            if n.startswith("w_") or n == "x":
+                p[n] = round_bf16(p[n])
+        dy = round_bf16(rng.standard_normal((T, d)))
+        monkeypatch.setattr(om, "mx_roundtrip", lambda a: np.asarray(a, dtype=np.float64))
+        mx = om.mx_layer(p, k, dy)
+        monkeypatch.undo()
+        fwd = layer_forward(p, k, "bf16")
+        bwd = layer_backward(p, fwd, dy, k, "bf16")
+        for n in ("y",):
+            assert np.array_equal(mx[n], fwd[n]), n
+        for n in ("dx", "dw_gate", "dw_up", "dw_down", "dtopk_w", "dy_perm"):
+            ref = bwd[n]
+            assert np.array_equal(mx[n], ref), n
+        if learned:
+            assert np.array_equal(mx["dw_r"], bwd["dw_r"])
