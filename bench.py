@@ -169,6 +169,32 @@ def timed(obj, step, steps, warmup):
     return (start.elapsed_time(end) / steps, {n: sum(v) / len(v) for n, v in stage_ms.items()}, wall)
 
 
+def mx_layer_leg(wl, t, steps, warmup, ms_base):
+    """The same routed workload with MXFP8 expert GEMMs and quantise-on-
+    dispatch (the permute writes E4M3 rows and scales, never bf16 rows):
+    step time and speed-up over the bf16 layer of the main measurement."""
+    import torch
+    from routing_grouped_expert_router_amd.layer import MoELayer
+    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
+                     routing="learned" if wl.routing == "learned" else "given", mxfp8=True)
+
+    def step():
+        layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
+                      topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
+        layer.backward(t["dy"])
+
+    ms, st, _ = timed(layer, step, steps, warmup)
+    del layer
+    torch.cuda.empty_cache()
+    gemm = sum(v for k, v in st.items() if k.startswith("mx_") and not k.startswith("mx_quantize"))
+    flops = 18.0 * wl.T * wl.k * wl.d * wl.F
+    return {"tokens_per_s": round(wl.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+            "speedup_vs_bf16": round(ms_base / ms, 3),
+            "gemm_tflops": round(flops / (gemm / 1e3) / 1e12, 1),
+            "gemm_frac_mxfp8_peak": round(flops / (gemm / 1e3) / 1e12 / PEAK_MXFP8_TFLOPS, 4),
+            "stages_us": {k: round(v * 1e3, 1) for k, v in st.items()}}
+
+
 def shared_leg(wl, t, cap, steps, warmup, ms_base):
     """The same workload with one shared expert (d_ff as a routed expert's)
     beside the routed ones: a dense SwiGLU on every token whose output joins
@@ -310,6 +336,7 @@ def main():
     ap.add_argument("--no-mxfp8", action="store_true", help="skip the MXFP8 expert-layer leg")
     ap.add_argument("--no-recompute", action="store_true", help="skip the per-layer recompute leg")
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-expert leg")
+    ap.add_argument("--no-mxfp8-layer", action="store_true", help="skip the MXFP8 routed-layer leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the reference "
@@ -422,6 +449,9 @@ def main():
     if not args.no_shared:
         log("shared-expert leg ...")
         out["shared_expert"] = shared_leg(wl, t, cap, args.steps, args.warmup, ms)
+    if not args.no_mxfp8_layer and cap == 0:
+        log("MXFP8 routed-layer leg ...")
+        out["mxfp8_layer"] = mx_layer_leg(wl, t, args.steps, args.warmup, ms)
     if not args.no_mxfp8:
         log("MXFP8 expert-layer leg ...")
         out["mxfp8_experts"] = experts_leg(args.steps, args.warmup)

@@ -286,6 +286,21 @@ int moe_mx_quantize_both(const void* src, int rows, int cols, const int32_t* gro
 int moe_mx_quantize(const void* src, int rows, int cols, int axis, const int32_t* group_offsets,
                     int n_groups, int col_stride, void* q, void* s, hipStream_t stream);
 
+/* moe_permute_mx: the permute of a dropless routed layer fused with the
+ * MXFP8 quantisation of its output ("quantise on dispatch": the pages credit
+ * MXFP8 with speeding up the movement of rows between experts as well as the
+ * GEMMs, unite.ai/hi, "पैरालेलिज़्म, प्रिसीजन, और मेमोरी तकनीकें"). Permuted
+ * row r holds x[src_slot[r] / k]; the rows are never written in bf16, only
+ * quantised, in both orientations of moe_mx_quantize_both with the experts
+ * as groups: q_rows/s_rows [n_rows, d] (blocks along d) and q_cols/s_cols
+ * [d, col_stride] (blocks along each expert's rows).
+ *   x [T,d] bf16; src_slot [n_rows] and group_offsets [E+1] on the device, as
+ *   written by moe_offsets; n_rows == T*k; d % 128 == 0; col_stride as for
+ *   moe_mx_quantize_both with device offsets. */
+int moe_permute_mx(const void* x, int T, int d, int k, const int32_t* src_slot,
+                   const int32_t* group_offsets, int E, int n_rows, int col_stride, void* q_rows,
+                   void* s_rows, void* q_cols, void* s_cols, hipStream_t stream);
+
 /* moe_grouped_gemm_mx: the six expert GEMMs of moe_grouped_gemm with every
  * operand MXFP8 (blocks of 32 along that GEMM's contraction), binary32
  * accumulation of the exact block products on the matrix cores, and bf16

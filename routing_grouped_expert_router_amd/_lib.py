@@ -68,6 +68,7 @@ SIGNATURES = {
     "moe_mx_col_stride": (_i, [_i, _i]),
     "moe_mx_quantize": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp]),
     "moe_mx_quantize_both": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "moe_permute_mx": (_i, [_vp, _i, _i, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "moe_grouped_gemm_mx": (_i, [C.POINTER(moe_mx_gg_desc), _vp]),
 }
 
@@ -247,6 +248,15 @@ def moe_mx_quantize_both(src, rows_out: MxTensor, cols_out: MxTensor, group_offs
     _check(lib().moe_mx_quantize_both(_p(src), rows, cols, _p(group_offsets), n_groups, col_stride,
                                       _p(rows_out.q), _p(rows_out.s), _p(cols_out.q), _p(cols_out.s),
                                       _stream(stream)), "moe_mx_quantize_both")
+
+
+def moe_permute_mx(x, k, src_slot, group_offsets, E, col_stride, rows_out: MxTensor, cols_out: MxTensor,
+                   stream=None):
+    T, d = x.shape
+    n_rows = src_slot.shape[0]
+    _check(lib().moe_permute_mx(_p(x), T, d, k, _p(src_slot), _p(group_offsets), E, n_rows, col_stride,
+                                _p(rows_out.q), _p(rows_out.s), _p(cols_out.q), _p(cols_out.s),
+                                _stream(stream)), "moe_permute_mx")
 
 
 def make_mx_gg_desc(op, E, d, F, n_rows, group_offsets, col_stride=0, a0=None, a1=None, b0=None,

@@ -180,17 +180,35 @@ MOE_DEV uint32_t quantize_block(const float (&v)[32], V16 (&out)[2]) {
 
 // Stage a tile of TC columns and 128 rows of one group into LDS (rows past the
 // group's end read as zeros).
+// Row gather of the staged tile: tile row r of group rows [r0 + row_in, ...)
+// reads src row `gather[grow] / gk` (the token of permuted row grow) when
+// gather is given, else src row grow.
+struct RowGather {
+  const int32_t* gather;
+  int gk;
+  int n_src;                // rows of src (a gathered index outside [0, n_src) reads zeros)
+};
+
+// Stage a tile of TC columns and 128 rows of one group into LDS (rows past the
+// group's end read as zeros).
 template <int TC, int LDW>
 MOE_DEV void stage_tile(const uint16_t* __restrict__ src, int cols, int r0, int n, int row_in, int c0,
-                        uint16_t* tile) {
+                        uint16_t* tile, RowGather rg = {nullptr, 1, 0}) {
   constexpr int CH = TC / 8;   // 16-byte chunks per row
 #pragma unroll
   for (int j = 0; j < kQRows * CH / 256; ++j) {
     const int qd = threadIdx.x + 256 * j;
     const int r = qd / CH, c = qd % CH;
     V16 v = {{0u, 0u, 0u, 0u}};
-    if (row_in + r < n)
-      v = *reinterpret_cast<const V16*>(src + static_cast<size_t>(r0 + row_in + r) * cols + c0 + c * 8);
+    if (row_in + r < n) {
+      long srow = r0 + row_in + r;
+      if (rg.gather) {
+        const int slot = rg.gather[srow];
+        srow = slot >= 0 ? slot / rg.gk : -1;
+      }
+      if (srow >= 0 && (!rg.gather || srow < rg.n_src))
+        v = *reinterpret_cast<const V16*>(src + static_cast<size_t>(srow) * cols + c0 + c * 8);
+    }
     *reinterpret_cast<V16*>(tile + r * LDW + c * 8) = v;
   }
 }
@@ -253,7 +271,7 @@ constexpr int kBCols = 128, kBLdw = kBCols + 8;
 __global__ void __launch_bounds__(256) mx_both_kernel(const uint16_t* __restrict__ src, int rows, int cols,
                                                       Groups1 gr, int col_stride, uint8_t* __restrict__ q_rows,
                                                       uint8_t* __restrict__ s_rows, uint8_t* __restrict__ q_cols,
-                                                      uint8_t* __restrict__ s_cols) {
+                                                      uint8_t* __restrict__ s_cols, RowGather rg) {
   __shared__ int tile_start[MOE_MAX_EXPERTS + 1];
   __shared__ __attribute__((aligned(16))) uint16_t tile[kQRows * kBLdw];
   __shared__ uint32_t words[64];
@@ -268,7 +286,7 @@ __global__ void __launch_bounds__(256) mx_both_kernel(const uint16_t* __restrict
   const int row_in = i * kQRows;
   const int c0 = ct * kBCols;
   if (p_g + row_in + kQRows > col_stride) return;
-  stage_tile<kBCols, kBLdw>(src, cols, r0, n, row_in, c0, tile);
+  stage_tile<kBCols, kBLdw>(src, cols, r0, n, row_in, c0, tile, rg);
   __syncthreads();
 
   // rows: thread (r, h) quantises blocks 2h, 2h+1 (64 values) of tile row r
@@ -382,6 +400,29 @@ extern "C" int moe_mx_quantize_both(const void* src, int rows, int cols, const i
   MOE_CHECK_SUPPORTED(grid < (1L << 31));
   mx_both_kernel<<<static_cast<int>(grid), 256, 0, stream>>>(
       static_cast<const uint16_t*>(src), rows, cols, gr, col_stride, static_cast<uint8_t*>(q_rows),
-      static_cast<uint8_t*>(s_rows), static_cast<uint8_t*>(q_cols), static_cast<uint8_t*>(s_cols));
+      static_cast<uint8_t*>(s_rows), static_cast<uint8_t*>(q_cols), static_cast<uint8_t*>(s_cols),
+      RowGather{nullptr, 1, 0});
+  return launch_status();
+}
+
+extern "C" int moe_permute_mx(const void* x, int T, int d, int k, const int32_t* src_slot,
+                              const int32_t* group_offsets, int E, int n_rows, int col_stride, void* q_rows,
+                              void* s_rows, void* q_cols, void* s_cols, hipStream_t stream) {
+  MOE_CHECK_ARG(T >= 0 && d > 0 && d % 128 == 0 && k >= 1 && E >= 1 && n_rows >= 0);
+  MOE_CHECK_SUPPORTED(k <= MOE_MAX_TOPK && E <= MOE_MAX_EXPERTS && static_cast<long>(T) * k < (1L << 31));
+  MOE_CHECK_ARG(static_cast<long>(n_rows) == static_cast<long>(T) * k);   // dropless rows only
+  MOE_CHECK_ARG(col_stride > 0 && col_stride % 128 == 0 && col_stride >= 128L * ((n_rows + 127L) / 128 + E));
+  MOE_CHECK_SUPPORTED(static_cast<long>(d) * col_stride < (1L << 40) && static_cast<long>(n_rows) * d < (1L << 40));
+  if (n_rows == 0) return MOE_OK;
+  MOE_CHECK_ARG(x && src_slot && group_offsets && aligned16(x));
+  MOE_CHECK_ARG(q_rows && s_rows && q_cols && s_cols && aligned16(q_rows) && aligned16(q_cols) &&
+                aligned4(s_rows) && aligned4(s_cols));
+  Groups1 gr{group_offsets, E, n_rows, 0};
+  const long grid = ((n_rows + kQRows - 1) / kQRows + E) * static_cast<long>(d / kBCols);
+  MOE_CHECK_SUPPORTED(grid < (1L << 31));
+  mx_both_kernel<<<static_cast<int>(grid), 256, 0, stream>>>(
+      static_cast<const uint16_t*>(x), n_rows, d, gr, col_stride, static_cast<uint8_t*>(q_rows),
+      static_cast<uint8_t*>(s_rows), static_cast<uint8_t*>(q_cols), static_cast<uint8_t*>(s_cols),
+      RowGather{src_slot, k, T});
   return launch_status();
 }

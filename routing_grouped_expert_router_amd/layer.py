@@ -21,6 +21,12 @@ dx inside the permute adjoint, so y and dx are still written once (the pages'
 production configurations pair top-four routing with one shared expert:
 bigchange.ai pt-BR, "O que um engenheiro pode realmente testar").
 
+With ``mxfp8=True`` (dropless, bf16 tensors) the six expert GEMMs run in
+MXFP8 (``mx_layer.MxExperts``) and the permute quantises on dispatch: the
+routed rows are gathered straight into E4M3 codes and scales, in the two
+orientations the GEMMs read, and never written in bf16. Routing, combine and
+their adjoints are the bf16 layer's.
+
 With ``recompute=True`` the expert activations G, U and H are treated as
 scratch that need not survive from the forward to the backward: the backward
 runs the gate/up grouped GEMM again from x_perm before its first expert
@@ -41,7 +47,8 @@ from . import _lib as L
 class MoELayer:
     def __init__(self, T: int, d: int, E: int, k: int, F: int, dtype=torch.bfloat16,
                  routing: str = "learned", capacity: int = 0, backward: bool = True,
-                 device: str = "cuda", recompute: bool = False, shared_ff: int = 0):
+                 device: str = "cuda", recompute: bool = False, shared_ff: int = 0,
+                 mxfp8: bool = False):
         if routing not in ("learned", "given"):
             raise ValueError(routing)
         self.T, self.d, self.E, self.k, self.F = T, d, E, k, F
@@ -65,7 +72,7 @@ class MoELayer:
         self.err_flag = torch.zeros(1, dtype=i32, device=dev)
         ws = max(L.moe_offsets_workspace_bytes(T, k, E), 16)
         self.ws_offsets = e((ws + 15) // 16 * 4, dt=i32)
-        self.x_perm = e(nr, d)
+        self.x_perm = None if mxfp8 else e(nr, d)   # the MXFP8 permute writes quantised rows only
         self.g, self.u, self.h = e(nr, F), e(nr, F), e(nr, F)
         self.y_perm = e(nr, d)
         self.y = e(T, d)
@@ -83,6 +90,17 @@ class MoELayer:
                 self.dw_r = e(d, E)
                 wsr = max(L.moe_router_bwd_workspace_bytes(T, d, E), 16)
                 self.ws_router = e((wsr + 15) // 16 * 4, dt=f32)
+        self.mxfp8 = mxfp8
+        if mxfp8:
+            if capacity > 0 or dtype != torch.bfloat16 or recompute or shared_ff > 0:
+                raise ValueError("the MXFP8 layer is dropless bf16, without recompute or shared expert")
+            from .mx_layer import MxExperts
+            self.mx = MxExperts(self.n_rows, d, E, F, device=device, outputs=False)
+            # the expert GEMMs write into the layer's buffers
+            self.mx.g, self.mx.u, self.mx.h, self.mx.y_perm = self.g, self.u, self.h, self.y_perm
+            if backward:
+                self.mx.dg, self.mx.du, self.mx.dx_perm = self.dg, self.du, self.dx_perm
+                self.mx.dw_gate, self.mx.dw_up, self.mx.dw_down = self.dw_gate, self.dw_up, self.dw_down
         self.shared_ff = shared_ff
         if shared_ff > 0:
             Fs = shared_ff
@@ -161,11 +179,22 @@ class MoELayer:
         self._mark("offsets")
 
     def permute(self):
+        if self.mxfp8:
+            L.moe_permute_mx(self.x, self.k, self.src_slot, self.offsets, self.E, self.mx.P,
+                             self.mx.xq.t, self.mx.x_c.t)
+            self._mark("permute_mx")
+            return
         L.moe_permute(self.x, self.k, self.row_of, self.src_slot if self.capacity > 0 else None,
                       self.x_perm)
         self._mark("permute")
 
     def experts_forward(self):
+        if self.mxfp8:
+            self.mx.offsets = self.offsets
+            self.mx.hook = self.hook
+            self.mx.quantize_weights(self.w_gate, self.w_up, self.w_down)
+            self.mx.forward_quantized()
+            return
         self._gg(L.MOE_GG_FWD_GATE_UP, x_perm=self.x_perm, w_gate=self.w_gate, w_up=self.w_up,
                  g=self.g, u=self.u, h=self.h)
         self._mark("gg_fwd_gate_up")
@@ -206,6 +235,10 @@ class MoELayer:
         return 0 if self.recompute else 3 * self.n_rows * self.F * self.g.element_size()
 
     def experts_backward(self):
+        if self.mxfp8:
+            self.mx.hook = self.hook
+            self.mx.backward(self.dy_perm)
+            return
         if self.recompute:
             self._gg(L.MOE_GG_FWD_GATE_UP, x_perm=self.x_perm, w_gate=self.w_gate, w_up=self.w_up,
                      g=self.g, u=self.u, h=self.h)

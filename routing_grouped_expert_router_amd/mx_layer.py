@@ -32,7 +32,9 @@ class _Q:
 
 
 class MxExperts:
-    def __init__(self, n_rows: int, d: int, E: int, F: int, device: str = "cuda"):
+    def __init__(self, n_rows: int, d: int, E: int, F: int, device: str = "cuda", outputs: bool = True):
+        """outputs=False leaves the bf16 results (g, u, h, y_perm, dg, du,
+        dx_perm, dw_*) for the caller to assign."""
         if d % 256 or F % 256:
             raise ValueError("d and F must be multiples of 256")
         self.n, self.d, self.E, self.F = n_rows, d, E, F
@@ -57,11 +59,12 @@ class MxExperts:
         self.dy_c = _Q(d, self.P, dev)
         self.dg_c, self.du_c = _Q(F, self.P, dev), _Q(F, self.P, dev)
         # bf16 results
-        self.g, self.u, self.h = bf(n, F), bf(n, F), bf(n, F)
-        self.y_perm = bf(n, d)
-        self.dg, self.du = bf(n, F), bf(n, F)
-        self.dx_perm = bf(n, d)
-        self.dw_gate, self.dw_up, self.dw_down = bf(E, d, F), bf(E, d, F), bf(E, F, d)
+        if outputs:
+            self.g, self.u, self.h = bf(n, F), bf(n, F), bf(n, F)
+            self.y_perm = bf(n, d)
+            self.dg, self.du = bf(n, F), bf(n, F)
+            self.dx_perm = bf(n, d)
+            self.dw_gate, self.dw_up, self.dw_down = bf(E, d, F), bf(E, d, F), bf(E, F, d)
         self.hook = None
 
     def _mark(self, name: str):
@@ -91,6 +94,12 @@ class MxExperts:
         self.quantize_weights(w_gate, w_up, w_down)
         self._both(x_perm, self.xq, self.x_c)
         self._mark("mx_quantize_x")
+        return self.forward_quantized()
+
+    def forward_quantized(self):
+        """The forward GEMMs once xq and x_c hold the quantised rows and the
+        weights are quantised (the routed layer fills xq and x_c in its
+        permute)."""
         self._gg(L.MOE_GG_FWD_GATE_UP, a0=self.xq.t, b0=self.wg_c.t, b1=self.wu_c.t,
                  out0=self.g, out1=self.u, out2=self.h)
         self._mark("mx_fwd_gate_up")

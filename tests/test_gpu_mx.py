@@ -392,3 +392,67 @@ def test_mx_full_size_sampled_experts():
             report[f"{name}[{e}]"] = (f"{err:.2e}", f"{same:.4f}")
             assert err <= 8e-3 and same > 0.95, report
     print("rel err, exact fraction", report)
+
+
+# ----------------------------------------------------------------------------- routed layer
+@pytest.mark.parametrize("T,E,k,d", [(300, 8, 2, 256), (1000, 16, 4, 384), (1, 4, 1, 128)])
+def test_permute_mx_is_quantised_permute_bitwise(T, E, k, d):
+    # quantise on dispatch: the gathered, quantised rows equal the oracle's
+    # quantiser applied to the oracle's permuted rows, in both orientations
+    rng = _rng(14, T, E, k, d)
+    x = _values(rng, T, d)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    meta = om.expert_offsets(idx, E)
+    xp = om.permute(x, meta["src_slot"], k)
+    n = meta["n_rows"]
+    P = L.moe_mx_col_stride(n, E)
+    sentinel = 0x33
+    rows_out = L.MxTensor(torch.full((n, d), sentinel, dtype=torch.uint8, device="cuda"),
+                          torch.full((n * d // 32,), sentinel, dtype=torch.uint8, device="cuda"))
+    cols_out = L.MxTensor(torch.full((d, P), sentinel, dtype=torch.uint8, device="cuda"),
+                          torch.full((d * P // 32,), sentinel, dtype=torch.uint8, device="cuda"))
+    L.moe_permute_mx(dev(f64_to_bf16_bits(x), "bf16"), k, dev(meta["src_slot"], "i32"),
+                     dev(meta["offsets"].astype(np.int32), "i32"), E, P, rows_out, cols_out)
+    rq, rs = mx_quantize(xp)
+    assert np.array_equal(host(rows_out.s), grouped_scales(rs))
+    assert np.array_equal(host(rows_out.q), rq)
+    eq, es = _expected_cols(xp, meta["offsets"][:-1], meta["counts"], P, sentinel)
+    assert np.array_equal(host(cols_out.s), grouped_scales(es))
+    assert np.array_equal(host(cols_out.q), eq)
+
+
+@pytest.mark.parametrize("name,over", [("e128_uniform_bf16", dict(T=1024, E=16, d=256, F=256)),
+                                       ("e128_uniform_bf16", dict(T=333, E=8, d=512, F=768)),
+                                       ("e128_zipf_bf16", dict(T=1024, E=32, d=256, F=256, capacity_factor=0.0))])
+def test_mx_routed_layer_parity(name, over):
+    from moe_inputs import make_inputs, workload
+    from oracle.numerics import bf16_bits_to_f64
+    from routing_grouped_expert_router_amd.layer import MoELayer
+    wl = workload(name).scaled(**over)
+    inp = make_inputs(wl)
+    t = {}
+    for n, a in inp.items():
+        if n in ("topk_idx",):
+            t[n] = dev(a.astype(np.int32), "i32")
+        elif n == "topk_w":
+            t[n] = dev(a.astype(np.float32), "f32")
+        else:
+            t[n] = dev(a, "bf16")
+    lay = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
+                   routing="learned" if wl.routing == "learned" else "given", mxfp8=True)
+    lay.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
+                topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
+    lay.backward(t["dy"])
+    torch.cuda.synchronize()
+    p = {n: bf16_bits_to_f64(inp[n]) for n in ("x", "w_gate", "w_up", "w_down", "w_r") if n in inp}
+    if "topk_idx" in inp:
+        p["topk_idx"], p["topk_w"] = inp["topk_idx"], inp["topk_w"].astype(np.float64)
+    ref = om.mx_layer(p, wl.k, bf16_bits_to_f64(inp["dy"]))
+    for n in ("counts", "offsets", "row_of", "src_slot"):
+        assert np.array_equal(host(getattr(lay, n)), ref[n]), n
+    errs = {}
+    for n, r in (("g", "G"), ("u", "U"), ("h", "H"), ("y_perm", "y_perm"), ("y", "y"), ("dg", "dG"),
+                 ("du", "dU"), ("dx_perm", "dx_perm"), ("dx", "dx"), ("dw_gate", "dw_gate"),
+                 ("dw_up", "dw_up"), ("dw_down", "dw_down"), ("dtopk_w", "dtopk_w")):
+        errs[n] = assert_close(host(getattr(lay, n)), ref[r], "mxfp8", n)
+    print("rel errs", {n: f"{v:.2e}" for n, v in errs.items()})
