@@ -10,6 +10,8 @@
 // +-448, sign kept. Inputs are finite.
 #include "common.h"
 
+#include <algorithm>
+
 namespace moe {
 
 namespace {
@@ -265,8 +267,113 @@ __global__ void __launch_bounds__(256) mx_cols_kernel(const uint16_t* __restrict
 // One pass, both orientations: a 128-row x 128-column tile of one group is
 // staged once; the column part writes the transposed codes as above, and the
 // row part quantises each valid row's 128 values (four blocks, one scale word)
-// into the row-oriented output.
+// into the row-oriented output. Workgroups are persistent: each walks the
+// tiles with a grid stride and holds the next tile's loads in registers while
+// it quantises the current one, so load latency overlaps the work.
 constexpr int kBCols = 128, kBLdw = kBCols + 8;
+constexpr int kBChunks = kQRows * kBCols / 8 / 256;   // 16-byte loads per thread per tile
+
+// Tiles per group prefix: tile_start[g] = sum_{h<g} ceil(n_h/128) (device
+// offsets); returns the number of row tiles. Every thread calls it.
+MOE_DEV int build_tile_prefix(const Groups1& gr, int* tile_start) {
+  if (!gr.offsets) return gr.G * ((gr.per + kQRows - 1) / kQRows);
+  const int tid = threadIdx.x;
+  constexpr int kMaxPer = (MOE_MAX_EXPERTS + 255) / 256;
+  const int per = (gr.G + 255) / 256;
+  const int g_lo = tid * per;
+  int loc[kMaxPer];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    int t = 0;
+    if (j < per && g_lo + j < gr.G) {
+      int r0, n;
+      group_range(gr, g_lo + j, r0, n);
+      t = (n + kQRows - 1) / kQRows;
+    }
+    loc[j] = t;
+    sum += t;
+  }
+  __shared__ int wtot[4];
+  const int lane = tid & 63, w = tid >> 6;
+  int incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wtot[w] = incl;
+  __syncthreads();
+  int before = incl - sum;
+  for (int j = 0; j < w; ++j) before += wtot[j];
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    if (j < per && g_lo + j < gr.G) tile_start[g_lo + j] = before;
+    before += loc[j];
+  }
+  if (tid == 255) tile_start[gr.G] = before;
+  __syncthreads();
+  return tile_start[gr.G];
+}
+
+// Group g, tile i within it and p_g of row tile rt < total row tiles.
+MOE_DEV void lookup_tile(const Groups1& gr, const int* tile_start, int rt, int& g, int& i, long& p_g) {
+  if (!gr.offsets) {
+    const int per_tiles = (gr.per + kQRows - 1) / kQRows;
+    g = rt / per_tiles;
+    i = rt % per_tiles;
+    p_g = static_cast<long>(g) * per_tiles * kQRows;
+    return;
+  }
+  int lo = 0, hi = gr.G - 1;   // last g with tile_start[g] <= rt
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_start[mid] <= rt) lo = mid;
+    else hi = mid - 1;
+  }
+  g = lo;
+  i = rt - tile_start[g];
+  p_g = 128L * tile_start[g];
+}
+
+struct BothTile {
+  int r0, n, row_in, c0;
+  long p_g;
+  bool skip;   // would write past col_stride (offsets that break the contract)
+};
+
+MOE_DEV BothTile both_tile(const Groups1& gr, const int* tile_start, int tiles_c, int col_stride, long b) {
+  BothTile t;
+  int g, i;
+  lookup_tile(gr, tile_start, static_cast<int>(b / tiles_c), g, i, t.p_g);
+  group_range(gr, g, t.r0, t.n);
+  t.row_in = i * kQRows;
+  t.c0 = static_cast<int>(b % tiles_c) * kBCols;
+  t.skip = t.p_g + t.row_in + kQRows > col_stride;
+  return t;
+}
+
+// The tile's 16-byte chunks of this thread (rows past the group's end, and
+// gathered rows outside the source, read as zeros).
+MOE_DEV void fetch_tile(const uint16_t* __restrict__ src, int cols, const BothTile& t, RowGather rg,
+                        V16 (&v)[kBChunks]) {
+  constexpr int CH = kBCols / 8;
+#pragma unroll
+  for (int j = 0; j < kBChunks; ++j) {
+    const int qd = threadIdx.x + 256 * j;
+    const int r = qd / CH, c = qd % CH;
+    v[j] = V16{{0u, 0u, 0u, 0u}};
+    if (t.row_in + r < t.n) {
+      long srow = t.r0 + t.row_in + r;
+      if (rg.gather) {
+        const int slot = rg.gather[srow];
+        srow = slot >= 0 ? slot / rg.gk : -1;
+      }
+      if (srow >= 0 && (!rg.gather || srow < rg.n_src))
+        v[j] = *reinterpret_cast<const V16*>(src + static_cast<size_t>(srow) * cols + t.c0 + c * 8);
+    }
+  }
+}
 
 __global__ void __launch_bounds__(256) mx_both_kernel(const uint16_t* __restrict__ src, int rows, int cols,
                                                       Groups1 gr, int col_stride, uint8_t* __restrict__ q_rows,
@@ -277,55 +384,71 @@ __global__ void __launch_bounds__(256) mx_both_kernel(const uint16_t* __restrict
   __shared__ uint32_t words[64];
   const int tid = threadIdx.x;
   const int tiles_c = cols / kBCols;
-  const int rt = blockIdx.x / tiles_c, ct = blockIdx.x % tiles_c;
-  int g, i;
-  long p_g;
-  if (!find_group_tile(gr, rt, tile_start, g, i, p_g)) return;
-  int r0, n;
-  group_range(gr, g, r0, n);
-  const int row_in = i * kQRows;
-  const int c0 = ct * kBCols;
-  if (p_g + row_in + kQRows > col_stride) return;
-  stage_tile<kBCols, kBLdw>(src, cols, r0, n, row_in, c0, tile, rg);
-  __syncthreads();
-
-  // rows: thread (r, h) quantises blocks 2h, 2h+1 (64 values) of tile row r
-  {
-    const int r = tid >> 1, h = tid & 1;
-    float v[2][32];
+  const long total = static_cast<long>(build_tile_prefix(gr, tile_start)) * tiles_c;
+  long b = blockIdx.x;
+  V16 pre[kBChunks];
+  if (b < total) fetch_tile(src, cols, both_tile(gr, tile_start, tiles_c, col_stride, b), rg, pre);
+  for (; b < total; b += gridDim.x) {
+    const BothTile t = both_tile(gr, tile_start, tiles_c, col_stride, b);
+    if (!t.skip) {
+      constexpr int CH = kBCols / 8;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float f[8];
-      unpack(*reinterpret_cast<const V16*>(tile + r * kBLdw + 64 * h + 8 * k), f);
+      for (int j = 0; j < kBChunks; ++j) {
+        const int qd = tid + 256 * j;
+        *reinterpret_cast<V16*>(tile + (qd / CH) * kBLdw + (qd % CH) * 8) = pre[j];
+      }
+    }
+    __syncthreads();
+    const long nb = b + gridDim.x;
+    if (nb < total) fetch_tile(src, cols, both_tile(gr, tile_start, tiles_c, col_stride, nb), rg, pre);
+    if (!t.skip) {
+      const int r0 = t.r0, n = t.n, row_in = t.row_in, c0 = t.c0;
+      // rows: thread (r, h) quantises blocks 2h, 2h+1 (64 values) of tile row r
+      {
+        const int r = tid >> 1, h = tid & 1;
+        float v[2][32];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) v[k >> 2][8 * (k & 3) + m] = f[m];
+        for (int k = 0; k < 8; ++k) {
+          float f[8];
+          unpack(*reinterpret_cast<const V16*>(tile + r * kBLdw + 64 * h + 8 * k), f);
+#pragma unroll
+          for (int m = 0; m < 8; ++m) v[k >> 2][8 * (k & 3) + m] = f[m];
+        }
+        V16 out[2][2];
+        const uint32_t c_lo = quantize_block(v[0], out[0]);
+        const uint32_t c_hi = quantize_block(v[1], out[1]);
+        const uint32_t pair = c_lo | (c_hi << 8);
+        const uint32_t other = __shfl_xor(pair, 1, 64);
+        if (row_in + r < n) {
+          const size_t grow = static_cast<size_t>(r0) + row_in + r;
+          V16* qp = reinterpret_cast<V16*>(q_rows + grow * cols + c0 + 64 * h);
+          qp[0] = out[0][0];
+          qp[1] = out[0][1];
+          qp[2] = out[1][0];
+          qp[3] = out[1][1];
+          if (h == 0)
+            *reinterpret_cast<uint32_t*>(s_rows + 4 * (static_cast<size_t>(rows) * (c0 / kBCols) + grow)) =
+                pair | (other << 16);
+        }
+      }
+      // columns, 64 at a time
+      cols_part<kBLdw>(tile, 0, c0, cols, t.p_g, row_in, col_stride, q_cols, s_cols, words);
+      cols_part<kBLdw>(tile, 64, c0, cols, t.p_g, row_in, col_stride, q_cols, s_cols, words);
     }
-    V16 out[2][2];
-    const uint32_t c_lo = quantize_block(v[0], out[0]);
-    const uint32_t c_hi = quantize_block(v[1], out[1]);
-    const uint32_t pair = c_lo | (c_hi << 8);
-    const uint32_t other = __shfl_xor(pair, 1, 64);
-    if (row_in + r < n) {
-      const size_t grow = static_cast<size_t>(r0) + row_in + r;
-      V16* qp = reinterpret_cast<V16*>(q_rows + grow * cols + c0 + 64 * h);
-      qp[0] = out[0][0];
-      qp[1] = out[0][1];
-      qp[2] = out[1][0];
-      qp[3] = out[1][1];
-      if (h == 0)
-        *reinterpret_cast<uint32_t*>(s_rows + 4 * (static_cast<size_t>(rows) * (c0 / kBCols) + grow)) =
-            pair | (other << 16);
-    }
+    __syncthreads();
   }
-  // columns, 64 at a time
-  cols_part<kBLdw>(tile, 0, c0, cols, p_g, row_in, col_stride, q_cols, s_cols, words);
-  cols_part<kBLdw>(tile, 64, c0, cols, p_g, row_in, col_stride, q_cols, s_cols, words);
 }
 
 }  // namespace
 }  // namespace moe
 
 using namespace moe;
+
+namespace {
+// persistent workgroups of the two-orientation quantiser: as many as are
+// resident at once (three per CU at its register use)
+constexpr long kBothGrid = 256 * 3;
+}  // namespace
 
 extern "C" int moe_mx_col_stride(int rows, int n_groups) {
   if (rows < 0 || n_groups < 1) return -1;
@@ -396,8 +519,7 @@ extern "C" int moe_mx_quantize_both(const void* src, int rows, int cols, const i
                 aligned16(q_cols) && aligned4(s_rows) && aligned4(s_cols));
   const long row_tiles = group_offsets ? (rows + kQRows - 1) / kQRows + n_groups
                                        : static_cast<long>(n_groups) * ((gr.per + kQRows - 1) / kQRows);
-  const long grid = row_tiles * (cols / kBCols);
-  MOE_CHECK_SUPPORTED(grid < (1L << 31));
+  const long grid = std::min(row_tiles * (cols / kBCols), kBothGrid);
   mx_both_kernel<<<static_cast<int>(grid), 256, 0, stream>>>(
       static_cast<const uint16_t*>(src), rows, cols, gr, col_stride, static_cast<uint8_t*>(q_rows),
       static_cast<uint8_t*>(s_rows), static_cast<uint8_t*>(q_cols), static_cast<uint8_t*>(s_cols),
@@ -418,8 +540,7 @@ extern "C" int moe_permute_mx(const void* x, int T, int d, int k, const int32_t*
   MOE_CHECK_ARG(q_rows && s_rows && q_cols && s_cols && aligned16(q_rows) && aligned16(q_cols) &&
                 aligned4(s_rows) && aligned4(s_cols));
   Groups1 gr{group_offsets, E, n_rows, 0};
-  const long grid = ((n_rows + kQRows - 1) / kQRows + E) * static_cast<long>(d / kBCols);
-  MOE_CHECK_SUPPORTED(grid < (1L << 31));
+  const long grid = std::min(((n_rows + kQRows - 1) / kQRows + E) * static_cast<long>(d / kBCols), kBothGrid);
   mx_both_kernel<<<static_cast<int>(grid), 256, 0, stream>>>(
       static_cast<const uint16_t*>(x), n_rows, d, gr, col_stride, static_cast<uint8_t*>(q_rows),
       static_cast<uint8_t*>(s_rows), static_cast<uint8_t*>(q_cols), static_cast<uint8_t*>(s_cols),
