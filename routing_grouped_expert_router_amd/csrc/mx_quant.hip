@@ -267,8 +267,8 @@ __global__ void __launch_bounds__(256) mx_cols_kernel(const uint16_t* __restrict
 // One pass, both orientations: a 128-row x 128-column tile of one group is
 // staged once; the column part writes the transposed codes as above, and the
 // row part quantises each valid row's 128 values (four blocks, one scale word)
-// into the row-oriented output. Workgroups are persistent: each walks the
-// tiles with a grid stride and holds the next tile's loads in registers while
+// into the row-oriented output. Workgroups are persistent: each takes a
+// contiguous run of tiles and holds the next tile's loads in registers while
 // it quantises the current one, so load latency overlaps the work.
 constexpr int kBCols = 128, kBLdw = kBCols + 8;
 constexpr int kBChunks = kQRows * kBCols / 8 / 256;   // 16-byte loads per thread per tile
@@ -342,13 +342,16 @@ struct BothTile {
   bool skip;   // would write past col_stride (offsets that break the contract)
 };
 
-MOE_DEV BothTile both_tile(const Groups1& gr, const int* tile_start, int tiles_c, int col_stride, long b) {
+// Tile j of the column-tile-major order: column tile j / total_rt, row tile
+// j % total_rt (a workgroup's consecutive tiles are row-adjacent, so its
+// transposed writes continue each output row where the last tile stopped).
+MOE_DEV BothTile both_tile(const Groups1& gr, const int* tile_start, int total_rt, int col_stride, long j) {
   BothTile t;
   int g, i;
-  lookup_tile(gr, tile_start, static_cast<int>(b / tiles_c), g, i, t.p_g);
+  lookup_tile(gr, tile_start, static_cast<int>(j % total_rt), g, i, t.p_g);
   group_range(gr, g, t.r0, t.n);
   t.row_in = i * kQRows;
-  t.c0 = static_cast<int>(b % tiles_c) * kBCols;
+  t.c0 = static_cast<int>(j / total_rt) * kBCols;
   t.skip = t.p_g + t.row_in + kQRows > col_stride;
   return t;
 }
@@ -384,12 +387,16 @@ __global__ void __launch_bounds__(256) mx_both_kernel(const uint16_t* __restrict
   __shared__ uint32_t words[64];
   const int tid = threadIdx.x;
   const int tiles_c = cols / kBCols;
-  const long total = static_cast<long>(build_tile_prefix(gr, tile_start)) * tiles_c;
-  long b = blockIdx.x;
+  const int total_rt = build_tile_prefix(gr, tile_start);
+  const long total = static_cast<long>(total_rt) * tiles_c;
+  // a contiguous run of tiles per workgroup
+  const long per = (total + gridDim.x - 1) / gridDim.x;
+  long b = blockIdx.x * per;
+  const long b_end = b + per < total ? b + per : total;
   V16 pre[kBChunks];
-  if (b < total) fetch_tile(src, cols, both_tile(gr, tile_start, tiles_c, col_stride, b), rg, pre);
-  for (; b < total; b += gridDim.x) {
-    const BothTile t = both_tile(gr, tile_start, tiles_c, col_stride, b);
+  if (b < b_end) fetch_tile(src, cols, both_tile(gr, tile_start, total_rt, col_stride, b), rg, pre);
+  for (; b < b_end; ++b) {
+    const BothTile t = both_tile(gr, tile_start, total_rt, col_stride, b);
     if (!t.skip) {
       constexpr int CH = kBCols / 8;
 #pragma unroll
@@ -399,8 +406,8 @@ __global__ void __launch_bounds__(256) mx_both_kernel(const uint16_t* __restrict
       }
     }
     __syncthreads();
-    const long nb = b + gridDim.x;
-    if (nb < total) fetch_tile(src, cols, both_tile(gr, tile_start, tiles_c, col_stride, nb), rg, pre);
+    const long nb = b + 1;
+    if (nb < b_end) fetch_tile(src, cols, both_tile(gr, tile_start, total_rt, col_stride, nb), rg, pre);
     if (!t.skip) {
       const int r0 = t.r0, n = t.n, row_in = t.row_in, c0 = t.c0;
       // rows: thread (r, h) quantises blocks 2h, 2h+1 (64 values) of tile row r
