@@ -44,9 +44,14 @@ TRAFFIC_BEGIN = "<!-- traffic-json -->"
 
 def stage_of(kernel):
     """Pipeline stage a kernel belongs to, or None for library kernels."""
+    m = re.search(r"moe::gg_mx_kernel<(\d+),", kernel)
+    if m:
+        return "mx" + GG_OPS[int(m.group(1))][2:]
     m = re.search(r"moe::gg_\w+_kernel<(\d+),", kernel)
     if m:
         return GG_OPS[int(m.group(1))]
+    if re.search(r"moe::(\(anonymous namespace\)::)?mx_(both|rows|cols)_kernel", kernel):
+        return "mx_quantize"
     for pat, st in ROW_KERNELS:
         if re.search(r"moe::" + pat + r"\b", kernel):
             return st

@@ -456,3 +456,96 @@ def test_mx_routed_layer_parity(name, over):
                  ("dw_up", "dw_up"), ("dw_down", "dw_down"), ("dtopk_w", "dtopk_w")):
         errs[n] = assert_close(host(getattr(lay, n)), ref[r], "mxfp8", n)
     print("rel errs", {n: f"{v:.2e}" for n, v in errs.items()})
+
+
+def test_mx_routed_layer_full_size_sampled_experts():
+    """The MXFP8 routed layer at the benchmark's size (16384 tokens, 128
+    experts, top-4, d = 2048, d_ff = 1024, uniform routing) in its launch
+    configuration: routing metadata in full, the quantise-on-dispatch output
+    of two sampled experts bit for bit, and each expert GEMM of those experts
+    on the oracle's inputs (their rows of dY_perm, H, dG, dU are replaced by
+    the oracle's and requantised before the op runs)."""
+    from moe_inputs import make_inputs, workload
+    from oracle.numerics import bf16_bits_to_f64, storer
+    from routing_grouped_expert_router_amd.layer import MoELayer
+
+    wl = workload("e128_uniform_bf16")
+    inp = make_inputs(wl)
+    T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.F
+    t = {n: dev(a, "bf16") for n, a in inp.items() if n not in ("topk_idx", "topk_w")}
+    t["topk_idx"] = dev(inp["topk_idx"].astype(np.int32), "i32")
+    t["topk_w"] = dev(inp["topk_w"].astype(np.float32), "f32")
+    lay = MoELayer(T, d, E, k, F, torch.bfloat16, routing="given", mxfp8=True)
+    lay.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], topk_idx=t["topk_idx"], topk_w=t["topk_w"])
+    lay.backward(t["dy"])
+    torch.cuda.synchronize()
+    meta = om.expert_offsets(inp["topk_idx"].astype(np.int32), E)
+    for n in ("counts", "offsets", "row_of", "src_slot"):
+        assert np.array_equal(host(getattr(lay, n)), meta[n]), n
+    off, counts = meta["offsets"], meta["counts"]
+    order = np.argsort(counts, kind="stable")
+    experts = [int(order[0]), int(order[E // 2])]
+    print("sampled experts", experts, "rows", [int(counts[e]) for e in experts], flush=True)
+    x = bf16_bits_to_f64(inp["x"])
+    dy = bf16_bits_to_f64(inp["dy"])
+    w = inp["topk_w"].astype(np.float32).astype(np.float64)
+    st = storer("bf16")
+    mx, P = lay.mx, lay.mx.P
+    pad = lambda n: -(-n // 128) * 128
+    refs = {}
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        src = meta["src_slot"][r0:r1]
+        xe = x[src // k]
+        dye = st(w.reshape(-1)[src][:, None] * dy[src // k])
+        refs[e] = om.mx_expert_layer(xe, dye, np.array([r1 - r0]), bf16_bits_to_f64(inp["w_gate"][e:e + 1]),
+                                     bf16_bits_to_f64(inp["w_up"][e:e + 1]),
+                                     bf16_bits_to_f64(inp["w_down"][e:e + 1]))
+        refs[e]["dy_perm"] = dye
+        # quantise on dispatch: rows and the expert's token columns, bit for bit
+        rq, rs = mx_quantize(xe)
+        assert np.array_equal(host(mx.xq.q[r0:r1]), rq), e
+        sq = host(mx.xq.s).reshape(d // 128, -1, 4)[:, r0:r1, :]
+        assert np.array_equal(sq, rs.reshape(r1 - r0, d // 128, 4).transpose(1, 0, 2)), e
+        p_e = 128 * int(sum(pad(int(c)) // 128 for c in counts[:e]))
+        cq, cs = mx_quantize(xe.T)
+        n_e = r1 - r0
+        assert np.array_equal(host(mx.x_c.q[:, p_e:p_e + n_e]), cq), e
+        assert not host(mx.x_c.q[:, p_e + n_e:p_e + pad(n_e)]).any(), e
+        # forward gate/up ran on the oracle's operands already
+        for name, tt in (("G", lay.g), ("U", lay.u), ("H", lay.h)):
+            got = host(tt[r0:r1])
+            assert_close(got, refs[e][name], "mxfp8", f"{name}[{e}]")
+            assert np.mean(got == refs[e][name]) > 0.95, (name, e)
+    # the other ops on the oracle's intermediates of the sampled experts
+    b = lambda a: dev(f64_to_bf16_bits(a), "bf16")
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        lay.dy_perm[r0:r1] = b(refs[e]["dy_perm"])
+        for name, tt in (("G", lay.g), ("U", lay.u), ("H", lay.h), ("dG", lay.dg), ("dU", lay.du)):
+            tt[r0:r1] = b(refs[e][name])
+    G, U, H, dG, dU = (tt.clone() for tt in (lay.g, lay.u, lay.h, lay.dg, lay.du))
+    both = lambda src, a, c: L.moe_mx_quantize_both(src, a.t, c.t, lay.offsets, E, P)
+    both(H, mx.hq, mx.h_c)
+    both(lay.dy_perm, mx.dyq, mx.dy_c)
+    both(dG, mx.dgq, mx.dg_c)
+    both(dU, mx.duq, mx.du_c)
+    mx._gg(L.MOE_GG_FWD_DOWN, a0=mx.hq.t, b0=mx.wd_c.t, out0=lay.y_perm)
+    mx._gg(L.MOE_GG_DGRAD_DOWN, a0=mx.dyq.t, b0=mx.wd_r.t, g=G, u=U, out0=lay.dg, out1=lay.du)
+    mx._gg(L.MOE_GG_WGRAD_DOWN, a0=mx.h_c.t, b0=mx.dy_c.t, out0=lay.dw_down)
+    mx._gg(L.MOE_GG_DGRAD_GATE_UP, a0=mx.dgq.t, a1=mx.duq.t, b0=mx.wg_r.t, b1=mx.wu_r.t, out0=lay.dx_perm)
+    mx._gg(L.MOE_GG_WGRAD_GATE_UP, a0=mx.x_c.t, b0=mx.dg_c.t, b1=mx.du_c.t, out0=lay.dw_gate, out1=lay.dw_up)
+    torch.cuda.synchronize()
+    report = {}
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        for name, got in (("y_perm", host(lay.y_perm[r0:r1])), ("dG", host(lay.dg[r0:r1])),
+                          ("dU", host(lay.du[r0:r1])), ("dx_perm", host(lay.dx_perm[r0:r1])),
+                          ("dw_gate", host(lay.dw_gate[e])), ("dw_up", host(lay.dw_up[e])),
+                          ("dw_down", host(lay.dw_down[e]))):
+            ref = refs[e][name] if not name.startswith("dw") else refs[e][name][0]
+            err = assert_close(got, ref, "mxfp8", f"{name}[{e}]")
+            same = float(np.mean(got == ref))
+            report[f"{name}[{e}]"] = (f"{err:.2e}", f"{same:.4f}")
+            assert err <= 8e-3 and same > 0.95, report
+    print("rel err, exact fraction", report)
