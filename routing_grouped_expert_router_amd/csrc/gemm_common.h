@@ -88,21 +88,31 @@ MOE_DEV void group_rows(const GGArgs& a, int e, int& r0, int& n) {
   if (r0 + n > a.n_rows) n = a.n_rows - r0 > 0 ? a.n_rows - r0 : 0;
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X; give
-// each XCD a contiguous range of tiles so that tiles sharing an expert's
-// weights and rows meet in the same L2.
-MOE_DEV int xcd_remap(int b, int nb) {
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X
+// (workgroup i runs on XCD i % 8). Map the i-th workgroup of an XCD to the
+// i-th tile of a contiguous range of the `tiles` real tiles, so that tiles
+// sharing an expert's weights and rows meet in the same L2 and every XCD gets
+// an equal share; returns -1 for a workgroup past its XCD's share. Needs
+// tiles <= nb (the launch may hold more workgroups than tiles: the grid of a
+// row-varying op is sized for the most m-tiles the expert split can need,
+// and its real tile count is known on the device only).
+MOE_DEV int xcd_tile(int blk, int nb, int tiles) {
   constexpr int kXcd = 8;
-  const int q = nb / kXcd, rmd = nb % kXcd;
-  const int x = b % kXcd, s = b / kXcd;
-  return x < rmd ? x * (q + 1) + s : rmd * (q + 1) + (x - rmd) * q + s;
+  (void)nb;
+  const int q = tiles / kXcd, r = tiles % kXcd;
+  const int x = blk % kXcd, s = blk / kXcd;
+  const int count = q + (x < r ? 1 : 0);
+  if (s >= count) return -1;
+  return x * q + (x < r ? x : r) + s;
 }
+MOE_DEV int xcd_remap(int b, int nb) { return xcd_tile(b, nb, nb); }
 
-// Row-varying ops: map a linear m-tile index to (expert, first row, rows).
-// tile_start[e] = number of BM-row tiles of experts < e, built once per
-// workgroup in LDS from the device-resident group offsets (E <= 1024).
+// Row-varying ops: tile_start[e] = number of BM-row tiles of experts < e
+// (tile_start[E] = all m-tiles), built once per workgroup in LDS from the
+// device-resident group offsets (E <= MOE_MAX_EXPERTS). Returns the m-tile
+// count; every thread of the workgroup must call it.
 template <int BM, int NT>
-MOE_DEV bool find_m_tile(const GGArgs& a, int tm, int* tile_start, int& e, int& row0, int& mv) {
+MOE_DEV int build_tile_prefix(const GGArgs& a, int* tile_start) {
   // per-thread partial sums over a contiguous run of experts
   constexpr int kMaxPer = (MOE_MAX_EXPERTS + NT - 1) / NT;
   const int per = (a.E + NT - 1) / NT;
@@ -140,6 +150,12 @@ MOE_DEV bool find_m_tile(const GGArgs& a, int tm, int* tile_start, int& e, int& 
   }
   if (threadIdx.x == NT - 1) tile_start[a.E] = before;
   __syncthreads();
+  return tile_start[a.E];
+}
+
+// m-tile tm -> (expert, first row, rows), from a built prefix.
+template <int BM>
+MOE_DEV bool m_tile_of(const GGArgs& a, int tm, const int* tile_start, int& e, int& row0, int& mv) {
   if (tm >= tile_start[a.E]) return false;
   int lo = 0, hi = a.E - 1;   // last e with tile_start[e] <= tm
   while (lo < hi) {
@@ -156,28 +172,30 @@ MOE_DEV bool find_m_tile(const GGArgs& a, int tm, int* tile_start, int& e, int& 
   return true;
 }
 
-// Row-varying ops, expert-grouped order: linear tile b runs over experts in
-// order; inside expert e (with mt_e m-tiles) the tiles are ordered n-tile
-// major, m-tile minor, so all m-tiles reading one weight slice are adjacent.
+// Both steps at once (for kernels that launch one workgroup per m-tile slot).
 template <int BM, int NT>
-MOE_DEV bool find_m_tile_grouped(const GGArgs& a, int b, int tilesN, int* tile_start, int& e,
-                                 int& row0, int& mv, int& tn) {
-  int dummy_r0, dummy_mv, dummy_e;
-  // builds tile_start[] (m-tile prefix over experts) as a side effect
-  (void)find_m_tile<BM, NT>(a, 0, tile_start, dummy_e, dummy_r0, dummy_mv);
-  const int tm_lin = b / tilesN;   // only used to bound the search
-  if (tm_lin >= tile_start[a.E]) return false;
-  // the tiles of experts < e are tile_start[e] * tilesN
-  const int tt = b;
+MOE_DEV bool find_m_tile(const GGArgs& a, int tm, int* tile_start, int& e, int& row0, int& mv) {
+  build_tile_prefix<BM, NT>(a, tile_start);
+  return m_tile_of<BM>(a, tm, tile_start, e, row0, mv);
+}
+
+// Row-varying ops, expert-grouped order, from a built prefix: linear tile b
+// runs over experts in order; inside expert e (with mt_e m-tiles) the tiles
+// are ordered n-tile major, m-tile minor, so all m-tiles reading one weight
+// slice are adjacent.
+template <int BM>
+MOE_DEV bool m_tile_grouped(const GGArgs& a, int b, int tilesN, const int* tile_start, int& e, int& row0,
+                            int& mv, int& tn) {
+  if (b >= tile_start[a.E] * tilesN) return false;
   int lo = 0, hi = a.E - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (tile_start[mid] * tilesN <= tt) lo = mid;
+    if (tile_start[mid] * tilesN <= b) lo = mid;
     else hi = mid - 1;
   }
   e = lo;
   const int mt_e = tile_start[e + 1] - tile_start[e];
-  const int rel = tt - tile_start[e] * tilesN;
+  const int rel = b - tile_start[e] * tilesN;
   tn = rel / mt_e;
   const int mt = rel % mt_e;
   int r0, n;

@@ -127,19 +127,21 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_dma_kernel(GGArgs a) {
   const int d = a.d, F = a.F;
   const int N = op_n(OP, d, F);
   const int tilesN = N / BNO;
-  const int b = xcd_remap(blockIdx.x, gridDim.x);
   int e, row0, mv, K, m0 = 0, tn;
   if (!KVAR) {
+    const int b = xcd_tile(blockIdx.x, gridDim.x, build_tile_prefix<BM, NT>(a, tile_start) * tilesN);
+    if (b < 0) return;
     if (a.order == 0) {
       tn = b % tilesN;
-      if (!find_m_tile<BM, NT>(a, b / tilesN, tile_start, e, row0, mv)) return;
+      if (!m_tile_of<BM>(a, b / tilesN, tile_start, e, row0, mv)) return;
     } else {
       // blocks of (expert's m-tiles) x (one n-tile): the m-tiles sharing a
       // weight slice run side by side; experts are visited in order
-      if (!find_m_tile_grouped<BM, NT>(a, b, tilesN, tile_start, e, row0, mv, tn)) return;
+      if (!m_tile_grouped<BM>(a, b, tilesN, tile_start, e, row0, mv, tn)) return;
     }
     K = op_k(OP, d, F);
   } else {
+    const int b = xcd_remap(blockIdx.x, gridDim.x);
     const int M = op_wgrad_m(OP, d, F);
     const int per = (M / BM) * tilesN;
     e = b / per;

@@ -101,15 +101,17 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_mx_kernel(MxArgs x) {
   const int d = a.d, F = a.F, E = a.E;
   const int N = op_n(OP, d, F);
   const int tilesN = N / BNO;
-  const int b = xcd_remap(blockIdx.x, gridDim.x);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int e, row0, mv, K, m0 = 0, tn, p_e = 0;
   if (!KVAR) {
+    const int b = xcd_tile(blockIdx.x, gridDim.x, build_tile_prefix<BM, NT>(a, tile_start) * tilesN);
+    if (b < 0) return;
     tn = b % tilesN;
-    if (!find_m_tile<BM, NT>(a, b / tilesN, tile_start, e, row0, mv)) return;
+    if (!m_tile_of<BM>(a, b / tilesN, tile_start, e, row0, mv)) return;
     K = op_k(OP, d, F);
   } else {
+    const int b = xcd_remap(blockIdx.x, gridDim.x);
     const int M = op_wgrad_m(OP, d, F);
     const int per = (M / BM) * tilesN;
     e = b / per;
