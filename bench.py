@@ -218,7 +218,7 @@ def shared_leg(wl, t, cap, steps, warmup, ms_base):
     ms, st, _ = timed(layer, step, steps, warmup)
     del layer
     torch.cuda.empty_cache()
-    sh_us = st.get("gg_shared_fwd", 0.0) + st.get("gg_shared_bwd", 0.0)
+    sh_us = st.get("gg_shared_fwd", 0.0) + st.get("gg_shared_bwd_data", 0.0) + st.get("gg_shared_bwd_weights", 0.0)
     flops = 18.0 * wl.T * wl.d * Fs
     return {"d_ff_shared": Fs, "tokens_per_s": round(wl.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
             "shared_gemm_us": round(sh_us * 1e3, 1),

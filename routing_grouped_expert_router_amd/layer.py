@@ -145,14 +145,22 @@ class MoELayer:
         self._mark("gg_shared_fwd")
 
     def shared_backward(self, dy):
+        self.shared_backward_data(dy)
+        self.shared_backward_weights(dy)
+
+    def shared_backward_data(self, dy):
+        """dG_s, dU_s and the shared expert's share of dx (dx_s)."""
         self._gg_shared(L.MOE_GG_DGRAD_DOWN, dy_perm=dy, w_down=self.w_down_s, g=self.g_s, u=self.u_s,
                         dg=self.dg_s, du=self.du_s)
-        self._gg_shared(L.MOE_GG_WGRAD_DOWN, h=self.h_s, dy_perm=dy, dw_down=self.dw_down_s)
         self._gg_shared(L.MOE_GG_DGRAD_GATE_UP, dg=self.dg_s, du=self.du_s, w_gate=self.w_gate_s,
                         w_up=self.w_up_s, dx_perm=self.dx_s)
+        self._mark("gg_shared_bwd_data")
+
+    def shared_backward_weights(self, dy):
+        self._gg_shared(L.MOE_GG_WGRAD_DOWN, h=self.h_s, dy_perm=dy, dw_down=self.dw_down_s)
         self._gg_shared(L.MOE_GG_WGRAD_GATE_UP, x_perm=self.x, dg=self.dg_s, du=self.du_s,
                         dw_gate=self.dw_gate_s, dw_up=self.dw_up_s)
-        self._mark("gg_shared_bwd")
+        self._mark("gg_shared_bwd_weights")
 
     def forward(self, x, w_gate, w_up, w_down, w_r=None, topk_idx=None, topk_w=None,
                 w_gate_s=None, w_up_s=None, w_down_s=None):
@@ -207,14 +215,17 @@ class MoELayer:
         self._mark("combine")
 
     def backward(self, dy):
+        """Data gradients first (dx is what the layer below, or an expert-
+        parallel exchange, waits on, and each data-gradient GEMM reads what
+        the one before it just wrote), weight gradients last."""
         L.moe_unpermute_combine_bwd(dy, self.y_perm, self.topk_w, self.row_of,
                                     self.src_slot if self.capacity > 0 else None,
                                     self.dy_perm, self.dtopk_w)
         self._mark("combine_bwd")
-        self.experts_backward()
+        self.experts_backward_data()
         dx_add = None
         if self.shared_ff > 0:
-            self.shared_backward(dy)
+            self.shared_backward_data(dy)
             dx_add = self.dx_s
         if self.routing == "learned":
             L.moe_route_bwd(self.topk_idx, self.topk_w, self.dtopk_w, self.E, self.dlogits)
@@ -226,6 +237,9 @@ class MoELayer:
         else:
             L.moe_permute_bwd(self.dx_perm, self.row_of, self.k, self.dx, dx_add=dx_add)
         self._mark("permute_bwd")
+        self.experts_backward_weights()
+        if self.shared_ff > 0:
+            self.shared_backward_weights(dy)
         return self.dx
 
     def activation_bytes_between_passes(self) -> int:
@@ -235,9 +249,15 @@ class MoELayer:
         return 0 if self.recompute else 3 * self.n_rows * self.F * self.g.element_size()
 
     def experts_backward(self):
+        self.experts_backward_data()
+        self.experts_backward_weights()
+
+    def experts_backward_data(self):
+        """dG, dU and dx_perm (after re-running the gate/up GEMM when the
+        forward kept no G, U, H)."""
         if self.mxfp8:
             self.mx.hook = self.hook
-            self.mx.backward(self.dy_perm)
+            self.mx.backward_data(self.dy_perm)
             return
         if self.recompute:
             self._gg(L.MOE_GG_FWD_GATE_UP, x_perm=self.x_perm, w_gate=self.w_gate, w_up=self.w_up,
@@ -246,11 +266,18 @@ class MoELayer:
         self._gg(L.MOE_GG_DGRAD_DOWN, dy_perm=self.dy_perm, w_down=self.w_down, g=self.g, u=self.u,
                  dg=self.dg, du=self.du)
         self._mark("gg_dgrad_down")
-        self._gg(L.MOE_GG_WGRAD_DOWN, h=self.h, dy_perm=self.dy_perm, dw_down=self.dw_down)
-        self._mark("gg_wgrad_down")
         self._gg(L.MOE_GG_DGRAD_GATE_UP, dg=self.dg, du=self.du, w_gate=self.w_gate, w_up=self.w_up,
                  dx_perm=self.dx_perm)
         self._mark("gg_dgrad_gate_up")
+
+    def experts_backward_weights(self):
+        """dW_down, dW_gate, dW_up."""
+        if self.mxfp8:
+            self.mx.hook = self.hook
+            self.mx.backward_weights()
+            return
+        self._gg(L.MOE_GG_WGRAD_DOWN, h=self.h, dy_perm=self.dy_perm, dw_down=self.dw_down)
+        self._mark("gg_wgrad_down")
         self._gg(L.MOE_GG_WGRAD_GATE_UP, x_perm=self.x_perm, dg=self.dg, du=self.du,
                  dw_gate=self.dw_gate, dw_up=self.dw_up)
         self._mark("gg_wgrad_gate_up")

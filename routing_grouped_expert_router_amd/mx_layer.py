@@ -110,23 +110,34 @@ class MxExperts:
         return self.y_perm
 
     def backward(self, dy_perm):
+        self.backward_data(dy_perm)
+        self.backward_weights()
+        return self.dx_perm
+
+    def backward_data(self, dy_perm):
+        """Quantises dY and dG/dU (both orientations: the weight gradients
+        read the token columns later) and runs the two data-gradient GEMMs."""
         self._both(dy_perm, self.dyq, self.dy_c)
         self._mark("mx_quantize_dy")
         self._gg(L.MOE_GG_DGRAD_DOWN, a0=self.dyq.t, b0=self.wd_r.t, g=self.g, u=self.u,
                  out0=self.dg, out1=self.du)
         self._mark("mx_dgrad_down")
-        self._gg(L.MOE_GG_WGRAD_DOWN, a0=self.h_c.t, b0=self.dy_c.t, out0=self.dw_down)
-        self._mark("mx_wgrad_down")
         self._both(self.dg, self.dgq, self.dg_c)
         self._both(self.du, self.duq, self.du_c)
         self._mark("mx_quantize_dg_du")
         self._gg(L.MOE_GG_DGRAD_GATE_UP, a0=self.dgq.t, a1=self.duq.t, b0=self.wg_r.t, b1=self.wu_r.t,
                  out0=self.dx_perm)
         self._mark("mx_dgrad_gate_up")
+        return self.dx_perm
+
+    def backward_weights(self):
+        """The weight-gradient GEMMs, from the token columns quantised by
+        forward_quantized and backward_data."""
+        self._gg(L.MOE_GG_WGRAD_DOWN, a0=self.h_c.t, b0=self.dy_c.t, out0=self.dw_down)
+        self._mark("mx_wgrad_down")
         self._gg(L.MOE_GG_WGRAD_GATE_UP, a0=self.x_c.t, b0=self.dg_c.t, b1=self.du_c.t,
                  out0=self.dw_gate, out1=self.dw_up)
         self._mark("mx_wgrad_gate_up")
-        return self.dx_perm
 
     def outputs(self) -> Dict[str, torch.Tensor]:
         return dict(G=self.g, U=self.u, H=self.h, y_perm=self.y_perm, dG=self.dg, dU=self.du,
