@@ -214,16 +214,6 @@ int tile_choice() {
   return t;
 }
 
-// Row-varying tile order; MOE_GG_ORDER=m puts the m-tiles of one expert's
-// n-tile next to each other (for tuning sweeps).
-int tile_order() {
-  static int t = [] {
-    const char* s = std::getenv("MOE_GG_ORDER");
-    return (s && std::string(s) == "m") ? 1 : 0;
-  }();
-  return t;
-}
-
 bool mfma_ok(const moe_gg_desc* g) {
   return g->dtype == MOE_BF16 && g->d % 256 == 0 && g->F % 256 == 0;
 }
@@ -293,6 +283,18 @@ long cdiv(long a, long b) { return (a + b - 1) / b; }
 
 }  // namespace
 
+namespace moe {
+// Row-varying tile order: expert-grouped (1) unless MOE_GG_ORDER=n asks for
+// the n-tiles of one m-tile side by side (0, for tuning sweeps).
+int gg_tile_order() {
+  static const int t = [] {
+    const char* s = std::getenv("MOE_GG_ORDER");
+    return (s && std::string(s) == "n") ? 0 : 1;
+  }();
+  return t;
+}
+}  // namespace moe
+
 extern "C" size_t moe_grouped_gemm_workspace_bytes(const moe_gg_desc* desc) {
   (void)desc;
   return 0;
@@ -333,7 +335,7 @@ extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
     default:
       MOE_CHECK_ARG(act(g->x_perm) && act(g->dg) && act(g->du) && need(g->dw_gate) && need(g->dw_up));
   }
-  GGArgs a{g->op, g->E, g->d, g->F, g->n_rows, g->capacity, tile_order(), g->group_offsets,
+  GGArgs a{g->op, g->E, g->d, g->F, g->n_rows, g->capacity, gg_tile_order(), g->group_offsets,
            g->x_perm, g->g, g->u, g->h, g->y_perm, g->dy_perm, g->dg, g->du, g->dx_perm,
            g->w_gate, g->w_up, g->w_down, g->dw_gate, g->dw_up, g->dw_down};
   const bool dual = g->op == MOE_GG_FWD_GATE_UP || g->op == MOE_GG_WGRAD_GATE_UP;

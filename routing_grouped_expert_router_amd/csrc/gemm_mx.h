@@ -107,8 +107,12 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_mx_kernel(MxArgs x) {
   if (!KVAR) {
     const int b = xcd_tile(blockIdx.x, gridDim.x, build_tile_prefix<BM, NT>(a, tile_start) * tilesN);
     if (b < 0) return;
-    tn = b % tilesN;
-    if (!m_tile_of<BM>(a, b / tilesN, tile_start, e, row0, mv)) return;
+    if (a.order == 0) {
+      tn = b % tilesN;
+      if (!m_tile_of<BM>(a, b / tilesN, tile_start, e, row0, mv)) return;
+    } else {
+      if (!m_tile_grouped<BM>(a, b, tilesN, tile_start, e, row0, mv, tn)) return;
+    }
     K = op_k(OP, d, F);
   } else {
     const int b = xcd_remap(blockIdx.x, gridDim.x);

@@ -94,7 +94,7 @@ extern "C" int moe_grouped_gemm_mx(const moe_mx_gg_desc* g, hipStream_t stream) 
   MOE_CHECK_SUPPORTED(span < (1L << 31) && d * F < (1L << 31));
 
   MxArgs x{};
-  x.o = GGArgs{g->op, g->E, g->d, g->F, g->n_rows, 0, 0, g->group_offsets,
+  x.o = GGArgs{g->op, g->E, g->d, g->F, g->n_rows, 0, gg_tile_order(), g->group_offsets,
                nullptr, const_cast<void*>(g->g), const_cast<void*>(g->u), nullptr, nullptr, nullptr,
                nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   switch (g->op) {
