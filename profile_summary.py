@@ -1,7 +1,7 @@
 """Turn rocprofv3 CSV output of bench.py runs into the text summaries kept
 under profiles/.
 
-    python profile_summary.py kernels  OUT.md KT_DIR  [--command CMD]
+    python profile_summary.py kernels  OUT.md KT_DIR  [--command CMD] [--skip N]
     python profile_summary.py traffic  OUT.md FETCH_CSV WRITE_CSV CAL_FETCH_CSV CAL_WRITE_CSV
                                        [--workload NAME] [--command CMD ...]
 
@@ -65,23 +65,43 @@ def short(kernel):
     return m.group(1) + (m.group(2) or "")
 
 
+def _timed_means(trace_path, skip):
+    """Mean duration (us) of each kernel over its launches after the first
+    `skip` (the warm-up steps of the traced bench run), in launch order."""
+    runs = {}
+    for r in csv.DictReader(open(trace_path)):
+        runs.setdefault(r["Kernel_Name"], []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    out = {}
+    for name, v in runs.items():
+        v.sort()
+        kept = [ns for _, ns in v[skip:]] or [ns for _, ns in v]
+        out[name] = sum(kept) / len(kept) / 1e3
+    return out
+
+
 def kernels(args):
     path = glob.glob(os.path.join(args.dir, "*kernel_stats.csv"))
     if len(path) != 1:
         sys.exit(f"expected one *kernel_stats.csv under {args.dir}, found {path}")
     rows = list(csv.DictReader(open(path[0])))
+    trace = glob.glob(os.path.join(args.dir, "*kernel_trace.csv"))
+    timed = _timed_means(trace[0], args.skip) if len(trace) == 1 else {}
     out = ["# Kernel durations", ""]
     if args.command:
         out += ["Command (from the repository root):", "", "```", args.command, "```", ""]
-    out += ["Source: rocprofv3 `--kernel-trace --stats` (kernel_stats.csv). Averages include "
-            "the warm-up launches.", "",
-            "| stage | kernel | calls | avg us | min us | max us | % of GPU time |",
-            "|---|---|---:|---:|---:|---:|---:|"]
+    out += ["Source: rocprofv3 `--kernel-trace --stats` (kernel_stats.csv, kernel_trace.csv). "
+            "`avg us` includes the warm-up launches; `timed avg us` leaves out each kernel's "
+            f"first {args.skip} launches (the bench's warm-up steps), which is what bench.py "
+            "times.", "",
+            "| stage | kernel | calls | avg us | timed avg us | min us | max us | % of GPU time |",
+            "|---|---|---:|---:|---:|---:|---:|---:|"]
     for r in rows:
-        out.append("| {} | `{}` | {} | {:.1f} | {:.1f} | {:.1f} | {:.2f} |".format(
+        t = timed.get(r["Name"])
+        out.append("| {} | `{}` | {} | {:.1f} | {} | {:.1f} | {:.1f} | {:.2f} |".format(
             stage_of(r["Name"]) or "-", short(r["Name"]), r["Calls"],
-            float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
-            float(r["Percentage"])))
+            float(r["AverageNs"]) / 1e3, "-" if t is None else f"{t:.1f}",
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     open(args.out, "w").write("\n".join(out) + "\n")
     print(args.out)
 
@@ -168,6 +188,7 @@ def main():
     k.add_argument("out")
     k.add_argument("dir")
     k.add_argument("--command")
+    k.add_argument("--skip", type=int, default=2, help="warm-up launches per kernel to leave out")
     t = sub.add_parser("traffic")
     t.add_argument("out")
     t.add_argument("fetch")
