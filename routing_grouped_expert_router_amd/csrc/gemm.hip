@@ -184,18 +184,13 @@ using Cfg128 = MfmaCfg<128, 256, 2, 2>;   // 4 waves, 64 x 128 each
 using Cfg256 = MfmaCfg<256, 256, 2, 4>;   // 8 waves, 128 x 64 each
 using CfgDma256 = DmaCfg<256, 256, 2, 4, 32, 4>;      // 8 waves, 128 x 64 each, 1 workgroup per CU
 using CfgDma128 = DmaCfg<128, 256, 2, 2, 32, 3, 2>;   // 4 waves, 64 x 128 each, 2 workgroups per CU
-using CfgDma4w = DmaCfg<256, 256, 2, 2, 32, 4>;       // 4 waves, 128 x 128 each
-using CfgDma128i = DmaCfg<128, 256, 2, 2, 32, 3, 2, 1>;   // loads interleaved with MFMAs
-using CfgDma128p = DmaCfg<128, 256, 2, 2, 32, 3, 2, 2>;   // priority raised around MFMAs
-using CfgDma128ip = DmaCfg<128, 256, 2, 2, 32, 3, 2, 3>;  // both
 using CfgDma128w8 = DmaCfg<128, 256, 2, 4, 32, 3, 2>;     // 8 waves, 64 x 64 each, 2 workgroups per CU
 
 // Kernel choice. The default is the direct-load kernel on 128 x 256 tiles,
 // eight waves of 64 x 64 and two workgroups per CU (16 waves per CU hide
 // the per-stage load issue, fragment reads and barriers of each other);
-// MOE_GG_TILE overrides it for tuning sweeps: dma128w8 | dma128 | dma256 |
-// dma4w | dma128i | dma128p | dma128ip (direct loads), 128 | 256
-// (register-staged).
+// MOE_GG_TILE overrides it for comparison runs: dma128w8 | dma128 | dma256
+// (direct loads), 128 | 256 (register-staged).
 int tile_choice() {
   static int t = [] {
     const char* s = std::getenv("MOE_GG_TILE");
@@ -204,10 +199,6 @@ int tile_choice() {
     if (v == "128") return 0;
     if (v == "256") return 1;
     if (v == "dma256") return 2;
-    if (v == "dma4w") return 4;
-    if (v == "dma128i") return 5;
-    if (v == "dma128p") return 6;
-    if (v == "dma128ip") return 7;
     if (v == "dma128") return 3;
     return 8;
   }();
@@ -350,10 +341,6 @@ extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
       switch (choice) {
         case 2: return launch_dma<CfgDma256>(g, a, kvar, dual, N, stream);
         case 3: return launch_dma<CfgDma128>(g, a, kvar, dual, N, stream);
-        case 4: return launch_dma<CfgDma4w>(g, a, kvar, dual, N, stream);
-        case 5: return launch_dma<CfgDma128i>(g, a, kvar, dual, N, stream);
-        case 6: return launch_dma<CfgDma128p>(g, a, kvar, dual, N, stream);
-        case 7: return launch_dma<CfgDma128ip>(g, a, kvar, dual, N, stream);
         case 8: return launch_dma<CfgDma128w8>(g, a, kvar, dual, N, stream);
 
         default: break;

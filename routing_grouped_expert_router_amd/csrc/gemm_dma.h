@@ -30,13 +30,12 @@ namespace moe {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 dbf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short ds4_t;
 
-// VAR_ bit 0: issue the next stage's loads one at a time between the last
-// sub-step's MFMAs instead of in one burst after the barrier; bit 1: raise
-// the wave's issue priority while it issues MFMAs.
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int ST_, int OCC_ = 1, int VAR_ = 0> struct DmaCfg {
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int ST_, int OCC_ = 1> struct DmaCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, STAGES = ST_;
   static constexpr int OCC = OCC_;                         // workgroups per CU
-  static constexpr bool INTERLEAVE = (VAR_ & 1) != 0, PRIO = (VAR_ & 2) != 0;
+  // waves per SIMD when OCC workgroups share a CU (HIP's second launch bound:
+  // it caps the VGPRs per wave at 512 / this)
+  static constexpr int WAVES_PER_SIMD = (WM_ * WN_ * OCC_ + 3) / 4;
   static constexpr int NT = WM * WN * 64;
   static constexpr int NW = WM * WN;
   static constexpr int WMR = BM / WM, WNR = BN / WN;
@@ -114,7 +113,7 @@ MOE_DEV dbf16x8_t read_tr8(const uint16_t* p0, const uint16_t* p1) {
 
 // ------------------------------------------------------------------ kernel
 template <int OP, class C>
-__global__ void __launch_bounds__(C::NT, C::OCC) gg_dma_kernel(GGArgs a) {
+__global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_dma_kernel(GGArgs a) {
   using I = OpInfo<OP>;
   constexpr bool DUAL = I::kDual, KVAR = I::kKVar, AK = I::kAKContig, BKC = I::kBKContig;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::STAGES, NT = C::NT;
@@ -337,29 +336,11 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_dma_kernel(GGArgs a) {
     }
   };
   auto mfmas = [&](const dbf16x8_t (&af)[MI], const dbf16x8_t (&bfr)[NI]) {
-    if (C::PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
-    if (C::PRIO) __builtin_amdgcn_s_setprio(0);
-  };
-  // the same MFMAs (when the wave has rows) with load i of K step kt issued
-  // after MFMA i (when `refill`): one instruction sequence for every case
-  auto mfmas_loading = [&](const dbf16x8_t (&af)[MI], const dbf16x8_t (&bfr)[NI], int kt, int slot, bool refill,
-                           bool act) {
-    static_assert(MI * NI >= PER_STAGE, "one load per MFMA at most");
-    if (C::PRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        if (act) acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
-        const int i = mi * NI + ni;
-        if (i < PER_STAGE && refill) issue_one(kt, slot, i);
-      }
-    if (C::PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- K loop over a ring of S slots. Step kt has KS sub-steps of 16. The
@@ -404,12 +385,8 @@ __global__ void __launch_bounds__(C::NT, C::OCC) gg_dma_kernel(GGArgs a) {
         __syncthreads();
         const bool refill = kt + S < nk;
         if (kt + 1 < nk && active) read_frags((kt + 1) % S, 0, af[nxt], bfr[nxt]);
-        if (C::INTERLEAVE) {
-          mfmas_loading(af[cur], bfr[cur], kt + S, slot, refill, active);
-        } else {
-          if (refill) issue(kt + S, slot);
-          if (active) mfmas(af[cur], bfr[cur]);
-        }
+        if (refill) issue(kt + S, slot);
+        if (active) mfmas(af[cur], bfr[cur]);
       }
     }
   }

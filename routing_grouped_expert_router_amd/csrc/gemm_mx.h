@@ -40,6 +40,8 @@ struct MxArgs {
 
 template <int BM_, int BN_, int WM_, int WN_, int ST_, int OCC_> struct MxCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = ST_, OCC = OCC_;
+  // waves per SIMD when OCC workgroups share a CU (HIP's second launch bound)
+  static constexpr int WAVES_PER_SIMD = (WM_ * WN_ * OCC_ + 3) / 4;
   static constexpr int BK = 64;                             // K values (bytes) per row per stage
   static constexpr int NT = WM * WN * 64, NW = WM * WN;
   static constexpr int WMR = BM / WM, WNR = BN / WN;
@@ -87,7 +89,7 @@ template <int PER, int MAXN> MOE_DEV void wait_stages(int n) {
 }
 
 template <int OP, class C>
-__global__ void __launch_bounds__(C::NT, C::OCC) gg_mx_kernel(MxArgs x) {
+__global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_mx_kernel(MxArgs x) {
   using I = OpInfo<OP>;
   constexpr bool DUAL = I::kDual, KVAR = I::kKVar;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, S = C::STAGES, NT = C::NT, NW = C::NW;

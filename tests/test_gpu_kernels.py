@@ -251,6 +251,9 @@ def _gg_case(kind, counts, d, F, seed, capacity=0):
     ("f32", [33, 0, 70, 1], 128, 256, 0),
     ("f32", [20, 9], 72, 40, 24),
     ("bf16", [0, 0, 0], 256, 256, 0),                                 # no rows at all
+    ("bf16", [300], 256, 256, 0),                                     # weight-gradient grids < 8 workgroups
+    ("bf16", [5, 3000], 256, 256, 0),
+    ("bf16", [0, 4000, 1, 0, 17, 2000, 0, 0, 3, 900], 512, 256, 0),  # skewed: work-balanced tile runs
 ])
 def test_grouped_gemm_parity(kind, counts, d, F, capacity):
     rng, E, n_rows, groups, st, T, grp = _gg_case(kind, counts, d, F, hash((tuple(counts), d, F)) % 1000, capacity)
