@@ -169,6 +169,56 @@ def timed(obj, step, steps, warmup):
     return (start.elapsed_time(end) / steps, {n: sum(v) / len(v) for n, v in stage_ms.items()}, wall)
 
 
+def upload_inputs(inp):
+    """Host arrays of a workload -> device tensors (bf16 bit patterns kept)."""
+    import numpy as np
+    import torch
+    devc = torch.device("cuda:0")
+    t = {}
+    for n, a in inp.items():
+        a = np.ascontiguousarray(a)
+        if n in ("topk_idx", "topk_w", "counts"):
+            t[n] = torch.from_numpy(a).to(devc)
+        else:
+            t[n] = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(devc)
+    torch.cuda.synchronize()
+    return t
+
+
+def workload_leg(name, capacity_factor, steps, warmup):
+    """One bf16 layer forward+backward on another workload of the same
+    shape family (its own seeded inputs): step time, grouped-GEMM rate and
+    the rows dropped at the given capacity factor (0: dropless)."""
+    import torch
+    from moe_inputs import make_inputs, workload
+    from routing_grouped_expert_router_amd.layer import MoELayer
+    wl = workload(name)
+    cap = wl.scaled(capacity_factor=capacity_factor).capacity() if capacity_factor > 0 else 0
+    t = upload_inputs(make_inputs(wl))
+    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
+                     routing="learned" if wl.routing == "learned" else "given", capacity=cap)
+
+    def step():
+        layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
+                      topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
+        layer.backward(t["dy"])
+
+    ms, st, _ = timed(layer, step, steps, warmup)
+    gemm_ms = sum(v for n, v in st.items() if n.startswith("gg_"))
+    flops = 18.0 * layer.n_rows * wl.d * wl.F
+    counts = layer.counts.cpu().numpy()
+    out = {"workload": name, "experts": wl.E, "routing": wl.routing, "capacity": cap,
+           "rows": int(layer.n_rows), "tokens_per_s": round(wl.T / (ms / 1e3), 1),
+           "ms_per_step": round(ms, 4),
+           "grouped_gemm_tflops": round(flops / (gemm_ms / 1e3) / 1e12, 1),
+           "expert_load": {"min": int(counts.min()), "max": int(counts.max()),
+                           "empty_experts": int((counts == 0).sum())},
+           "dropped": int(layer.n_dropped.cpu()[0])}
+    del layer, t
+    torch.cuda.empty_cache()
+    return out
+
+
 def mx_layer_leg(wl, t, steps, warmup, ms_base):
     """The same routed workload with MXFP8 expert GEMMs and quantise-on-
     dispatch (the permute writes E4M3 rows and scales, never bf16 rows):
@@ -178,12 +228,18 @@ def mx_layer_leg(wl, t, steps, warmup, ms_base):
     layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
                      routing="learned" if wl.routing == "learned" else "given", mxfp8=True)
 
-    def step():
-        layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
-                      topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
-        layer.backward(t["dy"])
+    def step(requantize):
+        def run():
+            if requantize:   # the weights changed since the last step (one optimiser step per step)
+                layer.mx.invalidate_weights()
+            layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
+                          topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
+            layer.backward(t["dy"])
+        return run
 
-    ms, st, _ = timed(layer, step, steps, warmup)
+    ms, st, _ = timed(layer, step(True), steps, warmup)
+    # gradient accumulation: same weights across micro-batches, quantised once
+    ms_acc, _, _ = timed(layer, step(False), steps, warmup)
     del layer
     torch.cuda.empty_cache()
     gemm = sum(v for k, v in st.items() if k.startswith("mx_") and not k.startswith("mx_quantize"))
@@ -192,6 +248,9 @@ def mx_layer_leg(wl, t, steps, warmup, ms_base):
             "speedup_vs_bf16": round(ms_base / ms, 3),
             "gemm_tflops": round(flops / (gemm / 1e3) / 1e12, 1),
             "gemm_frac_mxfp8_peak": round(flops / (gemm / 1e3) / 1e12 / PEAK_MXFP8_TFLOPS, 4),
+            "weights_unchanged_between_steps": {"tokens_per_s": round(wl.T / (ms_acc / 1e3), 1),
+                                                "ms_per_step": round(ms_acc, 4),
+                                                "speedup_vs_bf16": round(ms_base / ms_acc, 3)},
             "stages_us": {k: round(v * 1e3, 1) for k, v in st.items()}}
 
 
@@ -258,7 +317,9 @@ def experts_leg(steps, warmup):
     d_ff = 2048, 32768 rows arriving grouped by expert with Zipf(0.8) counts:
     the pages' expert-parallel microbenchmark shape), timed next to the bf16
     grouped GEMMs on the same rows. A step is every weight quantised in both
-    orientations, the forward and the backward of the experts. Inputs are drawn
+    orientations, the forward and the backward of the experts; a second
+    timing keeps the weights between steps (gradient accumulation), so they
+    are quantised once. Inputs are drawn
     on the device from a seeded generator (normal rows, weights scaled by
     fan-in) so that the leg adds seconds, not minutes, to a run."""
     import numpy as np
@@ -280,12 +341,17 @@ def experts_leg(steps, warmup):
 
     mx = MxExperts(n, d, E, F)
 
-    def mx_step():
-        mx.forward(x, off, wg, wu, wd)
-        mx.backward(dy)
+    def mx_step(requantize):
+        def run():
+            if requantize:   # new weights every step
+                mx.invalidate_weights()
+            mx.forward(x, off, wg, wu, wd)
+            mx.backward(dy)
+        return run
 
-    ms_mx, st_mx, _ = timed(mx, mx_step, steps, warmup)
+    ms_mx, st_mx, _ = timed(mx, mx_step(True), steps, warmup)
     gemm_mx = sum(v for k, v in st_mx.items() if not k.startswith("mx_quantize"))
+    ms_acc, _, _ = timed(mx, mx_step(False), steps, warmup)
     del mx
     torch.cuda.empty_cache()
 
@@ -315,6 +381,8 @@ def experts_leg(steps, warmup):
         "mxfp8_gemm_tflops": round(flops / (gemm_mx / 1e3) / 1e12, 1),
         "mxfp8_gemm_frac_peak": round(flops / (gemm_mx / 1e3) / 1e12 / PEAK_MXFP8_TFLOPS, 4),
         "mxfp8_quantize_ms": round(ms_mx - gemm_mx, 4),
+        "mxfp8_weights_unchanged_ms_per_step": round(ms_acc, 4),
+        "mxfp8_weights_unchanged_speedup": round(ms_bf / ms_acc, 3),
         "roofline": {"bound": "mfma", "kernel": dom, "avg_launch_us": round(st_mx[dom] * 1e3, 1),
                      "achieved": round(dom_flops / (st_mx[dom] / 1e3) / 1e12, 1),
                      "peak": PEAK_MXFP8_TFLOPS, "unit": "TFLOP/s",
@@ -337,6 +405,8 @@ def main():
     ap.add_argument("--no-recompute", action="store_true", help="skip the per-layer recompute leg")
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-expert leg")
     ap.add_argument("--no-mxfp8-layer", action="store_true", help="skip the MXFP8 routed-layer leg")
+    ap.add_argument("--no-pool", action="store_true", help="skip the 8-expert comparison leg")
+    ap.add_argument("--no-skew", action="store_true", help="skip the Zipf dropless/padded leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the reference "
@@ -371,17 +441,7 @@ def main():
     t0 = time.perf_counter()
     inp = make_inputs(wl)
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
-    devc = torch.device("cuda:0")
-
-    def up(a, kind):
-        if kind == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(devc)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(devc)
-
-    t = {}
-    for n, a in inp.items():
-        t[n] = up(a, "raw" if n in ("topk_idx", "topk_w", "counts") else "bf16")
-    torch.cuda.synchronize()
+    t = upload_inputs(inp)
     layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
                      routing="learned" if wl.routing == "learned" else "given", capacity=cap)
 
@@ -455,6 +515,20 @@ def main():
     if not args.no_mxfp8:
         log("MXFP8 expert-layer leg ...")
         out["mxfp8_experts"] = experts_leg(args.steps, args.warmup)
+    if not args.no_pool and wl.name == "e128_uniform_bf16" and cap == 0:
+        # the same layer with 8 experts (uniform routing, same T, d, k, d_ff),
+        # and the 8-expert learned-router configuration
+        log("expert-pool leg (E = 8) ...")
+        e8 = workload_leg("e8_uniform_bf16", 0.0, args.steps, args.warmup)
+        e8l = workload_leg("e8_learned_bf16", 0.0, args.steps, args.warmup)
+        out["expert_pool"] = {"e8_uniform": e8, "e8_learned": e8l,
+                              "throughput_loss_e8_to_e128": round(1.0 - out["value"] / e8["tokens_per_s"], 4)}
+    if not args.no_skew:
+        log("skewed-routing leg (dropless and padded) ...")
+        dl = workload_leg("e128_zipf_bf16", 0.0, args.steps, args.warmup)
+        pd = workload_leg("e128_zipf_bf16", 1.25, args.steps, args.warmup)
+        out["skewed_routing"] = {"dropless": dl, "padded_cf1.25": pd,
+                                 "padded_time_vs_dropless": round(pd["ms_per_step"] / dl["ms_per_step"], 3)}
     if not args.no_cpu_baseline:
         log("timing the oracle on the host for the CPU baseline ...")
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)

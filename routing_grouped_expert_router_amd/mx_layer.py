@@ -66,6 +66,7 @@ class MxExperts:
             self.dx_perm = bf(n, d)
             self.dw_gate, self.dw_up, self.dw_down = bf(E, d, F), bf(E, d, F), bf(E, F, d)
         self.hook = None
+        self._wkey = None   # which weights the quantised copies hold (see quantize_weights)
 
     def _mark(self, name: str):
         if self.hook is not None:
@@ -76,15 +77,35 @@ class MxExperts:
         L.moe_grouped_gemm_mx(desc)
 
     # ------------------------------------------------------------------ steps
-    def quantize_weights(self, w_gate, w_up, w_down):
-        """Both orientations of each weight in one pass (they change every
-        optimiser step)."""
+    @staticmethod
+    def _key(*ws):
+        # storage, layout and torch's in-place version counter of each weight
+        return tuple((w.data_ptr(), tuple(w.shape), tuple(w.stride()), w._version) for w in ws)
+
+    def quantize_weights(self, w_gate, w_up, w_down, force: bool = False) -> bool:
+        """Both orientations of each weight in one pass. The weights change
+        once per optimiser step, not per micro-batch: when the same tensors
+        come back unmodified (same storage, no in-place write since, by
+        torch's version counter) the quantised copies are current and
+        nothing runs. Writes that bypass torch's version counter need
+        invalidate_weights() or force=True. Returns whether it quantised."""
+        key = self._key(w_gate, w_up, w_down)
+        if not force and key == self._wkey:
+            self._mark("mx_quantize_weights")
+            return False
         E, d, F = self.E, self.d, self.F
         wg, wu, wd = w_gate.view(E * d, F), w_up.view(E * d, F), w_down.view(E * F, d)
         L.moe_mx_quantize_both(wg, self.wg_r.t, self.wg_c.t, None, E, E * d)
         L.moe_mx_quantize_both(wu, self.wu_r.t, self.wu_c.t, None, E, E * d)
         L.moe_mx_quantize_both(wd, self.wd_r.t, self.wd_c.t, None, E, E * F)
+        self._wkey = key
         self._mark("mx_quantize_weights")
+        return True
+
+    def invalidate_weights(self):
+        """Forget which weights the quantised copies hold: the next forward
+        quantises again."""
+        self._wkey = None
 
     def _both(self, src, rows_out, cols_out):
         L.moe_mx_quantize_both(src, rows_out.t, cols_out.t, self.offsets, self.E, self.P)

@@ -294,7 +294,10 @@ def _isolated_ops(x, dy, counts, wg, wu, wd, ref):
 
 @pytest.mark.parametrize("counts,d,F", [([0, 37, 300, 129], 256, 256),
                                         ([128, 1, 260], 512, 512),
-                                        ([5, 0, 0, 70, 3, 250, 64, 131], 256, 768)])
+                                        ([5, 0, 0, 70, 3, 250, 64, 131], 256, 768),
+                                        ([300], 256, 256),                  # weight-gradient grids < 8 workgroups
+                                        ([5, 3000], 256, 256),
+                                        ([0, 2500, 1, 0, 17, 1200, 3, 600], 256, 512)])   # skewed
 def test_mx_each_gemm_on_oracle_inputs(counts, d, F):
     # with identical quantised operands both sides sum the same exact products;
     # only the accumulation order (binary32 vs float64) and the epilogue's
@@ -549,3 +552,50 @@ def test_mx_routed_layer_full_size_sampled_experts():
             report[f"{name}[{e}]"] = (f"{err:.2e}", f"{same:.4f}")
             assert err <= 8e-3 and same > 0.95, report
     print("rel err, exact fraction", report)
+
+
+def test_mx_weight_quantisation_tracks_in_place_updates():
+    """The MXFP8 layer quantises its weights again exactly when they changed:
+    the same unmodified tensors reuse the quantised copies (results bit for
+    bit the same), an in-place update (an optimiser step) or invalidation
+    forces a new pass, and the results then match a fresh layer's."""
+    from moe_inputs import make_inputs, workload
+    from routing_grouped_expert_router_amd.layer import MoELayer
+    wl = workload("e128_uniform_bf16").scaled(T=300, E=8, d=256, F=256)
+    inp = make_inputs(wl)
+    t = {n: dev(a, "bf16") for n, a in inp.items() if n not in ("topk_idx", "topk_w")}
+    t["topk_idx"] = dev(inp["topk_idx"].astype(np.int32), "i32")
+    t["topk_w"] = dev(inp["topk_w"].astype(np.float32), "f32")
+    names = ("y", "dx", "dw_gate", "dw_up", "dw_down", "dtopk_w")
+
+    def run(lay):
+        lay.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], topk_idx=t["topk_idx"], topk_w=t["topk_w"])
+        lay.backward(t["dy"])
+        torch.cuda.synchronize()
+        return {n: host(getattr(lay, n)).copy() for n in names}
+
+    def fresh():
+        return MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16, routing="given", mxfp8=True)
+
+    lay = fresh()
+    first = run(lay)
+    key = lay.mx._wkey
+    again = run(lay)
+    assert lay.mx._wkey == key
+    for n in names:
+        assert np.array_equal(first[n], again[n]), n
+    # an optimiser-like in-place update of one weight
+    t["w_down"].mul_(0.5)
+    updated = run(lay)
+    assert lay.mx._wkey != key
+    ref = run(fresh())
+    for n in names:
+        assert np.array_equal(updated[n], ref[n]), n
+    assert not np.array_equal(updated["y"], first["y"])
+    # the return value says whether a pass ran
+    mx = lay.mx
+    assert mx.quantize_weights(t["w_gate"], t["w_up"], t["w_down"]) is False
+    assert mx.quantize_weights(t["w_gate"], t["w_up"], t["w_down"], force=True) is True
+    mx.invalidate_weights()
+    assert mx.quantize_weights(t["w_gate"], t["w_up"], t["w_down"]) is True
+    assert mx.quantize_weights(t["w_gate"], t["w_up"], t["w_down"]) is False
