@@ -7,6 +7,9 @@
 namespace moe {
 
 constexpr int kRowThreads = 256;   // 4 waves = 4 tokens per workgroup
+// 16-byte pieces per lane taken together: a wave moves 4 KB of one row (a
+// whole d = 2048 bf16 row) before it turns to the next row
+constexpr int kRowUnroll = 4;
 
 // Loads the token's row ids (k <= 16) into registers; ids outside [0, n_rows)
 // become -1 so that a bad id is skipped rather than dereferenced.
@@ -35,11 +38,21 @@ __global__ void __launch_bounds__(kRowThreads) permute_kernel(const T* __restric
   load_rows(row_of, t, k, n_rows, rows);
   const int nvec = d / V;
   const V16* src = reinterpret_cast<const V16*>(x + t * d);
-  for (int c = lane; c < nvec; c += 64) {
-    const V16 v = src[c];
+  for (int c0 = lane; c0 < nvec; c0 += 64 * kRowUnroll) {
+    // kRowUnroll 1 KB pieces of the row at once, then each destination row
+    // written piece after piece
+    V16 v[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u)
+      if (c0 + 64 * u < nvec) v[u] = src[c0 + 64 * u];
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j)
-      if (j < k && rows[j] >= 0) reinterpret_cast<V16*>(x_perm + (size_t)rows[j] * d)[c] = v;
+      if (j < k && rows[j] >= 0) {
+        V16* dst = reinterpret_cast<V16*>(x_perm + (size_t)rows[j] * d);
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; ++u)
+          if (c0 + 64 * u < nvec) dst[c0 + 64 * u] = v[u];
+      }
   }
 }
 
@@ -77,24 +90,38 @@ __global__ void __launch_bounds__(kRowThreads) combine_kernel(const T* __restric
 #pragma unroll
   for (int j = 0; j < MOE_MAX_TOPK; ++j) w[j] = j < k ? topk_w[t * k + j] : 0.f;
   const int nvec = d / V;
-  for (int c = lane; c < nvec; c += 64) {
-    float acc[V];
-    if (y_add) {
-      unpack(reinterpret_cast<const V16*>(y_add + t * d)[c], acc);
-    } else {
+  for (int c0 = lane; c0 < nvec; c0 += 64 * kRowUnroll) {
+    float acc[kRowUnroll][V];
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int u = 0; u < kRowUnroll; ++u) {
+      if (y_add && c0 + 64 * u < nvec) {
+        unpack(reinterpret_cast<const V16*>(y_add + t * d)[c0 + 64 * u], acc[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[u][i] = 0.f;
+      }
     }
+    // each source row read piece after piece, rows in slot order
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
       if (j < k && rows[j] >= 0) {
-        float v[V];
-        unpack(reinterpret_cast<const V16*>(y_perm + (size_t)rows[j] * d)[c], v);
+        const V16* src = reinterpret_cast<const V16*>(y_perm + (size_t)rows[j] * d);
+        V16 v[kRowUnroll];
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] = fmaf(w[j], v[i], acc[i]);
+        for (int u = 0; u < kRowUnroll; ++u)
+          if (c0 + 64 * u < nvec) v[u] = src[c0 + 64 * u];
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; ++u) {
+          float f[V];
+          unpack(v[u], f);
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[u][i] = fmaf(w[j], f[i], acc[u][i]);
+        }
       }
     }
-    reinterpret_cast<V16*>(y + t * d)[c] = pack(acc);
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u)
+      if (c0 + 64 * u < nvec) reinterpret_cast<V16*>(y + t * d)[c0 + 64 * u] = pack(acc[u]);
   }
 }
 
@@ -117,20 +144,35 @@ __global__ void __launch_bounds__(kRowThreads) combine_bwd_kernel(
     dot[j] = 0.f;
   }
   const int nvec = d / V;
-  for (int c = lane; c < nvec; c += 64) {
-    float g[V];
-    unpack(reinterpret_cast<const V16*>(dy + t * d)[c], g);
+  for (int c0 = lane; c0 < nvec; c0 += 64 * kRowUnroll) {
+    V16 gv[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u)
+      if (c0 + 64 * u < nvec) gv[u] = reinterpret_cast<const V16*>(dy + t * d)[c0 + 64 * u];
+    // each routed row read and written piece after piece
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
       if (j < k && rows[j] >= 0) {
-        float v[V], o[V];
-        unpack(reinterpret_cast<const V16*>(y_perm + (size_t)rows[j] * d)[c], v);
+        const V16* src = reinterpret_cast<const V16*>(y_perm + (size_t)rows[j] * d);
+        V16* dst = reinterpret_cast<V16*>(dy_perm + (size_t)rows[j] * d);
+        V16 v[kRowUnroll];
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-          dot[j] = fmaf(g[i], v[i], dot[j]);
-          o[i] = w[j] * g[i];
+        for (int u = 0; u < kRowUnroll; ++u)
+          if (c0 + 64 * u < nvec) v[u] = src[c0 + 64 * u];
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; ++u) {
+          if (c0 + 64 * u < nvec) {
+            float g[V], f[V], o[V];
+            unpack(gv[u], g);
+            unpack(v[u], f);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+              dot[j] = fmaf(g[i], f[i], dot[j]);
+              o[i] = w[j] * g[i];
+            }
+            dst[c0 + 64 * u] = pack(o);
+          }
         }
-        reinterpret_cast<V16*>(dy_perm + (size_t)rows[j] * d)[c] = pack(o);
       }
     }
   }
@@ -159,45 +201,62 @@ __global__ void __launch_bounds__(kRowThreads) permute_bwd_kernel(
   const int nvec = d / V;
   const bool router = dlogits != nullptr;
   const bool wide = router && (E % V == 0);
-  for (int c = lane; c < nvec; c += 64) {
-    float acc[V];
-    if (dx_add) {
-      unpack(reinterpret_cast<const V16*>(dx_add + t * d)[c], acc);
-    } else {
+  for (int c0 = lane; c0 < nvec; c0 += 64 * kRowUnroll) {
+    float acc[kRowUnroll][V];
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    for (int u = 0; u < kRowUnroll; ++u) {
+      if (dx_add && c0 + 64 * u < nvec) {
+        unpack(reinterpret_cast<const V16*>(dx_add + t * d)[c0 + 64 * u], acc[u]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[u][i] = 0.f;
+      }
     }
+    // each source row read piece after piece, rows in slot order
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
       if (j < k && rows[j] >= 0) {
-        float v[V];
-        unpack(reinterpret_cast<const V16*>(dx_perm + (size_t)rows[j] * d)[c], v);
+        const V16* src = reinterpret_cast<const V16*>(dx_perm + (size_t)rows[j] * d);
+        V16 v[kRowUnroll];
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] += v[i];
-      }
-    }
-    if (wide) {
-      // w_r rows c*V .. c*V+V-1 are contiguous runs of E values
-      for (int e0 = 0; e0 < E; e0 += V) {
-        float g[V];
+        for (int u = 0; u < kRowUnroll; ++u)
+          if (c0 + 64 * u < nvec) v[u] = src[c0 + 64 * u];
 #pragma unroll
-        for (int ee = 0; ee < V; ++ee) g[ee] = dlogits[t * E + e0 + ee];
+        for (int u = 0; u < kRowUnroll; ++u) {
+          float f[V];
+          unpack(v[u], f);
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-          float wv[V];
-          unpack(*reinterpret_cast<const V16*>(w_r + (size_t)(c * V + i) * E + e0), wv);
-#pragma unroll
-          for (int ee = 0; ee < V; ++ee) acc[i] = fmaf(g[ee], wv[ee], acc[i]);
+          for (int i = 0; i < V; ++i) acc[u][i] += f[i];
         }
       }
-    } else if (router) {
-      for (int e = 0; e < E; ++e) {
-        const float g = dlogits[t * E + e];
-#pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] = fmaf(g, Elem<T>::load(w_r, (size_t)(c * V + i) * E + e), acc[i]);
-      }
     }
-    reinterpret_cast<V16*>(dx + t * d)[c] = pack(acc);
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const int c = c0 + 64 * u;
+      if (c >= nvec) continue;
+      if (wide) {
+        // w_r rows c*V .. c*V+V-1 are contiguous runs of E values
+        for (int e0 = 0; e0 < E; e0 += V) {
+          float g[V];
+#pragma unroll
+          for (int ee = 0; ee < V; ++ee) g[ee] = dlogits[t * E + e0 + ee];
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            float wv[V];
+            unpack(*reinterpret_cast<const V16*>(w_r + (size_t)(c * V + i) * E + e0), wv);
+#pragma unroll
+            for (int ee = 0; ee < V; ++ee) acc[u][i] = fmaf(g[ee], wv[ee], acc[u][i]);
+          }
+        }
+      } else if (router) {
+        for (int e = 0; e < E; ++e) {
+          const float g = dlogits[t * E + e];
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[u][i] = fmaf(g, Elem<T>::load(w_r, (size_t)(c * V + i) * E + e), acc[u][i]);
+        }
+      }
+      reinterpret_cast<V16*>(dx + t * d)[c] = pack(acc[u]);
+    }
   }
 }
 
