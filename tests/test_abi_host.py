@@ -22,7 +22,7 @@ def declared():
     return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
 
 
-def test_header_declares_the_north_star_calls():
+def test_header_declares_the_layer_entry_points():
     names = declared()
     for n in ("moe_route", "moe_offsets", "moe_permute", "moe_grouped_gemm",
               "moe_unpermute_combine", "moe_unpermute_combine_bwd", "moe_permute_bwd",
