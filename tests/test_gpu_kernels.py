@@ -119,7 +119,9 @@ def test_offsets_bad_ids_raise_flag():
 # ----------------------------------------------------------------------------- rows
 @pytest.mark.parametrize("kind", ["bf16", "f32"])
 @pytest.mark.parametrize("T,d,E,k,C", [(333, 264, 8, 2, 0), (1000, 2048, 128, 4, 0),
-                                       (700, 136, 16, 4, 150), (1, 8, 1, 1, 0)])
+                                       (700, 136, 16, 4, 150), (1, 8, 1, 1, 0),
+                                       (200, 4104, 64, 16, 0),    # top-16, rows longer than one pass, ragged tail
+                                       (50, 2048, 1024, 16, 0)])  # the most experts and slots the ABI takes
 def test_row_movement_parity(kind, T, d, E, k, C):
     rng = _rng(3, T, d, E, k, C)
     idx = _draw(rng, T, E, k, 1.0)
@@ -253,7 +255,8 @@ def _gg_case(kind, counts, d, F, seed, capacity=0):
     ("bf16", [0, 0, 0], 256, 256, 0),                                 # no rows at all
     ("bf16", [300], 256, 256, 0),                                     # weight-gradient grids < 8 workgroups
     ("bf16", [5, 3000], 256, 256, 0),
-    ("bf16", [0, 4000, 1, 0, 17, 2000, 0, 0, 3, 900], 512, 256, 0),  # skewed: work-balanced tile runs
+    ("bf16", [0, 4000, 1, 0, 17, 2000, 0, 0, 3, 900], 512, 256, 0),  # strongly skewed
+    ("bf16", [(7 * i) % 5 for i in range(600)], 256, 256, 0),        # > 512 experts: two per prefix thread
 ])
 def test_grouped_gemm_parity(kind, counts, d, F, capacity):
     rng, E, n_rows, groups, st, T, grp = _gg_case(kind, counts, d, F, hash((tuple(counts), d, F)) % 1000, capacity)
