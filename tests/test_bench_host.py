@@ -44,3 +44,33 @@ def test_algorithmic_bytes():
     assert stage_algorithmic_bytes("gg_fwd_gate_up", wl, R, R) == R * wl.d * 2 + 2 * W + 3 * R * wl.F * 2
     # the weight gradient of the down projection writes exactly one weight tensor
     assert stage_algorithmic_bytes("gg_wgrad_down", wl, R, R) - W == R * (wl.d + wl.F) * 2
+
+
+@pytest.mark.parametrize("name,stage", [
+    ("void moe::gg_mx_kernel<2, moe::MxCfg<128, 256, 2, 4, 3, 2> >(moe::MxArgs)", "mx_dgrad_down"),
+    ("void moe::gg_mx_kernel<5, moe::MxCfg<128, 256, 2, 4, 3, 2> >(moe::MxArgs)", "mx_wgrad_gate_up"),
+    ("moe::(anonymous namespace)::mx_both_kernel(unsigned short const*, int)", "mx_quantize"),
+    ("void moe::permute_bwd_kernel<unsigned short>(unsigned short const*)", "permute_bwd"),
+])
+def test_stage_of_mxfp8_and_adjoints(name, stage):
+    from profile_summary import stage_of
+    assert stage_of(name) == stage
+
+
+def test_timed_means_leave_out_warmup_launches(tmp_path):
+    """The kernel summary's timed mean drops each kernel's first launches
+    (the traced run's warm-up steps) in launch order, whatever order the
+    trace lists them in."""
+    from profile_summary import _timed_means
+    rows = [("k_a", 300, 400), ("k_a", 100, 190), ("k_b", 150, 160), ("k_a", 500, 520),
+            ("k_a", 700, 730), ("k_b", 800, 830)]   # (name, start ns, end ns)
+    path = tmp_path / "kt_kernel_trace.csv"
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for n, s, e in rows:
+            f.write(f"{n},{s},{e}\n")
+    m = _timed_means(str(path), 2)
+    # k_a launches in time order last 90, 100, 20, 30 ns: the last two remain
+    assert m["k_a"] == pytest.approx(25e-3)
+    # k_b has only two launches: all are kept rather than none
+    assert m["k_b"] == pytest.approx(20e-3)
