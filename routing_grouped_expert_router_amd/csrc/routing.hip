@@ -11,10 +11,13 @@ namespace moe {
 constexpr int kRouterTok = 4;
 constexpr int kRouterEC = 8;
 
+// wide: E is a multiple of 8 and w_r 16-byte aligned, so each row's group of
+// eight experts is read as 16-byte vectors
 template <typename T>
 __global__ void __launch_bounds__(256) router_gemm_kernel(const T* __restrict__ x,
                                                           const T* __restrict__ w_r, int T_,
-                                                          int d, int E, float* __restrict__ logits) {
+                                                          int d, int E, bool wide,
+                                                          float* __restrict__ logits) {
   constexpr int V = kVec<T>;
   const int lane = threadIdx.x & 63;
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -42,12 +45,24 @@ __global__ void __launch_bounds__(256) router_gemm_kernel(const T* __restrict__ 
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         const T* wrow = w_r + (size_t)(c * V + i) * E + e0;
+        float wv[kRouterEC];
+        if (wide) {
+          // the eight weights of this row as 16-byte loads
 #pragma unroll
-        for (int b = 0; b < kRouterEC; ++b) {
-          const float wv = (e0 + b < E) ? Elem<T>::load(wrow, b) : 0.f;
+          for (int h = 0; h < kRouterEC / V; ++h) {
+            float f[V];
+            unpack(reinterpret_cast<const V16*>(wrow)[h], f);
 #pragma unroll
-          for (int a = 0; a < kRouterTok; ++a) acc[a][b] = fmaf(xv[a][i], wv, acc[a][b]);
+            for (int m = 0; m < V; ++m) wv[h * V + m] = f[m];
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < kRouterEC; ++b) wv[b] = (e0 + b < E) ? Elem<T>::load(wrow, b) : 0.f;
         }
+#pragma unroll
+        for (int b = 0; b < kRouterEC; ++b)
+#pragma unroll
+          for (int a = 0; a < kRouterTok; ++a) acc[a][b] = fmaf(xv[a][i], wv[b], acc[a][b]);
       }
     }
 #pragma unroll
@@ -340,7 +355,12 @@ __global__ void __launch_bounds__(256) route_bwd_kernel(const int32_t* __restric
 // of kRbTok tokens, then a fixed-order reduction over chunks.
 constexpr int kRbTok = 128;
 constexpr int kRbEC = 8;
+constexpr int kRbCols = 64;             // vector columns per workgroup (one per lane)
+constexpr int kRbWaveTok = kRbTok / 4;  // tokens of the chunk per wave
 
+// Workgroup (chunk, column block, expert group): lane = vector column, wave
+// = a quarter of the chunk's tokens (summed in order, eight rows in flight);
+// the four quarters are added in wave order through LDS.
 template <typename T>
 __global__ void __launch_bounds__(256) router_bwd_partial_kernel(const T* __restrict__ x,
                                                                  const float* __restrict__ dl,
@@ -348,48 +368,89 @@ __global__ void __launch_bounds__(256) router_bwd_partial_kernel(const T* __rest
                                                                  float* __restrict__ part) {
   constexpr int V = kVec<T>;
   __shared__ float sdl[kRbTok][kRbEC];
+  __shared__ float red[3][V * kRbEC][kRbCols];
   const int chunk = blockIdx.x;
   const int e0 = blockIdx.z * kRbEC;
-  const int c = blockIdx.y * 256 + threadIdx.x;          // vector column
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = blockIdx.y * kRbCols + lane;             // vector column
   const int t0 = chunk * kRbTok;
   for (int i = threadIdx.x; i < kRbTok * kRbEC; i += 256) {
     const int tt = i / kRbEC, ee = i % kRbEC;
     sdl[tt][ee] = (t0 + tt < T_ && e0 + ee < E) ? dl[(size_t)(t0 + tt) * E + e0 + ee] : 0.f;
   }
   __syncthreads();
-  if (c * V >= d) return;
+  const bool col = c * V < d;
   float acc[V][kRbEC];
 #pragma unroll
   for (int a = 0; a < V; ++a)
 #pragma unroll
     for (int b = 0; b < kRbEC; ++b) acc[a][b] = 0.f;
-  const int tn = min(kRbTok, T_ - t0);
-  for (int tt = 0; tt < tn; ++tt) {
-    float xv[V];
-    unpack(*reinterpret_cast<const V16*>(x + (size_t)(t0 + tt) * d + (size_t)c * V), xv);
+  const int tw0 = wave * kRbWaveTok;                      // first token of this wave (in the chunk)
+  const int tn = min(kRbWaveTok, T_ - t0 - tw0);
+  constexpr int kU = 8;
+  for (int t1 = 0; col && t1 < tn; t1 += kU) {
+    V16 xr[kU];
 #pragma unroll
-    for (int b = 0; b < kRbEC; ++b) {
-      const float g = sdl[tt][b];
+    for (int u = 0; u < kU; ++u)
+      if (t1 + u < tn) xr[u] = *reinterpret_cast<const V16*>(x + (size_t)(t0 + tw0 + t1 + u) * d + (size_t)c * V);
 #pragma unroll
-      for (int a = 0; a < V; ++a) acc[a][b] = fmaf(xv[a], g, acc[a][b]);
+    for (int u = 0; u < kU; ++u) {
+      if (t1 + u < tn) {
+        float xv[V];
+        unpack(xr[u], xv);
+#pragma unroll
+        for (int b = 0; b < kRbEC; ++b) {
+          const float g = sdl[tw0 + t1 + u][b];
+#pragma unroll
+          for (int a = 0; a < V; ++a) acc[a][b] = fmaf(xv[a], g, acc[a][b]);
+        }
+      }
     }
   }
+  if (wave > 0) {
 #pragma unroll
-  for (int a = 0; a < V; ++a)
+    for (int a = 0; a < V; ++a)
 #pragma unroll
-    for (int b = 0; b < kRbEC; ++b)
-      if (e0 + b < E) part[((size_t)chunk * d + c * V + a) * E + e0 + b] = acc[a][b];
+      for (int b = 0; b < kRbEC; ++b) red[wave - 1][a * kRbEC + b][lane] = acc[a][b];
+  }
+  __syncthreads();
+  if (wave == 0 && col) {
+#pragma unroll
+    for (int a = 0; a < V; ++a)
+#pragma unroll
+      for (int b = 0; b < kRbEC; ++b) {
+        const float s = ((acc[a][b] + red[0][a * kRbEC + b][lane]) + red[1][a * kRbEC + b][lane]) +
+                        red[2][a * kRbEC + b][lane];
+        if (e0 + b < E) part[((size_t)chunk * d + c * V + a) * E + e0 + b] = s;
+      }
+  }
 }
 
+// dw_r[i] = sum over chunks of part[chunk][i]: eight lanes per output, lane j
+// summing chunks j, j+8, ... in order, then a fixed shuffle tree.
+constexpr int kRbRed = 8;
 template <typename T>
 __global__ void __launch_bounds__(256) router_bwd_reduce_kernel(const float* __restrict__ part,
                                                                 int nchunk, int d, int E,
                                                                 T* __restrict__ dw_r) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (size_t)d * E) return;
+  const size_t g = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t i = g / kRbRed;
+  const int j = static_cast<int>(g % kRbRed);
+  const size_t stride = (size_t)d * E;
+  const bool live = i < stride;
   float s = 0.f;
-  for (int c = 0; c < nchunk; ++c) s += part[(size_t)c * d * E + i];
-  Elem<T>::store(dw_r, i, s);
+  constexpr int kU = 4;
+  for (int c = j; live && c < nchunk; c += kRbRed * kU) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = c + kRbRed * u < nchunk ? part[(size_t)(c + kRbRed * u) * stride + i] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (c + kRbRed * u < nchunk) s += v[u];
+  }
+#pragma unroll
+  for (int o = 1; o < kRbRed; o <<= 1) s += __shfl_xor(s, o, 64);
+  if (live && j == 0) Elem<T>::store(dw_r, i, s);
 }
 
 }  // namespace moe
@@ -405,13 +466,14 @@ extern "C" int moe_router_gemm(int dtype, const void* x, const void* w_r, int T,
   MOE_CHECK_ARG(x && w_r && logits && aligned16(x));
   const int waves = (T + kRouterTok - 1) / kRouterTok;
   const int blocks = (waves + 3) / 4;
+  const bool wide = E % kRouterEC == 0 && aligned16(w_r);
   if (dtype == MOE_BF16)
     router_gemm_kernel<uint16_t><<<blocks, 256, 0, stream>>>(
-        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_r), T, d, E, logits);
+        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_r), T, d, E, wide, logits);
   else
     router_gemm_kernel<float><<<blocks, 256, 0, stream>>>(static_cast<const float*>(x),
                                                           static_cast<const float*>(w_r), T, d, E,
-                                                          logits);
+                                                          wide, logits);
   return launch_status();
 }
 
@@ -504,7 +566,7 @@ extern "C" int moe_router_gemm_bwd(int dtype, const void* x, const float* dlogit
   float* part = static_cast<float*>(ws);
   const int V = dtype == MOE_BF16 ? 8 : 4;
   if (nchunk > 0) {
-    dim3 grid(nchunk, (d / V + 255) / 256, (E + kRbEC - 1) / kRbEC);
+    dim3 grid(nchunk, (d / V + kRbCols - 1) / kRbCols, (E + kRbEC - 1) / kRbEC);
     if (dtype == MOE_BF16)
       router_bwd_partial_kernel<uint16_t><<<grid, 256, 0, stream>>>(
           static_cast<const uint16_t*>(x), dlogits, T, d, E, part);
@@ -514,7 +576,7 @@ extern "C" int moe_router_gemm_bwd(int dtype, const void* x, const float* dlogit
     if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
   }
   const int nred = nchunk;   // T == 0: the reduction writes zeros
-  const unsigned blocks = static_cast<unsigned>(((size_t)d * E + 255) / 256);
+  const unsigned blocks = static_cast<unsigned>(((size_t)d * E * kRbRed + 255) / 256);
   if (dtype == MOE_BF16)
     router_bwd_reduce_kernel<uint16_t><<<blocks, 256, 0, stream>>>(part, nred, d, E,
                                                                    static_cast<uint16_t*>(dw_r));
