@@ -64,7 +64,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Text for a status code (static storage; never NULL). */
 const char* moe_status_string(int status);
 
-/* ABI version of this header: 3. */
+/* ABI version of this header: 4. */
 int moe_abi_version(void);
 
 /* ----------------------------------------------------------------- router
@@ -197,7 +197,13 @@ int moe_router_gemm_bwd(int dtype, const void* x, const float* dlogits, int T, i
  * every group are neither read nor written. The host cannot see the group
  * sizes: offsets must be non-decreasing with group_offsets[E] <= n_rows
  * (each group is clamped to [0, n_rows] on the device).
- * ws: at least moe_grouped_gemm_workspace_bytes(desc) bytes (may be 0). */
+ * ws: at least moe_grouped_gemm_workspace_bytes(desc) bytes, 4-byte aligned,
+ * device memory owned by the caller; MOE_ERR_WORKSPACE when missing or too
+ * small. The weight gradients over device-resident groups (capacity == 0)
+ * need 64 bytes: the call writes there how the launch splits its tiles over
+ * the chip, computed on the device from the group sizes (tiles of the experts
+ * with the most rows carry the most work); the other ops need none. Calls
+ * sharing one workspace must be ordered on one stream. */
 typedef enum {
   MOE_GG_FWD_GATE_UP = 0,
   MOE_GG_FWD_DOWN = 1,

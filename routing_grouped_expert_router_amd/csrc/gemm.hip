@@ -238,6 +238,15 @@ template <class C> struct Dma {
   };
 };
 
+template <class C> struct DmaSplit {
+  template <int OP> struct Launch {
+    static void go(const GGArgs& a, int grid, hipStream_t s) {
+      if constexpr (OpInfo<OP>::kKVar)
+        gg_wgrad_split_kernel<OP, C><<<1, 256, 0, s>>>(a, grid, const_cast<int*>(a.split));
+    }
+  };
+};
+
 template <class C>
 int launch_dma(const moe_gg_desc* g, const GGArgs& a, bool kvar, bool dual, int N, hipStream_t stream) {
   const int bno = dual ? C::BN / 2 : C::BN;
@@ -246,6 +255,9 @@ int launch_dma(const moe_gg_desc* g, const GGArgs& a, bool kvar, bool dual, int 
   else grid = ((g->n_rows + C::BM - 1) / C::BM + g->E) * (long)(N / bno);
   if (grid == 0) return MOE_OK;
   MOE_CHECK_SUPPORTED(grid < (1L << 31));
+  if (kvar && a.split) {   // the launch's tile split, from the device-resident group sizes
+    if (int st = dispatch_op<DmaSplit<C>::template Launch>(g->op, a, static_cast<int>(grid), stream)) return st;
+  }
   return dispatch_op<Dma<C>::template Launch>(g->op, a, static_cast<int>(grid), stream);
 }
 
@@ -286,9 +298,15 @@ int gg_tile_order() {
 }
 }  // namespace moe
 
+// Weight gradients over device-resident groups keep their launch's tile
+// split (kSplitInts ints) in the workspace.
+constexpr size_t kSplitBytes = 64;
+static_assert(kSplitInts * sizeof(int) <= kSplitBytes, "split fits the workspace");
+
 extern "C" size_t moe_grouped_gemm_workspace_bytes(const moe_gg_desc* desc) {
-  (void)desc;
-  return 0;
+  if (desc == nullptr) return 0;
+  const bool kvar = desc->op == MOE_GG_WGRAD_DOWN || desc->op == MOE_GG_WGRAD_GATE_UP;
+  return kvar && desc->capacity == 0 ? kSplitBytes : 0;
 }
 
 extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
@@ -326,9 +344,12 @@ extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
     default:
       MOE_CHECK_ARG(act(g->x_perm) && act(g->dg) && act(g->du) && need(g->dw_gate) && need(g->dw_up));
   }
+  const size_t ws_need = moe_grouped_gemm_workspace_bytes(g);
+  if (ws_need > 0 && (g->ws == nullptr || g->ws_bytes < ws_need || !aligned4(g->ws))) return MOE_ERR_WORKSPACE;
   GGArgs a{g->op, g->E, g->d, g->F, g->n_rows, g->capacity, gg_tile_order(), g->group_offsets,
            g->x_perm, g->g, g->u, g->h, g->y_perm, g->dy_perm, g->dg, g->du, g->dx_perm,
-           g->w_gate, g->w_up, g->w_down, g->dw_gate, g->dw_up, g->dw_down};
+           g->w_gate, g->w_up, g->w_down, g->dw_gate, g->dw_up, g->dw_down,
+           ws_need > 0 ? static_cast<const int*>(g->ws) : nullptr};
   const bool dual = g->op == MOE_GG_FWD_GATE_UP || g->op == MOE_GG_WGRAD_GATE_UP;
   const int N = op_n(g->op, g->d, g->F);
   if (mfma_ok(g)) {

@@ -29,6 +29,9 @@ struct GGArgs {
   void* dw_gate;
   void* dw_up;
   void* dw_down;
+  // weight gradients: the tile split of the launch written by
+  // gg_wgrad_split_kernel (kSplitInts ints), or null for the equal-count split
+  const int* split;
 };
 
 // Row-varying tile order of the launches (host side; MOE_GG_ORDER=n selects 0).
@@ -114,26 +117,21 @@ MOE_DEV int xcd_tile(int blk, int nb, int tiles) {
 }
 MOE_DEV int xcd_remap(int b, int nb) { return xcd_tile(b, nb, nb); }
 
-// Row-varying ops: tile_start[e] = number of BM-row tiles of experts < e
-// (tile_start[E] = all m-tiles), built once per workgroup in LDS from the
-// device-resident group offsets (E <= MOE_MAX_EXPERTS). Returns the m-tile
-// count; every thread of the workgroup must call it.
-template <int BM, int NT>
-MOE_DEV int build_tile_prefix(const GGArgs& a, int* tile_start) {
+// Exclusive prefix over the experts of a per-expert count v(e) >= 0, built
+// in LDS by one workgroup: out[e] = sum_{h<e} v(h), out[E] = the total
+// (E <= MOE_MAX_EXPERTS). Returns the total; every thread of the workgroup
+// must call it.
+template <int NT, class V>
+MOE_DEV int build_expert_prefix(int E, V v, int* out) {
   // per-thread partial sums over a contiguous run of experts
   constexpr int kMaxPer = (MOE_MAX_EXPERTS + NT - 1) / NT;
-  const int per = (a.E + NT - 1) / NT;
+  const int per = (E + NT - 1) / NT;
   const int e_lo = threadIdx.x * per;
   int loc[kMaxPer];
   int sum = 0;
 #pragma unroll
   for (int i = 0; i < kMaxPer; ++i) {
-    int t = 0;
-    if (i < per && e_lo + i < a.E) {
-      int r0, n;
-      group_rows(a, e_lo + i, r0, n);
-      t = (n + BM - 1) / BM;
-    }
+    const int t = (i < per && e_lo + i < E) ? v(e_lo + i) : 0;
     loc[i] = t;
     sum += t;
   }
@@ -143,8 +141,8 @@ MOE_DEV int build_tile_prefix(const GGArgs& a, int* tile_start) {
   int incl = sum;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
   }
   if (lane == 63) wtot[w] = incl;
   __syncthreads();
@@ -152,12 +150,116 @@ MOE_DEV int build_tile_prefix(const GGArgs& a, int* tile_start) {
   for (int i = 0; i < w; ++i) before += wtot[i];
 #pragma unroll
   for (int i = 0; i < kMaxPer; ++i) {
-    if (i < per && e_lo + i < a.E) tile_start[e_lo + i] = before;
+    if (i < per && e_lo + i < E) out[e_lo + i] = before;
     before += loc[i];
   }
-  if (threadIdx.x == NT - 1) tile_start[a.E] = before;
+  if (threadIdx.x == NT - 1) out[E] = before;
   __syncthreads();
-  return tile_start[a.E];
+  return out[E];
+}
+
+// Row-varying ops: tile_start[e] = number of BM-row tiles of experts < e
+// (tile_start[E] = all m-tiles), from the device-resident group offsets.
+template <int BM, int NT>
+MOE_DEV int build_tile_prefix(const GGArgs& a, int* tile_start) {
+  return build_expert_prefix<NT>(a.E, [&](int e) {
+    int r0, n;
+    group_rows(a, e, r0, n);
+    return (n + BM - 1) / BM;
+  }, tile_start);
+}
+
+// ------------------------------------------------------------------ weight-gradient tile split
+// A weight-gradient launch has one workgroup per tile: every expert has tpe
+// = (M/BM)(N/BNO) tiles (numbered expert-major) whose work grows with the
+// expert's rows (its K: K steps of BK plus kTileFixed for a tile's prologue
+// and epilogue). With experts of about equal size the XCDs split the tiles
+// into equal contiguous ranges and each workgroup takes one (xcd_remap). When
+// that split leaves one XCD more than kSkew times the mean work, the XCDs
+// split the work instead: each takes a contiguous range of tiles holding an
+// equal share of it, and its workgroups take consecutive chunks of
+// ceil(range / workgroups) tiles. One workgroup (gg_wgrad_split_kernel)
+// decides this once per launch and writes split[0] = 1 when balancing,
+// split[1 + x] = first tile of XCD x (x = 0..8, split[9] = all tiles).
+constexpr int kTileFixed = 3;
+constexpr float kSkew = 1.25f;
+constexpr int kXcdCount = 8;
+constexpr int kSplitInts = 2 + kXcdCount;
+
+template <int BK, int NT>
+MOE_DEV void wgrad_split(const GGArgs& a, int tpe, int nb, int* scratch, int* split) {
+  static_assert(NT >= 2 * kXcdCount + 1, "one thread per XCD check and per boundary");
+  auto work = [&](int e) {
+    int r0, n;
+    group_rows(a, e, r0, n);
+    return (n + BK - 1) / BK + kTileFixed;
+  };
+  build_expert_prefix<NT>(a.E, work, scratch);   // ends with a barrier
+  __shared__ long xcd_work[kXcdCount];
+  const int T = a.E * tpe;
+  const long total = (long)tpe * scratch[a.E];
+  auto work_before = [&](int u) -> long {   // work of tiles [0, u)
+    if (u >= T) return total;
+    const int e = u / tpe;
+    return (long)tpe * scratch[e] + (long)(u % tpe) * (scratch[e + 1] - scratch[e]);
+  };
+  const int tid = threadIdx.x;
+  const bool check = nb >= kXcdCount && nb == T;   // the equal-count split of xcd_remap applies
+  if (tid < kXcdCount) {
+    // XCD tid's work under the equal-count split
+    long w = 0;
+    if (check) {
+      const int q = nb / kXcdCount, r = nb % kXcdCount;
+      const int t0 = tid < r ? tid * (q + 1) : r * (q + 1) + (tid - r) * q;
+      const int t1 = t0 + q + (tid < r ? 1 : 0);
+      w = work_before(t1) - work_before(t0);
+    }
+    xcd_work[tid] = w;
+  } else if (tid < 2 * kXcdCount + 1) {
+    // boundary x: the first tile whose work starts at or after x / kXcdCount of the total
+    const int x = tid - kXcdCount;
+    const long target = total * x / kXcdCount;
+    int t;
+    if (target <= 0) {
+      t = 0;
+    } else if (target >= total) {
+      t = T;
+    } else {
+      int lo = 0, hi = a.E - 1;   // last e with tpe * scratch[e] <= target
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((long)tpe * scratch[mid] <= target) lo = mid;
+        else hi = mid - 1;
+      }
+      const long w = scratch[lo + 1] - scratch[lo];
+      const long j = (target - (long)tpe * scratch[lo] + w - 1) / w;   // tiles of expert lo before it
+      t = j >= tpe ? (lo + 1) * tpe : lo * tpe + (int)j;
+    }
+    split[1 + x] = t;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    long most = 0;
+    for (int x = 0; x < kXcdCount; ++x) most = xcd_work[x] > most ? xcd_work[x] : most;
+    split[0] = check && (float)most > kSkew * (float)total / kXcdCount ? 1 : 0;
+  }
+}
+
+// This workgroup's tiles [t, end) of a weight-gradient launch of nb
+// workgroups (one per tile) under the split (or the equal-count split when
+// it is null). Every tile falls in exactly one workgroup's range.
+MOE_DEV void wgrad_tiles(const int* __restrict__ split, int blk, int nb, int& t, int& end) {
+  if (split == nullptr || split[0] == 0) {
+    t = xcd_remap(blk, nb);
+    end = t + 1;
+    return;
+  }
+  const int x = blk % kXcdCount, s = blk / kXcdCount;
+  const int t0 = split[1 + x], t1 = split[2 + x];
+  const int wgs = nb / kXcdCount + (x < nb % kXcdCount ? 1 : 0);   // workgroups of this XCD
+  const int c = (t1 - t0 + wgs - 1) / wgs;
+  t = t0 + c * s < t1 ? t0 + c * s : t1;
+  end = t + c < t1 ? t + c : t1;
 }
 
 // m-tile tm -> (expert, first row, rows), from a built prefix.

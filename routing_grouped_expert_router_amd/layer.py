@@ -72,6 +72,10 @@ class MoELayer:
         self.err_flag = torch.zeros(1, dtype=i32, device=dev)
         ws = max(L.moe_offsets_workspace_bytes(T, k, E), 16)
         self.ws_offsets = e((ws + 15) // 16 * 4, dt=i32)
+        # Grouped-GEMM workspace (the weight-gradient tile split); one buffer serves every
+        # launch because they all run in order on one stream.
+        wgrad = L.make_gg_desc(L.MOE_GG_WGRAD_GATE_UP, L.MOE_BF16, E, d, F, nr, 0)
+        self.ws_gg = e((max(L.moe_grouped_gemm_workspace_bytes(wgrad), 4) + 3) // 4, dt=i32)
         self.x_perm = None if mxfp8 else e(nr, d)   # the MXFP8 permute writes quantised rows only
         self.g, self.u, self.h = e(nr, F), e(nr, F), e(nr, F)
         self.y_perm = e(nr, d)
@@ -124,7 +128,7 @@ class MoELayer:
     def _gg(self, op, **tensors):
         grp = None if self.capacity > 0 else self.offsets
         desc = L.make_gg_desc(op, self._dt, self.E, self.d, self.F, self.n_rows, self.capacity,
-                              grp, **tensors)
+                              grp, ws=self.ws_gg, **tensors)
         L.moe_grouped_gemm(desc)
 
     # ------------------------------------------------------------------ passes
@@ -135,7 +139,8 @@ class MoELayer:
         self._mark("route")
 
     def _gg_shared(self, op, **tensors):
-        desc = L.make_gg_desc(op, self._dt, 1, self.d, self.shared_ff, self.T, 0, self.offsets_s, **tensors)
+        desc = L.make_gg_desc(op, self._dt, 1, self.d, self.shared_ff, self.T, 0, self.offsets_s,
+                              ws=self.ws_gg, **tensors)
         L.moe_grouped_gemm(desc)
 
     def shared_forward(self):

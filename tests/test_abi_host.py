@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 def test_binding_covers_every_declared_symbol():
     assert sorted(L.SIGNATURES) == declared()
     lib = L.lib()
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(-3) == b"workspace missing or too small"
     assert lib.moe_status_string(12345) == b"unknown status"
@@ -130,6 +130,28 @@ def test_grouped_gemm_argument_errors():
     d.capacity = 16
     assert call(d) == INVALID
     assert lib.moe_grouped_gemm(None, None) == INVALID
+
+
+def test_grouped_gemm_workspace():
+    """Only weight gradients over device-resident groups need a workspace (their tile split)."""
+    lib = L.lib()
+    for op in (L.MOE_GG_FWD_GATE_UP, L.MOE_GG_FWD_DOWN, L.MOE_GG_DGRAD_DOWN, L.MOE_GG_DGRAD_GATE_UP):
+        for cap in (0, 16):
+            d = L.make_gg_desc(op, L.MOE_BF16, 4, 256, 256, 64, cap)
+            assert L.moe_grouped_gemm_workspace_bytes(d) == 0
+    for op in (L.MOE_GG_WGRAD_DOWN, L.MOE_GG_WGRAD_GATE_UP):
+        assert L.moe_grouped_gemm_workspace_bytes(L.make_gg_desc(op, L.MOE_BF16, 4, 256, 256, 64, 16)) == 0
+        need = L.moe_grouped_gemm_workspace_bytes(L.make_gg_desc(op, L.MOE_BF16, 4, 256, 256, 64, 0))
+        assert need >= 4 * 10 and need % 4 == 0
+    assert lib.moe_grouped_gemm_workspace_bytes(None) == 0
+    d = L.make_gg_desc(L.MOE_GG_WGRAD_DOWN, L.MOE_BF16, 4, 256, 256, 64, 0)
+    d.group_offsets, d.h, d.dy_perm, d.dw_down = FAKE, FAKE, FAKE, FAKE
+    call = lambda d: lib.moe_grouped_gemm(C.byref(d), None)
+    assert call(d) == WORKSPACE                          # no workspace
+    d.ws, d.ws_bytes = FAKE, need - 4
+    assert call(d) == WORKSPACE                          # too small
+    d.ws, d.ws_bytes = FAKE + 2, need
+    assert call(d) == WORKSPACE                          # misaligned
 
 
 def test_mx_quantize_argument_errors():

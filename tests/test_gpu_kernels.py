@@ -269,8 +269,10 @@ def test_grouped_gemm_parity(kind, counts, d, F, capacity):
     x, dyp = T["x_perm"], T["dy_perm"]
     wg, wu, wd = T["w_gate"], T["w_up"], T["w_down"]
 
+    ws = torch.zeros(16, dtype=torch.int32, device="cuda")
+
     def run(op, **kw):
-        L.moe_grouped_gemm(L.make_gg_desc(op, code, E, d, F, n_rows, capacity, grp, **kw))
+        L.moe_grouped_gemm(L.make_gg_desc(op, code, E, d, F, n_rows, capacity, grp, ws=ws, **kw))
 
     run(L.MOE_GG_FWD_GATE_UP, x_perm=x[0], w_gate=wg[0], w_up=wu[0], g=out["g"], u=out["u"], h=out["h"])
     run(L.MOE_GG_FWD_DOWN, h=out["h"], w_down=wd[0], y_perm=out["y_perm"])
