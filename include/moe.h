@@ -64,7 +64,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Text for a status code (static storage; never NULL). */
 const char* moe_status_string(int status);
 
-/* ABI version of this header: 4. */
+/* ABI version of this header: 5. */
 int moe_abi_version(void);
 
 /* ----------------------------------------------------------------- router
@@ -326,7 +326,14 @@ int moe_permute_mx(const void* x, int T, int d, int k, const int32_t* src_slot,
  *   WGRAD_GATE_UP K=n_e   x_perm cols   -         dg cols                du cols       dw_gate, dw_up
  *
  * Shapes of the bf16 tensors are those of moe_grouped_gemm. d % 256 == 0 and
- * F % 256 == 0. Weight gradients of experts with no rows are zeros. */
+ * F % 256 == 0. Weight gradients of experts with no rows are zeros.
+ *
+ * ws: at least moe_grouped_gemm_mx_workspace_bytes(desc) bytes, 4-byte
+ * aligned, device memory owned by the caller; MOE_ERR_WORKSPACE when missing
+ * or too small. The weight gradients need 4 * (E + 16) bytes: the call
+ * writes there the tile split of moe_grouped_gemm's weight gradients and each
+ * expert's first padded token column; the other ops need none. Calls sharing
+ * one workspace must be ordered on one stream. */
 typedef struct moe_mx_tensor {
   const void* q;   /* E4M3 codes */
   const void* s;   /* E8M0 scales */
@@ -344,8 +351,11 @@ typedef struct moe_mx_gg_desc {
   void* out0;
   void* out1;
   void* out2;
+  void* ws;                      /* workspace, see above */
+  size_t ws_bytes;
 } moe_mx_gg_desc;
 
+size_t moe_grouped_gemm_mx_workspace_bytes(const moe_mx_gg_desc* desc);
 int moe_grouped_gemm_mx(const moe_mx_gg_desc* desc, hipStream_t stream);
 
 #ifdef __cplusplus

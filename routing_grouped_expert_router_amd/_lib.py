@@ -45,6 +45,7 @@ class moe_mx_gg_desc(C.Structure):
         ("group_offsets", _vp),
         ("a0", moe_mx_tensor), ("a1", moe_mx_tensor), ("b0", moe_mx_tensor), ("b1", moe_mx_tensor),
         ("g", _vp), ("u", _vp), ("out0", _vp), ("out1", _vp), ("out2", _vp),
+        ("ws", _vp), ("ws_bytes", _sz),
     ]
 
 
@@ -69,6 +70,7 @@ SIGNATURES = {
     "moe_mx_quantize": (_i, [_vp, _i, _i, _i, _vp, _i, _i, _vp, _vp, _vp]),
     "moe_mx_quantize_both": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _vp]),
     "moe_permute_mx": (_i, [_vp, _i, _i, _i, _vp, _vp, _i, _i, _i, _vp, _vp, _vp, _vp, _vp]),
+    "moe_grouped_gemm_mx_workspace_bytes": (_sz, [C.POINTER(moe_mx_gg_desc)]),
     "moe_grouped_gemm_mx": (_i, [C.POINTER(moe_mx_gg_desc), _vp]),
 }
 
@@ -260,7 +262,7 @@ def moe_permute_mx(x, k, src_slot, group_offsets, E, col_stride, rows_out: MxTen
 
 
 def make_mx_gg_desc(op, E, d, F, n_rows, group_offsets, col_stride=0, a0=None, a1=None, b0=None,
-                    b1=None, g=None, u=None, out0=None, out1=None, out2=None) -> moe_mx_gg_desc:
+                    b1=None, g=None, u=None, out0=None, out1=None, out2=None, ws=None) -> moe_mx_gg_desc:
     desc = moe_mx_gg_desc()
     desc.op, desc.E, desc.d, desc.F, desc.n_rows, desc.col_stride = op, E, d, F, n_rows, col_stride
     desc.group_offsets = _p(group_offsets)
@@ -269,7 +271,13 @@ def make_mx_gg_desc(op, E, d, F, n_rows, group_offsets, col_stride=0, a0=None, a
             getattr(desc, name).q, getattr(desc, name).s = _p(t.q), _p(t.s)
     for name, t in (("g", g), ("u", u), ("out0", out0), ("out1", out1), ("out2", out2)):
         setattr(desc, name, _p(t))
+    if ws is not None:
+        desc.ws, desc.ws_bytes = _p(ws), ws.numel() * ws.element_size()
     return desc
+
+
+def moe_grouped_gemm_mx_workspace_bytes(desc: moe_mx_gg_desc) -> int:
+    return lib().moe_grouped_gemm_mx_workspace_bytes(C.byref(desc))
 
 
 def moe_grouped_gemm_mx(desc: moe_mx_gg_desc, stream=None):

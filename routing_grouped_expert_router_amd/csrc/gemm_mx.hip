@@ -28,7 +28,18 @@ template <int OP> void launch_mx_op(const MxArgs& x, int grid, hipStream_t s) {
   else gg_mx_kernel<OP, CfgMx><<<grid, CfgMx::NT, 0, s>>>(x);
 }
 
+template <int OP> void launch_mx_split(const MxArgs& x, int grid, int* ws, hipStream_t s) {
+  // both tile shapes share BM, BN and BK, hence the split
+  gg_mx_wgrad_split_kernel<OP, CfgMx><<<1, 256, 0, s>>>(x.o, grid, ws);
+}
+
 int launch_mx(int op, const MxArgs& x, int grid, hipStream_t s) {
+  if (op == MOE_GG_WGRAD_DOWN || op == MOE_GG_WGRAD_GATE_UP) {
+    int* ws = const_cast<int*>(x.o.split);
+    if (op == MOE_GG_WGRAD_DOWN) launch_mx_split<MOE_GG_WGRAD_DOWN>(x, grid, ws, s);
+    else launch_mx_split<MOE_GG_WGRAD_GATE_UP>(x, grid, ws, s);
+    if (int st = launch_status()) return st;
+  }
   switch (op) {
     case MOE_GG_FWD_GATE_UP: launch_mx_op<MOE_GG_FWD_GATE_UP>(x, grid, s); break;
     case MOE_GG_FWD_DOWN: launch_mx_op<MOE_GG_FWD_DOWN>(x, grid, s); break;
@@ -46,6 +57,13 @@ bool tensor_ok(const moe_mx_tensor& t) { return t.q != nullptr && t.s != nullptr
 }  // namespace moe
 
 using namespace moe;
+
+extern "C" size_t moe_grouped_gemm_mx_workspace_bytes(const moe_mx_gg_desc* desc) {
+  if (desc == nullptr) return 0;
+  const bool kvar = desc->op == MOE_GG_WGRAD_DOWN || desc->op == MOE_GG_WGRAD_GATE_UP;
+  const int E = desc->E > 0 ? desc->E : 0;
+  return kvar ? sizeof(int) * (size_t)(kMxColStart + E) : 0;
+}
 
 extern "C" int moe_grouped_gemm_mx(const moe_mx_gg_desc* g, hipStream_t stream) {
   MOE_CHECK_ARG(g != nullptr);
@@ -92,6 +110,8 @@ extern "C" int moe_grouped_gemm_mx(const moe_mx_gg_desc* g, hipStream_t stream) 
     span = span > cs ? span : cs;
   }
   MOE_CHECK_SUPPORTED(span < (1L << 31) && d * F < (1L << 31));
+  const size_t ws_need = moe_grouped_gemm_mx_workspace_bytes(g);
+  if (ws_need > 0 && (g->ws == nullptr || g->ws_bytes < ws_need || !aligned4(g->ws))) return MOE_ERR_WORKSPACE;
 
   MxArgs x{};
   x.o = GGArgs{g->op, g->E, g->d, g->F, g->n_rows, 0, gg_tile_order(), g->group_offsets,
@@ -114,6 +134,7 @@ extern "C" int moe_grouped_gemm_mx(const moe_mx_gg_desc* g, hipStream_t stream) 
   put(g->b0, x.bq[0], x.bs[0]);
   put(g->b1, x.bq[1], x.bs[1]);
   x.P = g->col_stride;
+  x.o.split = ws_need > 0 ? static_cast<const int*>(g->ws) : nullptr;
 
   const bool dual = g->op == MOE_GG_FWD_GATE_UP || g->op == MOE_GG_WGRAD_GATE_UP;
   const int N = op_n(g->op, g->d, g->F);

@@ -12,4 +12,4 @@ extern "C" const char* moe_status_string(int status) {
   }
 }
 
-extern "C" int moe_abi_version(void) { return 4; }
+extern "C" int moe_abi_version(void) { return 5; }

@@ -65,6 +65,11 @@ class MxExperts:
             self.dg, self.du = bf(n, F), bf(n, F)
             self.dx_perm = bf(n, d)
             self.dw_gate, self.dw_up, self.dw_down = bf(E, d, F), bf(E, d, F), bf(E, F, d)
+        # weight-gradient workspace (tile split and padded column starts); the
+        # GEMMs run in order on one stream, so one buffer serves them all
+        wgrad = L.make_mx_gg_desc(L.MOE_GG_WGRAD_GATE_UP, E, d, F, n, None, self.P)
+        self.ws = torch.empty((L.moe_grouped_gemm_mx_workspace_bytes(wgrad) + 3) // 4, dtype=torch.int32,
+                              device=dev)
         self.hook = None
         self._wkey = None   # which weights the quantised copies hold (see quantize_weights)
 
@@ -73,7 +78,7 @@ class MxExperts:
             self.hook(name)
 
     def _gg(self, op, **kw):
-        desc = L.make_mx_gg_desc(op, self.E, self.d, self.F, self.n, self.offsets, self.P, **kw)
+        desc = L.make_mx_gg_desc(op, self.E, self.d, self.F, self.n, self.offsets, self.P, ws=self.ws, **kw)
         L.moe_grouped_gemm_mx(desc)
 
     # ------------------------------------------------------------------ steps

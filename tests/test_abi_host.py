@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 def test_binding_covers_every_declared_symbol():
     assert sorted(L.SIGNATURES) == declared()
     lib = L.lib()
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(-3) == b"workspace missing or too small"
     assert lib.moe_status_string(12345) == b"unknown status"
@@ -50,7 +50,7 @@ def test_desc_layout_matches_header():
     assert C.sizeof(L.moe_gg_desc) == 7 * 4 + 4 + 8 * 17 + 8
     # int op..col_stride (6), group_offsets, 4 (codes, scales) pairs, g, u, 3 outputs
     assert C.sizeof(L.moe_mx_tensor) == 16
-    assert C.sizeof(L.moe_mx_gg_desc) == 6 * 4 + 8 + 4 * 16 + 5 * 8
+    assert C.sizeof(L.moe_mx_gg_desc) == 6 * 4 + 8 + 4 * 16 + 5 * 8 + 2 * 8
     assert L.moe_mx_gg_desc.a0.offset == 32 and L.moe_mx_gg_desc.g.offset == 96
 
 
@@ -203,6 +203,27 @@ def test_mx_gemm_argument_errors():
     d.op = 9
     assert call(d) == INVALID
     assert lib.moe_grouped_gemm_mx(None, None) == INVALID
+
+
+def test_mx_gemm_workspace():
+    """The MXFP8 weight gradients need 4 * (E + 16) bytes of workspace, the other ops none."""
+    lib = L.lib()
+    call = lambda d: lib.moe_grouped_gemm_mx(C.byref(d), None)
+    for op in (L.MOE_GG_FWD_GATE_UP, L.MOE_GG_FWD_DOWN, L.MOE_GG_DGRAD_DOWN, L.MOE_GG_DGRAD_GATE_UP):
+        assert L.moe_grouped_gemm_mx_workspace_bytes(L.make_mx_gg_desc(op, 4, 256, 256, 64, None)) == 0
+    for op in (L.MOE_GG_WGRAD_DOWN, L.MOE_GG_WGRAD_GATE_UP):
+        for E in (1, 4, 1024):
+            assert L.moe_grouped_gemm_mx_workspace_bytes(L.make_mx_gg_desc(op, E, 256, 256, 64, None)) == 4 * (E + 16)
+    assert lib.moe_grouped_gemm_mx_workspace_bytes(None) == 0
+    d = L.make_mx_gg_desc(L.MOE_GG_WGRAD_DOWN, 4, 256, 256, 64, None, col_stride=128 * 5)
+    d.group_offsets, d.out0 = FAKE, FAKE
+    d.a0.q, d.a0.s, d.b0.q, d.b0.s = FAKE, FAKE, FAKE, FAKE
+    need = 4 * (4 + 16)
+    assert call(d) == WORKSPACE                          # no workspace
+    d.ws, d.ws_bytes = FAKE, need - 4
+    assert call(d) == WORKSPACE                          # too small
+    d.ws, d.ws_bytes = FAKE + 2, need
+    assert call(d) == WORKSPACE                          # misaligned
 
 
 def test_mx_quantize_both_argument_errors():
