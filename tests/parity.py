@@ -136,3 +136,49 @@ def expert_weight_grads(x, W: Weights, meta, w, dy, experts: List[int], k: int, 
         dWg, dWu = om.expert_wgrad_gate_up(X, dG, dU, [(0, n)], d, F, store)
         out[e] = dict(dw_gate=dWg[0], dw_up=dWu[0], dw_down=dWd)
     return out
+
+
+def wgrad_split_reference(counts, tpe: int, bk: int, xcds: int = 8, fixed: int = 3,
+                          skew: float = 1.25) -> List[int]:
+    """What a weight-gradient launch writes as its tile split (host logic of
+    the scheduler, not of the method): tile work = K steps of bk rows + fixed;
+    split[0] = 1 when the equal-count split over the XCDs leaves one above
+    skew x the mean work, split[1 + x] = first tile at or after x / xcds of
+    the total work."""
+    work = [(int(n) + bk - 1) // bk + fixed for n in counts]
+    pre = [0]
+    for w_ in work:
+        pre.append(pre[-1] + w_)
+    E = len(counts)
+    T, total = E * tpe, tpe * pre[E]
+
+    def before(u):
+        if u >= T:
+            return total
+        e = u // tpe
+        return tpe * pre[e] + (u % tpe) * (pre[e + 1] - pre[e])
+
+    bal = 0
+    if T >= xcds:   # one workgroup per tile
+        q, r = divmod(T, xcds)
+        most = 0
+        for x in range(xcds):
+            t0 = x * (q + 1) if x < r else r * (q + 1) + (x - r) * q
+            t1 = t0 + q + (1 if x < r else 0)
+            most = max(most, before(t1) - before(t0))
+        bal = int(np.float32(most) > np.float32(skew) * np.float32(total) / np.float32(xcds))
+    out = [bal]
+    for x in range(xcds + 1):
+        target = total * x // xcds
+        if target <= 0:
+            t = 0
+        elif target >= total:
+            t = T
+        else:
+            lo = max(e for e in range(E) if tpe * pre[e] <= target)
+            w_ = pre[lo + 1] - pre[lo]
+            j = -(-(target - tpe * pre[lo]) // w_)
+            t = (lo + 1) * tpe if j >= tpe else lo * tpe + j
+        out.append(t)
+    return out
+

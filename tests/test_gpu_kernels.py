@@ -11,7 +11,7 @@ import oracle.moe as om
 from oracle.numerics import round_bf16, round_f32, storer
 from routing_grouped_expert_router_amd import _lib as L
 
-from parity import assert_close, dev, host, rel_err
+from parity import assert_close, dev, host, rel_err, wgrad_split_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -298,6 +298,47 @@ def test_grouped_gemm_parity(kind, counts, d, F, capacity):
     for e_ in range(E):
         if groups[e_][1] == 0 or (capacity and counts[e_] == 0):
             assert np.all(host(out["dw_down"][e_]) == 0) and np.all(host(out["dw_gate"][e_]) == 0)
+
+
+@pytest.mark.parametrize("counts,d,F", [
+    ([512] * 16, 512, 256),                                   # equal: the equal-count split stays
+    ([0, 4000, 1, 0, 17, 2000, 0, 0, 3, 900], 512, 256),     # skewed: balanced by work
+    ([(7 * i) % 5 for i in range(600)], 256, 256),            # many small experts
+    ([300], 256, 256),                                        # fewer tiles than XCDs
+])
+def test_wgrad_tile_split(counts, d, F):
+    """The weight gradients' tile split, as read back from the workspace, is
+    the documented rule applied to the group sizes (bit-exact integers), and
+    the GEMM that follows it is still correct."""
+    E = len(counts)
+    n_rows = int(sum(counts))
+    grp = dev(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), "i32")
+    r = lambda *s: (torch.rand(*s, device="cuda") - 0.5).to(torch.bfloat16)
+    nr = max(n_rows, 1)
+    x, h, dy, dg, du = r(nr, d), r(nr, F), r(nr, d), r(nr, F), r(nr, F)
+    dw_gate, dw_up, dw_down = r(E, d, F), r(E, d, F), r(E, F, d)
+    ws = torch.full((16,), -7, dtype=torch.int32, device="cuda")
+    BM, BN = 128, 256          # the default weight-gradient tile
+    for op, tpe, kw, check in (
+            (L.MOE_GG_WGRAD_DOWN, (F // BM) * (d // BN), dict(h=h, dy_perm=dy, dw_down=dw_down),
+             lambda: h[:n_rows].float().t().contiguous() @ dy[:n_rows].float()),
+            (L.MOE_GG_WGRAD_GATE_UP, (d // BM) * (F // (BN // 2)), dict(x_perm=x, dg=dg, du=du, dw_gate=dw_gate,
+                                                                    dw_up=dw_up),
+             lambda: x[:n_rows].float().t().contiguous() @ dg[:n_rows].float())):
+        desc = L.make_gg_desc(op, L.MOE_BF16, E, d, F, n_rows, 0, grp, ws=ws, **kw)
+        L.moe_grouped_gemm(desc)
+        torch.cuda.synchronize()
+        got = host(ws)[:10].tolist()
+        assert got == wgrad_split_reference(counts, tpe, 32), (op, got)
+        # the summed gradient over all experts (one check per op that every tile ran once)
+        out = dw_down if op == L.MOE_GG_WGRAD_DOWN else dw_gate
+        want = check()
+        err = float((out.float().sum(0) - want).abs().max() / (want.abs().max() + 1e-30))
+        assert err < 3e-2, (op, err)
+    if counts == [0, 4000, 1, 0, 17, 2000, 0, 0, 3, 900]:
+        assert got[0] == 1     # the skewed case takes the balanced split
+    if counts == [512] * 16:
+        assert got[0] == 0
 
 
 def test_grouped_gemm_rejects_bad_descriptors():

@@ -12,7 +12,7 @@ from oracle.numerics import f64_to_bf16_bits, mx_quantize, round_bf16
 from routing_grouped_expert_router_amd import _lib as L
 from routing_grouped_expert_router_amd.mx_layer import MxExperts
 
-from parity import assert_close, dev, host
+from parity import assert_close, dev, host, wgrad_split_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -313,6 +313,33 @@ def test_mx_each_gemm_on_oracle_inputs(counts, d, F):
         assert e <= 8e-3, (name, report)
         assert same > 0.95, (name, report)
     print("rel err, exact fraction", report)
+
+
+@pytest.mark.parametrize("counts", [[0, 2500, 1, 0, 17, 1200, 3, 600], [256] * 16])
+def test_mx_wgrad_workspace(counts):
+    """The MXFP8 weight gradients' workspace, read back: the tile split is the
+    documented rule on the group sizes (64-deep K steps) and each expert's
+    first padded token column is 128 x the count of 128-column blocks before it."""
+    d, F = 256, 512
+    E, n = len(counts), int(sum(counts))
+    off = np.zeros(E + 1, dtype=np.int32)
+    off[1:] = np.cumsum(counts)
+    lay = MxExperts(n, d, E, F)
+    lay.offsets = dev(off, "i32")
+    r = lambda *s: (torch.rand(*s, device="cuda") - 0.5).to(torch.bfloat16)
+    q_cols = lambda src, t: L.moe_mx_quantize(src, 1, t.q, t.s, lay.offsets, E, lay.P)
+    q_cols(r(n, F), lay.h_c)
+    q_cols(r(n, d), lay.dy_c)
+    lay.ws.fill_(-7)
+    lay._gg(L.MOE_GG_WGRAD_DOWN, a0=lay.h_c.t, b0=lay.dy_c.t, out0=lay.dw_down)
+    torch.cuda.synchronize()
+    ws = host(lay.ws)
+    tpe = (F // 128) * (d // 256)          # 128 x 256 tiles
+    assert ws[:10].tolist() == wgrad_split_reference(counts, tpe, 64)
+    cols = 128 * np.concatenate([[0], np.cumsum([(c + 127) // 128 for c in counts])])[:E]
+    assert np.array_equal(ws[16:16 + E], cols)
+    skewed = counts[0] == 0
+    assert ws[0] == (1 if skewed else 0)   # the skewed case takes the balanced split
 
 
 # ----------------------------------------------------------------------------- full size
