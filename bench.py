@@ -130,12 +130,13 @@ def cpu_baseline(wl, inp, budget_s):
                       f"{cores} host cores visible)"}
 
 
-def timed(obj, step, steps, warmup):
+def timed(obj, step, steps, warmup, per_step=None):
     """Run `warmup` untimed steps, then time exactly `steps` steps between two
     events on the stream the kernels run on (torch's current stream), with a
     synchronisation on both sides. obj.hook records one event after each
     stage, so stage times come from the same run. Returns (ms per step,
-    {stage: mean ms}, wall seconds of the timed region)."""
+    {stage: mean ms}, wall seconds of the timed region); each step's own ms
+    is appended to `per_step` when a list is given."""
     import torch
     for _ in range(warmup):
         step()
@@ -166,7 +167,28 @@ def timed(obj, step, steps, warmup):
         if b == "_step":
             continue
         stage_ms.setdefault(b, []).append(ea.elapsed_time(eb))
+    if per_step is not None:
+        bounds = [ev for n, ev in marks if n == "_step"] + [end]
+        per_step.extend(a.elapsed_time(b) for a, b in zip(bounds[:-1], bounds[1:]))
     return (start.elapsed_time(end) / steps, {n: sum(v) / len(v) for n, v in stage_ms.items()}, wall)
+
+
+def step_stats(ms):
+    """Median, 90th percentile and extremes of the timed steps' own durations."""
+    import numpy as np
+    a = np.asarray(ms, dtype=float)
+    return {"median": round(float(np.median(a)), 4), "p90": round(float(np.percentile(a, 90)), 4),
+            "min": round(float(a.min()), 4), "max": round(float(a.max()), 4), "n": int(a.size)}
+
+
+MALL_BYTES = 256 << 20    # MI355X Infinity Cache (last-level cache in front of HBM)
+
+
+def weight_residency(wl):
+    """Whether the layer's weights (expert and router) could sit in the MALL
+    between steps; at E = 128 they cannot, so every step streams them from HBM."""
+    w = 3 * wl.E * wl.d * wl.F * 2 + (wl.d * wl.E * 2 if wl.routing == "learned" else 0)
+    return {"weight_bytes": w, "mall_bytes": MALL_BYTES, "weights_fit_mall": w <= MALL_BYTES}
 
 
 def upload_inputs(inp):
@@ -450,7 +472,8 @@ def main():
                       topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
         layer.backward(t["dy"])
 
-    ms, stage_avg, wall = timed(layer, step, args.steps, args.warmup)
+    step_ms = []
+    ms, stage_avg, wall = timed(layer, step, args.steps, args.warmup, per_step=step_ms)
     n_rows = layer.n_rows
     R = wl.T * wl.k
     gemm_ms = sum(v for n, v in stage_avg.items() if n.startswith("gg_"))
@@ -500,6 +523,8 @@ def main():
         "stages": stages,
         "expert_load": {"min": int(counts.min()), "max": int(counts.max()),
                         "mean": float(counts.mean()), "dropped": int(layer.n_dropped.cpu()[0])},
+        "step_ms": step_stats(step_ms),
+        "memory": weight_residency(wl),
         "wall_s_timed": round(wall, 3),
         "kernel_sources": kernel_source_hash(),
     }

@@ -4,6 +4,7 @@ under profiles/.
     python profile_summary.py kernels  OUT.md KT_DIR  [--command CMD] [--skip N]
     python profile_summary.py traffic  OUT.md FETCH_CSV WRITE_CSV CAL_FETCH_CSV CAL_WRITE_CSV
                                        [--workload NAME] [--command CMD ...]
+    python profile_summary.py syncs    OUT.md TRACE_DIR [--command CMD]
 
 `kernels` summarises a `--kernel-trace --stats` run (the *_kernel_stats.csv
 file in KT_DIR). `traffic` takes one `--pmc FETCH_SIZE` and one
@@ -14,6 +15,12 @@ writes per-stage HBM bytes per launch: each counter is scaled by
 ends with a JSON block that bench.py reads for `roofline.traffic`; each entry
 carries the hash of the kernel sources it was measured on, so a later kernel
 change turns the figure back into null.
+
+`syncs` reads a `--kernel-trace --memory-copy-trace --hip-runtime-trace` run
+and checks each layer step, from the host call that launches its first
+kernel to the one that launches its last, for HIP calls that block the host,
+copy memory or allocate, and the GPU span of each step for device-to-host
+copies.
 """
 from __future__ import annotations
 
@@ -44,7 +51,7 @@ TRAFFIC_BEGIN = "<!-- traffic-json -->"
 
 def stage_of(kernel):
     """Pipeline stage a kernel belongs to, or None for library kernels."""
-    m = re.search(r"moe::gg_mx_kernel<(\d+),", kernel)
+    m = re.search(r"moe::gg_mx(?:_wgrad_split)?_kernel<(\d+),", kernel)
     if m:
         return "mx" + GG_OPS[int(m.group(1))][2:]
     m = re.search(r"moe::gg_\w+_kernel<(\d+),", kernel)
@@ -181,6 +188,72 @@ def read_traffic_table(path):
     return json.loads(body)
 
 
+# HIP runtime calls that block the host, copy memory or allocate
+HOST_BLOCKING = re.compile(r"^hip(DeviceSynchronize|StreamSynchronize|EventSynchronize|StreamWaitEvent|"
+                           r"Memcpy\w*|Memset\w*|Malloc\w*|Free\w*|HostMalloc|HostRegister|"
+                           r"MallocAsync|ModuleLoad\w*)$")
+
+
+def syncs(args):
+    one = lambda pat: (glob.glob(os.path.join(args.dir, pat)) or [None])[0]
+    kt, api, cp = one("*kernel_trace.csv"), one("*hip_api_trace.csv"), one("*memory_copy_trace.csv")
+    if kt is None or api is None:
+        sys.exit(f"need *kernel_trace.csv and *hip_api_trace.csv under {args.dir}")
+    calls = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Function"], int(r["Correlation_Id"]))
+             for r in csv.DictReader(open(api))]
+    by_corr = {c: (t0, t1) for t0, t1, _, c in calls}
+    kern = []
+    for r in csv.DictReader(open(kt)):
+        st = stage_of(r["Kernel_Name"])
+        if st is None:
+            continue
+        host = by_corr.get(int(r["Correlation_Id"]))
+        kern.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), st, host))
+    kern.sort()
+    # a step starts at its first offsets kernel (after the router when routing is learned)
+    first = "router_gemm" if any(k[2] == "router_gemm" for k in kern) else "offsets"
+    steps, prev = [], None
+    for k in kern:
+        if k[2] == first and prev != first:
+            steps.append([])
+        if steps:
+            steps[-1].append(k)
+        prev = k[2]
+    copies = []
+    if cp is not None:
+        copies = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Direction"])
+                  for r in csv.DictReader(open(cp))]
+    out = ["# Host synchronisation and copies inside the layer step", ""]
+    if args.command:
+        out += ["Command (from the repository root):", "", "```", args.command, "```", ""]
+    out += ["Source: rocprofv3 kernel, memory-copy and HIP runtime traces. For each step: the host "
+            "window from the call that launches the step's first kernel to the call that launches "
+            "its last, the HIP runtime calls made in it, and the device-to-host copies that overlap "
+            "the step's GPU span (its first kernel's start to its last kernel's end).", "",
+            "| step | layer kernels | host window us | GPU span us | HIP calls in the window | "
+            "blocking / copy / alloc calls | D2H copies |",
+            "|---:|---:|---:|---:|---|---:|---:|"]
+    bad_total = 0
+    for i, st in enumerate(steps):
+        hosts = [k[3] for k in st if k[3] is not None]
+        h0, h1 = min(h[0] for h in hosts), max(h[1] for h in hosts)
+        g0, g1 = st[0][0], max(k[1] for k in st)
+        inside = [f for t0, t1, f, _ in calls if t0 >= h0 and t1 <= h1]
+        hist = {}
+        for f in inside:
+            hist[f] = hist.get(f, 0) + 1
+        bad = sum(n for f, n in hist.items() if HOST_BLOCKING.match(f))
+        d2h = sum(1 for c0, c1, dr in copies if "DEVICE_TO_HOST" in dr and c1 >= g0 and c0 <= g1)
+        bad_total += bad + d2h
+        desc = ", ".join(f"{f} {n}" for f, n in sorted(hist.items(), key=lambda x: -x[1]))
+        out.append(f"| {i} | {len(st)} | {(h1 - h0) / 1e3:.1f} | {(g1 - g0) / 1e3:.1f} | {desc} | {bad} | {d2h} |")
+    out += ["", f"Steps: {len(steps)}. Blocking, copying or allocating calls and device-to-host copies "
+            f"inside the steps: {bad_total}."]
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print(args.out)
+    return bad_total
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -198,7 +271,13 @@ def main():
     t.add_argument("--workload", default="e128_uniform_bf16")
     t.add_argument("--copy-mib", type=int, default=1024)
     t.add_argument("--command", action="append")
+    y = sub.add_parser("syncs")
+    y.add_argument("out")
+    y.add_argument("dir")
+    y.add_argument("--command")
     a = ap.parse_args()
+    if a.mode == "syncs":
+        sys.exit(1 if syncs(a) else 0)
     (kernels if a.mode == "kernels" else traffic)(a)
 
 

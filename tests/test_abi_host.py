@@ -235,3 +235,25 @@ def test_mx_quantize_both_argument_errors():
     assert q(FAKE, 100, 128, FAKE, 2, 128 * 3, FAKE, FAKE, None, FAKE) == INVALID    # missing output
     assert q(FAKE, 100, 128, FAKE, 2, 128 * 3, FAKE, FAKE + 1, FAKE, FAKE) == INVALID
     assert q(FAKE, 0, 128, FAKE, 2, 128 * 2, None, None, None, None) == 0
+
+
+def test_library_never_syncs_copies_back_or_allocates():
+    """Group sizes and every other routing result stay on the device: the
+    library's sources call no HIP synchronisation, blocking or host copy,
+    allocation or memset, and the Python layers read no device value back."""
+    import pathlib
+    import re
+    root = pathlib.Path(__file__).resolve().parents[1] / "routing_grouped_expert_router_amd"
+    bad_c = re.compile(r"\bhip(DeviceSynchronize|StreamSynchronize|EventSynchronize|StreamQuery|"
+                       r"Memcpy\w*|Malloc\w*|Free\w*|Memset\w*|HostMalloc|HostRegister)\s*\(")
+    files = [f for f in sorted((root / "csrc").iterdir()) if f.suffix in (".hip", ".h", ".cpp")]
+    assert len(files) >= 5
+    for f in files:
+        m = bad_c.search(f.read_text())
+        assert m is None, (f.name, m and m.group(0))
+    bad_py = re.compile(r"\.(cpu|item|tolist|numpy)\(\)|synchronize\(")
+    for name in ("layer.py", "mx_layer.py", "_lib.py"):
+        for i, line in enumerate((root / name).read_text().splitlines(), 1):
+            code = line.split("#", 1)[0]
+            assert not bad_py.search(code), (name, i, line)
+

@@ -51,6 +51,10 @@ def test_algorithmic_bytes():
     ("void moe::gg_mx_kernel<5, moe::MxCfg<128, 256, 2, 4, 3, 2> >(moe::MxArgs)", "mx_wgrad_gate_up"),
     ("moe::(anonymous namespace)::mx_both_kernel(unsigned short const*, int)", "mx_quantize"),
     ("void moe::permute_bwd_kernel<unsigned short>(unsigned short const*)", "permute_bwd"),
+    ("void moe::gg_mx_wgrad_split_kernel<5, moe::MxCfg<128, 256, 2, 4, 3, 2> >(moe::GGArgs, int, int*)",
+     "mx_wgrad_gate_up"),
+    ("void moe::gg_wgrad_split_kernel<4, moe::DmaCfg<128, 256, 2, 4, 32, 3, 2> >(moe::GGArgs, int, int*)",
+     "gg_wgrad_down"),
 ])
 def test_stage_of_mxfp8_and_adjoints(name, stage):
     from profile_summary import stage_of
@@ -74,3 +78,36 @@ def test_timed_means_leave_out_warmup_launches(tmp_path):
     assert m["k_a"] == pytest.approx(25e-3)
     # k_b has only two launches: all are kept rather than none
     assert m["k_b"] == pytest.approx(20e-3)
+
+
+def test_sync_summary_flags_blocking_calls_inside_steps_only(tmp_path):
+    """The host-synchronisation summary counts a blocking call or a
+    device-to-host copy when it falls inside a layer step, not between steps."""
+    import argparse
+    from profile_summary import syncs
+    hist = "void moe::hist_kernel(int const*)"
+    gemm = "void moe::gg_dma_kernel<5, moe::DmaCfg<128, 256, 2, 4, 32, 3, 2> >(moe::GGArgs)"
+    # (name, correlation id, GPU start, GPU end); host launch calls at 10 * id
+    kern = [(hist, 1, 1000, 1100), (gemm, 2, 1200, 2000), (hist, 5, 3000, 3100), (gemm, 7, 3200, 4000)]
+    api = [("hipLaunchKernel", 1, 10, 11), ("hipLaunchKernel", 2, 20, 21),
+           ("hipDeviceSynchronize", 3, 30, 31),               # between the steps: allowed
+           ("hipLaunchKernel", 5, 50, 51), ("hipStreamSynchronize", 6, 60, 61),   # inside step 1
+           ("hipLaunchKernel", 7, 70, 71)]
+    with open(tmp_path / "t_kernel_trace.csv", "w") as f:
+        f.write("Kernel_Name,Correlation_Id,Start_Timestamp,End_Timestamp\n")
+        for n, c, a, b in kern:
+            f.write(f'"{n}",{c},{a},{b}\n')
+    with open(tmp_path / "t_hip_api_trace.csv", "w") as f:
+        f.write("Function,Correlation_Id,Start_Timestamp,End_Timestamp\n")
+        for n, c, a, b in api:
+            f.write(f"{n},{c},{a},{b}\n")
+    with open(tmp_path / "t_memory_copy_trace.csv", "w") as f:
+        f.write("Direction,Start_Timestamp,End_Timestamp\n")
+        f.write("MEMORY_COPY_DEVICE_TO_HOST,1500,1600\n")       # during step 0's GPU span
+        f.write("MEMORY_COPY_DEVICE_TO_HOST,2500,2600\n")       # between the steps
+    out = tmp_path / "s.md"
+    bad = syncs(argparse.Namespace(out=str(out), dir=str(tmp_path), command=None))
+    assert bad == 2
+    text = out.read_text()
+    assert "| 0 | 2 |" in text and "| 1 | 2 |" in text
+

@@ -307,3 +307,41 @@ def test_shared_expert_layer_full(name, over):
     assert_close(host(lay.dx)[agree], bwd["dx"][agree], "bf16", "dx")
     for n in ("dw_gate", "dw_up", "dw_down"):
         assert_close(host(getattr(lay, n)), bwd[n], "bf16", n)
+
+
+@pytest.mark.parametrize("name,opts", [("e128_uniform_bf16", {}),
+                                       ("e8_learned_bf16", {}),
+                                       ("e128_zipf_bf16", dict(capacity=40)),
+                                       ("e128_uniform_bf16", dict(mxfp8=True)),
+                                       ("e128_uniform_bf16", dict(shared_ff=256, recompute=True))])
+def test_layer_step_never_synchronises(name, opts):
+    """A whole forward+backward step makes no host-synchronising call: run
+    under torch's sync debug mode set to raise, after checking on this build
+    that the mode does raise for a call that synchronises."""
+    wl = workload(name).scaled(T=1024, d=256, F=256, E=min(workload(name).E, 32),
+                               shared_ff=opts.get("shared_ff", 0))
+    inp = make_inputs(wl)
+    t = _upload(inp, "bf16")
+    layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
+                     routing="learned" if wl.routing == "learned" else "given", **opts)
+    shared = {n: t[n] for n in ("w_gate_s", "w_up_s", "w_down_s")} if wl.shared_ff else {}
+    probe = torch.ones(4, device="cuda")
+    torch.cuda.synchronize()
+    torch.cuda.set_sync_debug_mode("error")
+    try:
+        try:
+            probe.sum().item()
+            active = False
+        except RuntimeError:
+            active = True
+        if not active:
+            pytest.skip("torch's sync debug mode does not raise on this build")
+        for _ in range(2):
+            layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
+                          topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"), **shared)
+            layer.backward(t["dy"])
+    finally:
+        torch.cuda.set_sync_debug_mode(0)
+    torch.cuda.synchronize()
+    assert np.isfinite(host(layer.dx)).all()
+
