@@ -5,6 +5,7 @@ under profiles/.
     python profile_summary.py traffic  OUT.md FETCH_CSV WRITE_CSV CAL_FETCH_CSV CAL_WRITE_CSV
                                        [--workload NAME] [--command CMD ...]
     python profile_summary.py syncs    OUT.md TRACE_DIR [--command CMD]
+    python profile_summary.py mfma     OUT.md COUNTER_CSV [--workload NAME] [--command CMD]
 
 `kernels` summarises a `--kernel-trace --stats` run (the *_kernel_stats.csv
 file in KT_DIR). `traffic` takes one `--pmc FETCH_SIZE` and one
@@ -188,6 +189,43 @@ def read_traffic_table(path):
     return json.loads(body)
 
 
+def mfma(args):
+    """Matrix-core busy fraction (rocprofv3's MfmaUtil: MFMA busy cycles over
+    active cycles x SIMDs) and executed bf16 MFMA work (SQ_INSTS_VALU_MFMA_MOPS_BF16
+    x 512 flops) per grouped-GEMM launch, against the algorithmic flops."""
+    from bench import stage_work
+    from moe_inputs import workload
+    wl = workload(args.workload)
+    R = wl.T * wl.k
+    vals = {}
+    for r in csv.DictReader(open(args.csv)):
+        st = stage_of(r["Kernel_Name"])
+        if st is None or not st.startswith("gg_") or "split_kernel" in r["Kernel_Name"]:
+            continue
+        vals.setdefault(st, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = ["# Matrix-core utilisation of the grouped GEMMs: " + wl.name, ""]
+    if args.command:
+        out += ["Command (from the repository root):", "", "```", args.command, "```", ""]
+    out += ["Source: rocprofv3 `--pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16`, means over the run's "
+            "launches. `MfmaUtil` is the fraction of SIMD cycles with the matrix core busy while the GPU "
+            "is active (so it is measured against the clock the box actually ran at); executed GFLOP "
+            "counts every MFMA issued, including the zero rows of partial tiles.", "",
+            "| stage | launches | MfmaUtil % | executed GFLOP | algorithmic GFLOP | executed / algorithmic |",
+            "|---|---:|---:|---:|---:|---:|"]
+    for st in GG_OPS:
+        v = vals.get(st)
+        if not v:
+            continue
+        util = v.get("MfmaUtil", [])
+        mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [])
+        ex = sum(mops) / len(mops) * 512 / 1e9 if mops else float("nan")
+        _, work = stage_work(st, wl, R, R)
+        out.append(f"| {st} | {len(util)} | {sum(util) / max(len(util), 1):.1f} | {ex:.1f} | "
+                   f"{work / 1e9:.1f} | {ex / (work / 1e9):.3f} |")
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print(args.out)
+
+
 # HIP runtime calls that block the host, copy memory or allocate
 HOST_BLOCKING = re.compile(r"^hip(DeviceSynchronize|StreamSynchronize|EventSynchronize|StreamWaitEvent|"
                            r"Memcpy\w*|Memset\w*|Malloc\w*|Free\w*|HostMalloc|HostRegister|"
@@ -275,7 +313,14 @@ def main():
     y.add_argument("out")
     y.add_argument("dir")
     y.add_argument("--command")
+    m = sub.add_parser("mfma")
+    m.add_argument("out")
+    m.add_argument("csv")
+    m.add_argument("--workload", default="e128_uniform_bf16")
+    m.add_argument("--command")
     a = ap.parse_args()
+    if a.mode == "mfma":
+        return mfma(a)
     if a.mode == "syncs":
         sys.exit(1 if syncs(a) else 0)
     (kernels if a.mode == "kernels" else traffic)(a)

@@ -111,3 +111,24 @@ def test_sync_summary_flags_blocking_calls_inside_steps_only(tmp_path):
     text = out.read_text()
     assert "| 0 | 2 |" in text and "| 1 | 2 |" in text
 
+
+def test_mfma_summary(tmp_path):
+    """The matrix-core summary averages MfmaUtil over launches and turns MFMA
+    ops into flops (512 per op) against the stage's algorithmic flops."""
+    import argparse
+    from profile_summary import mfma
+    k = "void moe::gg_dma_kernel<1, moe::DmaCfg<128, 256, 2, 4, 32, 3, 2> >(moe::GGArgs)"
+    split = "void moe::gg_wgrad_split_kernel<4, moe::DmaCfg<128, 256, 2, 4, 32, 3, 2> >(moe::GGArgs, int, int*)"
+    flops = 2 * 16384 * 4 * 2048 * 1024          # forward down projection at the headline size
+    with open(tmp_path / "m.csv", "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for util in (30.0, 50.0):
+            f.write(f'"{k}",MfmaUtil,{util}\n"{k}",SQ_INSTS_VALU_MFMA_MOPS_BF16,{flops * 1.5 / 512}\n')
+        f.write(f'"{split}",MfmaUtil,0.0\n')
+    out = tmp_path / "m.md"
+    mfma(argparse.Namespace(out=str(out), csv=str(tmp_path / "m.csv"), workload="e128_uniform_bf16",
+                            command=None))
+    line = [l for l in out.read_text().splitlines() if l.startswith("| gg_fwd_down")][0]
+    assert line == "| gg_fwd_down | 2 | 40.0 | 412.3 | 274.9 | 1.500 |"
+    assert "gg_wgrad_down" not in out.read_text()
+
