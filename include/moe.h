@@ -136,8 +136,11 @@ int moe_unpermute_combine(int dtype, const void* y_perm, const int32_t* row_of,
 /* moe_unpermute_combine_bwd: adjoint of moe_unpermute_combine.
  *   dy_perm[row_of[t,j]] = w[t,j] * dy[t]   (rounded once to `dtype`)
  *   dtopk_w[t,j] = <dy[t], y_perm[row_of[t,j]]>  (binary32; 0 if dropped)
- * If src_slot is not NULL, pad rows (src_slot == -1) of dy_perm are zeroed;
- * src_slot may be NULL only when n_rows == T*k. */
+ * If src_slot is not NULL, pad rows (src_slot == -1) of dy_perm are zeroed
+ * and the work runs in row order (row r from slot src_slot[r]: dy_perm
+ * written and y_perm read in address order, faster than token order, same
+ * results bit for bit); src_slot must then be the one moe_offsets wrote with
+ * row_of. src_slot may be NULL only when n_rows == T*k. */
 int moe_unpermute_combine_bwd(int dtype, const void* dy, const void* y_perm,
                               const float* topk_w, const int32_t* row_of,
                               const int32_t* src_slot, int T, int k, int d, int n_rows,

@@ -185,6 +185,73 @@ __global__ void __launch_bounds__(kRowThreads) combine_bwd_kernel(
   }
 }
 
+// The same adjoint in row order, for callers that have src_slot: wave r
+// handles routed row r, s = src_slot[r], t = s / k:
+//   dy_perm[r] = w[s] dy[t],  dtopk_w[s] = <dy[t], y_perm[r]>,
+// and writes a zero row for a pad row (s == -1). y_perm is then read and
+// dy_perm written in address order, while the dy rows (T x d, read k times)
+// come mostly from cache: faster than the token-order form, whose k routed
+// rows per token lie anywhere. The workgroups past the row grid give every
+// slot without a row (dropped, or a bad expert id) dtopk_w = 0.
+template <typename T>
+__global__ void __launch_bounds__(kRowThreads) combine_bwd_rows_kernel(
+    const T* __restrict__ dy, const T* __restrict__ y_perm, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ row_of, const int32_t* __restrict__ src_slot, int T_, int k, int d,
+    int n_rows, int row_blocks, T* __restrict__ dy_perm, float* __restrict__ dtopk_w) {
+  constexpr int V = kVec<T>;
+  const size_t slots = (size_t)T_ * k;
+  if ((int)blockIdx.x >= row_blocks) {
+    const size_t s = (size_t)(blockIdx.x - row_blocks) * kRowThreads + threadIdx.x;
+    if (s < slots) {
+      const int r = row_of[s];
+      if (r < 0 || r >= n_rows) dtopk_w[s] = 0.f;
+    }
+    return;
+  }
+  const size_t r = ((size_t)blockIdx.x * kRowThreads + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (r >= (size_t)n_rows) return;
+  const int s = src_slot[r];
+  const int nvec = d / V;
+  V16* dst = reinterpret_cast<V16*>(dy_perm + r * d);
+  if (s < 0 || (size_t)s >= slots) {
+    V16 z;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z.w[i] = 0u;
+    for (int c = lane; c < nvec; c += 64) dst[c] = z;
+    return;
+  }
+  const float w = topk_w[s];
+  const V16* g_row = reinterpret_cast<const V16*>(dy + (size_t)(s / k) * d);
+  const V16* y_row = reinterpret_cast<const V16*>(y_perm + r * d);
+  float dot = 0.f;
+  for (int c0 = lane; c0 < nvec; c0 += 64 * kRowUnroll) {
+    V16 gv[kRowUnroll], yv[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u)
+      if (c0 + 64 * u < nvec) {
+        gv[u] = g_row[c0 + 64 * u];
+        yv[u] = y_row[c0 + 64 * u];
+      }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      if (c0 + 64 * u < nvec) {
+        float g[V], f[V], o[V];
+        unpack(gv[u], g);
+        unpack(yv[u], f);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          dot = fmaf(g[i], f[i], dot);
+          o[i] = w * g[i];
+        }
+        dst[c0 + 64 * u] = pack(o);
+      }
+    }
+  }
+  dot = wave_sum(dot);
+  if (lane == 0) dtopk_w[s] = dot;
+}
+
 // dx[t] = dx_add[t] + sum_j dx_perm[row_of[t, j]] (+ sum_e dlogits[t, e] w_r[:, e]);
 // dx_add and the router term optional
 template <typename T>
@@ -333,9 +400,20 @@ extern "C" int moe_unpermute_combine_bwd(int dtype, const void* dy, const void* 
   MOE_CHECK_ARG(T == 0 || (dy && aligned16(dy) && topk_w && row_of && dtopk_w));
   MOE_CHECK_ARG(n_rows == 0 || (y_perm && dy_perm && aligned16(y_perm) && aligned16(dy_perm)));
   if (src_slot) {
-    const int st = dtype == MOE_BF16 ? zero_pads<uint16_t>(src_slot, n_rows, d, dy_perm, stream)
-                                     : zero_pads<float>(src_slot, n_rows, d, dy_perm, stream);
-    if (st) return st;
+    // row order: one wave per routed row, then one thread per slot
+    const long row_blocks = ((long)n_rows * 64 + kRowThreads - 1) / kRowThreads;
+    const long grid = row_blocks + ((long)T * k + kRowThreads - 1) / kRowThreads;
+    if (grid == 0) return MOE_OK;
+    MOE_CHECK_SUPPORTED(grid < (1L << 31));
+    if (dtype == MOE_BF16)
+      combine_bwd_rows_kernel<uint16_t><<<(int)grid, kRowThreads, 0, stream>>>(
+          static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(y_perm), topk_w, row_of, src_slot, T,
+          k, d, n_rows, (int)row_blocks, static_cast<uint16_t*>(dy_perm), dtopk_w);
+    else
+      combine_bwd_rows_kernel<float><<<(int)grid, kRowThreads, 0, stream>>>(
+          static_cast<const float*>(dy), static_cast<const float*>(y_perm), topk_w, row_of, src_slot, T, k,
+          d, n_rows, (int)row_blocks, static_cast<float*>(dy_perm), dtopk_w);
+    return launch_status();
   }
   if (T == 0) return MOE_OK;
   if (dtype == MOE_BF16)

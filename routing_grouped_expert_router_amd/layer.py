@@ -223,8 +223,8 @@ class MoELayer:
         """Data gradients first (dx is what the layer below, or an expert-
         parallel exchange, waits on, and each data-gradient GEMM reads what
         the one before it just wrote), weight gradients last."""
-        L.moe_unpermute_combine_bwd(dy, self.y_perm, self.topk_w, self.row_of,
-                                    self.src_slot if self.capacity > 0 else None,
+        # with src_slot the adjoint runs in row order (see moe_unpermute_combine_bwd)
+        L.moe_unpermute_combine_bwd(dy, self.y_perm, self.topk_w, self.row_of, self.src_slot,
                                     self.dy_perm, self.dtopk_w)
         self._mark("combine_bwd")
         self.experts_backward_data()

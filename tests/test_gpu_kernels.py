@@ -148,10 +148,20 @@ def test_row_movement_parity(kind, T, d, E, k, C):
     dyt, dy = _to(rng.standard_normal((T, d)), kind)
     dyp = torch.full((n_rows, d), 7.0, dtype=dt, device="cuda")
     dw = torch.empty(T, k, dtype=torch.float32, device="cuda")
-    L.moe_unpermute_combine_bwd(dyt, ypt, dev(wt, "f32"), row_of, src if padded else None, dyp, dw)
     rdyp, rdw = om.combine_bwd(dy, yp, w, meta["row_of"], n_rows, st)
-    assert_close(host(dyp), rdyp, kind, "dy_perm")
-    assert_close(host(dw), rdw, "f32" if kind == "f32" else "bf16", "dtopk_w")
+    # row order (src_slot given), and token order where the ABI allows it:
+    # both against the oracle, and bit for bit against each other
+    got = {}
+    for order, s_arg in [("rows", src)] + ([] if padded else [("tokens", None)]):
+        dyp = torch.full((n_rows, d), 7.0, dtype=dt, device="cuda")
+        dw = torch.full((T, k), 7.0, dtype=torch.float32, device="cuda")
+        L.moe_unpermute_combine_bwd(dyt, ypt, dev(wt, "f32"), row_of, s_arg, dyp, dw)
+        assert_close(host(dyp), rdyp, kind, "dy_perm " + order)
+        assert_close(host(dw), rdw, "f32" if kind == "f32" else "bf16", "dtopk_w " + order)
+        got[order] = (host(dyp), host(dw))
+    if len(got) == 2:
+        assert np.array_equal(got["rows"][0], got["tokens"][0])
+        assert np.array_equal(got["rows"][1], got["tokens"][1])
     # permute backward (with and without the router share)
     dxpt, dxp = _to(rng.standard_normal((n_rows, d)), kind)
     dx = torch.empty(T, d, dtype=dt, device="cuda")
