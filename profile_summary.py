@@ -39,7 +39,8 @@ sys.path.insert(0, ROOT)
 GG_OPS = ["gg_fwd_gate_up", "gg_fwd_down", "gg_dgrad_down", "gg_dgrad_gate_up",
           "gg_wgrad_down", "gg_wgrad_gate_up"]
 ROW_KERNELS = [
-    ("combine_bwd_kernel", "combine_bwd"), ("permute_bwd_kernel", "permute_bwd"),
+    ("combine_bwd_kernel", "combine_bwd"), ("combine_bwd_rows_kernel", "combine_bwd"),
+    ("permute_bwd_kernel", "permute_bwd"),
     ("combine_kernel", "combine"), ("permute_kernel", "permute"),
     ("zero_pad_rows_kernel", "permute"),
     ("hist_kernel", "offsets"), ("scan_kernel", "offsets"), ("rank_kernel", "offsets"),

@@ -51,6 +51,7 @@ def test_algorithmic_bytes():
     ("void moe::gg_mx_kernel<5, moe::MxCfg<128, 256, 2, 4, 3, 2> >(moe::MxArgs)", "mx_wgrad_gate_up"),
     ("moe::(anonymous namespace)::mx_both_kernel(unsigned short const*, int)", "mx_quantize"),
     ("void moe::permute_bwd_kernel<unsigned short>(unsigned short const*)", "permute_bwd"),
+    ("void moe::combine_bwd_rows_kernel<unsigned short>(unsigned short const*)", "combine_bwd"),
     ("void moe::gg_mx_wgrad_split_kernel<5, moe::MxCfg<128, 256, 2, 4, 3, 2> >(moe::GGArgs, int, int*)",
      "mx_wgrad_gate_up"),
     ("void moe::gg_wgrad_split_kernel<4, moe::DmaCfg<128, 256, 2, 4, 32, 3, 2> >(moe::GGArgs, int, int*)",
