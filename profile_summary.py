@@ -209,7 +209,7 @@ def mfma(args):
         out += ["Command (from the repository root):", "", "```", args.command, "```", ""]
     out += ["Source: rocprofv3 `--pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16`, means over the run's "
             "launches. `MfmaUtil` is the fraction of SIMD cycles with the matrix core busy while the GPU "
-            "is active (so it is measured against the clock the box actually ran at); executed GFLOP "
+            "is active (so it is measured against the clock the GPU actually ran at); executed GFLOP "
             "counts every MFMA issued, including the zero rows of partial tiles.", "",
             "| stage | launches | MfmaUtil % | executed GFLOP | algorithmic GFLOP | executed / algorithmic |",
             "|---|---:|---:|---:|---:|---:|"]

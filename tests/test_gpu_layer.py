@@ -316,7 +316,7 @@ def test_shared_expert_layer_full(name, over):
                                        ("e128_uniform_bf16", dict(shared_ff=256, recompute=True))])
 def test_layer_step_never_synchronises(name, opts):
     """A whole forward+backward step makes no host-synchronising call: run
-    under torch's sync debug mode set to raise, after checking on this build
+    under torch's sync debug mode set to raise, after checking with the installed torch
     that the mode does raise for a call that synchronises."""
     wl = workload(name).scaled(T=1024, d=256, F=256, E=min(workload(name).E, 32),
                                shared_ff=opts.get("shared_ff", 0))
@@ -335,7 +335,7 @@ def test_layer_step_never_synchronises(name, opts):
         except RuntimeError:
             active = True
         if not active:
-            pytest.skip("torch's sync debug mode does not raise on this build")
+            pytest.skip("the installed torch's sync debug mode does not raise")
         for _ in range(2):
             layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
                           topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"), **shared)
