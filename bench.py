@@ -127,7 +127,19 @@ def cpu_baseline(wl, inp, budget_s):
     return {"value": Ts / dt, "unit": "tokens/s", "cores": threads or cores, "kind": "oracle",
             "sample": f"first {Ts} of {wl.T} tokens of the workload, all {wl.E} experts and full "
                       f"weights, one float64 forward+backward ({dt:.1f} s wall, "
-                      f"{cores} host cores visible)"}
+                      f"{cores} host cores visible, {cpu_model()})"}
+
+
+def cpu_model():
+    """The host CPU's model name, as the kernel reports it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "CPU model unknown"
 
 
 def timed(obj, step, steps, warmup, per_step=None):
@@ -417,8 +429,8 @@ def experts_leg(steps, warmup):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="e128_uniform_bf16")
     ap.add_argument("--capacity-factor", type=float, default=0.0,
                     help="> 0: run the padded-to-capacity path")
