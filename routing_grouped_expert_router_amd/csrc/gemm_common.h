@@ -177,10 +177,10 @@ MOE_DEV int build_tile_prefix(const GGArgs& a, int* tile_start) {
 // into equal contiguous ranges and each workgroup takes one (xcd_remap). When
 // that split leaves one XCD more than kSkew times the mean work, the XCDs
 // split the work instead: each takes a contiguous range of tiles holding an
-// equal share of it, and its workgroups take consecutive chunks of
-// ceil(range / workgroups) tiles. One workgroup (gg_wgrad_split_kernel)
-// decides this once per launch and writes split[0] = 1 when balancing,
-// split[1 + x] = first tile of XCD x (x = 0..8, split[9] = all tiles).
+// equal share of it, dealt out to its workgroups in turn (wgrad_tiles). One
+// workgroup (gg_wgrad_split_kernel) decides this once per launch and writes
+// split[0] = 1 when balancing, split[1 + x] = first tile of XCD x (x = 0..8,
+// split[9] = all tiles).
 constexpr int kTileFixed = 3;
 constexpr float kSkew = 1.25f;
 constexpr int kXcdCount = 8;
@@ -245,21 +245,25 @@ MOE_DEV void wgrad_split(const GGArgs& a, int tpe, int nb, int* scratch, int* sp
   }
 }
 
-// This workgroup's tiles [t, end) of a weight-gradient launch of nb
-// workgroups (one per tile) under the split (or the equal-count split when
-// it is null). Every tile falls in exactly one workgroup's range.
-MOE_DEV void wgrad_tiles(const int* __restrict__ split, int blk, int nb, int& t, int& end) {
+// This workgroup's tiles t, t + step, ... (< end) of a weight-gradient
+// launch of nb workgroups (one per tile) under the split, or its one tile of
+// the equal-count split when the split is null or not balancing. Within its
+// XCD's range a workgroup takes every wgs-th tile (wgs = the XCD's
+// workgroups): the heaviest tiles of a range then go to different
+// workgroups instead of sitting back to back in one. Every tile falls to
+// exactly one workgroup.
+MOE_DEV void wgrad_tiles(const int* __restrict__ split, int blk, int nb, int& t, int& end, int& step) {
   if (split == nullptr || split[0] == 0) {
     t = xcd_remap(blk, nb);
     end = t + 1;
+    step = 1;
     return;
   }
   const int x = blk % kXcdCount, s = blk / kXcdCount;
   const int t0 = split[1 + x], t1 = split[2 + x];
-  const int wgs = nb / kXcdCount + (x < nb % kXcdCount ? 1 : 0);   // workgroups of this XCD
-  const int c = (t1 - t0 + wgs - 1) / wgs;
-  t = t0 + c * s < t1 ? t0 + c * s : t1;
-  end = t + c < t1 ? t + c : t1;
+  step = nb / kXcdCount + (x < nb % kXcdCount ? 1 : 0);   // workgroups of this XCD
+  t = t0 + s;
+  end = t1;
 }
 
 // m-tile tm -> (expert, first row, rows), from a built prefix.

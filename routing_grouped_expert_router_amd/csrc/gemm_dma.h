@@ -395,11 +395,11 @@ __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_dma_kernel(GGArgs
     const int tpe = (op_wgrad_m(OP, d, F) / BM) * tilesN;
     // The equal-count tile's group rows are fetched together with the split
     // flag, so a launch that does not balance waits on one load, not two.
-    int t = xcd_remap(blockIdx.x, gridDim.x), end = t + 1;
+    int t = xcd_remap(blockIdx.x, gridDim.x), end = t + 1, step = 1;
     int e = t / tpe, row0, K;
     group_rows(a, e, row0, K);
     if (a.split != nullptr && a.split[0] != 0) {
-      wgrad_tiles(a.split, blockIdx.x, gridDim.x, t, end);
+      wgrad_tiles(a.split, blockIdx.x, gridDim.x, t, end, step);
       if (t < end) {
         e = t / tpe;
         group_rows(a, e, row0, K);
@@ -407,7 +407,8 @@ __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_dma_kernel(GGArgs
     }
     while (t < end) {
       run_tile(e, row0, BM, K, ((t % tpe) / tilesN) * BM, t % tilesN);
-      if (++t == end) break;
+      t += step;
+      if (t >= end) break;
       __syncthreads();   // the staging area is read to the end before the next tile's loads land
       e = t / tpe;
       group_rows(a, e, row0, K);

@@ -355,12 +355,12 @@ __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_mx_kernel(MxArgs 
     const int tpe = (op_wgrad_m(OP, d, F) / BM) * tilesN;
     // the equal-count tile's rows and column start are fetched together with
     // the split flag
-    int t = xcd_remap(blockIdx.x, gridDim.x), end = t + 1;
+    int t = xcd_remap(blockIdx.x, gridDim.x), end = t + 1, step = 1;
     int e = t / tpe, row0, K;
     group_rows(a, e, row0, K);
     int p_e = ws[kMxColStart + e];
     if (ws[0] != 0) {
-      wgrad_tiles(ws, blockIdx.x, gridDim.x, t, end);
+      wgrad_tiles(ws, blockIdx.x, gridDim.x, t, end, step);
       if (t < end) {
         e = t / tpe;
         group_rows(a, e, row0, K);
@@ -369,7 +369,8 @@ __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_mx_kernel(MxArgs 
     }
     while (t < end) {
       run_tile(e, row0, BM, K, ((t % tpe) / tilesN) * BM, t % tilesN, p_e);
-      if (++t == end) break;
+      t += step;
+      if (t >= end) break;
       __syncthreads();   // the staging area is read to the end before the next tile's loads land
       e = t / tpe;
       group_rows(a, e, row0, K);
