@@ -78,6 +78,79 @@ __global__ void __launch_bounds__(256) router_gemm_kernel(const T* __restrict__ 
   }
 }
 
+// The same product for bf16 with w_r staged in LDS (E a multiple of 8 and
+// d x E small enough): every wave otherwise re-reads each 8-row group of w_r
+// from L1, 64 separate lines per load instruction, which made w_r rather than
+// x set the rate. Rows are stored in groups of eight with 16 bytes of padding
+// after each group, so the 16 lanes of a read phase, which read the same
+// expert columns of 16 consecutive groups, hit 16 distinct bank quads. The
+// arithmetic and its order are those of router_gemm_kernel.
+__host__ __device__ constexpr int router_lds_group_bytes(int E) { return 8 * E * 2 + 16; }
+
+__global__ void __launch_bounds__(256) router_gemm_lds_kernel(const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ w_r, int T_,
+                                                              int d, int E, float* __restrict__ logits) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t w_lds[];
+  constexpr int V = 8;
+  const int gb = router_lds_group_bytes(E);
+  // stage w_r: 16-byte pieces (8 experts of one row; E % 8 == 0)
+  const int pieces = d * E / 8;
+  for (int j = threadIdx.x; j < pieces; j += blockDim.x) {
+    const int row = j * 8 / E, col = j * 8 % E;
+    *reinterpret_cast<V16*>(w_lds + (row >> 3) * gb + (row & 7) * E * 2 + col * 2) =
+        reinterpret_cast<const V16*>(w_r)[j];
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int nvec = d / V;
+  // each wave takes groups of kRouterTok tokens, grid-strided (one group per
+  // wave at the launch's grid)
+  const int waves = gridDim.x * (blockDim.x >> 6);
+  for (int g = (blockIdx.x * blockDim.x + threadIdx.x) >> 6; g * kRouterTok < T_; g += waves) {
+    const int t0 = g * kRouterTok;
+    for (int e0 = 0; e0 < E; e0 += kRouterEC) {
+      float acc[kRouterTok][kRouterEC];
+#pragma unroll
+      for (int a = 0; a < kRouterTok; ++a)
+#pragma unroll
+        for (int b = 0; b < kRouterEC; ++b) acc[a][b] = 0.f;
+      for (int c = lane; c < nvec; c += 64) {
+        float xv[kRouterTok][V];
+#pragma unroll
+        for (int a = 0; a < kRouterTok; ++a) {
+          if (t0 + a < T_) {
+            V16 v = *reinterpret_cast<const V16*>(x + (size_t)(t0 + a) * d + (size_t)c * V);
+            unpack(v, xv[a]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < V; ++i) xv[a][i] = 0.f;
+          }
+        }
+        const uint8_t* grp = w_lds + c * gb + e0 * 2;   // rows c*8 .. c*8+7
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          float wv[kRouterEC];
+          unpack(*reinterpret_cast<const V16*>(grp + i * E * 2), wv);
+#pragma unroll
+          for (int b = 0; b < kRouterEC; ++b)
+#pragma unroll
+            for (int a = 0; a < kRouterTok; ++a) acc[a][b] = fmaf(xv[a][i], wv[b], acc[a][b]);
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < kRouterTok; ++a)
+#pragma unroll
+        for (int b = 0; b < kRouterEC; ++b) acc[a][b] = wave_sum(acc[a][b]);
+#pragma unroll
+      for (int a = 0; a < kRouterTok; ++a)
+#pragma unroll
+        for (int b = 0; b < kRouterEC; ++b)
+          if (lane == a * kRouterEC + b && t0 + a < T_ && e0 + b < E)
+            logits[(size_t)(t0 + a) * E + e0 + b] = acc[a][b];
+    }
+  }
+}
+
 // ============================================================== top-k gate
 // Order-preserving key of a binary32 value (-0 first mapped to +0), with the
 // expert id in the low word so that equal logits prefer the lower id.
@@ -467,6 +540,13 @@ extern "C" int moe_router_gemm(int dtype, const void* x, const void* w_r, int T,
   const int waves = (T + kRouterTok - 1) / kRouterTok;
   const int blocks = (waves + 3) / 4;
   const bool wide = E % kRouterEC == 0 && aligned16(w_r);
+  // w_r in LDS when it fits in 64 KB with its padding (four workgroups per CU)
+  const long lds_bytes = (long)(d / 8) * router_lds_group_bytes(E);
+  if (dtype == MOE_BF16 && wide && lds_bytes <= 64 * 1024) {
+    router_gemm_lds_kernel<<<blocks, 256, lds_bytes, stream>>>(
+        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_r), T, d, E, logits);
+    return launch_status();
+  }
   if (dtype == MOE_BF16)
     router_gemm_kernel<uint16_t><<<blocks, 256, 0, stream>>>(
         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_r), T, d, E, wide, logits);

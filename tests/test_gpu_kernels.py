@@ -183,7 +183,8 @@ def test_row_movement_parity(kind, T, d, E, k, C):
 # ----------------------------------------------------------------------------- router
 @pytest.mark.parametrize("kind", ["bf16", "f32"])
 @pytest.mark.parametrize("T,d,E,k", [(1000, 256, 8, 2), (129, 2048, 8, 4), (300, 136, 20, 3),
-                                     (64, 512, 128, 4)])
+                                     (64, 512, 128, 4),
+                                     (77, 1024, 16, 4), (500, 512, 32, 4)])   # w_r staged in LDS, E > 8
 def test_router_parity(kind, T, d, E, k):
     rng = _rng(4, T, d, E)
     xt, x = _to(rng.standard_normal((T, d)), kind)
