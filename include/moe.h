@@ -201,8 +201,8 @@ int moe_router_gemm_bwd(int dtype, const void* x, const float* dlogits, int T, i
  * sizes: offsets must be non-decreasing with group_offsets[E] <= n_rows
  * (each group is clamped to [0, n_rows] on the device).
  * ws: at least moe_grouped_gemm_workspace_bytes(desc) bytes, 4-byte aligned,
- * device memory owned by the caller; MOE_ERR_WORKSPACE when missing or too
- * small. The weight gradients over device-resident groups (capacity == 0)
+ * device memory owned by the caller; MOE_ERR_WORKSPACE when missing, too
+ * small or misaligned. The weight gradients over device-resident groups (capacity == 0)
  * need 64 bytes: the call writes there how the launch splits its tiles over
  * the chip, computed on the device from the group sizes (tiles of the experts
  * with the most rows carry the most work); the other ops need none. Calls
@@ -332,8 +332,8 @@ int moe_permute_mx(const void* x, int T, int d, int k, const int32_t* src_slot,
  * F % 256 == 0. Weight gradients of experts with no rows are zeros.
  *
  * ws: at least moe_grouped_gemm_mx_workspace_bytes(desc) bytes, 4-byte
- * aligned, device memory owned by the caller; MOE_ERR_WORKSPACE when missing
- * or too small. The weight gradients need 4 * (E + 16) bytes: the call
+ * aligned, device memory owned by the caller; MOE_ERR_WORKSPACE when missing,
+ * too small or misaligned. The weight gradients need 4 * (E + 16) bytes: the call
  * writes there the tile split of moe_grouped_gemm's weight gradients and each
  * expert's first padded token column; the other ops need none. Calls sharing
  * one workspace must be ordered on one stream. */
