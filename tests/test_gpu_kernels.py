@@ -180,6 +180,69 @@ def test_row_movement_parity(kind, T, d, E, k, C):
                  "dx+router+shared")
 
 
+@pytest.mark.parametrize("C", [0, 40])
+def test_combine_adjoint_with_bad_ids(C):
+    """Slots whose expert id is out of range (and, padded, dropped slots) have
+    no row: the combine adjoint gives them dtopk_w = 0 and writes no row for
+    them, in row order (src_slot given) and, dropless, in token order, the two
+    bit for bit alike."""
+    rng = _rng(9, C)
+    T, E, k, d = 300, 8, 2, 264
+    idx = _draw(rng, T, E, k)
+    idx[::7, 0] = E + 3          # bad ids
+    idx[5::11, 1] = -2
+    n_rows = E * C if C else T * k
+    tt = lambda n: torch.full((max(n, 1),), -7, dtype=torch.int32, device="cuda")
+    counts, offsets, row_of, src_slot = tt(E), tt(E + 1), tt(T * k), tt(n_rows)
+    nd, err = tt(1), torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(L.moe_offsets_workspace_bytes(T, k, E) // 4 + 1, dtype=torch.int32, device="cuda")
+    L.moe_offsets(dev(idx, "i32"), E, C, counts, offsets, row_of, src_slot, nd, err, ws)
+    assert int(host(err)[0]) == 1
+    ro = host(row_of)[:T * k]
+    bad = ((idx < 0) | (idx >= E)).ravel()
+    assert np.all(ro[bad] == -1)
+    dyt, dy = _to(rng.standard_normal((T, d)), "bf16")
+    ypt, yp = _to(rng.standard_normal((max(n_rows, 1), d)), "bf16")
+    wt = rng.dirichlet(np.ones(k), size=T).astype(np.float32)
+    # rows that some slot fills (dropless with bad ids leaves the tail rows
+    # unfilled; only row order, which has src_slot, zeroes them)
+    filled = np.zeros(n_rows, bool)
+    filled[ro[ro >= 0]] = True
+    rdyp, rdw = om.combine_bwd(dy, yp[:n_rows], wt.astype(np.float64), ro, n_rows, storer("bf16"))
+    got = {}
+    for order, s_arg in [("rows", src_slot)] + ([] if C else [("tokens", None)]):
+        dyp = torch.full((max(n_rows, 1), d), 7.0, dtype=torch.bfloat16, device="cuda")
+        dw = torch.full((T, k), 7.0, dtype=torch.float32, device="cuda")
+        L.moe_unpermute_combine_bwd(dyt, ypt, dev(wt, "f32"), row_of, s_arg, dyp, dw)
+        got[order] = (host(dyp)[:n_rows][filled], host(dw).ravel())
+        assert np.all(got[order][1][ro < 0] == 0), order
+        if order == "rows":
+            assert np.all(host(dyp)[:n_rows][~filled] == 0)
+        assert_close(got[order][0], rdyp[filled], "bf16", "dy_perm " + order)
+        assert_close(got[order][1].reshape(T, k), rdw, "bf16", "dtopk_w " + order)
+    if len(got) == 2:
+        assert np.array_equal(got["rows"][0], got["tokens"][0])
+        assert np.array_equal(got["rows"][1], got["tokens"][1])
+
+
+def test_router_gemm_lds_and_cache_paths_agree():
+    """The bf16 router GEMM with w_r staged in LDS and the one that reads w_r
+    through the cache (taken when w_r is not 16-byte aligned) compute the same
+    sums in the same order: identical logits."""
+    rng = _rng(8)
+    T, d, E = 333, 1024, 16
+    xt, _ = _to(rng.standard_normal((T, d)), "bf16")
+    wr = _to(rng.standard_normal((d, E)) / np.sqrt(d), "bf16")[0]
+    buf = torch.empty(d * E + 8, dtype=torch.bfloat16, device="cuda")
+    shifted = buf[1:1 + d * E].view(d, E)        # 2-byte offset: not 16-byte aligned
+    shifted.copy_(wr)
+    a = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    b = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    L.moe_router_gemm(xt, wr, a)
+    L.moe_router_gemm(xt, shifted, b)
+    assert np.array_equal(host(a), host(b))
+
+
 # ----------------------------------------------------------------------------- router
 @pytest.mark.parametrize("kind", ["bf16", "f32"])
 @pytest.mark.parametrize("T,d,E,k", [(1000, 256, 8, 2), (129, 2048, 8, 4), (300, 136, 20, 3),
