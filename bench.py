@@ -239,15 +239,20 @@ def workload_leg(name, capacity_factor, steps, warmup):
 
     ms, st, _ = timed(layer, step, steps, warmup)
     gemm_ms = sum(v for n, v in st.items() if n.startswith("gg_"))
-    flops = 18.0 * layer.n_rows * wl.d * wl.F
     counts = layer.counts.cpu().numpy()
+    dropped = int(layer.n_dropped.cpu()[0])
+    # executed: every row the GEMMs run, pad rows of the padded layout
+    # included; useful: only the routed rows that were kept
+    executed = 18.0 * layer.n_rows * wl.d * wl.F
+    useful = 18.0 * (wl.T * wl.k - dropped) * wl.d * wl.F
     out = {"workload": name, "experts": wl.E, "routing": wl.routing, "capacity": cap,
            "rows": int(layer.n_rows), "tokens_per_s": round(wl.T / (ms / 1e3), 1),
            "ms_per_step": round(ms, 4),
-           "grouped_gemm_tflops": round(flops / (gemm_ms / 1e3) / 1e12, 1),
+           "grouped_gemm_tflops": round(useful / (gemm_ms / 1e3) / 1e12, 1),
+           "grouped_gemm_tflops_executed": round(executed / (gemm_ms / 1e3) / 1e12, 1),
            "expert_load": {"min": int(counts.min()), "max": int(counts.max()),
                            "empty_experts": int((counts == 0).sum())},
-           "dropped": int(layer.n_dropped.cpu()[0])}
+           "dropped": dropped}
     del layer, t
     torch.cuda.empty_cache()
     return out
@@ -319,10 +324,50 @@ def shared_leg(wl, t, cap, steps, warmup, ms_base):
             "step_time_added": round(ms / ms_base - 1.0, 4)}
 
 
-def recompute_leg(wl, t, cap, steps, warmup, ms_base, base_layer):
-    """The same workload with per-layer recompute (the backward recomputes G,
-    U and H from x_perm): step time, the throughput given up, and the expert
-    activations no longer kept from the forward for the backward."""
+def memory_probe(wl, t, cap, recompute, n_layers=4):
+    """Device memory of the layer under torch's allocator, measured: a stack
+    of n_layers independent layers (same weights and inputs) runs every
+    forward, then every backward in reverse, as a model does, each layer
+    releasing its step's activations and scratch when its backward returns
+    (keep_intermediates=False). One warm-up step first allocates the
+    gradients (they stay, like parameter gradients). Returns the bytes each
+    forward leaves allocated for its backward and the peak of the stack above
+    the memory held before the forwards (weights, inputs, gradients)."""
+    import torch
+    from routing_grouped_expert_router_amd.layer import MoELayer
+    layers = [MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
+                       routing="learned" if wl.routing == "learned" else "given", capacity=cap,
+                       recompute=recompute, keep_intermediates=False) for _ in range(n_layers)]
+    fwd = lambda lay: lay.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
+                                  topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
+    for lay in layers:   # warm-up step: gradients allocated
+        fwd(lay)
+        lay.backward(t["dy"])
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    held = []
+    for lay in layers:
+        before = torch.cuda.memory_allocated()
+        fwd(lay)
+        held.append(torch.cuda.memory_allocated() - before)
+    for lay in reversed(layers):
+        lay.backward(t["dy"])
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated()
+    out = {"held_per_layer_bytes": int(held[-1]), "stack_layers": n_layers,
+           "stack_peak_above_resident_bytes": int(peak - base), "stack_peak_bytes": int(peak),
+           "resident_bytes": int(base)}
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
+def recompute_leg(wl, t, cap, steps, warmup, ms_base):
+    """The same workload with per-layer recompute (the forward writes H
+    alone, the backward recomputes G, U and H from x_perm): step time, the
+    throughput given up, and the device memory measured under torch's
+    allocator with and without recompute (memory_probe)."""
     import torch
     from routing_grouped_expert_router_amd.layer import MoELayer
     layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
@@ -334,16 +379,17 @@ def recompute_leg(wl, t, cap, steps, warmup, ms_base, base_layer):
         layer.backward(t["dy"])
 
     ms, _, _ = timed(layer, step, steps, warmup)
-    el = base_layer.x_perm.element_size()
-    kept_base = (base_layer.x_perm.numel() + base_layer.y_perm.numel()) * el \
-        + base_layer.activation_bytes_between_passes()
-    saved = base_layer.activation_bytes_between_passes() - layer.activation_bytes_between_passes()
     del layer
     torch.cuda.empty_cache()
+    stored = memory_probe(wl, t, cap, recompute=False)
+    recomp = memory_probe(wl, t, cap, recompute=True)
     return {"tokens_per_s": round(wl.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
             "throughput_cost": round(1.0 - ms_base / ms, 4),
-            "expert_activation_bytes_saved": int(saved),
-            "fraction_of_kept_activations_saved": round(saved / kept_base, 4)}
+            "memory_stored": stored, "memory_recompute": recomp,
+            "activation_memory_saved": round(1.0 - recomp["held_per_layer_bytes"] / stored["held_per_layer_bytes"], 4),
+            "stack_peak_above_resident_saved": round(
+                1.0 - recomp["stack_peak_above_resident_bytes"] / stored["stack_peak_above_resident_bytes"], 4),
+            "stack_peak_saved": round(1.0 - recomp["stack_peak_bytes"] / stored["stack_peak_bytes"], 4)}
 
 
 def experts_leg(steps, warmup):
@@ -390,6 +436,8 @@ def experts_leg(steps, warmup):
     torch.cuda.empty_cache()
 
     bf = MoELayer(n, d, E, 1, F, torch.bfloat16, routing="given")
+    bf.forward_buffers()
+    bf.backward_buffers()
     bf.x_perm, bf.offsets, bf.dy_perm = x, off, dy
     bf.w_gate, bf.w_up, bf.w_down = wg, wu, wd
 
@@ -489,7 +537,9 @@ def main():
     n_rows = layer.n_rows
     R = wl.T * wl.k
     gemm_ms = sum(v for n, v in stage_avg.items() if n.startswith("gg_"))
-    gemm_flops = 18 * n_rows * wl.d * wl.F
+    dropped = int(layer.n_dropped.cpu()[0])
+    gemm_flops = 18 * (R - dropped) * wl.d * wl.F        # useful: the kept routed rows
+    gemm_flops_executed = 18 * n_rows * wl.d * wl.F      # every row run, pad rows included
     dom = max(stage_avg, key=stage_avg.get)
     kind, work = stage_work(dom, wl, n_rows, R)
     dur_s = stage_avg[dom] / 1e3
@@ -531,10 +581,11 @@ def main():
         "roofline": roof,
         "grouped_gemm": {"tflops": round(gemm_flops / (gemm_ms / 1e3) / 1e12, 1),
                          "frac_mfma_peak": round(gemm_flops / (gemm_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "tflops_executed": round(gemm_flops_executed / (gemm_ms / 1e3) / 1e12, 1),
                          "ms": round(gemm_ms, 4)},
         "stages": stages,
         "expert_load": {"min": int(counts.min()), "max": int(counts.max()),
-                        "mean": float(counts.mean()), "dropped": int(layer.n_dropped.cpu()[0])},
+                        "mean": float(counts.mean()), "dropped": dropped},
         "step_ms": step_stats(step_ms),
         "memory": weight_residency(wl),
         "wall_s_timed": round(wall, 3),
@@ -542,7 +593,7 @@ def main():
     }
     if not args.no_recompute:
         log("recompute leg ...")
-        out["recompute"] = recompute_leg(wl, t, cap, args.steps, args.warmup, ms, layer)
+        out["recompute"] = recompute_leg(wl, t, cap, args.steps, args.warmup, ms)
     if not args.no_shared:
         log("shared-expert leg ...")
         out["shared_expert"] = shared_leg(wl, t, cap, args.steps, args.warmup, ms)

@@ -186,7 +186,12 @@ int moe_router_gemm_bwd(int dtype, const void* x, const float* dlogits, int T, i
  *
  *   op                     reads                        writes
  *   MOE_GG_FWD_GATE_UP     x_perm, w_gate, w_up         g, u, h    (h from the
- *                                                       rounded g and u)
+ *                                                       rounded g and u; g and
+ *                                                       u may both be NULL:
+ *                                                       then only h is written,
+ *                                                       the forward of a layer
+ *                                                       that recomputes g and u
+ *                                                       in its backward)
  *   MOE_GG_FWD_DOWN        h, w_down                    y_perm
  *   MOE_GG_DGRAD_DOWN      dy_perm, w_down, g, u        dg, du:  dH = dY Wd^T,
  *                          s = sigmoid(g), dg = dH*u*s*(1+g*(1-s)), du = dH*g*s
@@ -197,7 +202,11 @@ int moe_router_gemm_bwd(int dtype, const void* x, const float* dlogits, int T, i
  * Shapes: x_perm, y_perm, dy_perm, dx_perm [n_rows,d]; g, u, h, dg, du
  * [n_rows,F]; w_gate, w_up, dw_gate, dw_up [E,d,F]; w_down, dw_down [E,F,d].
  * Weight gradients of experts with no rows are written as zeros. Rows outside
- * every group are neither read nor written. The host cannot see the group
+ * every group are neither read nor written. The bf16 matrix-core path (d and
+ * F multiples of 256) addresses each operand with 32-bit byte offsets:
+ * n_rows * max(d, F) * 2 and d * F * 2 must stay below 2^31, otherwise the
+ * call returns MOE_ERR_UNSUPPORTED (binary32 and other shapes run a plain
+ * FMA kernel without this limit). The host cannot see the group
  * sizes: offsets must be non-decreasing with group_offsets[E] <= n_rows
  * (each group is clamped to [0, n_rows] on the device).
  * ws: at least moe_grouped_gemm_workspace_bytes(desc) bytes, 4-byte aligned,

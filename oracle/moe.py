@@ -376,9 +376,10 @@ def _mx_rows(a):
     return mx_roundtrip(a)
 
 
-def mx_expert_layer(x_perm, dy_perm, counts, w_gate, w_up, w_down) -> Dict[str, np.ndarray]:
-    """Forward and backward of the experts on pre-grouped rows with every GEMM
-    operand MXFP8-quantised along that GEMM's contraction axis, bf16 outputs.
+def mx_expert(X, dY, w_gate, w_up, w_down) -> Dict[str, np.ndarray]:
+    """Forward and backward of one expert on its rows X [n,d] (output
+    gradient rows dY [n,d]) with every GEMM operand MXFP8-quantised along
+    that GEMM's contraction axis, bf16 outputs.
 
     The pages credit MXFP8 mostly to the feed-forward GEMMs and to moving data
     between experts (unite.ai/hi, "पैरालेलिज़्म, प्रिसीजन, और मेमोरी तकनीकें").
@@ -391,6 +392,27 @@ def mx_expert_layer(x_perm, dy_perm, counts, w_gate, w_up, w_down) -> Dict[str, 
                    starting at the expert's first row, the last one zero-padded
     SwiGLU, its derivative and the rounding points are those of the bf16 layer."""
     st = storer("bf16")
+    Xq = _mx_rows(X)
+    G = st(Xq @ _mx_rows(w_gate.T).T)
+    U = st(Xq @ _mx_rows(w_up.T).T)
+    H = st(silu(G) * U)
+    Y = st(_mx_rows(H) @ _mx_rows(w_down.T).T)
+    dH = _mx_rows(dY) @ _mx_rows(w_down).T
+    s = 1.0 / (1.0 + np.exp(-G))
+    dG = st(dH * U * s * (1.0 + G * (1.0 - s)))
+    dU = st(dH * G * s)
+    dX = st(_mx_rows(dG) @ _mx_rows(w_gate).T + _mx_rows(dU) @ _mx_rows(w_up).T)
+    dWd = st(_mx_rows(H.T) @ _mx_rows(dY.T).T)
+    Xt = _mx_rows(X.T)
+    dWg = st(Xt @ _mx_rows(dG.T).T)
+    dWu = st(Xt @ _mx_rows(dU.T).T)
+    return dict(G=G, U=U, H=H, y_perm=Y, dG=dG, dU=dU, dx_perm=dX, dw_gate=dWg, dw_up=dWu, dw_down=dWd)
+
+
+def mx_expert_layer(x_perm, dy_perm, counts, w_gate, w_up, w_down, map_fn=map) -> Dict[str, np.ndarray]:
+    """``mx_expert`` for every expert on its block of the pre-grouped rows
+    (experts are independent; ``map_fn`` evaluates them, e.g. a thread
+    pool's map). Experts with no rows keep zero weight gradients."""
     E, d, F = w_gate.shape
     n = x_perm.shape[0]
     off = np.zeros(E + 1, dtype=np.int64)
@@ -398,34 +420,21 @@ def mx_expert_layer(x_perm, dy_perm, counts, w_gate, w_up, w_down) -> Dict[str, 
     G, U, H = np.zeros((n, F)), np.zeros((n, F)), np.zeros((n, F))
     Y, dG, dU, dX = np.zeros((n, d)), np.zeros((n, F)), np.zeros((n, F)), np.zeros((n, d))
     dWg, dWu, dWd = np.zeros((E, d, F)), np.zeros((E, d, F)), np.zeros((E, F, d))
-    for e in range(E):
+    live = [e for e in range(E) if off[e + 1] > off[e]]
+    run = lambda e: mx_expert(x_perm[off[e]:off[e + 1]], dy_perm[off[e]:off[e + 1]], w_gate[e], w_up[e],
+                              w_down[e])
+    for e, r in zip(live, map_fn(run, live)):
         r0, r1 = int(off[e]), int(off[e + 1])
-        if r1 == r0:
-            continue
-        X, dY = x_perm[r0:r1], dy_perm[r0:r1]
-        Xq = _mx_rows(X)
-        G[r0:r1] = st(Xq @ _mx_rows(w_gate[e].T).T)
-        U[r0:r1] = st(Xq @ _mx_rows(w_up[e].T).T)
-        H[r0:r1] = st(silu(G[r0:r1]) * U[r0:r1])
-        Y[r0:r1] = st(_mx_rows(H[r0:r1]) @ _mx_rows(w_down[e].T).T)
-        dH = _mx_rows(dY) @ _mx_rows(w_down[e]).T
-        g, u = G[r0:r1], U[r0:r1]
-        s = 1.0 / (1.0 + np.exp(-g))
-        dG[r0:r1] = st(dH * u * s * (1.0 + g * (1.0 - s)))
-        dU[r0:r1] = st(dH * g * s)
-        dX[r0:r1] = st(_mx_rows(dG[r0:r1]) @ _mx_rows(w_gate[e]).T
-                       + _mx_rows(dU[r0:r1]) @ _mx_rows(w_up[e]).T)
-        dWd[e] = st(_mx_rows(H[r0:r1].T) @ _mx_rows(dY.T).T)
-        Xt = _mx_rows(X.T)
-        dWg[e] = st(Xt @ _mx_rows(dG[r0:r1].T).T)
-        dWu[e] = st(Xt @ _mx_rows(dU[r0:r1].T).T)
+        for name, a in (("G", G), ("U", U), ("H", H), ("y_perm", Y), ("dG", dG), ("dU", dU), ("dx_perm", dX)):
+            a[r0:r1] = r[name]
+        dWg[e], dWu[e], dWd[e] = r["dw_gate"], r["dw_up"], r["dw_down"]
     return dict(G=G, U=U, H=H, y_perm=Y, dG=dG, dU=dU, dx_perm=dX,
                 dw_gate=dWg, dw_up=dWu, dw_down=dWd)
 
 
 # ----------------------------------------------------------------------------- MXFP8 routed layer
 def mx_layer(p: Dict[str, np.ndarray], k: int, dy: np.ndarray,
-             logits: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+             logits: Optional[np.ndarray] = None, map_fn=map) -> Dict[str, np.ndarray]:
     """Forward and backward of the whole routed layer with every expert GEMM
     in MXFP8 (``mx_expert_layer`` on the permuted rows) and everything else as
     in the bf16 layer: routing, offsets, permute, combine and their adjoints,
@@ -451,7 +460,7 @@ def mx_layer(p: Dict[str, np.ndarray], k: int, dy: np.ndarray,
     ro = meta["row_of"].reshape(T, k)
     for j in range(k):
         dyp[ro[:, j]] = st(w[:, j:j + 1] * dy)
-    ex = mx_expert_layer(xp, dyp, meta["counts"], p["w_gate"], p["w_up"], p["w_down"])
+    ex = mx_expert_layer(xp, dyp, meta["counts"], p["w_gate"], p["w_up"], p["w_down"], map_fn)
     out.update(x_perm=xp, dy_perm=dyp, **ex)
     out["y"] = combine(ex["y_perm"], meta["row_of"], w, T, k, st)
     _, out["dtopk_w"] = combine_bwd(dy, ex["y_perm"], w, meta["row_of"], meta["n_rows"], st, r32)

@@ -44,9 +44,9 @@ ROW_KERNELS = [
     ("combine_kernel", "combine"), ("permute_kernel", "permute"),
     ("zero_pad_rows_kernel", "permute"),
     ("hist_kernel", "offsets"), ("scan_kernel", "offsets"), ("rank_kernel", "offsets"),
-    ("router_gemm_kernel", "router_gemm"), ("route_bwd_kernel", "route_bwd"),
-    ("route_kernel", "route"), ("router_bwd_partial", "router_gemm_bwd"),
-    ("router_bwd_reduce", "router_gemm_bwd"),
+    ("router_gemm_kernel", "router_gemm"), ("router_gemm_lds_kernel", "router_gemm"),
+    ("route_bwd_kernel", "route_bwd"), ("route_kernel", "route"),
+    ("router_bwd_partial_kernel", "router_gemm_bwd"), ("router_bwd_reduce_kernel", "router_gemm_bwd"),
 ]
 TRAFFIC_BEGIN = "<!-- traffic-json -->"
 

@@ -104,12 +104,36 @@ def _check(status: int, name: str):
         raise MoEError(f"{name} failed: {msg} ({status})")
 
 
+class _HostTensor:
+    """Stands in for the address of a tensor that is not in device memory; a
+    call that receives one raises before reaching the library (after every
+    argument's layout has been checked)."""
+
+
+_HOST = _HostTensor()
+
+
 def _p(t: Optional[torch.Tensor]):
+    """Device address of a tensor (None -> NULL); the tensor must be a
+    contiguous device tensor, since the library reads dense row-major memory."""
     if t is None:
         return None
+    if not t.is_contiguous():
+        raise MoEError("libmoe needs contiguous tensors")
     if not t.is_cuda:
-        raise MoEError("libmoe needs device tensors")
+        return _HOST
     return t.data_ptr()
+
+
+def _call(name: str, *args):
+    """Call entry point `name` with marshalled arguments, raising MoEError for
+    host tensors or a non-zero status."""
+    if any(a is _HOST for a in args):
+        raise MoEError(f"{name}: libmoe needs device tensors")
+    _check(getattr(lib(), name)(*args), name)
+
+
+_FLOATS = (torch.bfloat16, torch.float32)
 
 
 def _dt(t: torch.Tensor) -> int:
@@ -120,9 +144,48 @@ def _dt(t: torch.Tensor) -> int:
     raise MoEError(f"unsupported dtype {t.dtype}")
 
 
+def _req(t: Optional[torch.Tensor], name: str, dtype, shape=None, optional: bool = False):
+    """Check one tensor argument before its address goes to the library:
+    dtype (one torch dtype or a tuple), contiguity, shape (-1 = any extent,
+    an int = element count) and device. Returns the address (None for an
+    absent optional tensor). Raises MoEError on any mismatch, because the
+    library would otherwise read the memory as if it had the declared layout."""
+    if t is None:
+        if optional:
+            return None
+        raise MoEError(f"{name} is required")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise MoEError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dts)}")
+    if not t.is_contiguous():
+        raise MoEError(f"{name}: must be contiguous (dense row-major)")
+    if isinstance(shape, int):
+        if t.numel() != shape:
+            raise MoEError(f"{name}: {t.numel()} elements, expected {shape}")
+    elif shape is not None:
+        if t.dim() != len(shape) or any(w >= 0 and w != v for w, v in zip(shape, t.shape)):
+            raise MoEError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)} (-1 = any)")
+    return _p(t)
+
+
+def _nbytes(ws: torch.Tensor) -> int:
+    return ws.numel() * ws.element_size()
+
+
 def _stream(stream=None):
+    if stream is None and not torch.cuda.is_available():
+        return None   # no device: the call raises on its (host) tensors first
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def _fill(desc, fields):
+    """Set descriptor pointer fields once every tensor has passed its layout
+    check; raise if any of them is in host memory."""
+    if any(v is _HOST for _, v in fields):
+        raise MoEError("libmoe needs device tensors")
+    for obj, name, v in ((o, n, v) for (o, n), v in fields):
+        setattr(obj, name, v)
 
 
 def moe_status_string(status: int) -> str:
@@ -136,14 +199,15 @@ def moe_abi_version() -> int:
 def moe_router_gemm(x, w_r, logits, stream=None):
     T, d = x.shape
     E = w_r.shape[1]
-    _check(lib().moe_router_gemm(_dt(x), _p(x), _p(w_r), T, d, E, _p(logits), _stream(stream)),
-           "moe_router_gemm")
+    _call("moe_router_gemm", _dt(x), _req(x, "x", _FLOATS, (T, d)), _req(w_r, "w_r", x.dtype, (d, E)), T, d,
+                                 E, _req(logits, "logits", torch.float32, (T, E)), _stream(stream))
 
 
 def moe_route(logits, k, topk_idx, topk_w, stream=None):
     T, E = logits.shape
-    _check(lib().moe_route(_p(logits), T, E, k, _p(topk_idx), _p(topk_w), _stream(stream)),
-           "moe_route")
+    _call("moe_route", _req(logits, "logits", torch.float32, (T, E)), T, E, k,
+                           _req(topk_idx, "topk_idx", torch.int32, (T, k)),
+                           _req(topk_w, "topk_w", torch.float32, (T, k)), _stream(stream))
 
 
 def moe_offsets_workspace_bytes(T, k, E) -> int:
@@ -153,44 +217,66 @@ def moe_offsets_workspace_bytes(T, k, E) -> int:
 def moe_offsets(topk_idx, E, capacity, counts, offsets, row_of, src_slot, n_dropped, err_flag,
                 ws, stream=None):
     T, k = topk_idx.shape
-    _check(lib().moe_offsets(_p(topk_idx), T, k, E, capacity, _p(counts), _p(offsets), _p(row_of),
-                             _p(src_slot), _p(n_dropped), _p(err_flag), _p(ws),
-                             ws.numel() * ws.element_size(), _stream(stream)), "moe_offsets")
+    n_rows = E * capacity if capacity > 0 else T * k
+    i32 = torch.int32
+    _call("moe_offsets", _req(topk_idx, "topk_idx", i32, (T, k)), T, k, E, capacity,
+                             _req(counts, "counts", i32, E), _req(offsets, "offsets", i32, E + 1),
+                             _req(row_of, "row_of", i32, T * k), _req(src_slot, "src_slot", i32, n_rows),
+                             _req(n_dropped, "n_dropped", i32, 1), _req(err_flag, "err_flag", i32, 1),
+                             _p(ws), _nbytes(ws), _stream(stream))
 
 
 def moe_permute(x, k, row_of, src_slot, x_perm, stream=None):
     T, d = x.shape
-    _check(lib().moe_permute(_dt(x), _p(x), T, d, k, _p(row_of), _p(src_slot), x_perm.shape[0],
-                             _p(x_perm), _stream(stream)), "moe_permute")
+    n = x_perm.shape[0]
+    i32 = torch.int32
+    _call("moe_permute", _dt(x), _req(x, "x", _FLOATS, (T, d)), T, d, k, _req(row_of, "row_of", i32, T * k),
+                             _req(src_slot, "src_slot", i32, n, optional=True), n,
+                             _req(x_perm, "x_perm", x.dtype, (n, d)), _stream(stream))
 
 
 def moe_unpermute_combine(y_perm, row_of, topk_w, y, y_add=None, stream=None):
     T, k = topk_w.shape
-    _check(lib().moe_unpermute_combine(_dt(y), _p(y_perm), _p(row_of), _p(topk_w), T, k, y.shape[1],
-                                       y_perm.shape[0], _p(y_add), _p(y), _stream(stream)),
-           "moe_unpermute_combine")
+    d = y.shape[1]
+    n = y_perm.shape[0]
+    _call("moe_unpermute_combine", _dt(y), _req(y_perm, "y_perm", y.dtype, (n, d)),
+                                       _req(row_of, "row_of", torch.int32, T * k),
+                                       _req(topk_w, "topk_w", torch.float32, (T, k)), T, k, d, n,
+                                       _req(y_add, "y_add", y.dtype, (T, d), optional=True),
+                                       _req(y, "y", _FLOATS, (T, d)), _stream(stream))
 
 
 def moe_unpermute_combine_bwd(dy, y_perm, topk_w, row_of, src_slot, dy_perm, dtopk_w, stream=None):
     T, k = topk_w.shape
-    _check(lib().moe_unpermute_combine_bwd(_dt(dy), _p(dy), _p(y_perm), _p(topk_w), _p(row_of),
-                                           _p(src_slot), T, k, dy.shape[1], y_perm.shape[0],
-                                           _p(dy_perm), _p(dtopk_w), _stream(stream)),
-           "moe_unpermute_combine_bwd")
+    d = dy.shape[1]
+    n = y_perm.shape[0]
+    i32, f32 = torch.int32, torch.float32
+    _call("moe_unpermute_combine_bwd", _dt(dy), _req(dy, "dy", _FLOATS, (T, d)),
+                                           _req(y_perm, "y_perm", dy.dtype, (n, d)),
+                                           _req(topk_w, "topk_w", f32, (T, k)), _req(row_of, "row_of", i32, T * k),
+                                           _req(src_slot, "src_slot", i32, n, optional=True), T, k, d, n,
+                                           _req(dy_perm, "dy_perm", dy.dtype, (n, d)),
+                                           _req(dtopk_w, "dtopk_w", f32, (T, k)), _stream(stream))
 
 
 def moe_permute_bwd(dx_perm, row_of, k, dx, dlogits=None, w_r=None, dx_add=None, stream=None):
     T, d = dx.shape
     E = 0 if w_r is None else w_r.shape[1]
-    _check(lib().moe_permute_bwd(_dt(dx), _p(dx_perm), _p(row_of), T, k, d, dx_perm.shape[0],
-                                 _p(dlogits), _p(w_r), E, _p(dx_add), _p(dx), _stream(stream)),
-           "moe_permute_bwd")
+    n = dx_perm.shape[0]
+    _call("moe_permute_bwd", _dt(dx), _req(dx_perm, "dx_perm", dx.dtype, (n, d)),
+                                 _req(row_of, "row_of", torch.int32, T * k), T, k, d, n,
+                                 _req(dlogits, "dlogits", torch.float32, (T, E), optional=True),
+                                 _req(w_r, "w_r", dx.dtype, (d, E), optional=True), E,
+                                 _req(dx_add, "dx_add", dx.dtype, (T, d), optional=True),
+                                 _req(dx, "dx", _FLOATS, (T, d)), _stream(stream))
 
 
 def moe_route_bwd(topk_idx, topk_w, dtopk_w, E, dlogits, stream=None):
     T, k = topk_idx.shape
-    _check(lib().moe_route_bwd(_p(topk_idx), _p(topk_w), _p(dtopk_w), T, E, k, _p(dlogits),
-                               _stream(stream)), "moe_route_bwd")
+    f32 = torch.float32
+    _call("moe_route_bwd", _req(topk_idx, "topk_idx", torch.int32, (T, k)), _req(topk_w, "topk_w", f32, (T, k)),
+                               _req(dtopk_w, "dtopk_w", f32, (T, k)), T, E, k,
+                               _req(dlogits, "dlogits", f32, (T, E)), _stream(stream))
 
 
 def moe_router_bwd_workspace_bytes(T, d, E) -> int:
@@ -200,9 +286,21 @@ def moe_router_bwd_workspace_bytes(T, d, E) -> int:
 def moe_router_gemm_bwd(x, dlogits, dw_r, ws, stream=None):
     T, d = x.shape
     E = dlogits.shape[1]
-    _check(lib().moe_router_gemm_bwd(_dt(x), _p(x), _p(dlogits), T, d, E, _p(dw_r), _p(ws),
-                                     ws.numel() * ws.element_size(), _stream(stream)),
-           "moe_router_gemm_bwd")
+    _call("moe_router_gemm_bwd", _dt(x), _req(x, "x", _FLOATS, (T, d)),
+                                     _req(dlogits, "dlogits", torch.float32, (T, E)), T, d, E,
+                                     _req(dw_r, "dw_r", x.dtype, (d, E)), _p(ws), _nbytes(ws), _stream(stream))
+
+
+# element count of each grouped-GEMM tensor, from (E, d, F, n_rows)
+_GG_NUMEL = {
+    "x_perm": lambda E, d, F, n: n * d, "y_perm": lambda E, d, F, n: n * d,
+    "dy_perm": lambda E, d, F, n: n * d, "dx_perm": lambda E, d, F, n: n * d,
+    "g": lambda E, d, F, n: n * F, "u": lambda E, d, F, n: n * F, "h": lambda E, d, F, n: n * F,
+    "dg": lambda E, d, F, n: n * F, "du": lambda E, d, F, n: n * F,
+    "w_gate": lambda E, d, F, n: E * d * F, "w_up": lambda E, d, F, n: E * d * F,
+    "w_down": lambda E, d, F, n: E * F * d, "dw_gate": lambda E, d, F, n: E * d * F,
+    "dw_up": lambda E, d, F, n: E * d * F, "dw_down": lambda E, d, F, n: E * F * d,
+}
 
 
 def make_gg_desc(op, dtype, E, d, F, n_rows, capacity=0, group_offsets=None, ws=None,
@@ -210,11 +308,16 @@ def make_gg_desc(op, dtype, E, d, F, n_rows, capacity=0, group_offsets=None, ws=
     desc = moe_gg_desc()
     desc.op, desc.dtype, desc.E, desc.d, desc.F = op, dtype, E, d, F
     desc.n_rows, desc.capacity = n_rows, capacity
-    desc.group_offsets = _p(group_offsets)
+    fields = [((desc, "group_offsets"), _req(group_offsets, "group_offsets", torch.int32, E + 1, optional=True))]
+    tdt = torch.bfloat16 if dtype == MOE_BF16 else torch.float32
     for name, t in tensors.items():
-        setattr(desc, name, _p(t))
+        if name not in _GG_NUMEL:
+            raise MoEError(f"moe_gg_desc has no tensor {name}")
+        fields.append(((desc, name), _req(t, name, tdt, _GG_NUMEL[name](E, d, F, n_rows), optional=True)))
     if ws is not None:
-        desc.ws, desc.ws_bytes = _p(ws), ws.numel() * ws.element_size()
+        fields.append(((desc, "ws"), _p(ws)))
+        desc.ws_bytes = _nbytes(ws)
+    _fill(desc, fields)
     return desc
 
 
@@ -223,7 +326,7 @@ def moe_grouped_gemm_workspace_bytes(desc: moe_gg_desc) -> int:
 
 
 def moe_grouped_gemm(desc: moe_gg_desc, stream=None):
-    _check(lib().moe_grouped_gemm(C.byref(desc), _stream(stream)), "moe_grouped_gemm")
+    _call("moe_grouped_gemm", C.byref(desc), _stream(stream))
 
 
 # ----------------------------------------------------------------- MXFP8
@@ -240,39 +343,50 @@ def moe_mx_col_stride(rows: int, n_groups: int) -> int:
 
 def moe_mx_quantize(src, axis, q, s, group_offsets=None, n_groups=1, col_stride=0, stream=None):
     rows, cols = src.shape
-    _check(lib().moe_mx_quantize(_p(src), rows, cols, axis, _p(group_offsets), n_groups, col_stride,
-                                 _p(q), _p(s), _stream(stream)), "moe_mx_quantize")
+    u8 = torch.uint8
+    _call("moe_mx_quantize", _req(src, "src", torch.bfloat16, (rows, cols)), rows, cols, axis,
+                                 _req(group_offsets, "group_offsets", torch.int32, n_groups + 1, optional=True),
+                                 n_groups, col_stride, _req(q, "q", u8), _req(s, "s", u8), _stream(stream))
 
 
 def moe_mx_quantize_both(src, rows_out: MxTensor, cols_out: MxTensor, group_offsets=None, n_groups=1,
                          col_stride=0, stream=None):
     rows, cols = src.shape
-    _check(lib().moe_mx_quantize_both(_p(src), rows, cols, _p(group_offsets), n_groups, col_stride,
-                                      _p(rows_out.q), _p(rows_out.s), _p(cols_out.q), _p(cols_out.s),
-                                      _stream(stream)), "moe_mx_quantize_both")
+    u8 = torch.uint8
+    _call("moe_mx_quantize_both", _req(src, "src", torch.bfloat16, (rows, cols)), rows, cols,
+                                      _req(group_offsets, "group_offsets", torch.int32, n_groups + 1, optional=True),
+                                      n_groups, col_stride, _req(rows_out.q, "q_rows", u8), _req(rows_out.s, "s_rows", u8),
+                                      _req(cols_out.q, "q_cols", u8), _req(cols_out.s, "s_cols", u8),
+                                      _stream(stream))
 
 
 def moe_permute_mx(x, k, src_slot, group_offsets, E, col_stride, rows_out: MxTensor, cols_out: MxTensor,
                    stream=None):
     T, d = x.shape
     n_rows = src_slot.shape[0]
-    _check(lib().moe_permute_mx(_p(x), T, d, k, _p(src_slot), _p(group_offsets), E, n_rows, col_stride,
-                                _p(rows_out.q), _p(rows_out.s), _p(cols_out.q), _p(cols_out.s),
-                                _stream(stream)), "moe_permute_mx")
+    u8, i32 = torch.uint8, torch.int32
+    _call("moe_permute_mx", _req(x, "x", torch.bfloat16, (T, d)), T, d, k, _req(src_slot, "src_slot", i32, n_rows),
+                                _req(group_offsets, "group_offsets", i32, E + 1), E, n_rows, col_stride,
+                                _req(rows_out.q, "q_rows", u8), _req(rows_out.s, "s_rows", u8),
+                                _req(cols_out.q, "q_cols", u8), _req(cols_out.s, "s_cols", u8),
+                                _stream(stream))
 
 
 def make_mx_gg_desc(op, E, d, F, n_rows, group_offsets, col_stride=0, a0=None, a1=None, b0=None,
                     b1=None, g=None, u=None, out0=None, out1=None, out2=None, ws=None) -> moe_mx_gg_desc:
     desc = moe_mx_gg_desc()
     desc.op, desc.E, desc.d, desc.F, desc.n_rows, desc.col_stride = op, E, d, F, n_rows, col_stride
-    desc.group_offsets = _p(group_offsets)
+    fields = [((desc, "group_offsets"), _req(group_offsets, "group_offsets", torch.int32, E + 1, optional=True))]
     for name, t in (("a0", a0), ("a1", a1), ("b0", b0), ("b1", b1)):
         if t is not None:
-            getattr(desc, name).q, getattr(desc, name).s = _p(t.q), _p(t.s)
+            fields.append(((getattr(desc, name), "q"), _req(t.q, f"{name}.q", torch.uint8)))
+            fields.append(((getattr(desc, name), "s"), _req(t.s, f"{name}.s", torch.uint8)))
     for name, t in (("g", g), ("u", u), ("out0", out0), ("out1", out1), ("out2", out2)):
-        setattr(desc, name, _p(t))
+        fields.append(((desc, name), _req(t, name, torch.bfloat16, optional=True)))
     if ws is not None:
-        desc.ws, desc.ws_bytes = _p(ws), ws.numel() * ws.element_size()
+        fields.append(((desc, "ws"), _p(ws)))
+        desc.ws_bytes = _nbytes(ws)
+    _fill(desc, fields)
     return desc
 
 
@@ -281,4 +395,4 @@ def moe_grouped_gemm_mx_workspace_bytes(desc: moe_mx_gg_desc) -> int:
 
 
 def moe_grouped_gemm_mx(desc: moe_mx_gg_desc, stream=None):
-    _check(lib().moe_grouped_gemm_mx(C.byref(desc), _stream(stream)), "moe_grouped_gemm_mx")
+    _call("moe_grouped_gemm_mx", C.byref(desc), _stream(stream))

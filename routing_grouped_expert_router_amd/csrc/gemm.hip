@@ -3,16 +3,13 @@
 // the device only ("device-scheduled grouped GEMM", deniz.in, "Yeni stack
 // nasıl çalışıyor").
 //
-// gg_mfma_kernel (gemm_mfma.h): bf16 operands, binary32 accumulation on the
-// matrix cores, LDS-staged tiles, an on-device group-tile scheduler.
+// gg_dma_kernel (gemm_dma.h): bf16 operands, binary32 accumulation on the
+// matrix cores, tiles loaded straight from memory into LDS, an on-device
+// group-tile scheduler.
 //
 // gg_simple_kernel: any dtype and shape, binary32 FMA on 64 x 64 tiles; it
 // serves binary32 layers and shapes outside the MFMA kernel's limits.
 #include "gemm_dma.h"
-#include "gemm_mfma.h"
-
-#include <cstdlib>
-#include <string>
 
 namespace moe {
 
@@ -79,8 +76,10 @@ MOE_DEV void simple_store(const GGArgs& a, int e, int row, int n, float c0, floa
       float g, u, h;
       swiglu_fwd<T>(c0, c1, g, u, h);
       const size_t i = (size_t)row * F + n;
-      Elem<T>::store((T*)a.g, i, g);
-      Elem<T>::store((T*)a.u, i, u);
+      if (a.g != nullptr) {   // null g and u: only h is written (recompute)
+        Elem<T>::store((T*)a.g, i, g);
+        Elem<T>::store((T*)a.u, i, u);
+      }
       Elem<T>::store((T*)a.h, i, h);
       break;
     }
@@ -178,32 +177,10 @@ using namespace moe;
 
 namespace {
 
-// Tile shapes: register-staged kernel {BM, BN, WM, WN}; direct-load kernel
-// {BM, BN, WM, WN, BK, STAGES}.
-using Cfg128 = MfmaCfg<128, 256, 2, 2>;   // 4 waves, 64 x 128 each
-using Cfg256 = MfmaCfg<256, 256, 2, 4>;   // 8 waves, 128 x 64 each
-using CfgDma256 = DmaCfg<256, 256, 2, 4, 32, 4>;      // 8 waves, 128 x 64 each, 1 workgroup per CU
-using CfgDma128 = DmaCfg<128, 256, 2, 2, 32, 3, 2>;   // 4 waves, 64 x 128 each, 2 workgroups per CU
-using CfgDma128w8 = DmaCfg<128, 256, 2, 4, 32, 3, 2>;     // 8 waves, 64 x 64 each, 2 workgroups per CU
-
-// Kernel choice. The default is the direct-load kernel on 128 x 256 tiles,
-// eight waves of 64 x 64 and two workgroups per CU (16 waves per CU hide
-// the per-stage load issue, fragment reads and barriers of each other);
-// MOE_GG_TILE overrides it for comparison runs: dma128w8 | dma128 | dma256
-// (direct loads), 128 | 256 (register-staged).
-int tile_choice() {
-  static int t = [] {
-    const char* s = std::getenv("MOE_GG_TILE");
-    if (!s) return 8;
-    const std::string v(s);
-    if (v == "128") return 0;
-    if (v == "256") return 1;
-    if (v == "dma256") return 2;
-    if (v == "dma128") return 3;
-    return 8;
-  }();
-  return t;
-}
+// The direct-load kernel on 128 x 256 tiles, eight waves of 64 x 64 and two
+// workgroups per CU (16 waves per CU hide the per-stage load issue, fragment
+// reads and barriers of each other).
+using CfgDma = DmaCfg<128, 256, 2, 4, 32, 3, 2>;
 
 bool mfma_ok(const moe_gg_desc* g) {
   return g->dtype == MOE_BF16 && g->d % 256 == 0 && g->F % 256 == 0;
@@ -221,14 +198,6 @@ int dispatch_op(int op, const GGArgs& a, int grid, hipStream_t s) {
   }
   return launch_status();
 }
-
-template <class C> struct Mfma {
-  template <int OP> struct Launch {
-    static void go(const GGArgs& a, int grid, hipStream_t s) {
-      gg_mfma_kernel<OP, C><<<grid, C::NT, 0, s>>>(a);
-    }
-  };
-};
 
 template <class C> struct Dma {
   template <int OP> struct Launch {
@@ -261,16 +230,6 @@ int launch_dma(const moe_gg_desc* g, const GGArgs& a, bool kvar, bool dual, int 
   return dispatch_op<Dma<C>::template Launch>(g->op, a, static_cast<int>(grid), stream);
 }
 
-template <class C>
-int launch_mfma(const moe_gg_desc* g, const GGArgs& a, bool kvar, bool dual, int N, hipStream_t stream) {
-  const int bno = dual ? C::BN / 2 : C::BN;
-  long grid;
-  if (kvar) grid = (long)g->E * (op_wgrad_m(g->op, g->d, g->F) / C::BM) * (N / bno);
-  else grid = ((g->n_rows + C::BM - 1) / C::BM + g->E) * (long)(N / bno);
-  if (grid == 0) return MOE_OK;
-  MOE_CHECK_SUPPORTED(grid < (1L << 31));
-  return dispatch_op<Mfma<C>::template Launch>(g->op, a, static_cast<int>(grid), stream);
-}
 template <int OP> struct LaunchSimpleBf16 {
   static void go(const GGArgs& a, int grid, hipStream_t s) {
     gg_simple_kernel<uint16_t, OP><<<grid, 256, 0, s>>>(a);
@@ -285,18 +244,6 @@ template <int OP> struct LaunchSimpleF32 {
 long cdiv(long a, long b) { return (a + b - 1) / b; }
 
 }  // namespace
-
-namespace moe {
-// Row-varying tile order: expert-grouped (1) unless MOE_GG_ORDER=n asks for
-// the n-tiles of one m-tile side by side (0, for tuning sweeps).
-int gg_tile_order() {
-  static const int t = [] {
-    const char* s = std::getenv("MOE_GG_ORDER");
-    return (s && std::string(s) == "n") ? 0 : 1;
-  }();
-  return t;
-}
-}  // namespace moe
 
 // Weight gradients over device-resident groups keep their launch's tile
 // split (kSplitInts ints) in the workspace.
@@ -327,7 +274,9 @@ extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
   auto act = [&](const void* p) { return !rows || (p != nullptr && aligned16(p)); };
   switch (g->op) {
     case MOE_GG_FWD_GATE_UP:
-      MOE_CHECK_ARG(need(g->x_perm) && need(g->w_gate) && need(g->w_up) && need(g->g) && need(g->u) && need(g->h));
+      MOE_CHECK_ARG(need(g->x_perm) && need(g->w_gate) && need(g->w_up) && need(g->h));
+      // g and u both written, or both NULL (only h is wanted)
+      MOE_CHECK_ARG((need(g->g) && need(g->u)) || (g->g == nullptr && g->u == nullptr));
       break;
     case MOE_GG_FWD_DOWN:
       MOE_CHECK_ARG(need(g->h) && need(g->w_down) && need(g->y_perm));
@@ -346,7 +295,7 @@ extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
   }
   const size_t ws_need = moe_grouped_gemm_workspace_bytes(g);
   if (ws_need > 0 && (g->ws == nullptr || g->ws_bytes < ws_need || !aligned4(g->ws))) return MOE_ERR_WORKSPACE;
-  GGArgs a{g->op, g->E, g->d, g->F, g->n_rows, g->capacity, gg_tile_order(), g->group_offsets,
+  GGArgs a{g->op, g->E, g->d, g->F, g->n_rows, g->capacity, g->group_offsets,
            g->x_perm, g->g, g->u, g->h, g->y_perm, g->dy_perm, g->dg, g->du, g->dx_perm,
            g->w_gate, g->w_up, g->w_down, g->dw_gate, g->dw_up, g->dw_down,
            ws_need > 0 ? static_cast<const int*>(g->ws) : nullptr};
@@ -356,19 +305,8 @@ extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
     // buffer-resource offsets are 32-bit: every expert's rows and weights
     // must span less than 2 GiB
     const long span = (long)g->n_rows * (g->d > g->F ? g->d : g->F) * 2;
-    const bool dma_fits = span < (1L << 31) && (long)g->d * g->F * 2 < (1L << 31);
-    const int choice = tile_choice();
-    if (dma_fits) {
-      switch (choice) {
-        case 2: return launch_dma<CfgDma256>(g, a, kvar, dual, N, stream);
-        case 3: return launch_dma<CfgDma128>(g, a, kvar, dual, N, stream);
-        case 8: return launch_dma<CfgDma128w8>(g, a, kvar, dual, N, stream);
-
-        default: break;
-      }
-    }
-    if (choice == 0) return launch_mfma<Cfg128>(g, a, kvar, dual, N, stream);
-    return launch_mfma<Cfg256>(g, a, kvar, dual, N, stream);
+    MOE_CHECK_SUPPORTED(span < (1L << 31) && (long)g->d * g->F * 2 < (1L << 31));
+    return launch_dma<CfgDma>(g, a, kvar, dual, N, stream);
   }
   long grid;
   if (kvar) grid = (long)g->E * cdiv(op_wgrad_m(g->op, g->d, g->F), kSBM) * cdiv(N, kSBN);

@@ -8,11 +8,6 @@ namespace moe {
 
 struct GGArgs {
   int op, E, d, F, n_rows, capacity;
-  // row-varying tile order: 0 = the n-tiles of one m-tile adjacent; 1 =
-  // expert-grouped, the m-tiles sharing one weight slice adjacent (they run
-  // side by side and fetch the slice from HBM once even when the experts'
-  // m-tile counts do not line up with what one XCD runs at a time)
-  int order;
   const int32_t* group_offsets;
   void* x_perm;
   void* g;
@@ -33,9 +28,6 @@ struct GGArgs {
   // gg_wgrad_split_kernel (kSplitInts ints), or null for the equal-count split
   const int* split;
 };
-
-// Row-varying tile order of the launches (host side; MOE_GG_ORDER=n selects 0).
-int gg_tile_order();
 
 // Static shape of each op as C[M x N] = sum_k A[m, k] B[k, n] per expert.
 template <int OP> struct OpInfo;

@@ -382,14 +382,10 @@ __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_dma_kernel(GGArgs
     int e, row0, mv, tn;
     const int b = xcd_tile(blockIdx.x, gridDim.x, build_tile_prefix<BM, NT>(a, tile_start) * tilesN);
     if (b < 0) return;
-    if (a.order == 0) {
-      tn = b % tilesN;
-      if (!m_tile_of<BM>(a, b / tilesN, tile_start, e, row0, mv)) return;
-    } else {
-      // blocks of (expert's m-tiles) x (one n-tile): the m-tiles sharing a
-      // weight slice run side by side; experts are visited in order
-      if (!m_tile_grouped<BM>(a, b, tilesN, tile_start, e, row0, mv, tn)) return;
-    }
+    // blocks of (expert's m-tiles) x (one n-tile): the m-tiles sharing a
+    // weight slice run side by side (and fetch it from HBM once); experts are
+    // visited in order
+    if (!m_tile_grouped<BM>(a, b, tilesN, tile_start, e, row0, mv, tn)) return;
     run_tile(e, row0, mv, op_k(OP, d, F), 0, tn);
   } else {
     const int tpe = (op_wgrad_m(OP, d, F) / BM) * tilesN;

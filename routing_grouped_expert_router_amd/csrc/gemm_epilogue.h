@@ -99,13 +99,16 @@ MOE_DEV void gg_store_tile(const GGArgs& a, const df32x16_t (&acc)[C::MI][C::NI]
       uint16_t* outg = (uint16_t*)a.g + rbase * F + n0;
       uint16_t* outu = (uint16_t*)a.u + rbase * F + n0;
       uint16_t* outh = (uint16_t*)a.h + rbase * F + n0;
+      const bool keep_gu = a.g != nullptr;   // null g and u: only h is written (recompute)
       for (int q = tid; q < rows_valid * CPRW; q += NT) {
         const int r = q / CPRW, c = q % CPRW;
         const V16 gv = *reinterpret_cast<const V16*>(stg0 + r * LDW + c * 8);
         const V16 uv = *reinterpret_cast<const V16*>(stg1 + r * LDW + c * 8);
         const size_t o = (size_t)r * F + c * 8;
-        *reinterpret_cast<V16*>(outg + o) = gv;
-        *reinterpret_cast<V16*>(outu + o) = uv;
+        if (keep_gu) {
+          *reinterpret_cast<V16*>(outg + o) = gv;
+          *reinterpret_cast<V16*>(outu + o) = uv;
+        }
         float gf[8], uf[8], hf[8];
         unpack(gv, gf);
         unpack(uv, uf);

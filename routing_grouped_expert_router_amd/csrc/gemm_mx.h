@@ -340,12 +340,7 @@ __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_mx_kernel(MxArgs 
     int e, row0, mv, tn;
     const int b = xcd_tile(blockIdx.x, gridDim.x, build_tile_prefix<BM, NT>(a, tile_start) * tilesN);
     if (b < 0) return;
-    if (a.order == 0) {
-      tn = b % tilesN;
-      if (!m_tile_of<BM>(a, b / tilesN, tile_start, e, row0, mv)) return;
-    } else {
-      if (!m_tile_grouped<BM>(a, b, tilesN, tile_start, e, row0, mv, tn)) return;
-    }
+    if (!m_tile_grouped<BM>(a, b, tilesN, tile_start, e, row0, mv, tn)) return;
     __syncthreads();   // every wave is past its reads of tile_start before the ring is filled
     run_tile(e, row0, mv, op_k(OP, d, F), 0, tn, 0);
   } else {

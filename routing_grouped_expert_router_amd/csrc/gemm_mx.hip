@@ -3,33 +3,18 @@
 // "Três números, três denominadores"); the kernel is in gemm_mx.h.
 #include "gemm_mx.h"
 
-#include <cstdlib>
-#include <string>
 
 namespace moe {
 namespace {
 
-// 128 x 256 tiles, a 3-deep ring, two workgroups per CU; 8 waves of 64 x 64
-// (default) or 4 waves of 64 x 128 (MOE_MX_TILE=w4, for tuning sweeps).
+// 128 x 256 tiles, a 3-deep ring, two workgroups per CU, 8 waves of 64 x 64.
 using CfgMx = MxCfg<128, 256, 2, 4, 3, 2>;
-using CfgMx4 = MxCfg<128, 256, 2, 2, 3, 2>;
-static_assert(CfgMx::BM == CfgMx4::BM && CfgMx::BN == CfgMx4::BN, "same grid for both shapes");
-
-bool mx_four_waves() {
-  static const bool v = [] {
-    const char* s = std::getenv("MOE_MX_TILE");
-    return s && std::string(s) == "w4";
-  }();
-  return v;
-}
 
 template <int OP> void launch_mx_op(const MxArgs& x, int grid, hipStream_t s) {
-  if (mx_four_waves()) gg_mx_kernel<OP, CfgMx4><<<grid, CfgMx4::NT, 0, s>>>(x);
-  else gg_mx_kernel<OP, CfgMx><<<grid, CfgMx::NT, 0, s>>>(x);
+  gg_mx_kernel<OP, CfgMx><<<grid, CfgMx::NT, 0, s>>>(x);
 }
 
 template <int OP> void launch_mx_split(const MxArgs& x, int grid, int* ws, hipStream_t s) {
-  // both tile shapes share BM, BN and BK, hence the split
   gg_mx_wgrad_split_kernel<OP, CfgMx><<<1, 256, 0, s>>>(x.o, grid, ws);
 }
 
@@ -114,7 +99,7 @@ extern "C" int moe_grouped_gemm_mx(const moe_mx_gg_desc* g, hipStream_t stream) 
   if (ws_need > 0 && (g->ws == nullptr || g->ws_bytes < ws_need || !aligned4(g->ws))) return MOE_ERR_WORKSPACE;
 
   MxArgs x{};
-  x.o = GGArgs{g->op, g->E, g->d, g->F, g->n_rows, 0, gg_tile_order(), g->group_offsets,
+  x.o = GGArgs{g->op, g->E, g->d, g->F, g->n_rows, 0, g->group_offsets,
                nullptr, const_cast<void*>(g->g), const_cast<void*>(g->u), nullptr, nullptr, nullptr,
                nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   switch (g->op) {

@@ -27,13 +27,25 @@ routed rows are gathered straight into E4M3 codes and scales, in the two
 orientations the GEMMs read, and never written in bf16. Routing, combine and
 their adjoints are the bf16 layer's.
 
-With ``recompute=True`` the expert activations G, U and H are treated as
-scratch that need not survive from the forward to the backward: the backward
-runs the gate/up grouped GEMM again from x_perm before its first expert
-GEMM. This is the pages' per-layer recompute, which trades activation memory
-for throughput (p1 deniz.in, "Ai2'nin raporladığı sayılar"; unite.ai/hi,
-"पैरालेलिज़्म, प्रिसीजन, और मेमोरी तकनीकें"). The recomputed values are
-bitwise those of the forward (the kernels are deterministic).
+With ``recompute=True`` the expert activations G, U and H are not kept from
+the forward for the backward: the forward's gate/up GEMM writes H alone (G
+and U never reach memory), H is scratch released after the down projection,
+and the backward runs the gate/up GEMM again from x_perm into scratch G, U, H
+that it releases when the weight gradients are done. This is the pages'
+per-layer recompute, which trades activation memory for throughput (p1
+deniz.in, "Ai2'nin raporladığı sayılar"; unite.ai/hi, "पैरालेलिज़्म, प्रिसीजन,
+और मेमोरी तकनीकें"). The recomputed values are bitwise those of the forward
+(the kernels are deterministic).
+
+Memory: routing metadata and workspaces are allocated with the layer; the
+tensors the forward writes (x_perm, y_perm, y and, without recompute, G, U,
+H) are allocated by the first forward and the gradient buffers by the first
+backward, then reused by later steps, so that the memory a forward leaves
+for its backward can be read off torch's allocator. With
+``keep_intermediates=False`` the backward releases, when it returns, what
+only the step needed (the forward's activations and outputs and its own
+dY_perm, dG, dU, dX_perm), as each layer of a stack would; the gradients
+(dx, the weight gradients, dtopk_w, dlogits) stay.
 """
 from __future__ import annotations
 
@@ -48,15 +60,16 @@ class MoELayer:
     def __init__(self, T: int, d: int, E: int, k: int, F: int, dtype=torch.bfloat16,
                  routing: str = "learned", capacity: int = 0, backward: bool = True,
                  device: str = "cuda", recompute: bool = False, shared_ff: int = 0,
-                 mxfp8: bool = False):
+                 mxfp8: bool = False, keep_intermediates: bool = True):
         if routing not in ("learned", "given"):
             raise ValueError(routing)
         self.T, self.d, self.E, self.k, self.F = T, d, E, k, F
         self.dtype, self.routing, self.capacity = dtype, routing, capacity
         self.recompute = recompute
+        self.keep_intermediates = keep_intermediates
         self.R = T * k
         self.n_rows = E * capacity if capacity > 0 else self.R
-        dev = torch.device(device)
+        self.dev = dev = torch.device(device)
         f32, i32 = torch.float32, torch.int32
         e = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=dev)
         nr = self.n_rows
@@ -76,35 +89,20 @@ class MoELayer:
         # launch because they all run in order on one stream.
         wgrad = L.make_gg_desc(L.MOE_GG_WGRAD_GATE_UP, L.MOE_BF16, E, d, F, nr, 0)
         self.ws_gg = e((max(L.moe_grouped_gemm_workspace_bytes(wgrad), 4) + 3) // 4, dt=i32)
-        self.x_perm = None if mxfp8 else e(nr, d)   # the MXFP8 permute writes quantised rows only
-        self.g, self.u, self.h = e(nr, F), e(nr, F), e(nr, F)
-        self.y_perm = e(nr, d)
-        self.y = e(T, d)
         self.has_bwd = backward
-        if backward:
-            self.dy_perm = e(nr, d)
-            self.dtopk_w = e(T, k, dt=f32)
-            self.dg, self.du = e(nr, F), e(nr, F)
-            self.dx_perm = e(nr, d)
-            self.dx = e(T, d)
-            self.dw_gate, self.dw_up = e(E, d, F), e(E, d, F)
-            self.dw_down = e(E, F, d)
-            if routing == "learned":
-                self.dlogits = e(T, E, dt=f32)
-                self.dw_r = e(d, E)
-                wsr = max(L.moe_router_bwd_workspace_bytes(T, d, E), 16)
-                self.ws_router = e((wsr + 15) // 16 * 4, dt=f32)
+        if backward and routing == "learned":
+            wsr = max(L.moe_router_bwd_workspace_bytes(T, d, E), 16)
+            self.ws_router = e((wsr + 15) // 16 * 4, dt=f32)
+        # activations and gradients: allocated on first use (see the module notes)
+        self.x_perm = self.g = self.u = self.h = self.y_perm = self.y = None
+        self.dy_perm = self.dtopk_w = self.dg = self.du = self.dx_perm = self.dx = None
+        self.dw_gate = self.dw_up = self.dw_down = self.dlogits = self.dw_r = None
         self.mxfp8 = mxfp8
         if mxfp8:
             if capacity > 0 or dtype != torch.bfloat16 or recompute or shared_ff > 0:
                 raise ValueError("the MXFP8 layer is dropless bf16, without recompute or shared expert")
             from .mx_layer import MxExperts
             self.mx = MxExperts(self.n_rows, d, E, F, device=device, outputs=False)
-            # the expert GEMMs write into the layer's buffers
-            self.mx.g, self.mx.u, self.mx.h, self.mx.y_perm = self.g, self.u, self.h, self.y_perm
-            if backward:
-                self.mx.dg, self.mx.du, self.mx.dx_perm = self.dg, self.du, self.dx_perm
-                self.mx.dw_gate, self.mx.dw_up, self.mx.dw_down = self.dw_gate, self.dw_up, self.dw_down
         self.shared_ff = shared_ff
         if shared_ff > 0:
             Fs = shared_ff
@@ -119,6 +117,40 @@ class MoELayer:
         # optional callable(stage_name) run after each stage is enqueued (used
         # by the benchmark to record per-stage events)
         self.hook = None
+
+    def _new(self, *shape, dt=None):
+        return torch.empty(*shape, dtype=self.dtype if dt is None else dt, device=self.dev)
+
+    def forward_buffers(self):
+        """Tensors the forward writes: x_perm (not for MXFP8, whose permute
+        writes quantised rows only), y_perm, y and, unless recomputing, G, U, H."""
+        nr, d, F = self.n_rows, self.d, self.F
+        if self.y is None:
+            if not self.mxfp8:
+                self.x_perm = self._new(nr, d)
+            self.y_perm, self.y = self._new(nr, d), self._new(self.T, d)
+        if not self.recompute and self.g is None:
+            self.g, self.u, self.h = self._new(nr, F), self._new(nr, F), self._new(nr, F)
+        if self.mxfp8:   # the MXFP8 expert GEMMs write into the layer's buffers
+            self.mx.g, self.mx.u, self.mx.h, self.mx.y_perm = self.g, self.u, self.h, self.y_perm
+
+    def backward_buffers(self):
+        """Gradient buffers (kept across steps) and the backward's scratch."""
+        nr, d, F, E, T = self.n_rows, self.d, self.F, self.E, self.T
+        if self.dy_perm is None:
+            self.dy_perm, self.dx_perm = self._new(nr, d), self._new(nr, d)
+            self.dg, self.du = self._new(nr, F), self._new(nr, F)
+        if self.dx is None:
+            self.dx = self._new(T, d)
+            self.dtopk_w = self._new(T, self.k, dt=torch.float32)
+            self.dw_gate, self.dw_up, self.dw_down = self._new(E, d, F), self._new(E, d, F), self._new(E, F, d)
+            if self.routing == "learned":
+                self.dlogits = self._new(T, E, dt=torch.float32)
+                self.dw_r = self._new(d, E)
+        if self.mxfp8:
+            mx = self.mx
+            mx.dg, mx.du, mx.dx_perm = self.dg, self.du, self.dx_perm
+            mx.dw_gate, mx.dw_up, mx.dw_down = self.dw_gate, self.dw_up, self.dw_down
 
     def _mark(self, name: str):
         if self.hook is not None:
@@ -174,6 +206,7 @@ class MoELayer:
             if w_gate_s is None or w_up_s is None or w_down_s is None:
                 raise ValueError("a layer with a shared expert needs its weights")
             self.w_gate_s, self.w_up_s, self.w_down_s = w_gate_s, w_up_s, w_down_s
+        self.forward_buffers()
         if self.routing == "learned":
             self.route(x, w_r)
         else:
@@ -208,6 +241,14 @@ class MoELayer:
             self.mx.quantize_weights(self.w_gate, self.w_up, self.w_down)
             self.mx.forward_quantized()
             return
+        if self.recompute:
+            # H alone, as scratch for the down projection; G and U are never written
+            h = self._new(self.n_rows, self.F)
+            self._gg(L.MOE_GG_FWD_GATE_UP, x_perm=self.x_perm, w_gate=self.w_gate, w_up=self.w_up, h=h)
+            self._mark("gg_fwd_gate_up")
+            self._gg(L.MOE_GG_FWD_DOWN, h=h, w_down=self.w_down, y_perm=self.y_perm)
+            self._mark("gg_fwd_down")
+            return
         self._gg(L.MOE_GG_FWD_GATE_UP, x_perm=self.x_perm, w_gate=self.w_gate, w_up=self.w_up,
                  g=self.g, u=self.u, h=self.h)
         self._mark("gg_fwd_gate_up")
@@ -223,6 +264,7 @@ class MoELayer:
         """Data gradients first (dx is what the layer below, or an expert-
         parallel exchange, waits on, and each data-gradient GEMM reads what
         the one before it just wrote), weight gradients last."""
+        self.backward_buffers()
         # with src_slot the adjoint runs in row order (see moe_unpermute_combine_bwd)
         L.moe_unpermute_combine_bwd(dy, self.y_perm, self.topk_w, self.row_of, self.src_slot,
                                     self.dy_perm, self.dtopk_w)
@@ -245,13 +287,16 @@ class MoELayer:
         self.experts_backward_weights()
         if self.shared_ff > 0:
             self.shared_backward_weights(dy)
+        if not self.keep_intermediates:
+            self.release_intermediates()
         return self.dx
 
-    def activation_bytes_between_passes(self) -> int:
-        """Bytes of expert activations the forward must leave for the backward
-        (besides x_perm, which both modes keep): G, U and H, or none when
-        recomputing."""
-        return 0 if self.recompute else 3 * self.n_rows * self.F * self.g.element_size()
+    def release_intermediates(self):
+        """Drop the step's activations and the backward's scratch (x_perm,
+        G, U, H, y_perm, y, dY_perm, dG, dU, dX_perm); the next step
+        allocates them again from torch's caching allocator."""
+        self.x_perm = self.g = self.u = self.h = self.y_perm = self.y = None
+        self.dy_perm = self.dg = self.du = self.dx_perm = None
 
     def experts_backward(self):
         self.experts_backward_data()
@@ -265,6 +310,8 @@ class MoELayer:
             self.mx.backward_data(self.dy_perm)
             return
         if self.recompute:
+            nr, F = self.n_rows, self.F
+            self.g, self.u, self.h = self._new(nr, F), self._new(nr, F), self._new(nr, F)
             self._gg(L.MOE_GG_FWD_GATE_UP, x_perm=self.x_perm, w_gate=self.w_gate, w_up=self.w_up,
                      g=self.g, u=self.u, h=self.h)
             self._mark("gg_recompute_gate_up")
@@ -286,6 +333,8 @@ class MoELayer:
         self._gg(L.MOE_GG_WGRAD_GATE_UP, x_perm=self.x_perm, dg=self.dg, du=self.du,
                  dw_gate=self.dw_gate, dw_up=self.dw_up)
         self._mark("gg_wgrad_gate_up")
+        if self.recompute and not self.keep_intermediates:
+            self.g = self.u = self.h = None   # the recomputed scratch goes at once
 
     def grads(self) -> Dict[str, torch.Tensor]:
         out = dict(dx=self.dx, dw_gate=self.dw_gate, dw_up=self.dw_up, dw_down=self.dw_down,

@@ -14,11 +14,36 @@ are the bf16 layer's and are not repeated here.
 """
 from __future__ import annotations
 
-from typing import Dict
+import weakref
+from typing import Dict, Sequence
 
 import torch
 
 from . import _lib as L
+
+
+class WeightVersion:
+    """Which weight tensors, at which in-place version, a set of quantised
+    copies was made from. A later call matches only with the very same tensor
+    objects (held by weak reference, so a freed tensor never matches, even if
+    a new one reuses its memory) and no in-place write since (torch's version
+    counter)."""
+
+    def __init__(self):
+        self._refs = None
+        self._versions = None
+
+    def matches(self, ws: Sequence[torch.Tensor]) -> bool:
+        if self._refs is None or len(ws) != len(self._refs):
+            return False
+        return all(r() is w and w._version == v for r, w, v in zip(self._refs, ws, self._versions))
+
+    def record(self, ws: Sequence[torch.Tensor]):
+        self._refs = [weakref.ref(w) for w in ws]
+        self._versions = [w._version for w in ws]
+
+    def clear(self):
+        self._refs = self._versions = None
 
 
 class _Q:
@@ -71,7 +96,7 @@ class MxExperts:
         self.ws = torch.empty((L.moe_grouped_gemm_mx_workspace_bytes(wgrad) + 3) // 4, dtype=torch.int32,
                               device=dev)
         self.hook = None
-        self._wkey = None   # which weights the quantised copies hold (see quantize_weights)
+        self._wver = WeightVersion()   # which weights the quantised copies hold
 
     def _mark(self, name: str):
         if self.hook is not None:
@@ -82,20 +107,15 @@ class MxExperts:
         L.moe_grouped_gemm_mx(desc)
 
     # ------------------------------------------------------------------ steps
-    @staticmethod
-    def _key(*ws):
-        # storage, layout and torch's in-place version counter of each weight
-        return tuple((w.data_ptr(), tuple(w.shape), tuple(w.stride()), w._version) for w in ws)
-
     def quantize_weights(self, w_gate, w_up, w_down, force: bool = False) -> bool:
         """Both orientations of each weight in one pass. The weights change
-        once per optimiser step, not per micro-batch: when the same tensors
-        come back unmodified (same storage, no in-place write since, by
-        torch's version counter) the quantised copies are current and
-        nothing runs. Writes that bypass torch's version counter need
+        once per optimiser step, not per micro-batch: when the same tensor
+        objects come back unmodified (no in-place write since, by torch's
+        version counter) the quantised copies are current and nothing runs.
+        A different tensor object always requantises, even at the same
+        address. Writes that bypass torch's version counter need
         invalidate_weights() or force=True. Returns whether it quantised."""
-        key = self._key(w_gate, w_up, w_down)
-        if not force and key == self._wkey:
+        if not force and self._wver.matches((w_gate, w_up, w_down)):
             self._mark("mx_quantize_weights")
             return False
         E, d, F = self.E, self.d, self.F
@@ -103,14 +123,14 @@ class MxExperts:
         L.moe_mx_quantize_both(wg, self.wg_r.t, self.wg_c.t, None, E, E * d)
         L.moe_mx_quantize_both(wu, self.wu_r.t, self.wu_c.t, None, E, E * d)
         L.moe_mx_quantize_both(wd, self.wd_r.t, self.wd_c.t, None, E, E * F)
-        self._wkey = key
+        self._wver.record((w_gate, w_up, w_down))
         self._mark("mx_quantize_weights")
         return True
 
     def invalidate_weights(self):
         """Forget which weights the quantised copies hold: the next forward
         quantises again."""
-        self._wkey = None
+        self._wver.clear()
 
     def _both(self, src, rows_out, cols_out):
         L.moe_mx_quantize_both(src, rows_out.t, cols_out.t, self.offsets, self.E, self.P)

@@ -130,6 +130,16 @@ def test_grouped_gemm_argument_errors():
     d.capacity = 16
     assert call(d) == INVALID
     assert lib.moe_grouped_gemm(None, None) == INVALID
+    # forward gate/up: g and u are both written or both NULL (h alone)
+    d = mk(op=L.MOE_GG_FWD_GATE_UP)
+    d.x_perm, d.w_gate, d.w_up, d.h = FAKE, FAKE, FAKE, FAKE
+    d.g = FAKE
+    assert call(d) == INVALID                            # u missing
+    d.g, d.u = None, FAKE
+    assert call(d) == INVALID                            # g missing
+    d.u, d.h = FAKE, None
+    d.g = FAKE
+    assert call(d) == INVALID                            # h is always written
 
 
 def test_grouped_gemm_workspace():
@@ -257,3 +267,44 @@ def test_library_never_syncs_copies_back_or_allocates():
             code = line.split("#", 1)[0]
             assert not bad_py.search(code), (name, i, line)
 
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The binding checks dtype, contiguity, shape and device of every tensor
+    before its address reaches the library (which reads dense row-major memory
+    of the declared element type), so a wrong tensor raises instead of being
+    misread."""
+    import torch
+    T, E, k, d = 8, 4, 2, 16
+    lg = torch.zeros(T, E)
+    idx32, w = torch.zeros(T, k, dtype=torch.int32), torch.zeros(T, k)
+    with pytest.raises(L.MoEError, match="topk_idx: dtype torch.int64"):
+        L.moe_route(lg, k, torch.zeros(T, k, dtype=torch.int64), w)       # torch.topk's default dtype
+    with pytest.raises(L.MoEError, match="logits: dtype"):
+        L.moe_route(lg.double(), k, idx32, w)
+    with pytest.raises(L.MoEError, match="topk_w: shape"):
+        L.moe_route(lg, k, idx32, torch.zeros(T, k + 1))
+    with pytest.raises(L.MoEError, match="logits: must be contiguous"):
+        L.moe_route(torch.zeros(E, T).t(), k, idx32, w)                    # a transposed view
+    with pytest.raises(L.MoEError, match="device tensors"):
+        L.moe_route(lg, k, idx32, w)                                       # right layout, host memory
+    x = torch.zeros(T, d, dtype=torch.bfloat16)
+    with pytest.raises(L.MoEError, match="x_perm: dtype torch.float32"):
+        L.moe_permute(x, k, torch.zeros(T * k, dtype=torch.int32), None, torch.zeros(T * k, d))
+    with pytest.raises(L.MoEError, match="row_of: 8 elements"):
+        L.moe_permute(x, k, torch.zeros(T, dtype=torch.int32), None, torch.zeros(T * k, d, dtype=torch.bfloat16))
+    with pytest.raises(L.MoEError, match="dy: must be contiguous"):
+        L.moe_unpermute_combine_bwd(torch.zeros(d, T, dtype=torch.bfloat16).t(), torch.zeros(T * k, d, dtype=torch.bfloat16),
+                                    w, idx32.view(-1), None, torch.zeros(T * k, d, dtype=torch.bfloat16), w)
+    # grouped-GEMM descriptors: every tensor of the descriptor's dtype and size
+    F = 32
+    with pytest.raises(L.MoEError, match="w_gate: dtype torch.float32"):
+        L.make_gg_desc(L.MOE_GG_FWD_GATE_UP, L.MOE_BF16, E, d, F, T * k, 0,
+                       torch.zeros(E + 1, dtype=torch.int32), w_gate=torch.zeros(E, d, F))
+    with pytest.raises(L.MoEError, match="g: 256 elements, expected 512"):
+        L.make_gg_desc(L.MOE_GG_FWD_GATE_UP, L.MOE_BF16, E, d, F, T * k, 0,
+                       torch.zeros(E + 1, dtype=torch.int32), g=torch.zeros(T, F, dtype=torch.bfloat16))
+    with pytest.raises(L.MoEError, match="group_offsets: dtype torch.int64"):
+        L.make_gg_desc(L.MOE_GG_FWD_GATE_UP, L.MOE_BF16, E, d, F, T * k, 0, torch.zeros(E + 1, dtype=torch.int64))
+    with pytest.raises(L.MoEError, match="no tensor"):
+        L.make_gg_desc(L.MOE_GG_FWD_GATE_UP, L.MOE_BF16, E, d, F, T * k, 0, None, w_gat=torch.zeros(1))

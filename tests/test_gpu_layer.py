@@ -1,21 +1,29 @@
-"""GPU parity of the whole layer (forward and backward) against the oracle:
-in full at sizes the oracle finishes in seconds, and at the full workload
-sizes on sampled tokens and experts (every row of the layer is independent
-until the weight gradients), in the same launch configuration the benchmark
-times. Routing metadata is compared bit for bit in full at every size."""
+"""GPU parity of the whole layer (forward and backward) against the oracle,
+element by element over every tensor: at sizes the oracle finishes in seconds
+and at the full workload sizes, in the launch configuration the benchmark
+times. Routing metadata is compared bit for bit.
+
+With a learned router the oracle routes from the GPU's binary32 logits (a
+different summation order in x . W_r can move a logit by a few ulps, and bit-
+exact routing cannot survive that): the logits are first checked against the
+oracle's own within the binary32 tolerance, and every token whose top-k from
+the oracle's own logits differs from the GPU's must be one whose k-th and
+(k+1)-th oracle logits are at most twice the measured logit error apart (no
+smaller perturbation can reorder a wider gap). Tokens whose gap is below
+1e-5 * max|logit| are reported as near-ties."""
 import numpy as np
 import pytest
 import torch
 
 import oracle.moe as om
 from moe_inputs import make_inputs, workload
-from oracle.numerics import round_f32, storer
 from routing_grouped_expert_router_amd.layer import MoELayer
 
-from parity import (Weights, assert_close, dev, expert_weight_grads, host,
-                    sampled_forward_backward, values)
+from parity import assert_close, dev, host, values
 
 pytestmark = pytest.mark.gpu
+
+NEAR_TIE = 1e-5   # reported: k-th/(k+1)-th logit gap below this times max|logit|
 
 
 def _upload(inp, kind):
@@ -30,12 +38,12 @@ def _upload(inp, kind):
     return out
 
 
-def _run_gpu(wl, inp, capacity=0, backward=True):
+def _run_gpu(wl, inp, capacity=0, backward=True, **opts):
     kind = "f32" if wl.dtype == "f32" else "bf16"
     t = _upload(inp, kind)
     layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.float32 if kind == "f32" else torch.bfloat16,
                      routing="learned" if wl.routing == "learned" else "given", capacity=capacity,
-                     backward=backward)
+                     backward=backward, **opts)
     layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
                   topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
     if backward:
@@ -44,80 +52,68 @@ def _run_gpu(wl, inp, capacity=0, backward=True):
     return layer, t
 
 
-def _margin_ok(logits, k, err):
-    """Tokens whose k-th and (k+1)-th logits are further apart than twice the
-    measured logit error (plus a little): no rounding can flip their top-k."""
+def gap_k(logits, k):
+    """k-th minus (k+1)-th largest logit of each token (inf when k = E)."""
     if k >= logits.shape[1]:
-        return np.ones(len(logits), bool)
+        return np.full(len(logits), np.inf)
     s = -np.sort(-logits, axis=1)
-    return (s[:, k - 1] - s[:, k]) > 2 * err + 1e-7 * np.abs(logits).max()
+    return s[:, k - 1] - s[:, k]
 
 
-def _check_routing(layer, lg_ref, k):
-    """Logits within binary32 tolerance; top-k identical except where the
-    oracle's own logits are a near-tie within the measured logit error.
-    Returns the oracle's routing and the per-token agreement mask."""
+def _check_logits(layer, lg_ref, k):
+    """GPU logits within the binary32 tolerance of the oracle's; any top-k
+    disagreement with the oracle's own routing sits at a gap of at most twice
+    the measured logit error. Returns the GPU logits (binary32) and the number
+    of near-ties."""
     lg_gpu = host(layer.logits)
     assert_close(lg_gpu, lg_ref, "f32", "logits")
-    err = np.abs(lg_gpu - lg_ref).max()
-    idx, w = om.route(lg_ref, k)
-    agree = np.all(host(layer.topk_idx) == idx, axis=1)
-    assert np.all(agree | ~_margin_ok(lg_ref, k, err)), "routing differs away from a near-tie"
-    assert_close(host(layer.topk_w)[agree], w[agree], "f32", "topk_w")
-    return idx, w, agree
+    err = float(np.abs(lg_gpu - lg_ref).max())
+    idx_own, _ = om.route(lg_ref, k)
+    differ = np.any(host(layer.topk_idx) != idx_own, axis=1)
+    gap = gap_k(lg_ref, k)
+    assert np.all(gap[differ] <= 2 * err), "routing differs away from a near-tie"
+    near = int(np.sum(gap < NEAR_TIE * np.abs(lg_ref).max()))
+    print(f"logit err {err:.3g}; tokens routed differently from the oracle's own logits: "
+          f"{int(differ.sum())}; near-ties (gap < {NEAR_TIE:g} max|logit|): {near}", flush=True)
+    return lg_gpu.astype(np.float32), near
 
 
-def _check_meta_valid(layer, T, k):
-    """Row maps are a stable expert-major bijection of the GPU's own top-k."""
-    R = T * k
-    ro, src = host(layer.row_of), host(layer.src_slot)
-    assert np.array_equal(np.sort(ro), np.arange(R)) and np.array_equal(src[ro], np.arange(R))
-    flat = host(layer.topk_idx).reshape(-1)
-    assert np.all(np.diff(flat[src]) >= 0)
-    assert np.all(np.diff(src)[np.diff(flat[src]) == 0] > 0)
-
-
-def _full_oracle_check(wl, capacity=0, backward=True):
-    """Whole-layer comparison at a size the oracle computes in full."""
+def _full_oracle_check(wl, capacity=0, backward=True, layer_opts=None):
+    """Whole-layer comparison, every element of every tensor. Returns the
+    GPU layer (for callers that compare further)."""
     kind = "f32" if wl.dtype == "f32" else "bf16"
     inp = make_inputs(wl)
-    layer, _ = _run_gpu(wl, inp, capacity, backward)
+    layer, _ = _run_gpu(wl, inp, capacity, backward, **(layer_opts or {}))
     p = {n: values(inp[n], kind) for n in ("x", "w_gate", "w_up", "w_down", "w_r") if n in inp}
     if "topk_idx" in inp:
         p["topk_idx"], p["topk_w"] = inp["topk_idx"], inp["topk_w"].astype(np.float64)
-    fwd = om.layer_forward(p, wl.k, kind, capacity)
-    agree = np.ones(wl.T, bool)
+    logits = None
     if "w_r" in p:
-        _, _, agree = _check_routing(layer, fwd["logits"], wl.k)
-    if agree.all():
-        for n in ("counts", "offsets", "row_of", "src_slot"):
-            assert np.array_equal(host(getattr(layer, n)), fwd[n]), n
-        assert int(host(layer.n_dropped)[0]) == fwd["n_dropped"]
-        assert np.array_equal(host(layer.x_perm), fwd["x_perm"])
-        for n, ref in (("g", "G"), ("u", "U"), ("h", "H"), ("y_perm", "y_perm")):
-            assert_close(host(getattr(layer, n)), fwd[ref], kind, n)
-    else:
-        # a near-tie flip moves single rows: compare token-order outputs of the
-        # agreeing tokens and check the GPU's own maps are valid
-        assert capacity == 0
-        _check_meta_valid(layer, wl.T, wl.k)
+        lg_ref = om.router_logits(p["x"], p["w_r"])
+        logits, _ = _check_logits(layer, lg_ref, wl.k)
+    fwd = om.layer_forward(p, wl.k, kind, capacity, logits=logits)
+    for n in ("topk_idx", "counts", "offsets", "row_of", "src_slot"):
+        assert np.array_equal(host(getattr(layer, n)), fwd[n]), n
+    assert int(host(layer.n_dropped)[0]) == fwd["n_dropped"]
     assert int(host(layer.err_flag)[0]) == 0
-    assert_close(host(layer.y)[agree], fwd["y"][agree], kind, "y")
+    assert_close(host(layer.topk_w), fwd["topk_w"], "f32", "topk_w")
+    assert np.array_equal(host(layer.x_perm), fwd["x_perm"])
+    pairs = [("y_perm", "y_perm"), ("y", "y")]
+    if layer.g is not None:   # kept by the forward, or recomputed by the backward
+        pairs += [("g", "G"), ("u", "U"), ("h", "H")]
+    for n, ref in pairs:
+        assert_close(host(getattr(layer, n)), fwd[ref], kind, n)
     if not backward:
-        return
-    dy = values(inp["dy"], kind)
-    bwd = om.layer_backward(p, fwd, dy, wl.k, kind, capacity)
-    if agree.all():
-        for n in ("dy_perm", "dg", "du", "dx_perm"):
-            ref = {"dg": "dG", "du": "dU"}.get(n, n)
-            assert_close(host(getattr(layer, n)), bwd[ref], kind, n)
-    for n in ("dtopk_w", "dx"):
-        assert_close(host(getattr(layer, n))[agree], bwd[n][agree], kind, n)
-    for n in ("dw_gate", "dw_up", "dw_down"):
-        assert_close(host(getattr(layer, n)), bwd[n], kind, n)
+        return layer
+    bwd = om.layer_backward(p, fwd, values(inp["dy"], kind), wl.k, kind, capacity)
+    for n, ref in (("dy_perm", "dy_perm"), ("dg", "dG"), ("du", "dU"), ("dx_perm", "dx_perm"),
+                   ("dtopk_w", "dtopk_w"), ("dx", "dx"), ("dw_gate", "dw_gate"), ("dw_up", "dw_up"),
+                   ("dw_down", "dw_down")):
+        assert_close(host(getattr(layer, n)), bwd[ref], kind, n)
     if "w_r" in p:
-        assert_close(host(layer.dlogits)[agree], bwd["dlogits"][agree], kind, "dlogits")
+        assert_close(host(layer.dlogits), bwd["dlogits"], kind, "dlogits")
         assert_close(host(layer.dw_r), bwd["dw_r"], kind, "dw_r")
+    return layer
 
 
 def test_tiny_f32_forward_full():
@@ -143,90 +139,33 @@ def test_layer_small_full(name, over, cf):
 
 
 # ----------------------------------------------------------------------------- full size
-def _unrounded_dx(x, W, idx, w, dy, tokens, st, keep):
-    """Per sampled token, the experts' share of dx before its final rounding."""
-    out = []
-    for t in tokens:
-        acc = np.zeros(x.shape[1])
-        for j, e in enumerate(idx[t]):
-            if not keep[t, j]:
-                continue
-            e = int(e)
-            G, U, H = om.expert_fwd_gate_up(x[t:t + 1], W("w_gate", e), W("w_up", e), [(0, 1)], st)
-            dyp = st(w[t, j] * dy[t:t + 1])
-            dG, dU = om.expert_dgrad_down(dyp, W("w_down", e), G, U, [(0, 1)], st)
-            acc += om.expert_dgrad_gate_up(dG, dU, W("w_gate", e), W("w_up", e), [(0, 1)], st)[0]
-        out.append(acc)
-    return np.stack(out)
+def _free(layer):
+    """Release a finished test's device memory before the next full-size run
+    (call as _free(check(...)) so that no other reference remains)."""
+    del layer
+    torch.cuda.empty_cache()
 
 
-def _sampled_check(wl, capacity=0, n_tok=48, seed=0):
-    kind = "bf16"
-    st = storer(kind)
-    inp = make_inputs(wl)
-    layer, t = _run_gpu(wl, inp, capacity)
-    x = values(inp["x"], kind)
-    dy = values(inp["dy"], kind)
-    W = Weights({n: inp[n] for n in ("w_gate", "w_up", "w_down")}, kind)
-    if wl.routing == "learned":
-        idx, w, agree = _check_routing(layer, round_f32(x @ values(inp["w_r"], kind)), wl.k)
-    else:
-        idx, w = inp["topk_idx"], inp["topk_w"].astype(np.float64)
-        agree = np.ones(wl.T, bool)
-    meta = om.expert_offsets(idx, wl.E, capacity)
-    if agree.all():
-        for n in ("counts", "offsets", "row_of", "src_slot"):
-            assert np.array_equal(host(getattr(layer, n)), meta[n]), n
-        assert int(host(layer.n_dropped)[0]) == meta["n_dropped"]
-    else:
-        assert capacity == 0
-        _check_meta_valid(layer, wl.T, wl.k)
-    rng = np.random.default_rng(seed)
-    tokens = [int(v) for v in rng.choice(np.nonzero(agree)[0], n_tok, replace=False)]
-    keep = (meta["row_of"] >= 0).reshape(wl.T, wl.k)
-    y, dx, dw = sampled_forward_backward(x, W, idx, w, dy, tokens, st, keep=keep)
-    gy, gdx, gdw = host(layer.y), host(layer.dx), host(layer.dtopk_w)
-    assert_close(gy[tokens], np.stack([y[t] for t in tokens]), kind, "y")
-    assert_close(gdw[tokens], np.stack([dw[t] for t in tokens]), kind, "dtopk_w")
-    if wl.routing == "learned":
-        # dx carries the router's share: dlogits of the sampled tokens from the
-        # oracle's dw, then dx = experts' share + dlogits W_r^T, rounded once
-        wr = values(inp["w_r"], kind)
-        dl = om.route_bwd(idx[tokens], w[tokens], np.stack([dw[t] for t in tokens]), wl.E)
-        assert_close(host(layer.dlogits)[tokens], dl, kind, "dlogits")
-        dx_exp = _unrounded_dx(x, W, idx, w, dy, tokens, st, keep)
-        assert_close(gdx[tokens], st(dx_exp + dl @ wr.T), kind, "dx")
-    else:
-        assert_close(gdx[tokens], np.stack([dx[t] for t in tokens]), kind, "dx")
-    counts = meta["counts"]
-    live = np.nonzero(counts > 0)[0]
-    experts = sorted({int(live[np.argmax(counts[live])]), int(live[np.argmin(counts[live])]),
-                      int(rng.choice(live))})
-    ref = expert_weight_grads(x, W, meta, w, dy, experts, wl.k, st, capacity)
-    for e in experts:
-        for n in ("dw_gate", "dw_up", "dw_down"):
-            assert_close(host(getattr(layer, n)[e]), ref[e][n], kind, f"{n}[{e}]")
-    for e in np.nonzero(counts == 0)[0][:4]:
-        assert np.all(host(layer.dw_gate[int(e)]) == 0)
-    return layer
+def test_full_e128_uniform_whole():
+    """The headline workload at full size (T 16384, d 2048, 128 experts,
+    top-4, d_ff 1024), every element of every output and gradient."""
+    _free(_full_oracle_check(workload("e128_uniform_bf16")))
 
 
-def test_full_e128_uniform_sampled():
-    _sampled_check(workload("e128_uniform_bf16"))
-
-
-def test_full_e8_learned_sampled():
-    _sampled_check(workload("e8_learned_bf16"))
+def test_full_e8_learned_whole():
+    """The 8-expert learned-router workload at full size, routed by the
+    oracle from the GPU's logits, near-ties reported."""
+    _free(_full_oracle_check(workload("e8_learned_bf16")))
 
 
 def test_full_e128_zipf_padded_and_dropless():
     wl = workload("e128_zipf_bf16")
     C = wl.capacity()
-    padded = _sampled_check(wl, capacity=C)
+    padded = _full_oracle_check(wl, capacity=C)
     y_pad = host(padded.y)
     del padded
     torch.cuda.empty_cache()
-    dropless = _sampled_check(wl, capacity=0)
+    dropless = _full_oracle_check(wl, capacity=0)
     # tokens none of whose slots were dropped see bitwise-identical rows
     inp = make_inputs(wl, with_weights=False)
     keep = (om.expert_offsets(inp["topk_idx"], wl.E, C)["row_of"] >= 0).reshape(wl.T, wl.k)
@@ -248,30 +187,55 @@ def test_deterministic_bitwise():
 
 @pytest.mark.parametrize("name,over", [("e128_uniform_bf16", dict(T=2048, E=16, d=512, F=256)),
                                        ("e8_learned_bf16", dict(T=1024, d=256, F=512))])
-def test_recompute_backward_matches_bitwise(name, over):
-    # per-layer recompute: the backward recomputes G, U, H from x_perm, so the
-    # forward's copies may be overwritten in between (they are filled with NaN
-    # here) and every gradient must still equal the stored-activation run's
+def test_recompute_against_oracle(name, over):
+    """Per-layer recompute: the forward leaves no G, U or H for the backward
+    (its gate/up GEMM writes H alone, as scratch), the backward recomputes
+    them from x_perm; every output and gradient, and the recomputed G, U, H,
+    against the oracle element by element, and bitwise equal to the
+    stored-activation run's."""
     wl = workload(name).scaled(**over)
     inp = make_inputs(wl)
     ref, _ = _run_gpu(wl, inp)
-    snap = {n: host(getattr(ref, n)).copy() for n in ("y", "dx", "dw_gate", "dw_up", "dw_down", "dtopk_w",
-                                                      "dg", "du")}
+    names = ["y", "dx", "dw_gate", "dw_up", "dw_down", "dtopk_w", "dg", "du", "g", "u", "h"]
     if wl.routing == "learned":
-        snap.update(dlogits=host(ref.dlogits).copy(), dw_r=host(ref.dw_r).copy())
+        names += ["dlogits", "dw_r"]
+    snap = {n: host(getattr(ref, n)).copy() for n in names}
     del ref
     t = _upload(inp, "bf16")
     lay = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
                    routing="learned" if wl.routing == "learned" else "given", recompute=True)
     lay.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
                 topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
-    for buf in (lay.g, lay.u, lay.h):
-        buf.fill_(float("nan"))
+    assert lay.g is None and lay.u is None and lay.h is None   # nothing kept for the backward
     lay.backward(t["dy"])
     torch.cuda.synchronize()
-    assert lay.activation_bytes_between_passes() == 0
     for n, v in snap.items():
-        assert np.array_equal(host(getattr(lay, n)), v, equal_nan=False), n
+        assert np.array_equal(host(getattr(lay, n)), v), n
+    del lay
+    torch.cuda.empty_cache()
+    _free(_full_oracle_check(wl, layer_opts=dict(recompute=True)))
+
+
+def test_intermediates_released_and_reallocated():
+    """keep_intermediates=False: the backward releases the step's activations
+    and scratch; the next step allocates them again and gives the same
+    results bit for bit (stored and recomputed activations alike)."""
+    wl = workload("e128_uniform_bf16").scaled(T=1024, E=16, d=256, F=256)
+    inp = make_inputs(wl)
+    t = _upload(inp, "bf16")
+    for rc in (False, True):
+        lay = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16, routing="given", recompute=rc,
+                       keep_intermediates=False)
+        outs = []
+        for _ in range(2):
+            y = lay.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], topk_idx=t["topk_idx"],
+                            topk_w=t["topk_w"]).clone()
+            lay.backward(t["dy"])
+            torch.cuda.synchronize()
+            assert lay.x_perm is None and lay.g is None and lay.dg is None and lay.y_perm is None
+            outs.append([host(v).copy() for v in (y, lay.dx, lay.dw_gate, lay.dw_down, lay.dtopk_w)])
+        for a, b in zip(*outs):
+            assert np.array_equal(a, b)
 
 
 @pytest.mark.parametrize("name,over", [("e128_uniform_bf16", dict(T=1024, E=16, d=256, F=256, shared_ff=256)),
@@ -293,20 +257,17 @@ def test_shared_expert_layer_full(name, over):
     p = {n: values(inp[n], "bf16") for n in names if n in inp}
     if "topk_idx" in inp:
         p["topk_idx"], p["topk_w"] = inp["topk_idx"], inp["topk_w"].astype(np.float64)
-    fwd = om.layer_forward(p, wl.k, "bf16")
-    agree = np.ones(wl.T, bool)
+    logits = None
     if "w_r" in p:
-        _, _, agree = _check_routing(lay, fwd["logits"], wl.k)
-    for n, ref in (("g_s", "G_s"), ("u_s", "U_s"), ("h_s", "H_s"), ("y_s", "y_s")):
+        logits, _ = _check_logits(lay, om.router_logits(p["x"], p["w_r"]), wl.k)
+    fwd = om.layer_forward(p, wl.k, "bf16", logits=logits)
+    for n, ref in (("g_s", "G_s"), ("u_s", "U_s"), ("h_s", "H_s"), ("y_s", "y_s"), ("y", "y")):
         assert_close(host(getattr(lay, n)), fwd[ref], "bf16", n)
-    assert_close(host(lay.y)[agree], fwd["y"][agree], "bf16", "y")
     bwd = om.layer_backward(p, fwd, values(inp["dy"], "bf16"), wl.k, "bf16")
     for n, ref in (("dg_s", "dG_s"), ("du_s", "dU_s"), ("dx_s", "dx_s"), ("dw_gate_s", "dw_gate_s"),
-                   ("dw_up_s", "dw_up_s"), ("dw_down_s", "dw_down_s")):
+                   ("dw_up_s", "dw_up_s"), ("dw_down_s", "dw_down_s"), ("dx", "dx"), ("dw_gate", "dw_gate"),
+                   ("dw_up", "dw_up"), ("dw_down", "dw_down")):
         assert_close(host(getattr(lay, n)), bwd[ref], "bf16", n)
-    assert_close(host(lay.dx)[agree], bwd["dx"][agree], "bf16", "dx")
-    for n in ("dw_gate", "dw_up", "dw_down"):
-        assert_close(host(getattr(lay, n)), bwd[n], "bf16", n)
 
 
 @pytest.mark.parametrize("name,opts", [("e128_uniform_bf16", {}),

@@ -488,6 +488,47 @@ def test_mx_routed_layer_parity(name, over):
     print("rel errs", {n: f"{v:.2e}" for n, v in errs.items()})
 
 
+def test_mx_routed_layer_full_size_whole():
+    """The MXFP8 routed layer end to end at the benchmark's size (16384
+    tokens, 128 experts, top-4, d = 2048, d_ff = 1024, uniform routing), in
+    its launch configuration, against the oracle's whole MXFP8 chain: every
+    element of every output and gradient within the MXFP8 bar. The oracle's
+    experts are independent and run on a thread pool."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    from moe_inputs import make_inputs, workload
+    from oracle.numerics import bf16_bits_to_f64
+    from routing_grouped_expert_router_amd.layer import MoELayer
+
+    wl = workload("e128_uniform_bf16")
+    inp = make_inputs(wl)
+    T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.F
+    t = {n: dev(a, "bf16") for n, a in inp.items() if n not in ("topk_idx", "topk_w")}
+    t["topk_idx"] = dev(inp["topk_idx"].astype(np.int32), "i32")
+    t["topk_w"] = dev(inp["topk_w"].astype(np.float32), "f32")
+    lay = MoELayer(T, d, E, k, F, torch.bfloat16, routing="given", mxfp8=True)
+    lay.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], topk_idx=t["topk_idx"], topk_w=t["topk_w"])
+    lay.backward(t["dy"])
+    torch.cuda.synchronize()
+    got = {n: host(getattr(lay, n)) for n in ("counts", "offsets", "row_of", "src_slot", "g", "u", "h",
+                                                 "y_perm", "y", "dg", "du", "dx_perm", "dx", "dw_gate",
+                                                 "dw_up", "dw_down", "dtopk_w")}
+    del lay, t
+    torch.cuda.empty_cache()
+    p = {n: bf16_bits_to_f64(inp[n]) for n in ("x", "w_gate", "w_up", "w_down")}
+    p["topk_idx"], p["topk_w"] = inp["topk_idx"], inp["topk_w"].astype(np.float64)
+    with ThreadPoolExecutor(min(16, len(os.sched_getaffinity(0)))) as ex:
+        ref = om.mx_layer(p, k, bf16_bits_to_f64(inp["dy"]), map_fn=ex.map)
+    for n in ("counts", "offsets", "row_of", "src_slot"):
+        assert np.array_equal(got[n], ref[n]), n
+    errs = {}
+    for n, r in (("g", "G"), ("u", "U"), ("h", "H"), ("y_perm", "y_perm"), ("y", "y"), ("dg", "dG"),
+                 ("du", "dU"), ("dx_perm", "dx_perm"), ("dx", "dx"), ("dw_gate", "dw_gate"),
+                 ("dw_up", "dw_up"), ("dw_down", "dw_down"), ("dtopk_w", "dtopk_w")):
+        errs[n] = f"{assert_close(got[n], ref[r], 'mxfp8', n):.2e}"
+    print("rel errs", errs, flush=True)
+
+
 def test_mx_routed_layer_full_size_sampled_experts():
     """The MXFP8 routed layer at the benchmark's size (16384 tokens, 128
     experts, top-4, d = 2048, d_ff = 1024, uniform routing) in its launch
