@@ -144,12 +144,14 @@ def _dt(t: torch.Tensor) -> int:
     raise MoEError(f"unsupported dtype {t.dtype}")
 
 
-def _req(t: Optional[torch.Tensor], name: str, dtype, shape=None, optional: bool = False):
+def _req(t: Optional[torch.Tensor], name: str, dtype, shape=None, optional: bool = False,
+         min_numel: int = 0):
     """Check one tensor argument before its address goes to the library:
     dtype (one torch dtype or a tuple), contiguity, shape (-1 = any extent,
-    an int = element count) and device. Returns the address (None for an
-    absent optional tensor). Raises MoEError on any mismatch, because the
-    library would otherwise read the memory as if it had the declared layout."""
+    an int = element count), at least min_numel elements, and device.
+    Returns the address (None for an absent optional tensor). Raises MoEError
+    on any mismatch, because the library would otherwise read the memory as
+    if it had the declared layout."""
     if t is None:
         if optional:
             return None
@@ -165,6 +167,8 @@ def _req(t: Optional[torch.Tensor], name: str, dtype, shape=None, optional: bool
     elif shape is not None:
         if t.dim() != len(shape) or any(w >= 0 and w != v for w, v in zip(shape, t.shape)):
             raise MoEError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)} (-1 = any)")
+    if t.numel() < min_numel:
+        raise MoEError(f"{name}: {t.numel()} elements, at least {min_numel} needed")
     return _p(t)
 
 
@@ -291,7 +295,7 @@ def moe_router_gemm_bwd(x, dlogits, dw_r, ws, stream=None):
                                      _req(dw_r, "dw_r", x.dtype, (d, E)), _p(ws), _nbytes(ws), _stream(stream))
 
 
-# element count of each grouped-GEMM tensor, from (E, d, F, n_rows)
+# elements each grouped-GEMM tensor must hold, from (E, d, F, n_rows)
 _GG_NUMEL = {
     "x_perm": lambda E, d, F, n: n * d, "y_perm": lambda E, d, F, n: n * d,
     "dy_perm": lambda E, d, F, n: n * d, "dx_perm": lambda E, d, F, n: n * d,
@@ -313,7 +317,8 @@ def make_gg_desc(op, dtype, E, d, F, n_rows, capacity=0, group_offsets=None, ws=
     for name, t in tensors.items():
         if name not in _GG_NUMEL:
             raise MoEError(f"moe_gg_desc has no tensor {name}")
-        fields.append(((desc, name), _req(t, name, tdt, _GG_NUMEL[name](E, d, F, n_rows), optional=True)))
+        # the call touches this many elements (a larger buffer is fine)
+        fields.append(((desc, name), _req(t, name, tdt, optional=True, min_numel=_GG_NUMEL[name](E, d, F, n_rows))))
     if ws is not None:
         fields.append(((desc, "ws"), _p(ws)))
         desc.ws_bytes = _nbytes(ws)

@@ -301,10 +301,11 @@ def test_binding_rejects_mismatched_tensors():
     with pytest.raises(L.MoEError, match="w_gate: dtype torch.float32"):
         L.make_gg_desc(L.MOE_GG_FWD_GATE_UP, L.MOE_BF16, E, d, F, T * k, 0,
                        torch.zeros(E + 1, dtype=torch.int32), w_gate=torch.zeros(E, d, F))
-    with pytest.raises(L.MoEError, match="g: 256 elements, expected 512"):
+    with pytest.raises(L.MoEError, match="g: 256 elements, at least 512 needed"):
         L.make_gg_desc(L.MOE_GG_FWD_GATE_UP, L.MOE_BF16, E, d, F, T * k, 0,
                        torch.zeros(E + 1, dtype=torch.int32), g=torch.zeros(T, F, dtype=torch.bfloat16))
     with pytest.raises(L.MoEError, match="group_offsets: dtype torch.int64"):
         L.make_gg_desc(L.MOE_GG_FWD_GATE_UP, L.MOE_BF16, E, d, F, T * k, 0, torch.zeros(E + 1, dtype=torch.int64))
     with pytest.raises(L.MoEError, match="no tensor"):
         L.make_gg_desc(L.MOE_GG_FWD_GATE_UP, L.MOE_BF16, E, d, F, T * k, 0, None, w_gat=torch.zeros(1))
+

@@ -645,17 +645,18 @@ def test_mx_weight_quantisation_tracks_in_place_updates():
     def fresh():
         return MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16, routing="given", mxfp8=True)
 
+    ws = lambda: (t["w_gate"], t["w_up"], t["w_down"])
     lay = fresh()
     first = run(lay)
-    key = lay.mx._wkey
+    assert lay.mx._wver.matches(ws())
     again = run(lay)
-    assert lay.mx._wkey == key
     for n in names:
         assert np.array_equal(first[n], again[n]), n
     # an optimiser-like in-place update of one weight
     t["w_down"].mul_(0.5)
+    assert not lay.mx._wver.matches(ws())
     updated = run(lay)
-    assert lay.mx._wkey != key
+    assert lay.mx._wver.matches(ws())
     ref = run(fresh())
     for n in names:
         assert np.array_equal(updated[n], ref[n]), n
@@ -667,3 +668,8 @@ def test_mx_weight_quantisation_tracks_in_place_updates():
     mx.invalidate_weights()
     assert mx.quantize_weights(t["w_gate"], t["w_up"], t["w_down"]) is True
     assert mx.quantize_weights(t["w_gate"], t["w_up"], t["w_down"]) is False
+    # a new weight tensor, even one that takes the freed tensor's memory, is quantised again
+    vals = t["w_up"].clone()
+    t["w_up"] = None
+    t["w_up"] = vals.clone()
+    assert mx.quantize_weights(t["w_gate"], t["w_up"], t["w_down"]) is True
