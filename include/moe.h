@@ -133,7 +133,8 @@ int moe_unpermute_combine(int dtype, const void* y_perm, const int32_t* row_of,
                           const float* topk_w, int T, int k, int d, int n_rows,
                           const void* y_add, void* y, hipStream_t stream);
 
-/* moe_unpermute_combine_bwd: adjoint of moe_unpermute_combine.
+/* moe_unpermute_combine_bwd: derived, the adjoint of moe_unpermute_combine
+ * (its chain rule with respect to y_perm and the gate weights).
  *   dy_perm[row_of[t,j]] = w[t,j] * dy[t]   (rounded once to `dtype`)
  *   dtopk_w[t,j] = <dy[t], y_perm[row_of[t,j]]>  (binary32; 0 if dropped)
  * If src_slot is not NULL, pad rows (src_slot == -1) of dy_perm are zeroed
@@ -146,7 +147,8 @@ int moe_unpermute_combine_bwd(int dtype, const void* dy, const void* y_perm,
                               const int32_t* src_slot, int T, int k, int d, int n_rows,
                               void* dy_perm, float* dtopk_w, hipStream_t stream);
 
-/* moe_permute_bwd: adjoint of moe_permute,
+/* moe_permute_bwd: derived, the adjoint of moe_permute (each token row
+ * receives the sum of its routed rows' gradients),
  *   dx[t] = dx_add[t] + sum_j dx_perm[row_of[t,j]]  (+ sum_e dlogits[t,e] * w_r[:,e])
  * binary32 accumulation, one rounding to `dtype`. The router term is added
  * when dlogits and w_r are not NULL (learned router); it is the router
@@ -159,14 +161,17 @@ int moe_permute_bwd(int dtype, const void* dx_perm, const int32_t* row_of, int T
                     void* dx, hipStream_t stream);
 
 /* ----------------------------------------------------------------- router backward
- * moe_route_bwd: dlogits through the renormalised top-k gate with the
- * selection held fixed: for selected e_j, dl = w_j (dw_j - sum_i w_i dw_i);
+ * moe_route_bwd: derived, the adjoint of moe_route with the selection held
+ * fixed (the chain rule of the renormalised top-k softmax), dlogits through
+ * the gate: for selected e_j, dl = w_j (dw_j - sum_i w_i dw_i);
  * exactly 0 for unselected experts.
  *   topk_idx, topk_w, dtopk_w [T,k] -> dlogits [T,E] binary32. */
 int moe_route_bwd(const int32_t* topk_idx, const float* topk_w, const float* dtopk_w, int T,
                   int E, int k, float* dlogits, hipStream_t stream);
 
-/* moe_router_gemm_bwd: dw_r = x^T dlogits, binary32 accumulation over tokens
+/* moe_router_gemm_bwd: derived, the adjoint of moe_router_gemm with respect
+ * to w_r (its share of dx is added by moe_permute_bwd):
+ * dw_r = x^T dlogits, binary32 accumulation over tokens
  * in a fixed order, one rounding to `dtype`.
  *   x [T,d], dw_r [d,E] of `dtype`; dlogits [T,E] binary32;
  *   ws of at least moe_router_bwd_workspace_bytes(T, d, E) bytes. */

@@ -168,3 +168,28 @@ def test_offsets_padded_invariants():
     for s in np.nonzero(m["row_of"] < 0)[0]:
         e = flat[s]
         assert s > m["src_slot"][e * C + C - 1]
+
+
+def test_router_logits_special_cases():
+    """The learned router's logits x . W_r [d, E] in binary32: a one-hot
+    token row picks out one row of W_r exactly; small-integer operands give
+    exact dot products that a per-element loop reproduces; each logit is
+    linear in the token and the result is [T, E] (a transposed operand or a
+    dropped term fails one of these)."""
+    from oracle.moe import router_logits
+    rng = np.random.default_rng(30)
+    d, E = 12, 5
+    w_r = rng.standard_normal((d, E)).astype(np.float32).astype(np.float64)
+    eye = np.eye(d)
+    assert np.array_equal(router_logits(eye, w_r), w_r)                 # one-hot rows
+    assert router_logits(eye[:3], w_r).shape == (3, E)
+    xi = rng.integers(-4, 5, size=(7, d)).astype(np.float64)
+    wi = rng.integers(-4, 5, size=(d, E)).astype(np.float64)
+    brute = np.array([[sum(xi[t, i] * wi[i, e] for i in range(d)) for e in range(E)] for t in range(7)])
+    assert np.array_equal(router_logits(xi, wi), brute)
+    x = rng.standard_normal((4, d))
+    lhs = router_logits(2.0 * x[:1] + x[1:2], w_r)[0]
+    rhs = 2.0 * (x[0] @ w_r) + x[1] @ w_r
+    assert np.allclose(lhs, rhs, rtol=1e-6, atol=1e-6)
+    # stored in binary32
+    assert np.array_equal(router_logits(x, w_r), router_logits(x, w_r).astype(np.float32))
