@@ -110,6 +110,23 @@ int moe_offsets(const int32_t* topk_idx, int T, int k, int E, int capacity, int3
                 int32_t* offsets, int32_t* row_of, int32_t* src_slot, int32_t* n_dropped,
                 int32_t* err_flag, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_offsets_noalloc: moe_offsets without a caller workspace and without
+ * any device allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments (minus ws, ws_bytes), results and errors as
+ * moe_offsets; the workspace is a static array of the library, one per GPU,
+ * MOE_OFFSETS_NOALLOC_MAX_BYTES long, held until the process ends. Calls whose
+ * moe_offsets_workspace_bytes(T, k, E) exceeds it return MOE_ERR_UNSUPPORTED
+ * (1 MiB: e.g. T*k up to 2M slots at E = 128, 256K slots at E = 1024).
+ * All calls on one GPU share that GPU's array: calls that overlap on one GPU
+ * (on different streams, or from different threads without ordering) race;
+ * calls ordered on one stream do not. A failure to resolve the array's
+ * device address returns MOE_ERR_HIP. */
+#define MOE_OFFSETS_NOALLOC_MAX_BYTES ((size_t)1 << 20)
+int moe_offsets_noalloc(const int32_t* topk_idx, int T, int k, int E, int capacity, int32_t* counts,
+                        int32_t* offsets, int32_t* row_of, int32_t* src_slot, int32_t* n_dropped,
+                        int32_t* err_flag, hipStream_t stream);
+
 /* ----------------------------------------------------------------- row movement
  * moe_permute: x_perm[row_of[s]] = x[s / k] for every kept slot s: each
  * selected token row is written straight into its expert's rows (unite.ai/hi,

@@ -57,6 +57,7 @@ SIGNATURES = {
     "moe_route": (_i, [_vp, _i, _i, _i, _vp, _vp, _vp]),
     "moe_offsets_workspace_bytes": (_sz, [_i, _i, _i]),
     "moe_offsets": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_offsets_noalloc": (_i, [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_permute": (_i, [_i, _vp, _i, _i, _i, _vp, _vp, _i, _vp, _vp]),
     "moe_unpermute_combine": (_i, [_i, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]),
     "moe_unpermute_combine_bwd": (_i, [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp]),
@@ -228,6 +229,17 @@ def moe_offsets(topk_idx, E, capacity, counts, offsets, row_of, src_slot, n_drop
                              _req(row_of, "row_of", i32, T * k), _req(src_slot, "src_slot", i32, n_rows),
                              _req(n_dropped, "n_dropped", i32, 1), _req(err_flag, "err_flag", i32, 1),
                              _p(ws), _nbytes(ws), _stream(stream))
+
+
+def moe_offsets_noalloc(topk_idx, E, capacity, counts, offsets, row_of, src_slot, n_dropped, err_flag,
+                        stream=None):
+    T, k = topk_idx.shape
+    n_rows = E * capacity if capacity > 0 else T * k
+    i32 = torch.int32
+    _call("moe_offsets_noalloc", _req(topk_idx, "topk_idx", i32, (T, k)), T, k, E, capacity,
+          _req(counts, "counts", i32, E), _req(offsets, "offsets", i32, E + 1),
+          _req(row_of, "row_of", i32, T * k), _req(src_slot, "src_slot", i32, n_rows),
+          _req(n_dropped, "n_dropped", i32, 1), _req(err_flag, "err_flag", i32, 1), _stream(stream))
 
 
 def moe_permute(x, k, row_of, src_slot, x_perm, stream=None):

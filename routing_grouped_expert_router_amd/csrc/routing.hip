@@ -2,6 +2,8 @@
 // backward (gfx950). See include/moe.h for the contract of each entry point.
 #include "common.h"
 
+#include <mutex>
+
 namespace moe {
 
 // ============================================================== router GEMM
@@ -590,6 +592,55 @@ extern "C" size_t moe_offsets_workspace_bytes(int T, int k, int E) {
   const long R = (long)T * k;
   const long nblk = (R + kSlotsPerBlock - 1) / kSlotsPerBlock;
   return static_cast<size_t>((nblk > 0 ? nblk : 1) * E * sizeof(int32_t));
+}
+
+// ---------------------------------------------------------------- no-allocation variant
+// moe_offsets_noalloc keeps the per-block histogram in this file-scope device
+// array instead of a caller workspace. Every GPU the library runs on holds
+// its own copy until the process ends. In host code the name `scratch` is
+// only a stand-in: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, looked up once per device with that device current
+// and kept in scratch_addr.
+constexpr size_t kOffsetsScratchBytes = MOE_OFFSETS_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) int32_t scratch[kOffsetsScratchBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, or nullptr when it
+// cannot be resolved.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_addr[dev] = p;
+  }
+  return scratch_addr[dev];
+}
+}  // namespace
+
+extern "C" int moe_offsets_noalloc(const int32_t* topk_idx, int T, int k, int E, int capacity,
+                                   int32_t* counts, int32_t* offsets, int32_t* row_of,
+                                   int32_t* src_slot, int32_t* n_dropped, int32_t* err_flag,
+                                   hipStream_t stream) {
+  // the same argument checks as moe_offsets, before the scratch is looked up
+  MOE_CHECK_ARG(counts && offsets && n_dropped && err_flag && T >= 0 && E > 0 && k >= 1 &&
+                k <= E && capacity >= 0);
+  MOE_CHECK_SUPPORTED(E <= MOE_MAX_EXPERTS && k <= MOE_MAX_TOPK);
+  const long R = (long)T * k;
+  MOE_CHECK_SUPPORTED(R < (1L << 31) && (long)E * capacity < (1L << 31));
+  const size_t need = moe_offsets_workspace_bytes(T, k, E);
+  MOE_CHECK_SUPPORTED(need <= kOffsetsScratchBytes);   // beyond the array: not this entry point
+  void* ws = device_scratch();
+  if (ws == nullptr) return MOE_ERR_HIP;
+  // every histogram entry the call reads is written by the call first: nothing to clear
+  return moe_offsets(topk_idx, T, k, E, capacity, counts, offsets, row_of, src_slot, n_dropped,
+                     err_flag, ws, kOffsetsScratchBytes, stream);
 }
 
 extern "C" int moe_offsets(const int32_t* topk_idx, int T, int k, int E, int capacity,

@@ -309,3 +309,21 @@ def test_binding_rejects_mismatched_tensors():
     with pytest.raises(L.MoEError, match="no tensor"):
         L.make_gg_desc(L.MOE_GG_FWD_GATE_UP, L.MOE_BF16, E, d, F, T * k, 0, None, w_gat=torch.zeros(1))
 
+
+def test_offsets_noalloc_argument_errors():
+    """The no-allocation routing-metadata call checks its arguments like
+    moe_offsets and rejects sizes whose histogram exceeds its static array,
+    before touching the device."""
+    lib = L.lib()
+    f = lambda T, k, E, cap=0, ptr=FAKE: lib.moe_offsets_noalloc(ptr, T, k, E, cap, FAKE, FAKE, FAKE, FAKE,
+                                                                 FAKE, FAKE, None)
+    assert f(100, 0, 8) == INVALID                       # k < 1
+    assert f(100, 9, 8) == INVALID                       # k > E
+    assert f(100, 2, 8, cap=-1) == INVALID
+    assert f(100, 2, 2000) == UNSUPPORTED                # E > 1024
+    limit = 1 << 20                                      # MOE_OFFSETS_NOALLOC_MAX_BYTES
+    fits = lambda T, k, E: L.moe_offsets_workspace_bytes(T, k, E) <= limit
+    assert not fits(600000, 4, 128) and fits(500000, 4, 128)
+    assert f(600000, 4, 128) == UNSUPPORTED              # histogram beyond the static array
+    assert f(300000, 1, 1024) == UNSUPPORTED
+    assert lib.moe_offsets_noalloc(FAKE, 10, 2, 8, 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
