@@ -64,7 +64,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 /* Text for a status code (static storage; never NULL). */
 const char* moe_status_string(int status);
 
-/* ABI version of this header: 5. */
+/* ABI version of this header: 6. */
 int moe_abi_version(void);
 
 /* ----------------------------------------------------------------- router
@@ -387,6 +387,14 @@ typedef struct moe_mx_gg_desc {
   void* out2;
   void* ws;                      /* workspace, see above */
   size_t ws_bytes;
+  /* Optional MXFP8 copies written by the epilogue from the rounded bf16
+   * outputs, exactly as moe_mx_quantize_both would write them from those
+   * outputs (with the experts as groups and col_stride): FWD_GATE_UP: H in
+   * qo0_rows [n_rows, F] and qo0_cols [F, col_stride]; DGRAD_DOWN: dG in
+   * qo0_*, dU in qo1_*. All NULL (nothing written) or all of the op's set;
+   * other ops take none. This fuses the quantisation of the next GEMMs'
+   * operands into the GEMM that produces them. */
+  moe_mx_tensor qo0_rows, qo0_cols, qo1_rows, qo1_cols;
 } moe_mx_gg_desc;
 
 size_t moe_grouped_gemm_mx_workspace_bytes(const moe_mx_gg_desc* desc);

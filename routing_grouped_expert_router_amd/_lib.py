@@ -46,6 +46,8 @@ class moe_mx_gg_desc(C.Structure):
         ("a0", moe_mx_tensor), ("a1", moe_mx_tensor), ("b0", moe_mx_tensor), ("b1", moe_mx_tensor),
         ("g", _vp), ("u", _vp), ("out0", _vp), ("out1", _vp), ("out2", _vp),
         ("ws", _vp), ("ws_bytes", _sz),
+        ("qo0_rows", moe_mx_tensor), ("qo0_cols", moe_mx_tensor),
+        ("qo1_rows", moe_mx_tensor), ("qo1_cols", moe_mx_tensor),
     ]
 
 
@@ -390,11 +392,13 @@ def moe_permute_mx(x, k, src_slot, group_offsets, E, col_stride, rows_out: MxTen
 
 
 def make_mx_gg_desc(op, E, d, F, n_rows, group_offsets, col_stride=0, a0=None, a1=None, b0=None,
-                    b1=None, g=None, u=None, out0=None, out1=None, out2=None, ws=None) -> moe_mx_gg_desc:
+                    b1=None, g=None, u=None, out0=None, out1=None, out2=None, ws=None, qo0_rows=None,
+                    qo0_cols=None, qo1_rows=None, qo1_cols=None) -> moe_mx_gg_desc:
     desc = moe_mx_gg_desc()
     desc.op, desc.E, desc.d, desc.F, desc.n_rows, desc.col_stride = op, E, d, F, n_rows, col_stride
     fields = [((desc, "group_offsets"), _req(group_offsets, "group_offsets", torch.int32, E + 1, optional=True))]
-    for name, t in (("a0", a0), ("a1", a1), ("b0", b0), ("b1", b1)):
+    for name, t in (("a0", a0), ("a1", a1), ("b0", b0), ("b1", b1), ("qo0_rows", qo0_rows),
+                    ("qo0_cols", qo0_cols), ("qo1_rows", qo1_rows), ("qo1_cols", qo1_cols)):
         if t is not None:
             fields.append(((getattr(desc, name), "q"), _req(t.q, f"{name}.q", torch.uint8)))
             fields.append(((getattr(desc, name), "s"), _req(t.s, f"{name}.s", torch.uint8)))

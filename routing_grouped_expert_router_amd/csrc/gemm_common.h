@@ -6,6 +6,16 @@
 
 namespace moe {
 
+// MXFP8 copies of one epilogue output in the two orientations the next GEMMs
+// read (the layout of moe_mx_quantize: rows = axis 0, cols = axis 1 with the
+// experts as groups); null pointers: not written.
+struct MxQOut {
+  uint8_t* q_rows;
+  uint8_t* s_rows;
+  uint8_t* q_cols;
+  uint8_t* s_cols;
+};
+
 struct GGArgs {
   int op, E, d, F, n_rows, capacity;
   const int32_t* group_offsets;
@@ -27,6 +37,11 @@ struct GGArgs {
   // weight gradients: the tile split of the launch written by
   // gg_wgrad_split_kernel (kSplitInts ints), or null for the equal-count split
   const int* split;
+  // MXFP8 quantised copies of H (FWD_GATE_UP, mxo[0]) or of dG and dU
+  // (DGRAD_DOWN, mxo[0] and mxo[1]) written by the epilogue, with the token
+  // stride of the column orientation; unused (null) elsewhere
+  MxQOut mxo[2];
+  int mx_P;
 };
 
 // Static shape of each op as C[M x N] = sum_k A[m, k] B[k, n] per expert.

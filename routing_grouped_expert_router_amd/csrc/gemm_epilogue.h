@@ -5,6 +5,7 @@
 #pragma once
 
 #include "gemm_common.h"
+#include "mx_common.h"
 
 namespace moe {
 
@@ -18,6 +19,60 @@ MOE_DEV void dunpack4(uint2 p, float* v) {
   v[3] = __uint_as_float(p.y & 0xffff0000u);
 }
 
+// MXFP8 quantisation of one staged plane (BM rows x CW bf16 columns, row
+// stride LDW) in both orientations, as moe_mx_quantize writes them with the
+// experts as groups:
+//  * rows: blocks of 32 along the columns; codes of the rows_valid valid rows
+//    at q_rows[(grow0 + r) * K + col0 + ...], scale bytes in the grouped
+//    layout of n_rows rows;
+//  * cols: blocks of 32 along the tile's 128 rows (which start a 128-row
+//    tile of the expert, so blocks restart at the expert's first row), the
+//    rows past rows_valid counting as zeros; codes of output row col0 + c at
+//    token column qcol0 + ..., scale bytes in the grouped layout of K rows.
+// Each thread takes one 32-value block of each orientation per NT blocks;
+// scale bytes are stored one by one.
+template <class C>
+MOE_DEV void mx_quantize_plane(const uint16_t* stg, const MxQOut& o, size_t grow0, int rows_valid, int col0,
+                               int K, int n_rows, int P, int qcol0, int tid) {
+  constexpr int BM = C::BM, CW = C::CW, LDW = C::LDW, NT = C::NT;
+  constexpr int RB = CW / 32, CB = BM / 32;        // blocks per tile row / per tile column
+  for (int it = tid; it < BM * RB; it += NT) {
+    const int r = it / RB, b = it % RB;
+    float v[32];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float f[8];
+      unpack(*reinterpret_cast<const V16*>(stg + r * LDW + 32 * b + 8 * k), f);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) v[8 * k + m] = f[m];
+    }
+    V16 out[2];
+    const uint32_t code = quantize_block(v, out);
+    if (r < rows_valid) {
+      const size_t grow = grow0 + r;
+      V16* qp = reinterpret_cast<V16*>(o.q_rows + grow * K + col0 + 32 * b);
+      qp[0] = out[0];
+      qp[1] = out[1];
+      o.s_rows[4 * ((size_t)n_rows * (col0 / 128) + grow) + b] = static_cast<uint8_t>(code);
+    }
+  }
+  for (int it = tid; it < CW * CB; it += NT) {
+    const int c = it % CW, b = it / CW;
+    float v[32];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const int row = 32 * b + r;
+      v[r] = row < rows_valid ? bf16_to_f32(stg[row * LDW + c]) : 0.f;
+    }
+    V16 out[2];
+    const uint32_t code = quantize_block(v, out);
+    V16* qp = reinterpret_cast<V16*>(o.q_cols + (size_t)(col0 + c) * P + qcol0 + 32 * b);
+    qp[0] = out[0];
+    qp[1] = out[1];
+    o.s_cols[4 * ((size_t)K * (qcol0 / 128) + col0 + c) + b] = static_cast<uint8_t>(code);
+  }
+}
+
 // Each 32x32 block of acc holds C^T (B fragment first): lane (lr, lk) has
 // tile row wm*WMR + mi*32 + lr and, for accumulator group g, the 4
 // consecutive columns 8g + 4lk .. +3 of block ni. Output columns are handled
@@ -27,9 +82,13 @@ MOE_DEV void dunpack4(uint2 p, float* v) {
 // over: this function begins with a barrier). rbase is the first output row
 // of the tile (permuted row, or weight row for the weight gradients) and n0
 // its first output column; rows_valid rows are written.
+// qcol0: token column of the tile's first row in the column orientation of
+// the MXFP8 copies (the expert's first padded column plus the tile's first
+// row within the expert), used when a.mxo is set.
 template <int OP, class C>
 MOE_DEV void gg_store_tile(const GGArgs& a, const df32x16_t (&acc)[C::MI][C::NI], uint16_t* lds, int e,
-                           size_t rbase, int n0, int rows_valid, int wm, int wn, int lane, int tid) {
+                           size_t rbase, int n0, int rows_valid, int wm, int wn, int lane, int tid,
+                           int qcol0 = 0) {
   using I = OpInfo<OP>;
   constexpr bool DUAL = I::kDual;
   constexpr int MI = C::MI, NI = C::NI, NT = C::NT, BM = C::BM, BN = C::BN;
@@ -114,7 +173,15 @@ MOE_DEV void gg_store_tile(const GGArgs& a, const df32x16_t (&acc)[C::MI][C::NI]
         unpack(uv, uf);
 #pragma unroll
         for (int i = 0; i < 8; ++i) hf[i] = gf[i] * uf[i] / (1.0f + expf(-gf[i]));
-        *reinterpret_cast<V16*>(outh + o) = pack(hf);
+        const V16 hv = pack(hf);
+        *reinterpret_cast<V16*>(outh + o) = hv;
+        // H replaces G in the staging plane (this thread's chunk only) for
+        // the MXFP8 copies below
+        *reinterpret_cast<V16*>(stg0 + r * LDW + c * 8) = hv;
+      }
+      if (a.mxo[0].q_rows != nullptr) {
+        __syncthreads();
+        mx_quantize_plane<C>(stg0, a.mxo[0], rbase, rows_valid, n0, F, a.n_rows, a.mx_P, qcol0, tid);
       }
     } else {
       store_plane(stg0, (uint16_t*)a.dw_gate + e * dF + rbase * F + n0, F, 0);
@@ -151,6 +218,10 @@ MOE_DEV void gg_store_tile(const GGArgs& a, const df32x16_t (&acc)[C::MI][C::NI]
       __syncthreads();
       store_plane(stg0, (uint16_t*)a.dg + rbase * F + n0, F, ch);
       store_plane(stg1, (uint16_t*)a.du + rbase * F + n0, F, ch);
+      if (a.mxo[0].q_rows != nullptr) {   // MXFP8 copies of this column chunk of dG and dU
+        mx_quantize_plane<C>(stg0, a.mxo[0], rbase, rows_valid, n0 + ch * CW, F, a.n_rows, a.mx_P, qcol0, tid);
+        mx_quantize_plane<C>(stg1, a.mxo[1], rbase, rows_valid, n0 + ch * CW, F, a.n_rows, a.mx_P, qcol0, tid);
+      }
       __syncthreads();
     }
   } else {

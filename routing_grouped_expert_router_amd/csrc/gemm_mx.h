@@ -101,6 +101,7 @@ __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_mx_kernel(MxArgs 
   constexpr int MI = C::MI, NI = C::NI;
   constexpr int BNO = DUAL ? BN / 2 : BN;          // output columns per matrix per tile
   static_assert(S - 2 <= 2, "wait_stages covers up to two stages in flight");
+  static_assert(KVAR || BM == 128, "the MXFP8 copies' column tiles are the 128-row m-tiles");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
   int* tile_start = reinterpret_cast<int*>(lds);    // used before the ring, then overwritten
 
@@ -332,8 +333,10 @@ __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_mx_kernel(MxArgs 
       }
     }
 
+    // the row-varying ops receive in p_e the column-orientation token column
+    // of their first row (for the MXFP8 copies the epilogue may write)
     gg_store_tile<OP, C>(a, acc, reinterpret_cast<uint16_t*>(lds), e, KVAR ? (size_t)m0 : (size_t)row0, n0, mv,
-                         wm, wn, lane, tid);
+                         wm, wn, lane, tid, KVAR ? 0 : p_e);
   };
 
   if constexpr (!KVAR) {
@@ -341,8 +344,14 @@ __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_mx_kernel(MxArgs 
     const int b = xcd_tile(blockIdx.x, gridDim.x, build_tile_prefix<BM, NT>(a, tile_start) * tilesN);
     if (b < 0) return;
     if (!m_tile_grouped<BM>(a, b, tilesN, tile_start, e, row0, mv, tn)) return;
+    // token column of the tile's first row in the column orientation: the
+    // expert's first padded column (128 per m-tile of the experts before it,
+    // BM = 128) plus the row's offset within the expert
+    int r0e, ne;
+    group_rows(a, e, r0e, ne);
+    const int qcol0 = 128 * tile_start[e] + (row0 - r0e);
     __syncthreads();   // every wave is past its reads of tile_start before the ring is filled
-    run_tile(e, row0, mv, op_k(OP, d, F), 0, tn, 0);
+    run_tile(e, row0, mv, op_k(OP, d, F), 0, tn, qcol0);
   } else {
     // the workspace holds the launch's tile split (wgrad_tiles) and each
     // expert's first padded token column (gg_mx_wgrad_split_kernel)

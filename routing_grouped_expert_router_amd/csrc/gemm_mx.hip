@@ -88,7 +88,18 @@ extern "C" int moe_grouped_gemm_mx(const moe_mx_gg_desc* g, hipStream_t stream) 
       MOE_CHECK_ARG(!rows || (tensor_ok(g->a0) && tensor_ok(g->b0) && tensor_ok(g->b1)));
       MOE_CHECK_ARG(out_ok(g->out0) && out_ok(g->out1));
   }
-  if (kvar) {
+  // MXFP8 copies written by the epilogue: H (FWD_GATE_UP) or dG and dU
+  // (DGRAD_DOWN), each in both orientations, all given or none
+  auto set = [](const moe_mx_tensor& t) { return t.q != nullptr || t.s != nullptr; };
+  const int n_qo = (g->op == MOE_GG_FWD_GATE_UP) ? 1 : (g->op == MOE_GG_DGRAD_DOWN ? 2 : 0);
+  const bool qo = set(g->qo0_rows) || set(g->qo0_cols) || set(g->qo1_rows) || set(g->qo1_cols);
+  if (qo) {
+    MOE_CHECK_ARG(n_qo > 0);
+    MOE_CHECK_ARG(tensor_ok(g->qo0_rows) && tensor_ok(g->qo0_cols));
+    if (n_qo == 2) MOE_CHECK_ARG(tensor_ok(g->qo1_rows) && tensor_ok(g->qo1_cols));
+    else MOE_CHECK_ARG(!set(g->qo1_rows) && !set(g->qo1_cols));
+  }
+  if (kvar || qo) {
     MOE_CHECK_ARG(g->col_stride > 0 && g->col_stride % 128 == 0);
     MOE_CHECK_ARG(g->col_stride >= 128L * ((g->n_rows + 127L) / 128 + E));
     const long cs = (long)(d > F ? d : F) * g->col_stride;
@@ -120,6 +131,15 @@ extern "C" int moe_grouped_gemm_mx(const moe_mx_gg_desc* g, hipStream_t stream) 
   put(g->b1, x.bq[1], x.bs[1]);
   x.P = g->col_stride;
   x.o.split = ws_need > 0 ? static_cast<const int*>(g->ws) : nullptr;
+  if (qo) {
+    auto out = [](const moe_mx_tensor& r, const moe_mx_tensor& c) {
+      return MxQOut{static_cast<uint8_t*>(const_cast<void*>(r.q)), static_cast<uint8_t*>(const_cast<void*>(r.s)),
+                    static_cast<uint8_t*>(const_cast<void*>(c.q)), static_cast<uint8_t*>(const_cast<void*>(c.s))};
+    };
+    x.o.mxo[0] = out(g->qo0_rows, g->qo0_cols);
+    if (n_qo == 2) x.o.mxo[1] = out(g->qo1_rows, g->qo1_cols);
+    x.o.mx_P = g->col_stride;
+  }
 
   const bool dual = g->op == MOE_GG_FWD_GATE_UP || g->op == MOE_GG_WGRAD_GATE_UP;
   const int N = op_n(g->op, g->d, g->F);

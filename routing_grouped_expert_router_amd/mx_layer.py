@@ -146,11 +146,11 @@ class MxExperts:
         """The forward GEMMs once xq and x_c hold the quantised rows and the
         weights are quantised (the routed layer fills xq and x_c in its
         permute)."""
+        # the epilogue also writes H quantised in both orientations (for the
+        # down projection and its weight gradient)
         self._gg(L.MOE_GG_FWD_GATE_UP, a0=self.xq.t, b0=self.wg_c.t, b1=self.wu_c.t,
-                 out0=self.g, out1=self.u, out2=self.h)
+                 out0=self.g, out1=self.u, out2=self.h, qo0_rows=self.hq.t, qo0_cols=self.h_c.t)
         self._mark("mx_fwd_gate_up")
-        self._both(self.h, self.hq, self.h_c)
-        self._mark("mx_quantize_h")
         self._gg(L.MOE_GG_FWD_DOWN, a0=self.hq.t, b0=self.wd_c.t, out0=self.y_perm)
         self._mark("mx_fwd_down")
         return self.y_perm
@@ -161,16 +161,16 @@ class MxExperts:
         return self.dx_perm
 
     def backward_data(self, dy_perm):
-        """Quantises dY and dG/dU (both orientations: the weight gradients
-        read the token columns later) and runs the two data-gradient GEMMs."""
+        """Quantises dY (both orientations: the weight gradients read the
+        token columns later) and runs the two data-gradient GEMMs; the first
+        one's epilogue writes dG and dU already quantised in both orientations."""
         self._both(dy_perm, self.dyq, self.dy_c)
         self._mark("mx_quantize_dy")
+        # the epilogue also writes dG and dU quantised in both orientations
         self._gg(L.MOE_GG_DGRAD_DOWN, a0=self.dyq.t, b0=self.wd_r.t, g=self.g, u=self.u,
-                 out0=self.dg, out1=self.du)
+                 out0=self.dg, out1=self.du, qo0_rows=self.dgq.t, qo0_cols=self.dg_c.t,
+                 qo1_rows=self.duq.t, qo1_cols=self.du_c.t)
         self._mark("mx_dgrad_down")
-        self._both(self.dg, self.dgq, self.dg_c)
-        self._both(self.du, self.duq, self.du_c)
-        self._mark("mx_quantize_dg_du")
         self._gg(L.MOE_GG_DGRAD_GATE_UP, a0=self.dgq.t, a1=self.duq.t, b0=self.wg_r.t, b1=self.wu_r.t,
                  out0=self.dx_perm)
         self._mark("mx_dgrad_gate_up")

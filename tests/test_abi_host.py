@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 def test_binding_covers_every_declared_symbol():
     assert sorted(L.SIGNATURES) == declared()
     lib = L.lib()
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(-3) == b"workspace missing or too small"
     assert lib.moe_status_string(12345) == b"unknown status"
@@ -50,7 +50,8 @@ def test_desc_layout_matches_header():
     assert C.sizeof(L.moe_gg_desc) == 7 * 4 + 4 + 8 * 17 + 8
     # int op..col_stride (6), group_offsets, 4 (codes, scales) pairs, g, u, 3 outputs
     assert C.sizeof(L.moe_mx_tensor) == 16
-    assert C.sizeof(L.moe_mx_gg_desc) == 6 * 4 + 8 + 4 * 16 + 5 * 8 + 2 * 8
+    # ... then ws, ws_bytes and the four epilogue-quantised (codes, scales) pairs
+    assert C.sizeof(L.moe_mx_gg_desc) == 6 * 4 + 8 + 4 * 16 + 5 * 8 + 2 * 8 + 4 * 16
     assert L.moe_mx_gg_desc.a0.offset == 32 and L.moe_mx_gg_desc.g.offset == 96
 
 
@@ -327,3 +328,40 @@ def test_offsets_noalloc_argument_errors():
     assert f(600000, 4, 128) == UNSUPPORTED              # histogram beyond the static array
     assert f(300000, 1, 1024) == UNSUPPORTED
     assert lib.moe_offsets_noalloc(FAKE, 10, 2, 8, 0, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+
+
+def test_mx_gemm_epilogue_copies_argument_errors():
+    """MXFP8 copies from the epilogue: only the forward gate/up (H) and the
+    data-gradient down (dG, dU) take them, all of the op's pairs or none,
+    with a valid token-column stride."""
+    lib = L.lib()
+    call = lambda d: lib.moe_grouped_gemm_mx(C.byref(d), None)
+    E, d_, F, n = 4, 256, 256, 64
+    P = 128 * (1 + E)
+
+    def mk(op):
+        desc = L.make_mx_gg_desc(op, E, d_, F, n, None, P)
+        desc.group_offsets = FAKE
+        for name in ("a0", "a1", "b0", "b1"):
+            getattr(desc, name).q, getattr(desc, name).s = FAKE, FAKE
+        desc.g, desc.u, desc.out0, desc.out1, desc.out2 = FAKE, FAKE, FAKE, FAKE, FAKE
+        return desc
+
+    d = mk(L.MOE_GG_FWD_DOWN)
+    d.qo0_rows.q, d.qo0_rows.s, d.qo0_cols.q, d.qo0_cols.s = FAKE, FAKE, FAKE, FAKE
+    assert call(d) == INVALID                            # an op without an epilogue copy
+    d = mk(L.MOE_GG_FWD_GATE_UP)
+    d.qo0_rows.q, d.qo0_rows.s = FAKE, FAKE
+    assert call(d) == INVALID                            # columns missing
+    d.qo0_cols.q, d.qo0_cols.s = FAKE, FAKE
+    d.qo1_rows.q = FAKE
+    assert call(d) == INVALID                            # a second matrix the op does not have
+    d = mk(L.MOE_GG_DGRAD_DOWN)
+    d.qo0_rows.q, d.qo0_rows.s, d.qo0_cols.q, d.qo0_cols.s = FAKE, FAKE, FAKE, FAKE
+    assert call(d) == INVALID                            # dU's copies missing
+    d.qo1_rows.q, d.qo1_rows.s, d.qo1_cols.q, d.qo1_cols.s = FAKE, FAKE, FAKE, FAKE
+    d.col_stride = 128 * E                               # below the stride bound
+    assert call(d) == INVALID
+    d.col_stride = P
+    d.qo1_cols.s = FAKE + 1                              # misaligned scales
+    assert call(d) == INVALID

@@ -256,6 +256,44 @@ def test_mx_expert_layer_parity(counts, d, F):
 
 
 
+@pytest.mark.parametrize("counts,d,F", [([0, 37, 300, 129], 256, 256),
+                                        ([5, 0, 0, 70, 3, 250, 64, 131], 256, 768)])
+def test_mx_epilogue_quantised_copies_bitwise(counts, d, F):
+    """The forward gate/up epilogue writes H, and the data-gradient down
+    epilogue dG and dU, already MXFP8-quantised in both orientations (rows:
+    blocks along F; columns: blocks along each expert's rows, each expert's
+    segment padded to 128 columns). Every code and scale byte equals the
+    oracle's quantiser applied to the GPU's own bf16 outputs."""
+    x, dy, cnt, wg, wu, wd = _layer_inputs(13, counts, d, F)
+    n, E = x.shape[0], len(counts)
+    off = np.zeros(E + 1, dtype=np.int32)
+    off[1:] = np.cumsum(cnt)
+    b = lambda a: dev(f64_to_bf16_bits(a), "bf16")
+    lay = MxExperts(n, d, E, F)
+    sentinel = 0x5A
+    for t in (lay.hq, lay.h_c, lay.dgq, lay.dg_c, lay.duq, lay.du_c):
+        t.q.fill_(sentinel)
+        t.s.fill_(sentinel)
+    lay.forward(b(x), dev(off, "i32"), b(wg), b(wu), b(wd))
+    lay.backward(b(dy))
+    torch.cuda.synchronize()
+    for name, src, rows_t, cols_t in (("H", lay.h, lay.hq, lay.h_c), ("dG", lay.dg, lay.dgq, lay.dg_c),
+                                      ("dU", lay.du, lay.duq, lay.du_c)):
+        v = host(src)
+        rq, rs = mx_quantize(v)
+        assert np.array_equal(host(rows_t.q), rq), name
+        assert np.array_equal(host(rows_t.s), grouped_scales(rs)), name
+        eq, es = _expected_cols(v, off[:-1], cnt, lay.P, sentinel)
+        got_q, got_s = host(cols_t.q), host(cols_t.s)
+        # the column segments of the experts are written; columns past the
+        # last expert's segment are not
+        span = 128 * int(np.sum(-(-cnt // 128)))
+        assert np.array_equal(got_q[:, :span], eq[:, :span]), name
+        # scale words of the column groups inside the segments come first in
+        # the grouped layout (byte 4 * (F * group + row) + block % 4)
+        assert np.array_equal(got_s[:F * span // 32], grouped_scales(es)[:F * span // 32]), name
+
+
 def _isolated_ops(x, dy, counts, wg, wu, wd, ref):
     """Each grouped GEMM on its own, fed the oracle's bf16 inputs (x, dy and
     the oracle's own G, U, H, dG, dU): quantised on the GPU, multiplied on the
