@@ -226,9 +226,9 @@ __global__ void __launch_bounds__(256) mx_cols_kernel(const uint16_t* __restrict
 
 // ------------------------------------------------------------------ both
 // One pass, both orientations: a 128-row x 128-column tile of one group is
-// staged once; the column part writes the transposed codes as above, and the
-// row part quantises each valid row's 128 values (four blocks, one scale word)
-// into the row-oriented output. Workgroups are persistent: each takes a
+// staged once; the column part (cols_quads) writes the transposed codes, and
+// the row part quantises each valid row's 128 values (four blocks, one scale
+// word) into the row-oriented output. Workgroups are persistent: each takes a
 // contiguous run of tiles and holds the next tile's loads in registers while
 // it quantises the current one, so load latency overlaps the work.
 constexpr int kBCols = 128, kBLdw = kBCols + 8;
@@ -339,13 +339,53 @@ MOE_DEV void fetch_tile(const uint16_t* __restrict__ src, int cols, const BothTi
   }
 }
 
+// Column part of the two-orientation pass: thread (quad of 4 columns, block b,
+// half h) reads 16 rows x 4 columns of the staged tile with 8-byte LDS reads
+// (a quarter of the LDS reads of cols_part), the two halves of a block combine
+// their column maxima with one lane shuffle, each thread encodes its 16 rows
+// of 4 columns (one 16-byte store per output row) and the first half stores
+// the block's four scale bytes.
+MOE_DEV void cols_quads(const uint16_t* tile, int c0, int cols, long p_g, int row_in, int col_stride,
+                        uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  const int tid = threadIdx.x;
+  const int h = tid & 1, b = (tid >> 1) & 3, qd = tid >> 3;   // 32 quads x 4 blocks x 2 halves
+  float v[16][4];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const uint2 w = *reinterpret_cast<const uint2*>(tile + (32 * b + 16 * h + r) * kBLdw + 4 * qd);
+    v[r][0] = __uint_as_float(w.x << 16);
+    v[r][1] = __uint_as_float(w.x & 0xffff0000u);
+    v[r][2] = __uint_as_float(w.y << 16);
+    v[r][3] = __uint_as_float(w.y & 0xffff0000u);
+  }
+  float amax[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) amax[j] = fmaxf(amax[j], fabsf(v[r][j]));
+  const size_t col = static_cast<size_t>(p_g) + row_in + 32 * b + 16 * h;   // first token column
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float m = fmaxf(amax[j], __shfl_xor(amax[j], 1, 64));
+    const int x = mx_exponent(m);
+    const float inv = pow2(-x);
+    V16 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      out.w[w] = e4m3_word(v[4 * w][j], v[4 * w + 1][j], v[4 * w + 2][j], v[4 * w + 3][j], inv);
+    const int c = 4 * qd + j;
+    *reinterpret_cast<V16*>(q + static_cast<size_t>(c0 + c) * col_stride + col) = out;
+    if (h == 0)
+      s[4 * (static_cast<size_t>(cols) * ((p_g + row_in) / kQRows) + c0 + c) + b] = static_cast<uint8_t>(x + 127);
+  }
+}
+
 __global__ void __launch_bounds__(256) mx_both_kernel(const uint16_t* __restrict__ src, int rows, int cols,
                                                       Groups1 gr, int col_stride, uint8_t* __restrict__ q_rows,
                                                       uint8_t* __restrict__ s_rows, uint8_t* __restrict__ q_cols,
                                                       uint8_t* __restrict__ s_cols, RowGather rg) {
   __shared__ int tile_start[MOE_MAX_EXPERTS + 1];
   __shared__ __attribute__((aligned(16))) uint16_t tile[kQRows * kBLdw];
-  __shared__ uint32_t words[64];
   const int tid = threadIdx.x;
   const int tiles_c = cols / kBCols;
   const int total_rt = build_tile_prefix(gr, tile_start);
@@ -399,9 +439,7 @@ __global__ void __launch_bounds__(256) mx_both_kernel(const uint16_t* __restrict
                 pair | (other << 16);
         }
       }
-      // columns, 64 at a time
-      cols_part<kBLdw>(tile, 0, c0, cols, t.p_g, row_in, col_stride, q_cols, s_cols, words);
-      cols_part<kBLdw>(tile, 64, c0, cols, t.p_g, row_in, col_stride, q_cols, s_cols, words);
+      cols_quads(tile, c0, cols, t.p_g, row_in, col_stride, q_cols, s_cols);
     }
     __syncthreads();
   }
