@@ -231,13 +231,23 @@ int moe_router_gemm_bwd(int dtype, const void* x, const float* dlogits, int T, i
  * FMA kernel without this limit). The host cannot see the group
  * sizes: offsets must be non-decreasing with group_offsets[E] <= n_rows
  * (each group is clamped to [0, n_rows] on the device).
- * ws: at least moe_grouped_gemm_workspace_bytes(desc) bytes, 4-byte aligned,
- * device memory owned by the caller; MOE_ERR_WORKSPACE when missing, too
- * small or misaligned. The weight gradients over device-resident groups (capacity == 0)
- * need 64 bytes: the call writes there how the launch splits its tiles over
- * the chip, computed on the device from the group sizes (tiles of the experts
- * with the most rows carry the most work); the other ops need none. Calls
- * sharing one workspace must be ordered on one stream. */
+ * ws: moe_grouped_gemm_workspace_bytes(desc) bytes, 4-byte aligned,
+ * device memory owned by the caller. The weight gradients over
+ * device-resident groups (capacity == 0) need at least 64 bytes, 4-byte
+ * aligned (else MOE_ERR_WORKSPACE): the call writes there how the launch
+ * splits its tiles over the chip, computed on the device from the group sizes
+ * (tiles of the experts with the most rows carry the most work). A bf16
+ * matrix-core weight gradient with fewer than 512 output tiles (128 x 256
+ * outputs each; 128 x 128 per matrix for the gate/up pair, e.g. a shared
+ * expert, E == 1) would leave compute units idle: when the workspace holds
+ * the size this function reports and is 16-byte aligned, the call splits each
+ * expert's rows (K) into min(8, ceil(512 / tiles)) chunks of whole 32-row
+ * steps, writes each chunk's binary32 sums from byte 256 of the workspace
+ * ([chunk][E][M][N] floats, M x N the gradient's shape; the gate/up pair as
+ * one [d][2F] block) and adds the chunks in chunk order before one rounding
+ * to bf16, so the result is deterministic; with a workspace of 64 bytes up to
+ * that size the same call runs K unsplit. The other ops need no workspace.
+ * Calls sharing one workspace must be ordered on one stream. */
 typedef enum {
   MOE_GG_FWD_GATE_UP = 0,
   MOE_GG_FWD_DOWN = 1,

@@ -56,7 +56,7 @@ def stage_of(kernel):
     m = re.search(r"moe::gg_mx(?:_wgrad_split)?_kernel<(\d+),", kernel)
     if m:
         return "mx" + GG_OPS[int(m.group(1))][2:]
-    m = re.search(r"moe::gg_\w+_kernel<(\d+),", kernel)
+    m = re.search(r"moe::gg_\w+_kernel<(\d+)[,>]", kernel)
     if m:
         return GG_OPS[int(m.group(1))]
     if re.search(r"moe::(\(anonymous namespace\)::)?mx_(both|rows|cols)_kernel", kernel):

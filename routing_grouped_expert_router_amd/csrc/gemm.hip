@@ -207,6 +207,12 @@ template <class C> struct Dma {
   };
 };
 
+template <int OP> struct SplitReduce {
+  static void go(const GGArgs& a, int grid, hipStream_t s) {
+    if constexpr (OpInfo<OP>::kKVar) gg_splitk_reduce_kernel<OP><<<grid, 256, 0, s>>>(a);
+  }
+};
+
 template <class C> struct DmaSplit {
   template <int OP> struct Launch {
     static void go(const GGArgs& a, int grid, hipStream_t s) {
@@ -223,7 +229,12 @@ int launch_dma(const moe_gg_desc* g, const GGArgs& a, bool kvar, bool dual, int 
   if (kvar) grid = (long)g->E * (op_wgrad_m(g->op, g->d, g->F) / C::BM) * (N / bno);
   else grid = ((g->n_rows + C::BM - 1) / C::BM + g->E) * (long)(N / bno);
   if (grid == 0) return MOE_OK;
-  MOE_CHECK_SUPPORTED(grid < (1L << 31));
+  MOE_CHECK_SUPPORTED(grid * (a.ksplit > 1 ? a.ksplit : 1) < (1L << 31));
+  if (a.ksplit > 1) {   // K split into chunks, then the ordered reduction of their partial sums
+    const long nout = (long)g->E * op_wgrad_m(g->op, g->d, g->F) * N * (dual ? 2 : 1);
+    if (int st = dispatch_op<Dma<C>::template Launch>(g->op, a, static_cast<int>(grid * a.ksplit), stream)) return st;
+    return dispatch_op<SplitReduce>(g->op, a, static_cast<int>((nout / 8 + 255) / 256), stream);
+  }
   if (kvar && a.split) {   // the launch's tile split, from the device-resident group sizes
     if (int st = dispatch_op<DmaSplit<C>::template Launch>(g->op, a, static_cast<int>(grid), stream)) return st;
   }
@@ -250,10 +261,38 @@ long cdiv(long a, long b) { return (a + b - 1) / b; }
 constexpr size_t kSplitBytes = 64;
 static_assert(kSplitInts * sizeof(int) <= kSplitBytes, "split fits the workspace");
 
+// A weight-gradient launch of fewer tiles than this leaves CUs idle (two
+// workgroups fit on each of the 256 CUs): its K (the expert's rows) is split
+// into up to kMaxKSplit chunks whose binary32 partial sums start at byte
+// kPartialOffset of the workspace.
+constexpr long kSplitKTiles = 512;
+constexpr int kMaxKSplit = 8;
+constexpr size_t kPartialOffset = 256;
+
+namespace {
+bool is_kvar(int op) { return op == MOE_GG_WGRAD_DOWN || op == MOE_GG_WGRAD_GATE_UP; }
+
+// K chunks of a weight-gradient launch (1: not split).
+int wgrad_ksplit(const moe_gg_desc* g) {
+  if (!is_kvar(g->op) || g->capacity != 0 || !mfma_ok(g)) return 1;
+  const int bno = g->op == MOE_GG_WGRAD_GATE_UP ? CfgDma::BN / 2 : CfgDma::BN;
+  const long tiles = (long)g->E * (op_wgrad_m(g->op, g->d, g->F) / CfgDma::BM) * (op_n(g->op, g->d, g->F) / bno);
+  if (tiles >= kSplitKTiles) return 1;
+  const long ks = (kSplitKTiles + tiles - 1) / tiles;
+  return ks > kMaxKSplit ? kMaxKSplit : static_cast<int>(ks);
+}
+
+size_t splitk_bytes(const moe_gg_desc* g, int ks) {
+  const size_t np = (size_t)op_n(g->op, g->d, g->F) * (g->op == MOE_GG_WGRAD_GATE_UP ? 2 : 1);
+  return (size_t)ks * g->E * op_wgrad_m(g->op, g->d, g->F) * np * sizeof(float);
+}
+}  // namespace
+
 extern "C" size_t moe_grouped_gemm_workspace_bytes(const moe_gg_desc* desc) {
-  if (desc == nullptr) return 0;
-  const bool kvar = desc->op == MOE_GG_WGRAD_DOWN || desc->op == MOE_GG_WGRAD_GATE_UP;
-  return kvar && desc->capacity == 0 ? kSplitBytes : 0;
+  if (desc == nullptr || !is_kvar(desc->op) || desc->capacity != 0) return 0;
+  if (desc->E < 1 || desc->d <= 0 || desc->F <= 0) return kSplitBytes;
+  const int ks = wgrad_ksplit(desc);
+  return ks > 1 ? kPartialOffset + splitk_bytes(desc, ks) : kSplitBytes;
 }
 
 extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
@@ -293,12 +332,20 @@ extern "C" int moe_grouped_gemm(const moe_gg_desc* g, hipStream_t stream) {
     default:
       MOE_CHECK_ARG(act(g->x_perm) && act(g->dg) && act(g->du) && need(g->dw_gate) && need(g->dw_up));
   }
-  const size_t ws_need = moe_grouped_gemm_workspace_bytes(g);
+  // the tile split needs kSplitBytes; a launch that would split K does so only
+  // when the workspace also holds the partial sums (16-byte aligned)
+  const size_t ws_need = kvar && g->capacity == 0 ? kSplitBytes : 0;
   if (ws_need > 0 && (g->ws == nullptr || g->ws_bytes < ws_need || !aligned4(g->ws))) return MOE_ERR_WORKSPACE;
+  int ksplit = wgrad_ksplit(g);
+  if (ksplit > 1 && (g->ws_bytes < kPartialOffset + splitk_bytes(g, ksplit) || !aligned16(g->ws))) ksplit = 1;
   GGArgs a{g->op, g->E, g->d, g->F, g->n_rows, g->capacity, g->group_offsets,
            g->x_perm, g->g, g->u, g->h, g->y_perm, g->dy_perm, g->dg, g->du, g->dx_perm,
            g->w_gate, g->w_up, g->w_down, g->dw_gate, g->dw_up, g->dw_down,
            ws_need > 0 ? static_cast<const int*>(g->ws) : nullptr};
+  if (ksplit > 1) {
+    a.partial = reinterpret_cast<float*>(static_cast<char*>(g->ws) + kPartialOffset);
+    a.ksplit = ksplit;
+  }
   const bool dual = g->op == MOE_GG_FWD_GATE_UP || g->op == MOE_GG_WGRAD_GATE_UP;
   const int N = op_n(g->op, g->d, g->F);
   if (mfma_ok(g)) {

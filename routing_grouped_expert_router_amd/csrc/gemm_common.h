@@ -42,6 +42,11 @@ struct GGArgs {
   // stride of the column orientation; unused (null) elsewhere
   MxQOut mxo[2];
   int mx_P;
+  // weight gradients with K split over ksplit > 1 chunks: binary32 partial
+  // sums [ksplit][E][M][NP] (NP = N, or 2N for gate then up), reduced in a
+  // fixed order by gg_splitk_reduce_kernel; null and 0 otherwise
+  float* partial;
+  int ksplit;
 };
 
 // Static shape of each op as C[M x N] = sum_k A[m, k] B[k, n] per expert.

@@ -127,7 +127,7 @@ __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_dma_kernel(GGArgs
   const int N = op_n(OP, d, F);
   const int tilesN = N / BNO;
   // one output tile: (expert, first row or weight row, valid rows, K, m0, n-tile)
-  auto run_tile = [&](int e, int row0, int mv, int K, int m0, int tn) {
+  auto run_tile = [&](int e, int row0, int mv, int K, int m0, int tn, int kchunk = -1) {
     // the tile decode read LDS; its results are the same in every lane
     e = __builtin_amdgcn_readfirstlane(e);
     row0 = __builtin_amdgcn_readfirstlane(row0);
@@ -375,7 +375,8 @@ __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_dma_kernel(GGArgs
       }
     }
 
-    gg_store_tile<OP, C>(a, acc, lds, e, KVAR ? (size_t)m0 : (size_t)row0, n0, mv, wm, wn, lane, tid);
+    gg_store_tile<OP, C>(a, acc, lds, e, KVAR ? (size_t)m0 : (size_t)row0, n0, mv, wm, wn, lane, tid, 0,
+                         kchunk);
   };
 
   if constexpr (!KVAR) {
@@ -387,6 +388,21 @@ __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_dma_kernel(GGArgs
     // visited in order
     if (!m_tile_grouped<BM>(a, b, tilesN, tile_start, e, row0, mv, tn)) return;
     run_tile(e, row0, mv, op_k(OP, d, F), 0, tn);
+  } else if (a.ksplit > 1) {
+    // K split: workgroup b takes chunk c of tile t, chunk-major (the tiles of
+    // one chunk, which read the same rows, run side by side on an XCD); the
+    // chunk is a run of whole K steps of the expert's rows
+    const int tpe = (op_wgrad_m(OP, d, F) / BM) * tilesN;
+    const int tiles = a.E * tpe;
+    const int b = xcd_remap(blockIdx.x, gridDim.x);
+    const int c = b / tiles, t = b % tiles;
+    if (c >= a.ksplit) return;
+    const int e = t / tpe;
+    int row0, K;
+    group_rows(a, e, row0, K);
+    const int per = ((K + BK - 1) / BK + a.ksplit - 1) / a.ksplit * BK;
+    const int k0 = min(K, c * per), k1 = min(K, k0 + per);
+    run_tile(e, row0 + k0, BM, k1 - k0, ((t % tpe) / tilesN) * BM, t % tilesN, c);
   } else {
     const int tpe = (op_wgrad_m(OP, d, F) / BM) * tilesN;
     // The equal-count tile's group rows are fetched together with the split
@@ -410,6 +426,33 @@ __global__ void __launch_bounds__(C::NT, C::WAVES_PER_SIMD) gg_dma_kernel(GGArgs
       group_rows(a, e, row0, K);
     }
   }
+}
+
+// Sum of the K chunks' binary32 partials of a split weight gradient, in
+// chunk order (deterministic), rounded once to bf16: thread i takes the 8
+// consecutive outputs 8i..8i+7 of the [E][M][NP] result.
+template <int OP>
+__global__ void __launch_bounds__(256) gg_splitk_reduce_kernel(GGArgs a) {
+  constexpr bool DUAL = OpInfo<OP>::kDual;
+  const int M = op_wgrad_m(OP, a.d, a.F), Nn = op_n(OP, a.d, a.F), NP = DUAL ? 2 * Nn : Nn;
+  const size_t per = (size_t)a.E * M * NP;
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= per) return;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < a.ksplit; ++c) {
+    const float4* p = reinterpret_cast<const float4*>(a.partial + (size_t)c * per + i);
+    const float4 v0 = p[0], v1 = p[1];
+    s[0] += v0.x; s[1] += v0.y; s[2] += v0.z; s[3] += v0.w;
+    s[4] += v1.x; s[5] += v1.y; s[6] += v1.z; s[7] += v1.w;
+  }
+  const size_t e = i / ((size_t)M * NP), rem = i % ((size_t)M * NP);
+  const int m = (int)(rem / NP), n = (int)(rem % NP);
+  const size_t dF = (size_t)a.d * a.F;
+  uint16_t* out;
+  if (OP == MOE_GG_WGRAD_DOWN) out = (uint16_t*)a.dw_down + e * dF + (size_t)m * Nn + n;
+  else if (n < Nn) out = (uint16_t*)a.dw_gate + e * dF + (size_t)m * Nn + n;
+  else out = (uint16_t*)a.dw_up + e * dF + (size_t)m * Nn + (n - Nn);
+  *reinterpret_cast<V16*>(out) = pack(s);
 }
 
 // The tile split of one weight-gradient launch of nb workgroups (one

@@ -85,10 +85,13 @@ MOE_DEV void mx_quantize_plane(const uint16_t* stg, const MxQOut& o, size_t grow
 // qcol0: token column of the tile's first row in the column orientation of
 // the MXFP8 copies (the expert's first padded column plus the tile's first
 // row within the expert), used when a.mxo is set.
+// kchunk >= 0 (weight gradients with K split): the tile's binary32 sums over
+// its K chunk go to a.partial as they are, straight from the accumulators
+// (16-byte stores of four columns), for gg_splitk_reduce_kernel.
 template <int OP, class C>
 MOE_DEV void gg_store_tile(const GGArgs& a, const df32x16_t (&acc)[C::MI][C::NI], uint16_t* lds, int e,
                            size_t rbase, int n0, int rows_valid, int wm, int wn, int lane, int tid,
-                           int qcol0 = 0) {
+                           int qcol0 = 0, int kchunk = -1) {
   using I = OpInfo<OP>;
   constexpr bool DUAL = I::kDual;
   constexpr int MI = C::MI, NI = C::NI, NT = C::NT, BM = C::BM, BN = C::BN;
@@ -130,6 +133,24 @@ MOE_DEV void gg_store_tile(const GGArgs& a, const df32x16_t (&acc)[C::MI][C::NI]
   auto put4 = [&](uint16_t* stg, int row, int col, const float* v) {
     *reinterpret_cast<uint2*>(stg + row * LDW + col) = dpack4(v);
   };
+
+  if (I::kKVar && kchunk >= 0) {
+    const int M = op_wgrad_m(OP, d, F), Nn = op_n(OP, d, F), NP = DUAL ? 2 * Nn : Nn;
+    constexpr int NIH = DUAL ? NI / 2 : NI;   // column blocks per matrix
+    float* base = a.partial + ((size_t)kchunk * a.E + e) * (size_t)M * NP;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const size_t row = rbase + row_of_acc(mi);
+          const int col = (DUAL && ni >= NIH ? Nn : 0) + n0 + wcol0 + (ni % NIH) * 32 + 8 * g + 4 * lk;
+          *reinterpret_cast<float4*>(base + row * NP + col) =
+              make_float4(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2], acc[mi][ni][4 * g + 3]);
+        }
+    return;
+  }
 
   __syncthreads();   // every wave is done with the ring
 

@@ -85,10 +85,17 @@ class MoELayer:
         self.err_flag = torch.zeros(1, dtype=i32, device=dev)
         ws = max(L.moe_offsets_workspace_bytes(T, k, E), 16)
         self.ws_offsets = e((ws + 15) // 16 * 4, dt=i32)
-        # Grouped-GEMM workspace (the weight-gradient tile split); one buffer serves every
-        # launch because they all run in order on one stream.
-        wgrad = L.make_gg_desc(L.MOE_GG_WGRAD_GATE_UP, L.MOE_BF16, E, d, F, nr, 0)
-        self.ws_gg = e((max(L.moe_grouped_gemm_workspace_bytes(wgrad), 4) + 3) // 4, dt=i32)
+        # Grouped-GEMM workspace (the weight-gradient tile split, and the partial sums of a
+        # weight gradient whose K is split); one buffer, sized for the largest weight-gradient
+        # launch of the routed and the shared experts, serves every launch because they all
+        # run in order on one stream.
+        gdt = L.MOE_BF16 if dtype == torch.bfloat16 else L.MOE_F32
+        wsb = 4
+        for op in (L.MOE_GG_WGRAD_DOWN, L.MOE_GG_WGRAD_GATE_UP):
+            wsb = max(wsb, L.moe_grouped_gemm_workspace_bytes(L.make_gg_desc(op, gdt, E, d, F, nr, capacity)))
+            if shared_ff > 0:
+                wsb = max(wsb, L.moe_grouped_gemm_workspace_bytes(L.make_gg_desc(op, gdt, 1, d, shared_ff, T, 0)))
+        self.ws_gg = e((wsb + 15) // 16 * 4, dt=i32)
         self.has_bwd = backward
         if backward and routing == "learned":
             wsr = max(L.moe_router_bwd_workspace_bytes(T, d, E), 16)

@@ -144,7 +144,8 @@ def test_grouped_gemm_argument_errors():
 
 
 def test_grouped_gemm_workspace():
-    """Only weight gradients over device-resident groups need a workspace (their tile split)."""
+    """Only weight gradients over device-resident groups need a workspace (their tile split, and
+    the partial sums when their K is split)."""
     lib = L.lib()
     for op in (L.MOE_GG_FWD_GATE_UP, L.MOE_GG_FWD_DOWN, L.MOE_GG_DGRAD_DOWN, L.MOE_GG_DGRAD_GATE_UP):
         for cap in (0, 16):
@@ -154,13 +155,30 @@ def test_grouped_gemm_workspace():
         assert L.moe_grouped_gemm_workspace_bytes(L.make_gg_desc(op, L.MOE_BF16, 4, 256, 256, 64, 16)) == 0
         need = L.moe_grouped_gemm_workspace_bytes(L.make_gg_desc(op, L.MOE_BF16, 4, 256, 256, 64, 0))
         assert need >= 4 * 10 and need % 4 == 0
+    # K split: a launch of fewer than 512 tiles (128 x 256 outputs each, 128 x 128 per matrix for
+    # the gate/up pair) asks for min(8, ceil(512 / tiles)) binary32 partial copies of its result
+    # after 256 bytes; one of 512 tiles or more, or in binary32, asks for the tile split alone
+    for op, E, d, F, tiles in ((L.MOE_GG_WGRAD_DOWN, 1, 2048, 1024, 64),
+                               (L.MOE_GG_WGRAD_GATE_UP, 1, 2048, 1024, 128),
+                               (L.MOE_GG_WGRAD_DOWN, 4, 2048, 1024, 256),
+                               (L.MOE_GG_WGRAD_GATE_UP, 3, 512, 256, 24)):
+        m, n, np_ = (F, d, d) if op == L.MOE_GG_WGRAD_DOWN else (d, F, 2 * F)
+        assert tiles == E * (m // 128) * (n // (256 if op == L.MOE_GG_WGRAD_DOWN else 128))
+        ks = min(8, -(-512 // tiles))
+        got = L.moe_grouped_gemm_workspace_bytes(L.make_gg_desc(op, L.MOE_BF16, E, d, F, 1000, 0))
+        assert got == 256 + ks * E * m * np_ * 4, (op, E, got)
+        assert L.moe_grouped_gemm_workspace_bytes(L.make_gg_desc(op, L.MOE_F32, E, d, F, 1000, 0)) == 64
+    for op in (L.MOE_GG_WGRAD_DOWN, L.MOE_GG_WGRAD_GATE_UP):
+        assert L.moe_grouped_gemm_workspace_bytes(L.make_gg_desc(op, L.MOE_BF16, 8, 2048, 1024, 1000, 0)) == 64
+        assert L.moe_grouped_gemm_workspace_bytes(L.make_gg_desc(op, L.MOE_BF16, 128, 2048, 1024, 1000, 0)) == 64
     assert lib.moe_grouped_gemm_workspace_bytes(None) == 0
     d = L.make_gg_desc(L.MOE_GG_WGRAD_DOWN, L.MOE_BF16, 4, 256, 256, 64, 0)
     d.group_offsets, d.h, d.dy_perm, d.dw_down = FAKE, FAKE, FAKE, FAKE
     call = lambda d: lib.moe_grouped_gemm(C.byref(d), None)
     assert call(d) == WORKSPACE                          # no workspace
-    d.ws, d.ws_bytes = FAKE, need - 4
-    assert call(d) == WORKSPACE                          # too small
+    d.ws, d.ws_bytes = FAKE, 60
+    assert call(d) == WORKSPACE                          # too small for the tile split (a workspace
+                                                         # of 64 bytes up to `need` runs K unsplit)
     d.ws, d.ws_bytes = FAKE + 2, need
     assert call(d) == WORKSPACE                          # misaligned
 
@@ -231,8 +249,9 @@ def test_mx_gemm_workspace():
     d.a0.q, d.a0.s, d.b0.q, d.b0.s = FAKE, FAKE, FAKE, FAKE
     need = 4 * (4 + 16)
     assert call(d) == WORKSPACE                          # no workspace
-    d.ws, d.ws_bytes = FAKE, need - 4
-    assert call(d) == WORKSPACE                          # too small
+    d.ws, d.ws_bytes = FAKE, 60
+    assert call(d) == WORKSPACE                          # too small for the tile split (a workspace
+                                                         # of 64 bytes up to `need` runs K unsplit)
     d.ws, d.ws_bytes = FAKE + 2, need
     assert call(d) == WORKSPACE                          # misaligned
 

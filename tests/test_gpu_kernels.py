@@ -332,7 +332,13 @@ def _gg_case(kind, counts, d, F, seed, capacity=0):
     ("bf16", [0, 4000, 1, 0, 17, 2000, 0, 0, 3, 900], 512, 256, 0),  # strongly skewed
     ("bf16", [(7 * i) % 5 for i in range(600)], 256, 256, 0),        # > 512 experts: two per prefix thread
 ])
-def test_grouped_gemm_parity(kind, counts, d, F, capacity):
+@pytest.mark.parametrize("ws_kind", ["tile_split", "sized"])
+def test_grouped_gemm_parity(kind, counts, d, F, capacity, ws_kind):
+    """ws_kind "tile_split": a 64-byte workspace (weight gradients unsplit in
+    K); "sized": the workspace the library asks for, so launches of few tiles
+    split K into chunks and reduce their partial sums."""
+    if ws_kind == "sized" and (kind != "bf16" or capacity):
+        pytest.skip("K is split only for bf16 weight gradients over device-resident groups")
     rng, E, n_rows, groups, st, T, grp = _gg_case(kind, counts, d, F, hash((tuple(counts), d, F)) % 1000, capacity)
     dt = torch.bfloat16 if kind == "bf16" else torch.float32
     code = L.MOE_BF16 if kind == "bf16" else L.MOE_F32
@@ -343,7 +349,11 @@ def test_grouped_gemm_parity(kind, counts, d, F, capacity):
     x, dyp = T["x_perm"], T["dy_perm"]
     wg, wu, wd = T["w_gate"], T["w_up"], T["w_down"]
 
-    ws = torch.zeros(16, dtype=torch.int32, device="cuda")
+    wsb = 64
+    if ws_kind == "sized":
+        wsb = max(L.moe_grouped_gemm_workspace_bytes(L.make_gg_desc(op, code, E, d, F, n_rows, capacity))
+                  for op in (L.MOE_GG_WGRAD_DOWN, L.MOE_GG_WGRAD_GATE_UP))
+    ws = torch.zeros(wsb // 4, dtype=torch.int32, device="cuda")
 
     def run(op, **kw):
         L.moe_grouped_gemm(L.make_gg_desc(op, code, E, d, F, n_rows, capacity, grp, ws=ws, **kw))
@@ -413,6 +423,43 @@ def test_wgrad_tile_split(counts, d, F):
         assert got[0] == 1     # the skewed case takes the balanced split
     if counts == [512] * 16:
         assert got[0] == 0
+
+
+@pytest.mark.parametrize("counts,d,F", [
+    ([16384], 1024, 512),          # a shared expert: one group of every token
+    ([3000, 0, 77], 512, 256),     # an empty expert and chunks past its rows
+])
+def test_wgrad_split_k(counts, d, F):
+    """Weight gradients of few tiles split K into chunks: the result matches
+    the oracle, is bitwise the same on a second run (the partial sums are
+    reduced in chunk order), and a 64-byte workspace still gives the unsplit
+    result to the same bar."""
+    E, n_rows = len(counts), int(sum(counts))
+    groups = [(int(o), int(c)) for o, c in zip(np.concatenate([[0], np.cumsum(counts)]), counts)]
+    grp = dev(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), "i32")
+    rng = _rng(11, n_rows)
+    mk = lambda *s: _to(rng.standard_normal(s), "bf16")
+    x, h, dy, dg, du = mk(n_rows, d), mk(n_rows, F), mk(n_rows, d), mk(n_rows, F), mk(n_rows, F)
+    st = storer("bf16")
+    dWd = om.expert_wgrad_down(h[1], dy[1], groups, F, d, st)
+    dWg, dWu = om.expert_wgrad_gate_up(x[1], dg[1], du[1], groups, d, F, st)
+    for op, kw, names, refs in (
+            (L.MOE_GG_WGRAD_DOWN, dict(h=h[0], dy_perm=dy[0]), ("dw_down",), (dWd,)),
+            (L.MOE_GG_WGRAD_GATE_UP, dict(x_perm=x[0], dg=dg[0], du=du[0]), ("dw_gate", "dw_up"), (dWg, dWu))):
+        need = L.moe_grouped_gemm_workspace_bytes(L.make_gg_desc(op, L.MOE_BF16, E, d, F, n_rows, 0))
+        assert need > 64, "this launch splits K"
+        results = []
+        for wsb in (need, need, 64):
+            ws = torch.full((wsb // 4,), -1, dtype=torch.int32, device="cuda")
+            outs = {n: torch.full((E,) + ref.shape[1:], float("nan"), dtype=torch.bfloat16, device="cuda")
+                    for n, ref in zip(names, refs)}
+            L.moe_grouped_gemm(L.make_gg_desc(op, L.MOE_BF16, E, d, F, n_rows, 0, grp, ws=ws, **kw, **outs))
+            torch.cuda.synchronize()
+            results.append([host(outs[n]) for n in names])
+            for n, ref in zip(names, refs):
+                assert_close(results[-1][names.index(n)], ref, "bf16", f"{n} ws={wsb}")
+        for a, b in zip(results[0], results[1]):
+            assert np.array_equal(a, b), "split K is deterministic"
 
 
 def test_grouped_gemm_rejects_bad_descriptors():

@@ -17,6 +17,7 @@ import torch
 
 import oracle.moe as om
 from moe_inputs import make_inputs, workload
+from routing_grouped_expert_router_amd import _lib as L
 from routing_grouped_expert_router_amd.layer import MoELayer
 
 from parity import assert_close, dev, host, values
@@ -44,8 +45,9 @@ def _run_gpu(wl, inp, capacity=0, backward=True, **opts):
     layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.float32 if kind == "f32" else torch.bfloat16,
                      routing="learned" if wl.routing == "learned" else "given", capacity=capacity,
                      backward=backward, **opts)
+    shared = {n: t[n] for n in ("w_gate_s", "w_up_s", "w_down_s") if n in t}
     layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], w_r=t.get("w_r"),
-                  topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"))
+                  topk_idx=t.get("topk_idx"), topk_w=t.get("topk_w"), **shared)
     if backward:
         layer.backward(t["dy"])
     torch.cuda.synchronize()
@@ -174,13 +176,23 @@ def test_full_e128_zipf_padded_and_dropless():
     assert np.array_equal(host(dropless.y)[whole], y_pad[whole])
 
 
-def test_deterministic_bitwise():
-    wl = workload("e128_uniform_bf16").scaled(T=4096)
+@pytest.mark.parametrize("shared_ff", [0, 1024])
+def test_deterministic_bitwise(shared_ff):
+    """Two runs of a step give the same bits. With a shared expert (one group
+    of every token) its weight gradients split K into chunks whose partial
+    sums are reduced in a fixed order; that workspace is in use here."""
+    wl = workload("e128_uniform_bf16").scaled(T=4096, shared_ff=shared_ff)
     inp = make_inputs(wl)
-    a, _ = _run_gpu(wl, inp)
-    snap = {n: host(getattr(a, n)).copy() for n in ("y", "dx", "dw_gate", "dw_up", "dw_down", "dtopk_w")}
+    a, _ = _run_gpu(wl, inp, shared_ff=shared_ff)
+    names = ["y", "dx", "dw_gate", "dw_up", "dw_down", "dtopk_w"]
+    if shared_ff:
+        names += ["dw_gate_s", "dw_up_s", "dw_down_s", "dx_s"]
+        need = L.moe_grouped_gemm_workspace_bytes(L.make_gg_desc(L.MOE_GG_WGRAD_GATE_UP, L.MOE_BF16, 1, wl.d,
+                                                                  shared_ff, wl.T, 0))
+        assert need > 64 and a.ws_gg.numel() * 4 >= need, "the shared expert's K is split"
+    snap = {n: host(getattr(a, n)).copy() for n in names}
     del a
-    b, _ = _run_gpu(wl, inp)
+    b, _ = _run_gpu(wl, inp, shared_ff=shared_ff)
     for n, v in snap.items():
         assert np.array_equal(host(getattr(b, n)), v), n
 
