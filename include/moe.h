@@ -72,7 +72,10 @@ int moe_abi_version(void);
  * The learned router of the pages' small configurations (bigchange.ai pt-BR,
  * "O que um engenheiro pode realmente testar").
  *   x [T,d] and w_r [d,E] of `dtype`; logits [T,E] binary32.
- *   Accumulation is binary32 in a fixed order. */
+ *   Accumulation is binary32 in a fixed order (the bf16 products are exact in
+ *   binary32). bf16 with E in {8, 16}, d % 256 == 0, d * E <= 32768 and w_r
+ *   16-byte aligned runs on the matrix cores; the other shapes on FMA
+ *   kernels with another (fixed) summation order. */
 int moe_router_gemm(int dtype, const void* x, const void* w_r, int T, int d, int E,
                     float* logits, hipStream_t stream);
 
@@ -189,7 +192,11 @@ int moe_route_bwd(const int32_t* topk_idx, const float* topk_w, const float* dto
 /* moe_router_gemm_bwd: derived, the adjoint of moe_router_gemm with respect
  * to w_r (its share of dx is added by moe_permute_bwd):
  * dw_r = x^T dlogits, binary32 accumulation over tokens
- * in a fixed order, one rounding to `dtype`.
+ * in a fixed order, one rounding to `dtype`. bf16 with E <= 16, E % 4 == 0,
+ * d % 256 == 0 and x and dlogits 16-byte aligned runs on the matrix cores
+ * with each dlogits value carried as two bf16 terms (hi = bf16(v), lo =
+ * bf16(v - hi)): the products are within 2^-16 of x * dlogits relative to
+ * it, far below the final bf16 rounding.
  *   x [T,d], dw_r [d,E] of `dtype`; dlogits [T,E] binary32;
  *   ws of at least moe_router_bwd_workspace_bytes(T, d, E) bytes. */
 size_t moe_router_bwd_workspace_bytes(int T, int d, int E);

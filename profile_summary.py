@@ -45,6 +45,7 @@ ROW_KERNELS = [
     ("zero_pad_rows_kernel", "permute"),
     ("hist_kernel", "offsets"), ("scan_kernel", "offsets"), ("rank_kernel", "offsets"),
     ("router_gemm_kernel", "router_gemm"), ("router_gemm_lds_kernel", "router_gemm"),
+    ("router_gemm_mfma_kernel", "router_gemm"), ("router_bwd_mfma_kernel", "router_gemm_bwd"),
     ("route_bwd_kernel", "route_bwd"), ("route_kernel", "route"),
     ("router_bwd_partial_kernel", "router_gemm_bwd"), ("router_bwd_reduce_kernel", "router_gemm_bwd"),
 ]

@@ -2,6 +2,7 @@
 // backward (gfx950). See include/moe.h for the contract of each entry point.
 #include "common.h"
 
+#include <algorithm>
 #include <mutex>
 
 namespace moe {
@@ -33,16 +34,13 @@ __global__ void __launch_bounds__(256) router_gemm_kernel(const T* __restrict__ 
 #pragma unroll
       for (int b = 0; b < kRouterEC; ++b) acc[a][b] = 0.f;
     for (int c = lane; c < nvec; c += 64) {
+      // rows past T read row T-1 (a token's row feeds only its own logits,
+      // which are not stored); a per-row branch would serialise the loads
       float xv[kRouterTok][V];
 #pragma unroll
       for (int a = 0; a < kRouterTok; ++a) {
-        if (t0 + a < T_) {
-          V16 v = *reinterpret_cast<const V16*>(x + (size_t)(t0 + a) * d + (size_t)c * V);
-          unpack(v, xv[a]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < V; ++i) xv[a][i] = 0.f;
-        }
+        V16 v = *reinterpret_cast<const V16*>(x + (size_t)min(t0 + a, T_ - 1) * d + (size_t)c * V);
+        unpack(v, xv[a]);
       }
 #pragma unroll
       for (int i = 0; i < V; ++i) {
@@ -120,13 +118,8 @@ __global__ void __launch_bounds__(256) router_gemm_lds_kernel(const uint16_t* __
         float xv[kRouterTok][V];
 #pragma unroll
         for (int a = 0; a < kRouterTok; ++a) {
-          if (t0 + a < T_) {
-            V16 v = *reinterpret_cast<const V16*>(x + (size_t)(t0 + a) * d + (size_t)c * V);
-            unpack(v, xv[a]);
-          } else {
-#pragma unroll
-            for (int i = 0; i < V; ++i) xv[a][i] = 0.f;
-          }
+          V16 v = *reinterpret_cast<const V16*>(x + (size_t)min(t0 + a, T_ - 1) * d + (size_t)c * V);
+          unpack(v, xv[a]);
         }
         const uint8_t* grp = w_lds + c * gb + e0 * 2;   // rows c*8 .. c*8+7
 #pragma unroll
@@ -150,6 +143,121 @@ __global__ void __launch_bounds__(256) router_gemm_lds_kernel(const uint16_t* __
           if (lane == a * kRouterEC + b && t0 + a < T_ && e0 + b < E)
             logits[(size_t)(t0 + a) * E + e0 + b] = acc[a][b];
     }
+  }
+}
+
+// The bf16 product on the matrix cores (E <= 16, E % 8 == 0, d % 256 == 0,
+// d * E * 2 bytes of w_r fit in 64 KB). One wave per block of 16 tokens:
+// v_mfma_f32_16x16x32_bf16 with the tokens as rows (A: lane (r, g) holds
+// x[t0 + r][k(s, g) .. + 7]) and the experts as columns (B: lane (r, g)
+// holds w_r[k(s, g) .. + 7][r]). K step s takes the k order
+// k(s, g) = 64 (s / 2) + 16 g + 8 (s % 2) (any order of the sum is the same
+// product): each load instruction then touches whole 128-byte lines of its 16
+// rows (the four lanes of a row 32 bytes apart, the next step filling the
+// gaps), which streams at about 5.4 TB/s where the plain order's 64-byte
+// halves of 16 rows stay near 4.2. The wave streams its 16 rows over the
+// whole of d in chunks of kRmCh K steps, the next chunk's loads issued
+// before the current chunk's MFMAs, and stores its 16 x E logits itself (no
+// cross-wave reduction, no barrier after staging). w_r is staged once per
+// workgroup in LDS in fragment order (the 64 lanes of one K step read one
+// contiguous 1 KB). Columns r >= E read column E-1 and rows past T read row
+// T-1: an A row or B column feeds only its own output, which is not stored.
+constexpr int kRmCh = 8;   // K steps (of 32) per chunk (even): 8 KB of x per wave in flight per chunk
+constexpr int kRmMaxLds = 64 * 1024;
+
+static bool router_mfma_shape(int d, int E) {
+  return E <= 16 && E % 8 == 0 && d % (32 * kRmCh) == 0 && (long)d * E * 2 <= kRmMaxLds;
+}
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 rbf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float rf32x4_t;
+
+__global__ void __launch_bounds__(256) router_gemm_mfma_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ w_r, int T_,
+                                                               int d, int E, float* __restrict__ logits) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t wfrag[];   // [d/32][4][E][8]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r = lane & 15;
+  const int nblk = (T_ + 15) / 16;
+  const int nch = d / (32 * kRmCh);
+  int blk = blockIdx.x * 4 + wave;
+  // k(s, g) = 64 (s / 2) + 16 g + 8 (s % 2); kRmCh is even, so step c kRmCh + s
+  // of chunk c starts at column 32 c kRmCh + k(s, g)
+  const uint16_t* xr = x + (size_t)min(blk * 16 + r, T_ - 1) * d + g * 16;
+  rbf16x8_t a0[kRmCh], a1[kRmCh], a2[kRmCh];
+  auto load = [&](int c, rbf16x8_t (&dst)[kRmCh]) {
+#pragma unroll
+    for (int s = 0; s < kRmCh; ++s)
+      dst[s] = *reinterpret_cast<const rbf16x8_t*>(xr + c * kRmCh * 32 + (s >> 1) * 64 + (s & 1) * 8);
+  };
+  // the first two chunks are in flight while w_r is staged (a clamped chunk
+  // index re-reads the last chunk, from cache, when d has fewer chunks)
+  load(0, a0);
+  load(min(1, nch - 1), a1);
+  // stage w_r: 16-byte pieces (8 experts of one row k) to fragment order,
+  // eight loads per thread in flight before their LDS writes
+  const int pieces = d * E / 8;
+  for (int p0 = 0; p0 < pieces; p0 += 256 * 8) {
+    V16 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = reinterpret_cast<const V16*>(w_r)[min(p0 + j * 256 + (int)threadIdx.x, pieces - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = p0 + j * 256 + threadIdx.x;
+      if (p >= pieces) break;
+      // row k of w_r belongs to step s = 2 (k / 64) + (k / 8) % 2, lane group
+      // g = (k % 64) / 16, element k % 8 of the fragment
+      const int k = p * 8 / E, n0 = p * 8 % E;
+      const int kk = k >> 3, st = (kk >> 3) * 2 + (kk & 1), gg = (kk >> 1) & 3;
+      uint16_t* dst = wfrag + ((st * 4 + gg) * E + n0) * 8 + (k & 7);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dst[(2 * i) * 8] = static_cast<uint16_t>(v[j].w[i] & 0xffffu);
+        dst[(2 * i + 1) * 8] = static_cast<uint16_t>(v[j].w[i] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  const uint16_t* wl = wfrag + (g * E + min(r, E - 1)) * 8;
+  for (; blk < nblk; blk += gridDim.x * 4) {
+    rf32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    auto mfmas = [&](int c, const rbf16x8_t (&src)[kRmCh]) {
+#pragma unroll
+      for (int s = 0; s < kRmCh; ++s) {
+        const rbf16x8_t b = *reinterpret_cast<const rbf16x8_t*>(wl + (c * kRmCh + s) * 32 * E);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(src[s], b, acc, 0, 0, 0);
+      }
+    };
+    // three chunk buffers in rotation: while chunk c is multiplied, chunks
+    // c + 1 and c + 2 are in flight. Every load is unconditional (clamped to
+    // the last chunk) and fenced from the MFMAs so that it is issued early.
+    for (int c = 0; c < nch; c += 3) {
+      load(min(c + 2, nch - 1), a2);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(c, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c + 1 >= nch) break;
+      load(min(c + 3, nch - 1), a0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(c + 1, a1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (c + 2 >= nch) break;
+      load(min(c + 4, nch - 1), a1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(c + 2, a2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // lane (r, g) holds tokens 4g .. 4g+3 of the block, expert r
+    if (r < E) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = blk * 16 + 4 * g + i;
+        if (t < T_) logits[(size_t)t * E + r] = acc[i];
+      }
+    }
+    xr = x + (size_t)min((blk + (int)gridDim.x * 4) * 16 + r, T_ - 1) * d + g * 16;
+    load(0, a0);
+    load(min(1, nch - 1), a1);
   }
 }
 
@@ -501,6 +609,145 @@ __global__ void __launch_bounds__(256) router_bwd_partial_kernel(const T* __rest
   }
 }
 
+// The bf16 adjoint on the matrix cores (E <= 16, E % 4 == 0, d % 256 == 0): per
+// workgroup a chunk of kRmTok tokens and 256 columns of x, part[chunk][i][e]
+// = sum over the chunk of x[t][i] dl[t][e] as v_mfma_f32_16x16x32_bf16 with
+// the experts as rows (A = dl^T) and the columns of x as columns (B = x, the
+// contraction over tokens). dl is binary32; each value is carried as two
+// bf16 terms, hi = bf16(dl) and lo = bf16(dl - hi) (dl - hi is exact), two
+// MFMAs per fragment, so the products keep about 16 significant bits of dl
+// against the 8 of one bf16 term. x tiles of 32 tokens x 256 columns move
+// global -> registers (two K steps ahead) -> LDS (two buffers, 16-byte chunks
+// XOR-swizzled by row) and are read down their columns with
+// ds_read_b64_tr_b16. Tokens past T carry zero rows of x and zero dl.
+constexpr int kRmTok = 256;               // tokens per chunk: eight K steps of 32
+constexpr int kRmCols = 256;              // columns of x per workgroup (64 per wave)
+constexpr int kRmDlLd = kRmTok + 8;       // dl^T row stride in LDS (bf16)
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short rs4_t;
+MOE_DEV rbf16x8_t lds_tr8(const uint16_t* p0, const uint16_t* p1) {
+  const rs4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) rs4_t*)p0);
+  const rs4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) rs4_t*)p1);
+  typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s8_t;
+  const s8_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(rbf16x8_t, v);
+}
+// 16-byte chunk position of chunk c in LDS row k of an x tile: the 16 rows
+// one transposed read touches (k = 8 tg + tj, tg, tj < 4) land on 16
+// different chunk pairs
+MOE_DEV int rm_chunk(int k, int c) { return c ^ (((k & 3) | ((k >> 3) & 3) << 2) << 1); }
+
+__global__ void __launch_bounds__(256) router_bwd_mfma_kernel(const uint16_t* __restrict__ x,
+                                                              const float* __restrict__ dl, int T_, int d,
+                                                              int E, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][32 * kRmCols];
+  __shared__ __attribute__((aligned(16))) uint16_t dlh[16 * kRmDlLd];
+  __shared__ __attribute__((aligned(16))) uint16_t dll[16 * kRmDlLd];
+  const int chunk = blockIdx.x, c0 = blockIdx.y * kRmCols;
+  const int t0 = chunk * kRmTok;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // x tile loads: thread tid moves 16-byte chunks tid + 256 j (j < 4) of the
+  // 32 x 32-chunk tile: row (tid >> 5) + 8 j, chunk tid & 31
+  const int lrow = tid >> 5, lch = tid & 31;
+  auto load = [&](int ks, V16 (&v)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = min(t0 + ks * 32 + lrow + 8 * j, T_ - 1);
+      v[j] = *reinterpret_cast<const V16*>(x + (size_t)t * d + c0 + lch * 8);
+    }
+  };
+  auto store = [&](int ks, const V16 (&v)[4], uint16_t* buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = lrow + 8 * j;
+      const bool ok = t0 + ks * 32 + k < T_;
+      V16 o;   // selected word by word (a select of whole vectors went through scratch memory)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o.w[i] = ok ? v[j].w[i] : 0u;
+      *reinterpret_cast<V16*>(buf + k * kRmCols + rm_chunk(k, lch) * 8) = o;
+    }
+  };
+  V16 ra[4], rb[4];
+  load(0, ra);
+  load(1, rb);
+  // dl^T of the chunk as hi/lo bf16 pairs: the chunk's kRmTok x E binary32
+  // values are contiguous; four 16-byte loads per thread (E % 4 == 0, so a
+  // piece never straddles two tokens), issued together, tokens past T zero.
+  // Rows e >= E of dl^T stay unwritten: an A row feeds only its own output
+  // row, which is not stored.
+  {
+    const float4* src = reinterpret_cast<const float4*>(dl + (size_t)t0 * E);
+    const int np = kRmTok * E / 4, nvalid = (min(kRmTok, T_ - t0) * E) / 4;
+    float4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = src[min(tid + 256 * j, nvalid - 1)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = tid + 256 * j;
+      if (q < np) {
+        const int t = q * 4 / E, e0 = q * 4 % E;
+        const float f[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float fv = q < nvalid ? f[i] : 0.f;
+          const uint16_t h = f32_to_bf16(fv);
+          dlh[(e0 + i) * kRmDlLd + t] = h;
+          dll[(e0 + i) * kRmDlLd + t] = f32_to_bf16(fv - bf16_to_f32(h));
+        }
+      }
+    }
+  }
+  store(0, ra, xs[0]);
+  load(2, ra);
+  __syncthreads();
+
+  const int g = lane >> 4, r = lane & 15;
+  const int tj = (lane & 15) >> 2, tq = lane & 3;
+  rf32x4_t acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) acc[n] = rf32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int ks, const uint16_t* buf) {
+    const rbf16x8_t ah = *reinterpret_cast<const rbf16x8_t*>(dlh + r * kRmDlLd + ks * 32 + 8 * g);
+    const rbf16x8_t al = *reinterpret_cast<const rbf16x8_t*>(dll + r * kRmDlLd + ks * 32 + 8 * g);
+    const int k0 = 8 * g + tj, k1 = k0 + 4;
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int col = wave * 64 + n * 16 + 4 * tq;
+      const rbf16x8_t b = lds_tr8(buf + k0 * kRmCols + rm_chunk(k0, col >> 3) * 8 + (col & 7),
+                                  buf + k1 * kRmCols + rm_chunk(k1, col >> 3) * 8 + (col & 7));
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc[n], 0, 0, 0);
+      acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc[n], 0, 0, 0);
+    }
+  };
+  // eight K steps, two buffers; step ks + 1 waits in registers and goes to
+  // LDS after step ks, whose barrier also ends every read of that buffer's
+  // previous contents (step ks - 1)
+#pragma unroll
+  for (int ks = 0; ks < kRmTok / 32; ++ks) {
+    compute(ks, xs[ks & 1]);
+    if (ks + 1 < kRmTok / 32) {
+      if (ks & 1) {
+        store(ks + 1, ra, xs[(ks + 1) & 1]);
+        if (ks + 3 < kRmTok / 32) load(ks + 3, ra);
+      } else {
+        store(ks + 1, rb, xs[(ks + 1) & 1]);
+        if (ks + 3 < kRmTok / 32) load(ks + 3, rb);
+      }
+    }
+    __syncthreads();
+  }
+  // lane (r, g) holds experts 4g .. 4g+3 of column r of each 16-column tile
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int col = c0 + wave * 64 + n * 16 + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * g + i;
+      if (e < E) part[((size_t)chunk * d + col) * E + e] = acc[n][i];
+    }
+  }
+}
+
 // dw_r[i] = sum over chunks of part[chunk][i]: eight lanes per output, lane j
 // summing chunks j, j+8, ... in order, then a fixed shuffle tree.
 constexpr int kRbRed = 8;
@@ -539,9 +786,17 @@ extern "C" int moe_router_gemm(int dtype, const void* x, const void* w_r, int T,
   MOE_CHECK_SUPPORTED(E <= MOE_MAX_EXPERTS);
   if (T == 0) return MOE_OK;
   MOE_CHECK_ARG(x && w_r && logits && aligned16(x));
+  const bool wide = E % kRouterEC == 0 && aligned16(w_r);
+  if (dtype == MOE_BF16 && wide && router_mfma_shape(d, E)) {
+    // one wave per 16 tokens, at most 256 workgroups of four waves (one per CU)
+    const long nblk = (T + 15) / 16;
+    const int blocks = static_cast<int>(std::min<long>(256, (nblk + 3) / 4));
+    router_gemm_mfma_kernel<<<blocks, 256, (size_t)d * E * 2, stream>>>(
+        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_r), T, d, E, logits);
+    return launch_status();
+  }
   const int waves = (T + kRouterTok - 1) / kRouterTok;
   const int blocks = (waves + 3) / 4;
-  const bool wide = E % kRouterEC == 0 && aligned16(w_r);
   // w_r in LDS when it fits in 64 KB with its padding (four workgroups per CU)
   const long lds_bytes = (long)(d / 8) * router_lds_group_bytes(E);
   if (dtype == MOE_BF16 && wide && lds_bytes <= 64 * 1024) {
@@ -693,8 +948,19 @@ extern "C" int moe_router_gemm_bwd(int dtype, const void* x, const float* dlogit
   MOE_CHECK_ARG(T == 0 || (x && dlogits && aligned16(x)));
   MOE_CHECK_SUPPORTED(E <= MOE_MAX_EXPERTS);
   if (!ws || ws_bytes < moe_router_bwd_workspace_bytes(T, d, E)) return MOE_ERR_WORKSPACE;
-  const int nchunk = (T + kRbTok - 1) / kRbTok;
   float* part = static_cast<float*>(ws);
+  if (dtype == MOE_BF16 && E <= 16 && E % 4 == 0 && d % kRmCols == 0 && aligned16(x) && aligned16(dlogits)) {
+    const int nch = (T + kRmTok - 1) / kRmTok;   // fewer chunks than the workspace is sized for
+    if (nch > 0) {
+      router_bwd_mfma_kernel<<<dim3(nch, d / kRmCols), 256, 0, stream>>>(static_cast<const uint16_t*>(x), dlogits,
+                                                                        T, d, E, part);
+      if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    }
+    const unsigned blocks = static_cast<unsigned>(((size_t)d * E * kRbRed + 255) / 256);
+    router_bwd_reduce_kernel<uint16_t><<<blocks, 256, 0, stream>>>(part, nch, d, E, static_cast<uint16_t*>(dw_r));
+    return launch_status();
+  }
+  const int nchunk = (T + kRbTok - 1) / kRbTok;
   const int V = dtype == MOE_BF16 ? 8 : 4;
   if (nchunk > 0) {
     dim3 grid(nchunk, (d / V + kRbCols - 1) / kRbCols, (E + kRbEC - 1) / kRbEC);

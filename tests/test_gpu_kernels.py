@@ -225,29 +225,35 @@ def test_combine_adjoint_with_bad_ids(C):
         assert np.array_equal(got["rows"][1], got["tokens"][1])
 
 
-def test_router_gemm_lds_and_cache_paths_agree():
-    """The bf16 router GEMM with w_r staged in LDS and the one that reads w_r
-    through the cache (taken when w_r is not 16-byte aligned) compute the same
-    sums in the same order: identical logits."""
-    rng = _rng(8)
-    T, d, E = 333, 1024, 16
-    xt, _ = _to(rng.standard_normal((T, d)), "bf16")
-    wr = _to(rng.standard_normal((d, E)) / np.sqrt(d), "bf16")[0]
+@pytest.mark.parametrize("T,d,E", [(333, 1024, 16), (2000, 512, 8)])
+def test_router_gemm_matrix_core_and_cache_paths(T, d, E):
+    """The bf16 router GEMM on the matrix cores (w_r 16-byte aligned) and the
+    FMA kernel that reads w_r through the cache (w_r at a 2-byte offset) both
+    match the oracle; they sum in different orders, so their logits may
+    differ in the last bits but not beyond the binary32 tolerance."""
+    rng = _rng(8, T, d, E)
+    xt, x = _to(rng.standard_normal((T, d)), "bf16")
+    wrt, wr = _to(rng.standard_normal((d, E)) / np.sqrt(d), "bf16")
     buf = torch.empty(d * E + 8, dtype=torch.bfloat16, device="cuda")
     shifted = buf[1:1 + d * E].view(d, E)        # 2-byte offset: not 16-byte aligned
-    shifted.copy_(wr)
-    a = torch.empty(T, E, dtype=torch.float32, device="cuda")
-    b = torch.empty(T, E, dtype=torch.float32, device="cuda")
-    L.moe_router_gemm(xt, wr, a)
+    shifted.copy_(wrt)
+    a = torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda")
+    b = torch.full((T, E), float("nan"), dtype=torch.float32, device="cuda")
+    L.moe_router_gemm(xt, wrt, a)
     L.moe_router_gemm(xt, shifted, b)
-    assert np.array_equal(host(a), host(b))
+    ref = om.router_logits(x, wr)
+    assert_close(host(a), ref, "f32", "logits (matrix cores)")
+    assert_close(host(b), ref, "f32", "logits (cache path)")
 
 
 # ----------------------------------------------------------------------------- router
 @pytest.mark.parametrize("kind", ["bf16", "f32"])
 @pytest.mark.parametrize("T,d,E,k", [(1000, 256, 8, 2), (129, 2048, 8, 4), (300, 136, 20, 3),
                                      (64, 512, 128, 4),
-                                     (77, 1024, 16, 4), (500, 512, 32, 4)])   # w_r staged in LDS, E > 8
+                                     (77, 1024, 16, 4),                   # matrix cores, one partial chunk
+                                     (700, 512, 12, 3),                   # E % 8 != 0: FMA forward, MFMA adjoint
+                                     (500, 512, 32, 4),                   # w_r staged in LDS, E > 16
+                                     (20000, 256, 8, 2)])                 # > 1024 token blocks: waves take two
 def test_router_parity(kind, T, d, E, k):
     rng = _rng(4, T, d, E)
     xt, x = _to(rng.standard_normal((T, d)), kind)
