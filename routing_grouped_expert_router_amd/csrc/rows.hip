@@ -11,18 +11,35 @@ constexpr int kRowThreads = 256;   // 4 waves = 4 tokens per workgroup
 // whole d = 2048 bf16 row) before it turns to the next row
 constexpr int kRowUnroll = 4;
 
-// Loads the token's row ids (k <= 16) into registers; ids outside [0, n_rows)
-// become -1 so that a bad id is skipped rather than dereferenced.
-MOE_DEV void load_rows(const int32_t* row_of, size_t t, int k, int n_rows, int (&rows)[MOE_MAX_TOPK]) {
+// Every load below is unconditional: a piece index past the row is clamped to
+// the row's last piece and a missing row is replaced by a valid one, the
+// result then discarded or zeroed by a select. A load under a per-lane or
+// per-row branch is followed by a wait for it at the branch's end, which
+// leaves one load in flight per wave; these kernels move rows and live on
+// the loads they keep in flight.
+
+// The token's row ids (k <= 16 <= 64): lane j < k holds slot j's row, -1 for
+// a slot past k or an id outside [0, n_rows) (skipped, never dereferenced).
+// One load per lane; slot j's row is then slot_row(rid, j), wave-uniform.
+MOE_DEV int load_row_ids(const int32_t* row_of, size_t t, int k, int n_rows, int lane) {
+  const int r = row_of[t * k + min(lane, k - 1)];
+  return lane < k && r >= 0 && r < n_rows ? r : -1;
+}
+MOE_DEV int slot_row(int rid, int j) { return __builtin_amdgcn_readlane(rid, j); }
+MOE_DEV float slot_val(float v, int j) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j)); }
+
+// Holds a loaded vector in registers from here on. Without it the compiler
+// may move a load down to each of its conditional uses (a store per routed
+// row, an FMA per valid slot) and reload it there, one wait per use.
+MOE_DEV void pin(V16& v) { asm volatile("" : "+v"(v.w[0]), "+v"(v.w[1]), "+v"(v.w[2]), "+v"(v.w[3])); }
+
+// V16 that is v when ok, else zero (word by word: a select of whole vectors
+// can go through scratch memory)
+MOE_DEV V16 keep_if(bool ok, const V16& v) {
+  V16 o;
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    int r = -1;
-    if (j < k) {
-      r = row_of[t * k + j];
-      if (r >= n_rows) r = -1;
-    }
-    rows[j] = r;
-  }
+  for (int i = 0; i < 4; ++i) o.w[i] = ok ? v.w[i] : 0u;
+  return o;
 }
 
 // x_perm[row_of[t, j]] = x[t]
@@ -34,25 +51,32 @@ __global__ void __launch_bounds__(kRowThreads) permute_kernel(const T* __restric
   const size_t t = ((size_t)blockIdx.x * kRowThreads + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (t >= (size_t)T_) return;
-  int rows[MOE_MAX_TOPK];
-  load_rows(row_of, t, k, n_rows, rows);
   const int nvec = d / V;
   const V16* src = reinterpret_cast<const V16*>(x + t * d);
-  for (int c0 = lane; c0 < nvec; c0 += 64 * kRowUnroll) {
-    // kRowUnroll 1 KB pieces of the row at once, then each destination row
-    // written piece after piece
-    V16 v[kRowUnroll];
+  // kRowUnroll 1 KB pieces of the row at once, then each destination row
+  // written piece after piece; the first pieces are in flight before the row
+  // ids are asked for
+  V16 v[kRowUnroll];
+  auto load = [&](int c0) {
 #pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u)
-      if (c0 + 64 * u < nvec) v[u] = src[c0 + 64 * u];
+    for (int u = 0; u < kRowUnroll; ++u) v[u] = src[min(c0 + 64 * u, nvec - 1)];
+  };
+  load(lane);
+  const int rid = load_row_ids(row_of, t, k, n_rows, lane);
+  for (int c0 = lane;;) {
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j)
-      if (j < k && rows[j] >= 0) {
-        V16* dst = reinterpret_cast<V16*>(x_perm + (size_t)rows[j] * d);
+    for (int u = 0; u < kRowUnroll; ++u) pin(v[u]);
+    for (int j = 0; j < k; ++j) {
+      const int r = slot_row(rid, j);
+      if (r < 0) continue;
+      V16* dst = reinterpret_cast<V16*>(x_perm + (size_t)r * d);
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u)
-          if (c0 + 64 * u < nvec) dst[c0 + 64 * u] = v[u];
-      }
+      for (int u = 0; u < kRowUnroll; ++u)
+        if (c0 + 64 * u < nvec) dst[c0 + 64 * u] = v[u];
+    }
+    c0 += 64 * kRowUnroll;
+    if (c0 - lane >= nvec) break;   // wave-uniform
+    load(c0);
   }
 }
 
@@ -72,7 +96,10 @@ __global__ void __launch_bounds__(kRowThreads) zero_pad_rows_kernel(const int32_
 }
 
 // y[t] = y_add[t] + sum_j w[t, j] y_perm[row_of[t, j]]  (binary32, slot order;
-// y_add optional)
+// y_add optional). Source rows are read in groups of kRowGroup slots, all
+// their pieces in flight together; a missing row reads the token's first
+// valid row and adds nothing.
+constexpr int kRowGroup = 4;
 template <typename T>
 __global__ void __launch_bounds__(kRowThreads) combine_kernel(const T* __restrict__ y_perm,
                                                               const int32_t* __restrict__ row_of,
@@ -84,38 +111,50 @@ __global__ void __launch_bounds__(kRowThreads) combine_kernel(const T* __restric
   const size_t t = ((size_t)blockIdx.x * kRowThreads + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (t >= (size_t)T_) return;
-  int rows[MOE_MAX_TOPK];
-  float w[MOE_MAX_TOPK];
-  load_rows(row_of, t, k, n_rows, rows);
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) w[j] = j < k ? topk_w[t * k + j] : 0.f;
+  const int rid = load_row_ids(row_of, t, k, n_rows, lane);
+  const float wl = topk_w[t * k + min(lane, k - 1)];
+  int first = -1;
+  for (int j = k - 1; j >= 0; --j) first = slot_row(rid, j) >= 0 ? slot_row(rid, j) : first;
   const int nvec = d / V;
   for (int c0 = lane; c0 < nvec; c0 += 64 * kRowUnroll) {
     float acc[kRowUnroll][V];
+    if (y_add) {
+      V16 a[kRowUnroll];
 #pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u) {
-      if (y_add && c0 + 64 * u < nvec) {
-        unpack(reinterpret_cast<const V16*>(y_add + t * d)[c0 + 64 * u], acc[u]);
-      } else {
+      for (int u = 0; u < kRowUnroll; ++u) a[u] = reinterpret_cast<const V16*>(y_add + t * d)[min(c0 + 64 * u, nvec - 1)];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) unpack(a[u], acc[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u)
 #pragma unroll
         for (int i = 0; i < V; ++i) acc[u][i] = 0.f;
-      }
     }
-    // each source row read piece after piece, rows in slot order
+    if (first >= 0) {
+      for (int j0 = 0; j0 < k; j0 += kRowGroup) {
+        V16 v[kRowGroup][kRowUnroll];
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      if (j < k && rows[j] >= 0) {
-        const V16* src = reinterpret_cast<const V16*>(y_perm + (size_t)rows[j] * d);
-        V16 v[kRowUnroll];
+        for (int jj = 0; jj < kRowGroup; ++jj) {
+          const int r = slot_row(rid, min(j0 + jj, 63));
+          const V16* src = reinterpret_cast<const V16*>(y_perm + (size_t)(r >= 0 ? r : first) * d);
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u)
-          if (c0 + 64 * u < nvec) v[u] = src[c0 + 64 * u];
+          for (int u = 0; u < kRowUnroll; ++u) v[jj][u] = src[min(c0 + 64 * u, nvec - 1)];
+        }
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u) {
-          float f[V];
-          unpack(v[u], f);
+        for (int jj = 0; jj < kRowGroup; ++jj)
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc[u][i] = fmaf(w[j], f[i], acc[u][i]);
+          for (int u = 0; u < kRowUnroll; ++u) pin(v[jj][u]);
+#pragma unroll
+        for (int jj = 0; jj < kRowGroup; ++jj) {
+          if (slot_row(rid, min(j0 + jj, 63)) < 0) continue;   // wave-uniform
+          const float w = slot_val(wl, j0 + jj);
+#pragma unroll
+          for (int u = 0; u < kRowUnroll; ++u) {
+            float f[V];
+            unpack(v[jj][u], f);
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[u][i] = fmaf(w, f[i], acc[u][i]);
+          }
         }
       }
     }
@@ -126,6 +165,9 @@ __global__ void __launch_bounds__(kRowThreads) combine_kernel(const T* __restric
 }
 
 // dy_perm[row_of[t, j]] = w[t, j] dy[t];  dw[t, j] = <dy[t], y_perm[row_of[t, j]]>
+// Slots in groups of kRowGroup: the token's dy pieces and the group's routed
+// rows are in flight together; a missing row reads the token's first valid
+// row, its product and store skipped.
 template <typename T>
 __global__ void __launch_bounds__(kRowThreads) combine_bwd_kernel(
     const T* __restrict__ dy, const T* __restrict__ y_perm, const float* __restrict__ topk_w,
@@ -135,54 +177,61 @@ __global__ void __launch_bounds__(kRowThreads) combine_bwd_kernel(
   const size_t t = ((size_t)blockIdx.x * kRowThreads + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (t >= (size_t)T_) return;
-  int rows[MOE_MAX_TOPK];
-  float w[MOE_MAX_TOPK], dot[MOE_MAX_TOPK];
-  load_rows(row_of, t, k, n_rows, rows);
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    w[j] = j < k ? topk_w[t * k + j] : 0.f;
-    dot[j] = 0.f;
-  }
+  const int rid = load_row_ids(row_of, t, k, n_rows, lane);
+  const float wl = topk_w[t * k + min(lane, k - 1)];
+  int first = -1;
+  for (int j = k - 1; j >= 0; --j) first = slot_row(rid, j) >= 0 ? slot_row(rid, j) : first;
   const int nvec = d / V;
-  for (int c0 = lane; c0 < nvec; c0 += 64 * kRowUnroll) {
-    V16 gv[kRowUnroll];
+  const V16* g_row = reinterpret_cast<const V16*>(dy + t * d);
+  float dotl = 0.f;   // lane j: slot j's dot product
+  for (int j0 = 0; first >= 0 && j0 < k; j0 += kRowGroup) {
+    float dot[kRowGroup] = {};
+    int rr[kRowGroup];
 #pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u)
-      if (c0 + 64 * u < nvec) gv[u] = reinterpret_cast<const V16*>(dy + t * d)[c0 + 64 * u];
-    // each routed row read and written piece after piece
+    for (int jj = 0; jj < kRowGroup; ++jj) rr[jj] = slot_row(rid, min(j0 + jj, 63));
+    for (int c0 = lane; c0 < nvec; c0 += 64 * kRowUnroll) {
+      V16 gv[kRowUnroll], v[kRowGroup][kRowUnroll];
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      if (j < k && rows[j] >= 0) {
-        const V16* src = reinterpret_cast<const V16*>(y_perm + (size_t)rows[j] * d);
-        V16* dst = reinterpret_cast<V16*>(dy_perm + (size_t)rows[j] * d);
-        V16 v[kRowUnroll];
+      for (int u = 0; u < kRowUnroll; ++u) gv[u] = g_row[min(c0 + 64 * u, nvec - 1)];
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u)
-          if (c0 + 64 * u < nvec) v[u] = src[c0 + 64 * u];
+      for (int jj = 0; jj < kRowGroup; ++jj) {
+        const V16* src = reinterpret_cast<const V16*>(y_perm + (size_t)(rr[jj] >= 0 ? rr[jj] : first) * d);
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; ++u) v[jj][u] = src[min(c0 + 64 * u, nvec - 1)];
+      }
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) {
+        pin(gv[u]);
+#pragma unroll
+        for (int jj = 0; jj < kRowGroup; ++jj) pin(v[jj][u]);
+      }
+#pragma unroll
+      for (int jj = 0; jj < kRowGroup; ++jj) {
+        if (rr[jj] < 0) continue;   // wave-uniform
+        const float w = slot_val(wl, j0 + jj);
+        V16* dst = reinterpret_cast<V16*>(dy_perm + (size_t)rr[jj] * d);
 #pragma unroll
         for (int u = 0; u < kRowUnroll; ++u) {
-          if (c0 + 64 * u < nvec) {
-            float g[V], f[V], o[V];
-            unpack(gv[u], g);
-            unpack(v[u], f);
+          if (c0 + 64 * u >= nvec) continue;
+          float g[V], f[V], o[V];
+          unpack(gv[u], g);
+          unpack(v[jj][u], f);
 #pragma unroll
-            for (int i = 0; i < V; ++i) {
-              dot[j] = fmaf(g[i], f[i], dot[j]);
-              o[i] = w[j] * g[i];
-            }
-            dst[c0 + 64 * u] = pack(o);
+          for (int i = 0; i < V; ++i) {
+            dot[jj] = fmaf(g[i], f[i], dot[jj]);
+            o[i] = w * g[i];
           }
+          dst[c0 + 64 * u] = pack(o);
         }
       }
     }
-  }
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    if (j < k) {
-      const float s = wave_sum(dot[j]);
-      if (lane == j) dtopk_w[t * k + j] = rows[j] >= 0 ? s : 0.f;
+    for (int jj = 0; jj < kRowGroup; ++jj) {
+      const float sdot = wave_sum(dot[jj]);
+      if (lane == j0 + jj) dotl = sdot;
     }
   }
+  if (lane < k) dtopk_w[t * k + lane] = rid >= 0 ? dotl : 0.f;
 }
 
 // The same adjoint in row order, for callers that have src_slot: wave r
@@ -211,9 +260,15 @@ __global__ void __launch_bounds__(kRowThreads) combine_bwd_rows_kernel(
   const size_t r = ((size_t)blockIdx.x * kRowThreads + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (r >= (size_t)n_rows) return;
-  const int s = src_slot[r];
   const int nvec = d / V;
   V16* dst = reinterpret_cast<V16*>(dy_perm + r * d);
+  const V16* y_row = reinterpret_cast<const V16*>(y_perm + r * d);
+  // the routed row's first pieces do not depend on its slot: in flight
+  // before the slot id arrives
+  V16 yv[kRowUnroll];
+#pragma unroll
+  for (int u = 0; u < kRowUnroll; ++u) yv[u] = y_row[min(lane + 64 * u, nvec - 1)];
+  const int s = __builtin_amdgcn_readfirstlane(src_slot[r]);
   if (s < 0 || (size_t)s >= slots) {
     V16 z;
 #pragma unroll
@@ -223,16 +278,20 @@ __global__ void __launch_bounds__(kRowThreads) combine_bwd_rows_kernel(
   }
   const float w = topk_w[s];
   const V16* g_row = reinterpret_cast<const V16*>(dy + (size_t)(s / k) * d);
-  const V16* y_row = reinterpret_cast<const V16*>(y_perm + r * d);
   float dot = 0.f;
   for (int c0 = lane; c0 < nvec; c0 += 64 * kRowUnroll) {
-    V16 gv[kRowUnroll], yv[kRowUnroll];
+    V16 gv[kRowUnroll];
+    if (c0 != lane) {
 #pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u)
-      if (c0 + 64 * u < nvec) {
-        gv[u] = g_row[c0 + 64 * u];
-        yv[u] = y_row[c0 + 64 * u];
-      }
+      for (int u = 0; u < kRowUnroll; ++u) yv[u] = y_row[min(c0 + 64 * u, nvec - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) gv[u] = g_row[min(c0 + 64 * u, nvec - 1)];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      pin(gv[u]);
+      pin(yv[u]);
+    }
 #pragma unroll
     for (int u = 0; u < kRowUnroll; ++u) {
       if (c0 + 64 * u < nvec) {
@@ -263,37 +322,52 @@ __global__ void __launch_bounds__(kRowThreads) permute_bwd_kernel(
   const size_t t = ((size_t)blockIdx.x * kRowThreads + threadIdx.x) >> 6;
   const int lane = threadIdx.x & 63;
   if (t >= (size_t)T_) return;
-  int rows[MOE_MAX_TOPK];
-  load_rows(row_of, t, k, n_rows, rows);
+  const int rid = load_row_ids(row_of, t, k, n_rows, lane);
+  int first = -1;
+  for (int j = k - 1; j >= 0; --j) first = slot_row(rid, j) >= 0 ? slot_row(rid, j) : first;
   const int nvec = d / V;
   const bool router = dlogits != nullptr;
   const bool wide = router && (E % V == 0);
   for (int c0 = lane; c0 < nvec; c0 += 64 * kRowUnroll) {
     float acc[kRowUnroll][V];
+    if (dx_add) {
+      V16 a[kRowUnroll];
 #pragma unroll
-    for (int u = 0; u < kRowUnroll; ++u) {
-      if (dx_add && c0 + 64 * u < nvec) {
-        unpack(reinterpret_cast<const V16*>(dx_add + t * d)[c0 + 64 * u], acc[u]);
-      } else {
+      for (int u = 0; u < kRowUnroll; ++u) a[u] = reinterpret_cast<const V16*>(dx_add + t * d)[min(c0 + 64 * u, nvec - 1)];
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u) unpack(a[u], acc[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kRowUnroll; ++u)
 #pragma unroll
         for (int i = 0; i < V; ++i) acc[u][i] = 0.f;
-      }
     }
-    // each source row read piece after piece, rows in slot order
+    // source rows in groups of kRowGroup slots, all their pieces in flight
+    // together, added in slot order
+    if (first >= 0) {
+      for (int j0 = 0; j0 < k; j0 += kRowGroup) {
+        V16 v[kRowGroup][kRowUnroll];
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      if (j < k && rows[j] >= 0) {
-        const V16* src = reinterpret_cast<const V16*>(dx_perm + (size_t)rows[j] * d);
-        V16 v[kRowUnroll];
+        for (int jj = 0; jj < kRowGroup; ++jj) {
+          const int r = slot_row(rid, min(j0 + jj, 63));
+          const V16* src = reinterpret_cast<const V16*>(dx_perm + (size_t)(r >= 0 ? r : first) * d);
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u)
-          if (c0 + 64 * u < nvec) v[u] = src[c0 + 64 * u];
+          for (int u = 0; u < kRowUnroll; ++u) v[jj][u] = src[min(c0 + 64 * u, nvec - 1)];
+        }
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u) {
-          float f[V];
-          unpack(v[u], f);
+        for (int jj = 0; jj < kRowGroup; ++jj)
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc[u][i] += f[i];
+          for (int u = 0; u < kRowUnroll; ++u) pin(v[jj][u]);
+#pragma unroll
+        for (int jj = 0; jj < kRowGroup; ++jj) {
+          if (slot_row(rid, min(j0 + jj, 63)) < 0) continue;   // wave-uniform
+#pragma unroll
+          for (int u = 0; u < kRowUnroll; ++u) {
+            float f[V];
+            unpack(v[jj][u], f);
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[u][i] += f[i];
+          }
         }
       }
     }
