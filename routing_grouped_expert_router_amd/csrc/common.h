@@ -66,6 +66,15 @@ MOE_DEV V16 pack(const float (&o)[4]) {
   return v;
 }
 
+// V16 that is v when ok, else zero (word by word: a select of whole vectors
+// can be compiled through scratch memory)
+MOE_DEV V16 keep_if(bool ok, const V16& v) {
+  V16 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o.w[i] = ok ? v.w[i] : 0u;
+  return o;
+}
+
 // Elements per 16-byte vector.
 template <typename T> constexpr int kVec = 16 / sizeof(T);
 

@@ -153,26 +153,27 @@ struct RowGather {
 };
 
 // Stage a tile of TC columns and 128 rows of one group into LDS (rows past the
-// group's end read as zeros).
+// group's end read as zeros). Every load is unconditional (a row past the end
+// reads the group's last row of the tile, then zeroed): loads under a per-row
+// branch would each be waited for before the next is issued.
 template <int TC, int LDW>
 MOE_DEV void stage_tile(const uint16_t* __restrict__ src, int cols, int r0, int n, int row_in, int c0,
-                        uint16_t* tile, RowGather rg = {nullptr, 1, 0}) {
+                        uint16_t* tile) {
   constexpr int CH = TC / 8;   // 16-byte chunks per row
+  constexpr int NJ = kQRows * CH / 256;
+  V16 v[NJ];
+  const int last = n - row_in - 1;   // >= 0: the tile holds at least one row
 #pragma unroll
-  for (int j = 0; j < kQRows * CH / 256; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     const int qd = threadIdx.x + 256 * j;
     const int r = qd / CH, c = qd % CH;
-    V16 v = {{0u, 0u, 0u, 0u}};
-    if (row_in + r < n) {
-      long srow = r0 + row_in + r;
-      if (rg.gather) {
-        const int slot = rg.gather[srow];
-        srow = slot >= 0 ? slot / rg.gk : -1;
-      }
-      if (srow >= 0 && (!rg.gather || srow < rg.n_src))
-        v = *reinterpret_cast<const V16*>(src + static_cast<size_t>(srow) * cols + c0 + c * 8);
-    }
-    *reinterpret_cast<V16*>(tile + r * LDW + c * 8) = v;
+    v[j] = *reinterpret_cast<const V16*>(src + static_cast<size_t>(r0 + row_in + min(r, last)) * cols + c0 + c * 8);
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int qd = threadIdx.x + 256 * j;
+    const int r = qd / CH, c = qd % CH;
+    *reinterpret_cast<V16*>(tile + r * LDW + c * 8) = keep_if(r <= last, v[j]);
   }
 }
 
@@ -236,7 +237,9 @@ constexpr int kBChunks = kQRows * kBCols / 8 / 256;   // 16-byte loads per threa
 
 // Tiles per group prefix: tile_start[g] = sum_{h<g} ceil(n_h/128) (device
 // offsets); returns the number of row tiles. Every thread calls it.
-MOE_DEV int build_tile_prefix(const Groups1& gr, int* tile_start) {
+// grp_rows (optional, 2 G ints in LDS): each group's clamped first row and row
+// count, so that the tile loop reads group ranges from LDS, not memory.
+MOE_DEV int build_tile_prefix(const Groups1& gr, int* tile_start, int* grp_rows = nullptr) {
   if (!gr.offsets) return gr.G * ((gr.per + kQRows - 1) / kQRows);
   const int tid = threadIdx.x;
   constexpr int kMaxPer = (MOE_MAX_EXPERTS + 255) / 256;
@@ -251,6 +254,10 @@ MOE_DEV int build_tile_prefix(const Groups1& gr, int* tile_start) {
       int r0, n;
       group_range(gr, g_lo + j, r0, n);
       t = (n + kQRows - 1) / kQRows;
+      if (grp_rows) {
+        grp_rows[2 * (g_lo + j)] = r0;
+        grp_rows[2 * (g_lo + j) + 1] = n;
+      }
     }
     loc[j] = t;
     sum += t;
@@ -306,36 +313,57 @@ struct BothTile {
 // Tile j of the column-tile-major order: column tile j / total_rt, row tile
 // j % total_rt (a workgroup's consecutive tiles are row-adjacent, so its
 // transposed writes continue each output row where the last tile stopped).
-MOE_DEV BothTile both_tile(const Groups1& gr, const int* tile_start, int total_rt, int col_stride, long j) {
+MOE_DEV BothTile both_tile(const Groups1& gr, const int* tile_start, const int* grp_rows, int total_rt,
+                           int col_stride, long j) {
   BothTile t;
   int g, i;
   lookup_tile(gr, tile_start, static_cast<int>(j % total_rt), g, i, t.p_g);
-  group_range(gr, g, t.r0, t.n);
+  if (gr.offsets) {
+    t.r0 = grp_rows[2 * g];
+    t.n = grp_rows[2 * g + 1];
+  } else {
+    group_range(gr, g, t.r0, t.n);
+  }
   t.row_in = i * kQRows;
   t.c0 = static_cast<int>(j / total_rt) * kBCols;
   t.skip = t.p_g + t.row_in + kQRows > col_stride;
   return t;
 }
 
-// The tile's 16-byte chunks of this thread (rows past the group's end, and
-// gathered rows outside the source, read as zeros).
+// The tile's 16-byte chunks of this thread. Rows past the group's end, and
+// gathered rows outside the source, read as zeros: every load is issued
+// unconditionally (a missing row reads a valid one) and `valid` records
+// which chunks keep their value (applied when the chunks go to LDS). With a
+// gather, the eight row indices are loaded first, then the eight chunks.
+template <bool GATHER>
 MOE_DEV void fetch_tile(const uint16_t* __restrict__ src, int cols, const BothTile& t, RowGather rg,
-                        V16 (&v)[kBChunks]) {
+                        V16 (&v)[kBChunks], uint32_t& valid) {
   constexpr int CH = kBCols / 8;
+  const int last = t.n - t.row_in - 1;   // >= 0: the tile holds at least one row
+  long srow[kBChunks];
+  valid = 0;
 #pragma unroll
   for (int j = 0; j < kBChunks; ++j) {
-    const int qd = threadIdx.x + 256 * j;
-    const int r = qd / CH, c = qd % CH;
-    v[j] = V16{{0u, 0u, 0u, 0u}};
-    if (t.row_in + r < t.n) {
-      long srow = t.r0 + t.row_in + r;
-      if (rg.gather) {
-        const int slot = rg.gather[srow];
-        srow = slot >= 0 ? slot / rg.gk : -1;
-      }
-      if (srow >= 0 && (!rg.gather || srow < rg.n_src))
-        v[j] = *reinterpret_cast<const V16*>(src + static_cast<size_t>(srow) * cols + t.c0 + c * 8);
+    const int r = (threadIdx.x + 256 * j) / CH;
+    srow[j] = static_cast<long>(t.r0) + t.row_in + min(r, last);
+    if (r <= last) valid |= 1u << j;
+  }
+  if constexpr (GATHER) {
+    int slot[kBChunks];
+#pragma unroll
+    for (int j = 0; j < kBChunks; ++j) slot[j] = rg.gather[srow[j]];
+#pragma unroll
+    for (int j = 0; j < kBChunks; ++j) {
+      const long sr = slot[j] >= 0 ? slot[j] / rg.gk : -1;
+      const bool ok = sr >= 0 && sr < rg.n_src;
+      if (!ok) valid &= ~(1u << j);
+      srow[j] = ok ? sr : 0;
     }
+  }
+#pragma unroll
+  for (int j = 0; j < kBChunks; ++j) {
+    const int c = (threadIdx.x + 256 * j) % CH;
+    v[j] = *reinterpret_cast<const V16*>(src + static_cast<size_t>(srow[j]) * cols + t.c0 + c * 8);
   }
 }
 
@@ -380,35 +408,39 @@ MOE_DEV void cols_quads(const uint16_t* tile, int c0, int cols, long p_g, int ro
   }
 }
 
+template <bool GATHER>
 __global__ void __launch_bounds__(256) mx_both_kernel(const uint16_t* __restrict__ src, int rows, int cols,
                                                       Groups1 gr, int col_stride, uint8_t* __restrict__ q_rows,
                                                       uint8_t* __restrict__ s_rows, uint8_t* __restrict__ q_cols,
                                                       uint8_t* __restrict__ s_cols, RowGather rg) {
   __shared__ int tile_start[MOE_MAX_EXPERTS + 1];
+  __shared__ int grp_rows[2 * MOE_MAX_EXPERTS];
   __shared__ __attribute__((aligned(16))) uint16_t tile[kQRows * kBLdw];
   const int tid = threadIdx.x;
   const int tiles_c = cols / kBCols;
-  const int total_rt = build_tile_prefix(gr, tile_start);
+  const int total_rt = build_tile_prefix(gr, tile_start, grp_rows);
   const long total = static_cast<long>(total_rt) * tiles_c;
   // a contiguous run of tiles per workgroup
   const long per = (total + gridDim.x - 1) / gridDim.x;
   long b = blockIdx.x * per;
   const long b_end = b + per < total ? b + per : total;
   V16 pre[kBChunks];
-  if (b < b_end) fetch_tile(src, cols, both_tile(gr, tile_start, total_rt, col_stride, b), rg, pre);
+  uint32_t valid = 0;
+  if (b < b_end) fetch_tile<GATHER>(src, cols, both_tile(gr, tile_start, grp_rows, total_rt, col_stride, b), rg, pre, valid);
   for (; b < b_end; ++b) {
-    const BothTile t = both_tile(gr, tile_start, total_rt, col_stride, b);
+    const BothTile t = both_tile(gr, tile_start, grp_rows, total_rt, col_stride, b);
     if (!t.skip) {
       constexpr int CH = kBCols / 8;
 #pragma unroll
       for (int j = 0; j < kBChunks; ++j) {
         const int qd = tid + 256 * j;
-        *reinterpret_cast<V16*>(tile + (qd / CH) * kBLdw + (qd % CH) * 8) = pre[j];
+        *reinterpret_cast<V16*>(tile + (qd / CH) * kBLdw + (qd % CH) * 8) = keep_if((valid >> j) & 1u, pre[j]);
       }
     }
     __syncthreads();
     const long nb = b + 1;
-    if (nb < b_end) fetch_tile(src, cols, both_tile(gr, tile_start, total_rt, col_stride, nb), rg, pre);
+    if (nb < b_end)
+      fetch_tile<GATHER>(src, cols, both_tile(gr, tile_start, grp_rows, total_rt, col_stride, nb), rg, pre, valid);
     if (!t.skip) {
       const int r0 = t.r0, n = t.n, row_in = t.row_in, c0 = t.c0;
       // rows: thread (r, h) quantises blocks 2h, 2h+1 (64 values) of tile row r
@@ -526,7 +558,7 @@ extern "C" int moe_mx_quantize_both(const void* src, int rows, int cols, const i
   const long row_tiles = group_offsets ? (rows + kQRows - 1) / kQRows + n_groups
                                        : static_cast<long>(n_groups) * ((gr.per + kQRows - 1) / kQRows);
   const long grid = std::min(row_tiles * (cols / kBCols), kBothGrid);
-  mx_both_kernel<<<static_cast<int>(grid), 256, 0, stream>>>(
+  mx_both_kernel<false><<<static_cast<int>(grid), 256, 0, stream>>>(
       static_cast<const uint16_t*>(src), rows, cols, gr, col_stride, static_cast<uint8_t*>(q_rows),
       static_cast<uint8_t*>(s_rows), static_cast<uint8_t*>(q_cols), static_cast<uint8_t*>(s_cols),
       RowGather{nullptr, 1, 0});
@@ -547,7 +579,7 @@ extern "C" int moe_permute_mx(const void* x, int T, int d, int k, const int32_t*
                 aligned4(s_rows) && aligned4(s_cols));
   Groups1 gr{group_offsets, E, n_rows, 0};
   const long grid = std::min(((n_rows + kQRows - 1) / kQRows + E) * static_cast<long>(d / kBCols), kBothGrid);
-  mx_both_kernel<<<static_cast<int>(grid), 256, 0, stream>>>(
+  mx_both_kernel<true><<<static_cast<int>(grid), 256, 0, stream>>>(
       static_cast<const uint16_t*>(x), n_rows, d, gr, col_stride, static_cast<uint8_t*>(q_rows),
       static_cast<uint8_t*>(s_rows), static_cast<uint8_t*>(q_cols), static_cast<uint8_t*>(s_cols),
       RowGather{src_slot, k, T});

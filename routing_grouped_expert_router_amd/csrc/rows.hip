@@ -33,15 +33,6 @@ MOE_DEV float slot_val(float v, int j) { return __int_as_float(__builtin_amdgcn_
 // row, an FMA per valid slot) and reload it there, one wait per use.
 MOE_DEV void pin(V16& v) { asm volatile("" : "+v"(v.w[0]), "+v"(v.w[1]), "+v"(v.w[2]), "+v"(v.w[3])); }
 
-// V16 that is v when ok, else zero (word by word: a select of whole vectors
-// can go through scratch memory)
-MOE_DEV V16 keep_if(bool ok, const V16& v) {
-  V16 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o.w[i] = ok ? v.w[i] : 0u;
-  return o;
-}
-
 // x_perm[row_of[t, j]] = x[t]
 template <typename T>
 __global__ void __launch_bounds__(kRowThreads) permute_kernel(const T* __restrict__ x, int T_, int d,
