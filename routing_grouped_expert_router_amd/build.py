@@ -9,10 +9,11 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
-from typing import List
+from typing import Dict, List
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -41,17 +42,45 @@ def sources() -> List[str]:
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+RESOURCE_REMARK = "-Rpass-analysis=kernel-resource-usage"
+
+
+def resource_report(src: str) -> str:
+    """Path of the per-kernel resource summary (registers, scratch, spills,
+    LDS) that the last build wrote for `src`."""
+    return os.path.join(BUILD, os.path.basename(src)[:-4] + ".resources.txt")
+
+
+def parse_resources(text: str) -> Dict[str, Dict[str, str]]:
+    """{kernel: {field: value}} from the compiler's kernel-resource remarks."""
+    out: Dict[str, Dict[str, str]] = {}
+    cur = None
+    for line in text.splitlines():
+        m = re.search(r"remark:\s+(.*?) \[-Rpass-analysis=kernel-resource-usage\]", line)
+        if not m:
+            continue
+        key, _, val = m.group(1).strip().partition(": ")
+        if key == "Function Name":
+            cur = out.setdefault(val.strip(), {})
+        elif cur is not None:
+            cur[key] = val.strip()
+    return out
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [_hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *HIPCC_FLAGS, RESOURCE_REMARK, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{err}")
-    if err.strip() and verbose:
-        print(err)
+    with open(resource_report(src), "w") as f:
+        f.write("\n".join(l for l in err.splitlines() if "kernel-resource-usage" in l) + "\n")
+    rest = "\n".join(l for l in err.splitlines() if "kernel-resource-usage" not in l and "remark" not in l)
+    if rest.strip() and verbose:
+        print(rest)
     return obj
 
 
