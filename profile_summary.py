@@ -273,7 +273,7 @@ def syncs(args):
             "| step | layer kernels | host window us | GPU span us | HIP calls in the window | "
             "blocking / copy / alloc calls | D2H copies |",
             "|---:|---:|---:|---:|---|---:|---:|"]
-    bad_total = 0
+    bad_total = warm_bad = 0
     for i, st in enumerate(steps):
         hosts = [k[3] for k in st if k[3] is not None]
         h0, h1 = min(h[0] for h in hosts), max(h[1] for h in hosts)
@@ -284,11 +284,18 @@ def syncs(args):
             hist[f] = hist.get(f, 0) + 1
         bad = sum(n for f, n in hist.items() if HOST_BLOCKING.match(f))
         d2h = sum(1 for c0, c1, dr in copies if "DEVICE_TO_HOST" in dr and c1 >= g0 and c0 <= g1)
-        bad_total += bad + d2h
+        if i < args.warmup:
+            warm_bad += bad + d2h
+        else:
+            bad_total += bad + d2h
         desc = ", ".join(f"{f} {n}" for f, n in sorted(hist.items(), key=lambda x: -x[1]))
-        out.append(f"| {i} | {len(st)} | {(h1 - h0) / 1e3:.1f} | {(g1 - g0) / 1e3:.1f} | {desc} | {bad} | {d2h} |")
-    out += ["", f"Steps: {len(steps)}. Blocking, copying or allocating calls and device-to-host copies "
-            f"inside the steps: {bad_total}."]
+        tag = " (warm-up)" if i < args.warmup else ""
+        out.append(f"| {i}{tag} | {len(st)} | {(h1 - h0) / 1e3:.1f} | {(g1 - g0) / 1e3:.1f} | {desc} | {bad} | {d2h} |")
+    timed = max(len(steps) - args.warmup, 0)
+    out += ["", f"Steps: {len(steps)}, of which the first {min(args.warmup, len(steps))} are the bench's warm-up: "
+            "the layer allocates its activation and gradient buffers on first use, through torch's caching "
+            f"allocator ({warm_bad} such calls there). Blocking, copying or allocating calls and device-to-host "
+            f"copies inside the {timed} steps after the warm-up: {bad_total}."]
     open(args.out, "w").write("\n".join(out) + "\n")
     print(args.out)
     return bad_total
@@ -315,6 +322,7 @@ def main():
     y.add_argument("out")
     y.add_argument("dir")
     y.add_argument("--command")
+    y.add_argument("--warmup", type=int, default=1, help="leading steps that are the bench's warm-up")
     m = sub.add_parser("mfma")
     m.add_argument("out")
     m.add_argument("csv")

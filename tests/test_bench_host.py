@@ -107,7 +107,7 @@ def test_sync_summary_flags_blocking_calls_inside_steps_only(tmp_path):
         f.write("MEMORY_COPY_DEVICE_TO_HOST,1500,1600\n")       # during step 0's GPU span
         f.write("MEMORY_COPY_DEVICE_TO_HOST,2500,2600\n")       # between the steps
     out = tmp_path / "s.md"
-    bad = syncs(argparse.Namespace(out=str(out), dir=str(tmp_path), command=None))
+    bad = syncs(argparse.Namespace(out=str(out), dir=str(tmp_path), command=None, warmup=0))
     assert bad == 2
     text = out.read_text()
     assert "| 0 | 2 |" in text and "| 1 | 2 |" in text
