@@ -265,7 +265,8 @@ def mx_layer_leg(wl, t, steps, warmup, ms_base):
     import torch
     from routing_grouped_expert_router_amd.layer import MoELayer
     layer = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16,
-                     routing="learned" if wl.routing == "learned" else "given", mxfp8=True)
+                     routing="learned" if wl.routing == "learned" else "given", mxfp8=True,
+                     mx_bf16_intermediates=False)
 
     def step(requantize):
         def run():
@@ -419,7 +420,9 @@ def experts_leg(steps, warmup):
     wg, wu, wd = rnd(E, d, F, scale=d ** -0.5), rnd(E, d, F, scale=d ** -0.5), rnd(E, F, d, scale=F ** -0.5)
     flops = 18.0 * n * d * F
 
-    mx = MxExperts(n, d, E, F)
+    # H, dG and dU exist only as the MXFP8 copies the next GEMMs read (the
+    # bf16 copies are for inspection; the results are the same bits)
+    mx = MxExperts(n, d, E, F, bf16_intermediates=False)
 
     def mx_step(requantize):
         def run():

@@ -410,7 +410,10 @@ typedef struct moe_mx_gg_desc {
    * qo0_rows [n_rows, F] and qo0_cols [F, col_stride]; DGRAD_DOWN: dG in
    * qo0_*, dU in qo1_*. All NULL (nothing written) or all of the op's set;
    * other ops take none. This fuses the quantisation of the next GEMMs'
-   * operands into the GEMM that produces them. */
+   * operands into the GEMM that produces them. With the copies given, the
+   * bf16 tensor they are made from may be left out: out2 (H) NULL for
+   * FWD_GATE_UP, or out0 and out1 (dG, dU) both NULL for DGRAD_DOWN; the
+   * copies are the same either way (they come from the rounded values). */
   moe_mx_tensor qo0_rows, qo0_cols, qo1_rows, qo1_cols;
 } moe_mx_gg_desc;
 

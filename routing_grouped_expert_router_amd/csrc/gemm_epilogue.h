@@ -180,6 +180,7 @@ MOE_DEV void gg_store_tile(const GGArgs& a, const df32x16_t (&acc)[C::MI][C::NI]
       uint16_t* outu = (uint16_t*)a.u + rbase * F + n0;
       uint16_t* outh = (uint16_t*)a.h + rbase * F + n0;
       const bool keep_gu = a.g != nullptr;   // null g and u: only h is written (recompute)
+      const bool keep_h = a.h != nullptr;    // null h: H only as its MXFP8 copies
       for (int q = tid; q < rows_valid * CPRW; q += NT) {
         const int r = q / CPRW, c = q % CPRW;
         const V16 gv = *reinterpret_cast<const V16*>(stg0 + r * LDW + c * 8);
@@ -195,7 +196,7 @@ MOE_DEV void gg_store_tile(const GGArgs& a, const df32x16_t (&acc)[C::MI][C::NI]
 #pragma unroll
         for (int i = 0; i < 8; ++i) hf[i] = gf[i] * uf[i] / (1.0f + expf(-gf[i]));
         const V16 hv = pack(hf);
-        *reinterpret_cast<V16*>(outh + o) = hv;
+        if (keep_h) *reinterpret_cast<V16*>(outh + o) = hv;
         // H replaces G in the staging plane (this thread's chunk only) for
         // the MXFP8 copies below
         *reinterpret_cast<V16*>(stg0 + r * LDW + c * 8) = hv;
@@ -237,8 +238,10 @@ MOE_DEV void gg_store_tile(const GGArgs& a, const df32x16_t (&acc)[C::MI][C::NI]
             }
       }
       __syncthreads();
-      store_plane(stg0, (uint16_t*)a.dg + rbase * F + n0, F, ch);
-      store_plane(stg1, (uint16_t*)a.du + rbase * F + n0, F, ch);
+      if (a.dg != nullptr) {   // null dg and du: dG and dU only as their MXFP8 copies
+        store_plane(stg0, (uint16_t*)a.dg + rbase * F + n0, F, ch);
+        store_plane(stg1, (uint16_t*)a.du + rbase * F + n0, F, ch);
+      }
       if (a.mxo[0].q_rows != nullptr) {   // MXFP8 copies of this column chunk of dG and dU
         mx_quantize_plane<C>(stg0, a.mxo[0], rbase, rows_valid, n0 + ch * CW, F, a.n_rows, a.mx_P, qcol0, tid);
         mx_quantize_plane<C>(stg1, a.mxo[1], rbase, rows_valid, n0 + ch * CW, F, a.n_rows, a.mx_P, qcol0, tid);

@@ -62,10 +62,15 @@ extern "C" int moe_grouped_gemm_mx(const moe_mx_gg_desc* g, hipStream_t stream) 
   auto out_ok = [](const void* p) { return p != nullptr && aligned16(p); };
   // 32-bit buffer offsets: every operand's span from its expert base < 2 GiB
   long span = (long)g->n_rows * (d > F ? d : F);
+  // MXFP8 copies written by the epilogue: H (FWD_GATE_UP) or dG and dU
+  // (DGRAD_DOWN), each in both orientations, all given or none
+  auto set = [](const moe_mx_tensor& t) { return t.q != nullptr || t.s != nullptr; };
+  const bool qo = set(g->qo0_rows) || set(g->qo0_cols) || set(g->qo1_rows) || set(g->qo1_cols);
   switch (g->op) {
     case MOE_GG_FWD_GATE_UP:
       MOE_CHECK_ARG(tensor_ok(g->a0) && tensor_ok(g->b0) && tensor_ok(g->b1));
-      MOE_CHECK_ARG(out_ok(g->out0) && out_ok(g->out1) && out_ok(g->out2));
+      // H in bf16 may be left out when its MXFP8 copies are written
+      MOE_CHECK_ARG(out_ok(g->out0) && out_ok(g->out1) && (out_ok(g->out2) || (qo && g->out2 == nullptr)));
       span = span > F * E * d ? span : F * E * d;
       break;
     case MOE_GG_FWD_DOWN:
@@ -73,7 +78,9 @@ extern "C" int moe_grouped_gemm_mx(const moe_mx_gg_desc* g, hipStream_t stream) 
       span = span > F * E * d ? span : F * E * d;
       break;
     case MOE_GG_DGRAD_DOWN:
-      MOE_CHECK_ARG(tensor_ok(g->a0) && tensor_ok(g->b0) && out_ok(g->out0) && out_ok(g->out1));
+      // dG and dU in bf16 may be left out (both) when their MXFP8 copies are written
+      MOE_CHECK_ARG(tensor_ok(g->a0) && tensor_ok(g->b0));
+      MOE_CHECK_ARG((out_ok(g->out0) && out_ok(g->out1)) || (qo && g->out0 == nullptr && g->out1 == nullptr));
       MOE_CHECK_ARG(out_ok(g->g) && out_ok(g->u));
       break;
     case MOE_GG_DGRAD_GATE_UP:
@@ -88,11 +95,7 @@ extern "C" int moe_grouped_gemm_mx(const moe_mx_gg_desc* g, hipStream_t stream) 
       MOE_CHECK_ARG(!rows || (tensor_ok(g->a0) && tensor_ok(g->b0) && tensor_ok(g->b1)));
       MOE_CHECK_ARG(out_ok(g->out0) && out_ok(g->out1));
   }
-  // MXFP8 copies written by the epilogue: H (FWD_GATE_UP) or dG and dU
-  // (DGRAD_DOWN), each in both orientations, all given or none
-  auto set = [](const moe_mx_tensor& t) { return t.q != nullptr || t.s != nullptr; };
   const int n_qo = (g->op == MOE_GG_FWD_GATE_UP) ? 1 : (g->op == MOE_GG_DGRAD_DOWN ? 2 : 0);
-  const bool qo = set(g->qo0_rows) || set(g->qo0_cols) || set(g->qo1_rows) || set(g->qo1_cols);
   if (qo) {
     MOE_CHECK_ARG(n_qo > 0);
     MOE_CHECK_ARG(tensor_ok(g->qo0_rows) && tensor_ok(g->qo0_cols));

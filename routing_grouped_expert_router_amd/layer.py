@@ -60,7 +60,7 @@ class MoELayer:
     def __init__(self, T: int, d: int, E: int, k: int, F: int, dtype=torch.bfloat16,
                  routing: str = "learned", capacity: int = 0, backward: bool = True,
                  device: str = "cuda", recompute: bool = False, shared_ff: int = 0,
-                 mxfp8: bool = False, keep_intermediates: bool = True):
+                 mxfp8: bool = False, keep_intermediates: bool = True, mx_bf16_intermediates: bool = True):
         if routing not in ("learned", "given"):
             raise ValueError(routing)
         self.T, self.d, self.E, self.k, self.F = T, d, E, k, F
@@ -109,7 +109,8 @@ class MoELayer:
             if capacity > 0 or dtype != torch.bfloat16 or recompute or shared_ff > 0:
                 raise ValueError("the MXFP8 layer is dropless bf16, without recompute or shared expert")
             from .mx_layer import MxExperts
-            self.mx = MxExperts(self.n_rows, d, E, F, device=device, outputs=False)
+            self.mx = MxExperts(self.n_rows, d, E, F, device=device, outputs=False,
+                                bf16_intermediates=mx_bf16_intermediates)
         self.shared_ff = shared_ff
         if shared_ff > 0:
             Fs = shared_ff
@@ -137,7 +138,9 @@ class MoELayer:
                 self.x_perm = self._new(nr, d)
             self.y_perm, self.y = self._new(nr, d), self._new(self.T, d)
         if not self.recompute and self.g is None:
-            self.g, self.u, self.h = self._new(nr, F), self._new(nr, F), self._new(nr, F)
+            self.g, self.u = self._new(nr, F), self._new(nr, F)
+            if not (self.mxfp8 and not self.mx.bf16_intermediates):   # else H only as MXFP8 copies
+                self.h = self._new(nr, F)
         if self.mxfp8:   # the MXFP8 expert GEMMs write into the layer's buffers
             self.mx.g, self.mx.u, self.mx.h, self.mx.y_perm = self.g, self.u, self.h, self.y_perm
 
@@ -146,7 +149,8 @@ class MoELayer:
         nr, d, F, E, T = self.n_rows, self.d, self.F, self.E, self.T
         if self.dy_perm is None:
             self.dy_perm, self.dx_perm = self._new(nr, d), self._new(nr, d)
-            self.dg, self.du = self._new(nr, F), self._new(nr, F)
+            if not (self.mxfp8 and not self.mx.bf16_intermediates):   # else dG, dU only as MXFP8 copies
+                self.dg, self.du = self._new(nr, F), self._new(nr, F)
         if self.dx is None:
             self.dx = self._new(T, d)
             self.dtopk_w = self._new(T, self.k, dt=torch.float32)

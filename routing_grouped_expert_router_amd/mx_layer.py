@@ -57,9 +57,13 @@ class _Q:
 
 
 class MxExperts:
-    def __init__(self, n_rows: int, d: int, E: int, F: int, device: str = "cuda", outputs: bool = True):
+    def __init__(self, n_rows: int, d: int, E: int, F: int, device: str = "cuda", outputs: bool = True,
+                 bf16_intermediates: bool = True):
         """outputs=False leaves the bf16 results (g, u, h, y_perm, dg, du,
-        dx_perm, dw_*) for the caller to assign."""
+        dx_perm, dw_*) for the caller to assign. bf16_intermediates=False
+        writes H, dG and dU only as the MXFP8 copies the next GEMMs read (the
+        copies, and every output and gradient, are the same bits either way;
+        h, dg and du stay None)."""
         if d % 256 or F % 256:
             raise ValueError("d and F must be multiples of 256")
         self.n, self.d, self.E, self.F = n_rows, d, E, F
@@ -84,10 +88,14 @@ class MxExperts:
         self.dy_c = _Q(d, self.P, dev)
         self.dg_c, self.du_c = _Q(F, self.P, dev), _Q(F, self.P, dev)
         # bf16 results
+        self.bf16_intermediates = bf16_intermediates
+        self.h = self.dg = self.du = None
         if outputs:
-            self.g, self.u, self.h = bf(n, F), bf(n, F), bf(n, F)
+            self.g, self.u = bf(n, F), bf(n, F)
             self.y_perm = bf(n, d)
-            self.dg, self.du = bf(n, F), bf(n, F)
+            if bf16_intermediates:
+                self.h = bf(n, F)
+                self.dg, self.du = bf(n, F), bf(n, F)
             self.dx_perm = bf(n, d)
             self.dw_gate, self.dw_up, self.dw_down = bf(E, d, F), bf(E, d, F), bf(E, F, d)
         # weight-gradient workspace (tile split and padded column starts); the

@@ -13,7 +13,7 @@ from routing_grouped_expert_router_amd import _lib as L
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
 
-INVALID, UNSUPPORTED, WORKSPACE = -1, -2, -3
+INVALID, UNSUPPORTED, WORKSPACE, HIP_ERR = -1, -2, -3, -4
 
 
 def declared():
@@ -384,3 +384,18 @@ def test_mx_gemm_epilogue_copies_argument_errors():
     d.col_stride = P
     d.qo1_cols.s = FAKE + 1                              # misaligned scales
     assert call(d) == INVALID
+    # with the copies given, the bf16 tensor they come from may be left out:
+    # validation passes (on a host without a GPU the launch then fails with
+    # MOE_ERR_HIP); without the copies it is required
+    d.qo1_cols.s = FAKE
+    d.out0 = d.out1 = None
+    assert call(d) == HIP_ERR                            # dG and dU only as MXFP8 copies
+    d.out1 = FAKE
+    assert call(d) == INVALID                            # both or neither
+    d = mk(L.MOE_GG_FWD_GATE_UP)
+    d.out2 = None
+    assert call(d) == INVALID                            # H needed without copies
+    d.qo0_rows.q, d.qo0_rows.s, d.qo0_cols.q, d.qo0_cols.s = FAKE, FAKE, FAKE, FAKE
+    assert call(d) == HIP_ERR                            # H only as MXFP8 copies
+    d.out0 = None
+    assert call(d) == INVALID                            # G and U are always written

@@ -711,3 +711,43 @@ def test_mx_weight_quantisation_tracks_in_place_updates():
     t["w_up"] = None
     t["w_up"] = vals.clone()
     assert mx.quantize_weights(t["w_gate"], t["w_up"], t["w_down"]) is True
+
+
+@pytest.mark.parametrize("full_size", [False, True])
+def test_mx_layer_without_bf16_intermediates_same_bits(full_size):
+    """The benchmark's setting writes H, dG and dU only as the MXFP8 copies
+    the next GEMMs read. Every output, gradient and copy is bit for bit the
+    one the run that also writes the bf16 tensors gives (which the oracle
+    tests check), at a small size and at the benchmark's size."""
+    from moe_inputs import make_inputs, workload
+    from routing_grouped_expert_router_amd.layer import MoELayer
+    wl = workload("e128_uniform_bf16")
+    if not full_size:
+        wl = wl.scaled(T=1024, E=16, d=512, F=256)
+    inp = make_inputs(wl)
+    t = {n: dev(a, "bf16") for n, a in inp.items() if n not in ("topk_idx", "topk_w")}
+    t["topk_idx"], t["topk_w"] = dev(inp["topk_idx"].astype(np.int32), "i32"), dev(inp["topk_w"].astype(np.float32), "f32")
+    got = []
+    for keep in (True, False):
+        lay = MoELayer(wl.T, wl.d, wl.E, wl.k, wl.F, torch.bfloat16, routing="given", mxfp8=True,
+                       mx_bf16_intermediates=keep)
+        for _ in range(2):   # a second step reuses every buffer
+            lay.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], topk_idx=t["topk_idx"], topk_w=t["topk_w"])
+            lay.backward(t["dy"])
+        torch.cuda.synchronize()
+        assert (lay.h is None and lay.dg is None and lay.du is None) == (not keep)
+        mx = lay.mx
+        snap = {n: getattr(lay, n).clone() for n in ("y", "dx", "dtopk_w", "dw_gate", "dw_up", "dw_down", "g", "u")}
+        for n in ("hq", "dgq", "duq"):
+            snap[n + ".q"], snap[n + ".s"] = getattr(mx, n).q.clone(), getattr(mx, n).s.clone()
+        # column copies: only the groups' 128-padded spans are written
+        span = int(sum(-(-c // 128) * 128 for c in host(lay.counts).tolist()))
+        for n in ("h_c", "dg_c", "du_c"):
+            c = getattr(mx, n)
+            snap[n + ".q"] = c.q[:, :span].clone()
+            snap[n + ".s"] = c.s.view(-1)[:wl.F * span // 32].clone()
+        got.append(snap)
+        del lay
+        torch.cuda.empty_cache()
+    for n in got[0]:
+        assert torch.equal(got[0][n], got[1][n]), n
