@@ -26,23 +26,18 @@ __global__ void __launch_bounds__(256) mx_rows_kernel(const uint16_t* __restrict
   const long stride = static_cast<long>(gridDim.x) * 256;   // a multiple of 8: groups stay together
   for (long h = static_cast<long>(blockIdx.x) * 256 + threadIdx.x; h < n_half; h += stride) {
     const V16* p = reinterpret_cast<const V16*>(src + h * 16);
-    float v[16];
-    float lo[8], hi[8];
-    unpack(p[0], lo);
-    unpack(p[1], hi);
-    float amax = 0.f;
+    const V16 lo = p[0], hi = p[1];
+    uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[i] = lo[i];
-      v[8 + i] = hi[i];
-      amax = fmaxf(amax, fmaxf(fabsf(lo[i]), fabsf(hi[i])));
-    }
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    const int x = mx_exponent(amax);
-    const float inv = pow2(-x);
+    for (int i = 0; i < 4; ++i) m = mag_max2(mag_max2(m, lo.w[i]), hi.w[i]);
+    m = max2(m, __shfl_xor(m, 1, 64));
+    const BlockScale bs = block_scale(max_half(m));
+    const int x = bs.x;
     V16 out;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) out.w[w] = e4m3_word(v[4 * w], v[4 * w + 1], v[4 * w + 2], v[4 * w + 3], inv);
+    out.w[0] = encode_quad(lo.w[0], lo.w[1], bs);
+    out.w[1] = encode_quad(lo.w[2], lo.w[3], bs);
+    out.w[2] = encode_quad(hi.w[0], hi.w[1], bs);
+    out.w[3] = encode_quad(hi.w[2], hi.w[3], bs);
     *reinterpret_cast<V16*>(q + h * 16) = out;
     const uint32_t code = static_cast<uint32_t>(x + 127);
     const uint32_t c1 = __shfl_down(code, 2, 64), c2 = __shfl_down(code, 4, 64), c3 = __shfl_down(code, 6, 64);
@@ -185,11 +180,13 @@ MOE_DEV void cols_part(const uint16_t* tile, int c_lo, int c0, int cols, long p_
                        uint8_t* __restrict__ q, uint8_t* __restrict__ s, uint32_t* words) {
   const int tid = threadIdx.x;
   const int c = c_lo + (tid & 63), b = tid >> 6;
-  float v[32];
+  uint32_t w[16];
 #pragma unroll
-  for (int r = 0; r < 32; ++r) v[r] = bf16_to_f32(tile[(32 * b + r) * LDW + c]);
+  for (int r = 0; r < 16; ++r)
+    w[r] = static_cast<uint32_t>(tile[(32 * b + 2 * r) * LDW + c]) |
+           static_cast<uint32_t>(tile[(32 * b + 2 * r + 1) * LDW + c]) << 16;
   V16 out[2];
-  const uint32_t code = quantize_block(v, out);
+  const uint32_t code = quantize_block_bf16(w, out);
   const size_t col = static_cast<size_t>(p_g) + row_in + 32 * b;   // output column of the block
   uint8_t* qp = q + static_cast<size_t>(c0 + c) * col_stride + col;
   reinterpret_cast<V16*>(qp)[0] = out[0];
@@ -377,34 +374,39 @@ MOE_DEV void cols_quads(const uint16_t* tile, int c0, int cols, long p_g, int ro
                         uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
   const int tid = threadIdx.x;
   const int h = tid & 1, b = (tid >> 1) & 3, qd = tid >> 3;   // 32 quads x 4 blocks x 2 halves
-  float v[16][4];
+  // words of tile rows 32b + 16h + r: columns (4qd, 4qd+1) and (4qd+2, 4qd+3)
+  uint32_t w01[16], w23[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const uint2 w = *reinterpret_cast<const uint2*>(tile + (32 * b + 16 * h + r) * kBLdw + 4 * qd);
-    v[r][0] = __uint_as_float(w.x << 16);
-    v[r][1] = __uint_as_float(w.x & 0xffff0000u);
-    v[r][2] = __uint_as_float(w.y << 16);
-    v[r][3] = __uint_as_float(w.y & 0xffff0000u);
+    w01[r] = w.x;
+    w23[r] = w.y;
   }
-  float amax[4] = {0.f, 0.f, 0.f, 0.f};
+  uint32_t m01 = 0, m23 = 0;
 #pragma unroll
-  for (int r = 0; r < 16; ++r)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) amax[j] = fmaxf(amax[j], fabsf(v[r][j]));
+  for (int r = 0; r < 16; ++r) {
+    m01 = mag_max2(m01, w01[r]);
+    m23 = mag_max2(m23, w23[r]);
+  }
+  m01 = max2(m01, __shfl_xor(m01, 1, 64));
+  m23 = max2(m23, __shfl_xor(m23, 1, 64));
   const size_t col = static_cast<size_t>(p_g) + row_in + 32 * b + 16 * h;   // first token column
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float m = fmaxf(amax[j], __shfl_xor(amax[j], 1, 64));
-    const int x = mx_exponent(m);
-    const float inv = pow2(-x);
+    const uint32_t m = j < 2 ? m01 : m23;
+    const BlockScale bs = block_scale(j & 1 ? m >> 16 : m & 0xffffu);
+    // rows 2i, 2i+1 of column j side by side: the low (j even) or high halves
+    const uint32_t sel = j & 1 ? 0x07060302u : 0x05040100u;
+    const uint32_t* wj = j < 2 ? w01 : w23;
     V16 out;
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-      out.w[w] = e4m3_word(v[4 * w][j], v[4 * w + 1][j], v[4 * w + 2][j], v[4 * w + 3][j], inv);
+    for (int q = 0; q < 4; ++q)
+      out.w[q] = encode_quad(__builtin_amdgcn_perm(wj[4 * q + 1], wj[4 * q], sel),
+                             __builtin_amdgcn_perm(wj[4 * q + 3], wj[4 * q + 2], sel), bs);
     const int c = 4 * qd + j;
     *reinterpret_cast<V16*>(q + static_cast<size_t>(c0 + c) * col_stride + col) = out;
     if (h == 0)
-      s[4 * (static_cast<size_t>(cols) * ((p_g + row_in) / kQRows) + c0 + c) + b] = static_cast<uint8_t>(x + 127);
+      s[4 * (static_cast<size_t>(cols) * ((p_g + row_in) / kQRows) + c0 + c) + b] = static_cast<uint8_t>(bs.x + 127);
   }
 }
 
@@ -446,17 +448,16 @@ __global__ void __launch_bounds__(256) mx_both_kernel(const uint16_t* __restrict
       // rows: thread (r, h) quantises blocks 2h, 2h+1 (64 values) of tile row r
       {
         const int r = tid >> 1, h = tid & 1;
-        float v[2][32];
+        uint32_t w[32];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          float f[8];
-          unpack(*reinterpret_cast<const V16*>(tile + r * kBLdw + 64 * h + 8 * k), f);
+          const V16 t8 = *reinterpret_cast<const V16*>(tile + r * kBLdw + 64 * h + 8 * k);
 #pragma unroll
-          for (int m = 0; m < 8; ++m) v[k >> 2][8 * (k & 3) + m] = f[m];
+          for (int m = 0; m < 4; ++m) w[4 * k + m] = t8.w[m];
         }
         V16 out[2][2];
-        const uint32_t c_lo = quantize_block(v[0], out[0]);
-        const uint32_t c_hi = quantize_block(v[1], out[1]);
+        const uint32_t c_lo = quantize_block_bf16(w, out[0]);
+        const uint32_t c_hi = quantize_block_bf16(w + 16, out[1]);
         const uint32_t pair = c_lo | (c_hi << 8);
         const uint32_t other = __shfl_xor(pair, 1, 64);
         if (row_in + r < n) {
