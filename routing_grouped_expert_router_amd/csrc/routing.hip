@@ -333,13 +333,12 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
 }
 
 // ============================================================== routing metadata
-// Three short passes over the R = T*k slots, never leaving the GPU:
+// Two short passes over the R = T*k slots, never leaving the GPU:
 //   1. per-block expert histogram (blocks of kSlotsPerBlock slots)
-//   2. one workgroup: per-expert exclusive scan over blocks, counts,
-//      offsets = exclusive scan over experts, n_dropped
-//   3. per block: stable rank of each slot among the block's slots of the
-//      same expert (wave ballots over the id bits, waves in slot order),
-//      giving row_of and src_slot.
+//   2. per block: the experts' counts and offsets (exclusive scan over
+//      experts), n_dropped, the block's per-expert bases (sums over earlier
+//      blocks), then the stable rank of each slot among the block's slots
+//      of the same expert, giving row_of and src_slot.
 constexpr int kSlotsPerBlock = 1024;
 constexpr int kMetaThreads = 256;
 
@@ -368,9 +367,11 @@ __global__ void __launch_bounds__(kMetaThreads) hist_kernel(const int32_t* __res
     src_slot[r] = -1;
 }
 
-// Block-wide exclusive scan of one int per thread (blockDim.x == 1024).
-__device__ int block_exclusive_scan_1024(int v, int* total) {
-  __shared__ int wsum[16];
+// Exclusive scan over the workgroup (kMetaThreads threads) of one int per
+// thread; *total gets the sum.
+__device__ int block_exclusive_scan(int v, int* total) {
+  constexpr int kWaves = kMetaThreads / 64;
+  __shared__ int wsum[kWaves];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int incl = v;
 #pragma unroll
@@ -380,90 +381,68 @@ __device__ int block_exclusive_scan_1024(int v, int* total) {
   }
   if (lane == 63) wsum[w] = incl;
   __syncthreads();
-  if (w == 0) {
-    int s = lane < 16 ? wsum[lane] : 0;
+  int before = incl - v, all = 0;
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int n = __shfl_up(s, o, 64);
-      if (lane >= o) s += n;
-    }
-    if (lane < 16) wsum[lane] = s;   // inclusive over waves
+  for (int j = 0; j < kWaves; ++j) {
+    if (j < w) before += wsum[j];
+    all += wsum[j];
   }
-  __syncthreads();
-  const int before = (w > 0 ? wsum[w - 1] : 0) + incl - v;
-  *total = wsum[15];
+  __syncthreads();   // wsum may be reused by the next call
+  *total = all;
   return before;
 }
 
-// G threads (a power of two, G <= 64, within one wave) share expert e: each
-// sums a run of blocks with independent loads, the group scans those sums,
-// and each thread then writes the exclusive per-block bases of its run.
-__global__ void __launch_bounds__(1024) scan_kernel(int32_t* __restrict__ hist, int nblk, int E,
-                                                    int capacity, int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ n_dropped) {
-  int G = 1;
-  while (G * 2 * E <= 1024 && G * 2 <= 64) G *= 2;
-  const int e = threadIdx.x / G, g = threadIdx.x % G;
-  const bool live = e < E;
-  const int per = (nblk + G - 1) / G;
-  const int b0 = min(nblk, g * per), b1 = min(nblk, b0 + per);
-  constexpr int kBurst = 16;
-  int part = 0;
-  if (live) {
-    for (int b = b0; b < b1; b += kBurst) {
-      int v[kBurst];
-#pragma unroll
-      for (int i = 0; i < kBurst; ++i) v[i] = b + i < b1 ? hist[(size_t)(b + i) * E + e] : 0;
-#pragma unroll
-      for (int i = 0; i < kBurst; ++i) part += v[i];
-    }
-  }
-  // inclusive scan of the partial sums over the G lanes of this expert
-  const int lane = threadIdx.x & 63;
-  int incl = part;
-  for (int o = 1; o < G; o <<= 1) {
-    const int n = __shfl_up(incl, o, 64);
-    if ((lane % G) >= o) incl += n;
-  }
-  const int total = __shfl(incl, (lane / G) * G + G - 1, 64);
-  if (live) {
-    int run = incl - part;
-    for (int b = b0; b < b1; b += kBurst) {
-      int v[kBurst];
-#pragma unroll
-      for (int i = 0; i < kBurst; ++i) v[i] = b + i < b1 ? hist[(size_t)(b + i) * E + e] : 0;
-#pragma unroll
-      for (int i = 0; i < kBurst; ++i) {
-        if (b + i < b1) hist[(size_t)(b + i) * E + e] = run;
-        run += v[i];
-      }
-    }
-    if (g == 0) counts[e] = total;
-  }
-  __syncthreads();
-  // exclusive scan of counts over experts: one thread per expert
-  const int ce = threadIdx.x < E ? counts[threadIdx.x] : 0;
-  int tot;
-  const int off = block_exclusive_scan_1024(ce, &tot);
-  if (threadIdx.x < E) offsets[threadIdx.x] = off;
-  if (threadIdx.x == 0) offsets[E] = tot;
-  const int drop = (capacity > 0 && threadIdx.x < E && ce > capacity) ? ce - capacity : 0;
-  int dtotal;
-  __syncthreads();
-  (void)block_exclusive_scan_1024(drop, &dtotal);
-  if (threadIdx.x == 0) *n_dropped = dtotal;
-}
-
+// Passes 2 and 3 in one launch. Every block sums the histogram's columns
+// itself: over all blocks (the experts' counts, hence offsets and drops,
+// the same in every block) and over the blocks before it (its own bases);
+// block 0 writes counts, offsets and n_dropped. Then the stable rank of
+// each of the block's slots among its slots of the same expert (wave
+// ballots over the id bits, waves in slot order) gives row_of and src_slot.
 __global__ void __launch_bounds__(kMetaThreads) rank_kernel(
-    const int32_t* __restrict__ idx, int R, int E, int capacity, const int32_t* __restrict__ hist,
-    const int32_t* __restrict__ offsets, int32_t* __restrict__ row_of, int32_t* __restrict__ src_slot) {
+    const int32_t* __restrict__ idx, int R, int E, int capacity, const int32_t* __restrict__ hist, int nblk,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ src_slot) {
   constexpr int kWaves = kMetaThreads / 64;
   constexpr int kPerWave = kSlotsPerBlock / kWaves;
+  constexpr int kBurst = 16;
+  __shared__ int tot_s[MOE_MAX_EXPERTS], pre_s[MOE_MAX_EXPERTS], off_s[MOE_MAX_EXPERTS];
   __shared__ int base[kWaves][MOE_MAX_EXPERTS];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < kWaves * E; i += kMetaThreads) base[i / E][i % E] = 0;
+  __shared__ int dropped_s;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int e = tid; e < E; e += kMetaThreads) {
+    tot_s[e] = 0;
+    pre_s[e] = 0;
+  }
+  for (int i = tid; i < kWaves * E; i += kMetaThreads) base[i / E][i % E] = 0;
+  if (tid == 0) dropped_s = 0;
   __syncthreads();
+  // column sums: P parts of the blocks per expert, bursts of independent
+  // loads (indices clamped to the part, values past it masked)
+  {
+    const int P = E >= kMetaThreads ? 1 : kMetaThreads / E;
+    const int per = (nblk + P - 1) / P;
+    for (int i = tid; i < E * P; i += kMetaThreads) {
+      const int e = i % E, part = i / E;
+      const int b0 = min(nblk, part * per), b1 = min(nblk, b0 + per);
+      int tot = 0, pre = 0;
+      for (int bb = b0; bb < b1; bb += kBurst) {
+        int v[kBurst];
+#pragma unroll
+        for (int j = 0; j < kBurst; ++j) v[j] = hist[(size_t)min(bb + j, b1 - 1) * E + e];
+#pragma unroll
+        for (int j = 0; j < kBurst; ++j) {
+          const int x = bb + j < b1 ? v[j] : 0;
+          tot += x;
+          pre += bb + j < (int)blockIdx.x ? x : 0;
+        }
+      }
+      if (b0 < b1) {
+        atomicAdd(&tot_s[e], tot);
+        atomicAdd(&pre_s[e], pre);
+      }
+    }
+  }
+  // slots per wave and expert of this block
   const int s_wave = blockIdx.x * kSlotsPerBlock + w * kPerWave;
   for (int c = 0; c < kPerWave; c += 64) {
     const int s = s_wave + c + lane;
@@ -471,8 +450,45 @@ __global__ void __launch_bounds__(kMetaThreads) rank_kernel(
     if (e >= 0 && e < E) atomicAdd(&base[w][e], 1);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kMetaThreads) {
-    int b = offsets[e] + hist[(size_t)blockIdx.x * E + e];
+  // offsets: exclusive scan of the counts over experts (a run of consecutive
+  // experts per thread); drops past the capacity
+  {
+    constexpr int kMaxRun = (MOE_MAX_EXPERTS + kMetaThreads - 1) / kMetaThreads;
+    const int run = (E + kMetaThreads - 1) / kMetaThreads;
+    const int e0 = tid * run;
+    int sum = 0, drop = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxRun; ++j) {
+      const int e = e0 + j;
+      if (j < run && e < E) {
+        const int c = tot_s[e];
+        sum += c;
+        drop += capacity > 0 && c > capacity ? c - capacity : 0;
+      }
+    }
+    int total;
+    int before = block_exclusive_scan(sum, &total);
+#pragma unroll
+    for (int j = 0; j < kMaxRun; ++j) {
+      const int e = e0 + j;
+      if (j < run && e < E) {
+        off_s[e] = before;
+        before += tot_s[e];
+      }
+    }
+    if (drop) atomicAdd(&dropped_s, drop);
+    if (blockIdx.x == 0 && tid == 0) offsets[E] = total;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int e = tid; e < E; e += kMetaThreads) {
+      counts[e] = tot_s[e];
+      offsets[e] = off_s[e];
+    }
+    if (tid == 0) *n_dropped = dropped_s;
+  }
+  for (int e = tid; e < E; e += kMetaThreads) {
+    int b = off_s[e] + pre_s[e];
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
       const int n = base[ww][e];
@@ -504,7 +520,7 @@ __global__ void __launch_bounds__(kMetaThreads) rank_kernel(
       int row = -1;
       if (ok) {
         if (capacity > 0) {
-          const int r = pos - offsets[e];
+          const int r = pos - off_s[e];
           row = r < capacity ? e * capacity + r : -1;
         } else {
           row = pos;
@@ -916,10 +932,8 @@ extern "C" int moe_offsets(const int32_t* topk_idx, int T, int k, int E, int cap
   hist_kernel<<<nblk, kMetaThreads, 0, stream>>>(topk_idx, static_cast<int>(R), E, hist, src_slot,
                                                  static_cast<int>(n_rows), err_flag);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
-  scan_kernel<<<1, 1024, 0, stream>>>(hist, nblk, E, capacity, counts, offsets, n_dropped);
-  if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
-  rank_kernel<<<nblk, kMetaThreads, 0, stream>>>(topk_idx, static_cast<int>(R), E, capacity, hist,
-                                                 offsets, row_of, src_slot);
+  rank_kernel<<<nblk, kMetaThreads, 0, stream>>>(topk_idx, static_cast<int>(R), E, capacity, hist, nblk,
+                                                 counts, offsets, n_dropped, row_of, src_slot);
   return launch_status();
 }
 

@@ -26,7 +26,7 @@ def test_traffic_summaries_parse():
     ("void moe::gg_dma_kernel<5, moe::DmaCfg<128, 256, 2, 2, 32, 3, 2> >(moe::GGArgs)", "gg_wgrad_gate_up"),
     ("void moe::combine_bwd_kernel<unsigned short>(unsigned short const*)", "combine_bwd"),
     ("void moe::combine_kernel<unsigned short>(unsigned short const*)", "combine"),
-    ("moe::scan_kernel(int*, int, int, int, int*, int*, int*)", "offsets"),
+    ("moe::rank_kernel(int const*, int, int, int, int const*, int, int*, int*, int*, int*, int*)", "offsets"),
     ("__amd_rocclr_copyBuffer", None),
 ])
 def test_stage_of(name, stage):
