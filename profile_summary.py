@@ -43,7 +43,7 @@ ROW_KERNELS = [
     ("permute_bwd_kernel", "permute_bwd"),
     ("combine_kernel", "combine"), ("permute_kernel", "permute"),
     ("zero_pad_rows_kernel", "permute"),
-    ("hist_kernel", "offsets"), ("rank_kernel", "offsets"),
+    ("hist_kernel", "offsets"), ("scan_kernel", "offsets"), ("rank_kernel", "offsets"),
     ("router_gemm_kernel", "router_gemm"), ("router_gemm_lds_kernel", "router_gemm"),
     ("router_gemm_mfma_kernel", "router_gemm"), ("router_bwd_mfma_kernel", "router_gemm_bwd"),
     ("route_bwd_kernel", "route_bwd"), ("route_kernel", "route"),

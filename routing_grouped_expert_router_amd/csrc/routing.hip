@@ -333,14 +333,18 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ lo
 }
 
 // ============================================================== routing metadata
-// Two short passes over the R = T*k slots, never leaving the GPU:
+// Short passes over the R = T*k slots, never leaving the GPU:
 //   1. per-block expert histogram (blocks of kSlotsPerBlock slots)
-//   2. per block: the experts' counts and offsets (exclusive scan over
-//      experts), n_dropped, the block's per-expert bases (sums over earlier
-//      blocks), then the stable rank of each slot among the block's slots
-//      of the same expert, giving row_of and src_slot.
+//   2. counts, offsets (exclusive scan over experts), n_dropped and each
+//      block's per-expert bases (sums over earlier blocks): inside pass 3
+//      for small histograms, else one workgroup of its own
+//   3. per block: stable rank of each slot among the block's slots of the
+//      same expert, giving row_of and src_slot.
 constexpr int kSlotsPerBlock = 1024;
 constexpr int kMetaThreads = 256;
+// Largest histogram (blocks x experts) every rank block sums itself: 64 KB of
+// reads per block; larger ones go through scan_kernel first.
+constexpr long kLocalScanMax = 16384;
 
 __global__ void __launch_bounds__(kMetaThreads) hist_kernel(const int32_t* __restrict__ idx, int R,
                                                             int E, int32_t* __restrict__ hist,
@@ -365,6 +369,95 @@ __global__ void __launch_bounds__(kMetaThreads) hist_kernel(const int32_t* __res
   // every row starts as a pad row; pass 3 fills the live ones
   for (int r = blockIdx.x * kMetaThreads + threadIdx.x; r < n_rows; r += gridDim.x * kMetaThreads)
     src_slot[r] = -1;
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim.x == 1024).
+__device__ int block_exclusive_scan_1024(int v, int* total) {
+  __shared__ int wsum[16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += n;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  if (w == 0) {
+    int s = lane < 16 ? wsum[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int n = __shfl_up(s, o, 64);
+      if (lane >= o) s += n;
+    }
+    if (lane < 16) wsum[lane] = s;   // inclusive over waves
+  }
+  __syncthreads();
+  const int before = (w > 0 ? wsum[w - 1] : 0) + incl - v;
+  *total = wsum[15];
+  return before;
+}
+
+// Pass 2 for large histograms (nblk * E above kLocalScanMax): one
+// workgroup. G threads (a power of two, G <= 64, within one wave) share
+// expert e: each sums a run of blocks with independent loads, the group
+// scans those sums, and each thread then writes the exclusive per-block
+// bases of its run over the histogram; then counts, offsets, n_dropped.
+__global__ void __launch_bounds__(1024) scan_kernel(int32_t* __restrict__ hist, int nblk, int E,
+                                                    int capacity, int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ n_dropped) {
+  int G = 1;
+  while (G * 2 * E <= 1024 && G * 2 <= 64) G *= 2;
+  const int e = threadIdx.x / G, g = threadIdx.x % G;
+  const bool live = e < E;
+  const int per = (nblk + G - 1) / G;
+  const int b0 = min(nblk, g * per), b1 = min(nblk, b0 + per);
+  constexpr int kBurst = 16;
+  int part = 0;
+  if (live) {
+    for (int b = b0; b < b1; b += kBurst) {
+      int v[kBurst];
+#pragma unroll
+      for (int i = 0; i < kBurst; ++i) v[i] = b + i < b1 ? hist[(size_t)(b + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBurst; ++i) part += v[i];
+    }
+  }
+  // inclusive scan of the partial sums over the G lanes of this expert
+  const int lane = threadIdx.x & 63;
+  int incl = part;
+  for (int o = 1; o < G; o <<= 1) {
+    const int n = __shfl_up(incl, o, 64);
+    if ((lane % G) >= o) incl += n;
+  }
+  const int total = __shfl(incl, (lane / G) * G + G - 1, 64);
+  if (live) {
+    int run = incl - part;
+    for (int b = b0; b < b1; b += kBurst) {
+      int v[kBurst];
+#pragma unroll
+      for (int i = 0; i < kBurst; ++i) v[i] = b + i < b1 ? hist[(size_t)(b + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBurst; ++i) {
+        if (b + i < b1) hist[(size_t)(b + i) * E + e] = run;
+        run += v[i];
+      }
+    }
+    if (g == 0) counts[e] = total;
+  }
+  __syncthreads();
+  // exclusive scan of counts over experts: one thread per expert
+  const int ce = threadIdx.x < E ? counts[threadIdx.x] : 0;
+  int tot;
+  const int off = block_exclusive_scan_1024(ce, &tot);
+  if (threadIdx.x < E) offsets[threadIdx.x] = off;
+  if (threadIdx.x == 0) offsets[E] = tot;
+  const int drop = (capacity > 0 && threadIdx.x < E && ce > capacity) ? ce - capacity : 0;
+  int dtotal;
+  __syncthreads();
+  (void)block_exclusive_scan_1024(drop, &dtotal);
+  if (threadIdx.x == 0) *n_dropped = dtotal;
 }
 
 // Exclusive scan over the workgroup (kMetaThreads threads) of one int per
@@ -392,16 +485,19 @@ __device__ int block_exclusive_scan(int v, int* total) {
   return before;
 }
 
-// Passes 2 and 3 in one launch. Every block sums the histogram's columns
+// Pass 3, with pass 2 folded in for small histograms (local_scan: nblk * E
+// at most kLocalScanMax). Then every block sums the histogram's columns
 // itself: over all blocks (the experts' counts, hence offsets and drops,
 // the same in every block) and over the blocks before it (its own bases);
-// block 0 writes counts, offsets and n_dropped. Then the stable rank of
-// each of the block's slots among its slots of the same expert (wave
-// ballots over the id bits, waves in slot order) gives row_of and src_slot.
+// block 0 writes counts, offsets and n_dropped. Otherwise scan_kernel has
+// left each block's bases in the histogram and the offsets in `offsets`.
+// Then the stable rank of each of the block's slots among its slots of the
+// same expert (wave ballots over the id bits, waves in slot order) gives
+// row_of and src_slot.
 __global__ void __launch_bounds__(kMetaThreads) rank_kernel(
     const int32_t* __restrict__ idx, int R, int E, int capacity, const int32_t* __restrict__ hist, int nblk,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ n_dropped,
-    int32_t* __restrict__ row_of, int32_t* __restrict__ src_slot) {
+    int32_t* __restrict__ row_of, int32_t* __restrict__ src_slot, bool local_scan) {
   constexpr int kWaves = kMetaThreads / 64;
   constexpr int kPerWave = kSlotsPerBlock / kWaves;
   constexpr int kBurst = 16;
@@ -418,7 +514,7 @@ __global__ void __launch_bounds__(kMetaThreads) rank_kernel(
   __syncthreads();
   // column sums: P parts of the blocks per expert, bursts of independent
   // loads (indices clamped to the part, values past it masked)
-  {
+  if (local_scan) {
     const int P = E >= kMetaThreads ? 1 : kMetaThreads / E;
     const int per = (nblk + P - 1) / P;
     for (int i = tid; i < E * P; i += kMetaThreads) {
@@ -452,7 +548,12 @@ __global__ void __launch_bounds__(kMetaThreads) rank_kernel(
   __syncthreads();
   // offsets: exclusive scan of the counts over experts (a run of consecutive
   // experts per thread); drops past the capacity
-  {
+  if (!local_scan) {
+    for (int e = tid; e < E; e += kMetaThreads) {
+      off_s[e] = offsets[e];
+      pre_s[e] = hist[(size_t)blockIdx.x * E + e];
+    }
+  } else {
     constexpr int kMaxRun = (MOE_MAX_EXPERTS + kMetaThreads - 1) / kMetaThreads;
     const int run = (E + kMetaThreads - 1) / kMetaThreads;
     const int e0 = tid * run;
@@ -480,7 +581,7 @@ __global__ void __launch_bounds__(kMetaThreads) rank_kernel(
     if (blockIdx.x == 0 && tid == 0) offsets[E] = total;
   }
   __syncthreads();
-  if (blockIdx.x == 0) {
+  if (local_scan && blockIdx.x == 0) {
     for (int e = tid; e < E; e += kMetaThreads) {
       counts[e] = tot_s[e];
       offsets[e] = off_s[e];
@@ -932,8 +1033,13 @@ extern "C" int moe_offsets(const int32_t* topk_idx, int T, int k, int E, int cap
   hist_kernel<<<nblk, kMetaThreads, 0, stream>>>(topk_idx, static_cast<int>(R), E, hist, src_slot,
                                                  static_cast<int>(n_rows), err_flag);
   if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+  const bool local_scan = static_cast<long>(nblk) * E <= kLocalScanMax;
+  if (!local_scan) {
+    scan_kernel<<<1, 1024, 0, stream>>>(hist, nblk, E, capacity, counts, offsets, n_dropped);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+  }
   rank_kernel<<<nblk, kMetaThreads, 0, stream>>>(topk_idx, static_cast<int>(R), E, capacity, hist, nblk,
-                                                 counts, offsets, n_dropped, row_of, src_slot);
+                                                 counts, offsets, n_dropped, row_of, src_slot, local_scan);
   return launch_status();
 }
 

@@ -86,7 +86,10 @@ def _draw(rng, T, E, k, skew=0.0):
 @pytest.mark.parametrize("T,E,k,C,skew", [
     (1, 1, 1, 0, 0), (7, 4, 4, 0, 0), (1000, 8, 2, 0, 0), (3000, 128, 4, 0, 1.2),
     (3000, 128, 4, 96, 1.2), (16384, 128, 4, 640, 1.2), (5000, 1024, 16, 0, 0.5),
-    (2049, 3, 1, 0, 0), (2000, 16, 4, 10, 0.0), (600, 8, 4, 400, 0.0)])
+    (2049, 3, 1, 0, 0), (2000, 16, 4, 10, 0.0), (600, 8, 4, 400, 0.0),
+    # 64 blocks of 1024 slots x 256 experts: the largest histogram each rank
+    # block sums itself; one block more goes through the separate scan pass
+    (16384, 256, 4, 0, 0.8), (16385, 256, 4, 0, 0.8), (16385, 256, 4, 200, 0.8)])
 def test_offsets_parity(T, E, k, C, skew):
     rng = _rng(2, T, E, k, C)
     idx = _draw(rng, T, E, k, skew)
