@@ -477,6 +477,72 @@ def experts_leg(steps, warmup):
     }
 
 
+def vendor_gemm_leg(wl, t, steps, warmup):
+    """The six expert GEMMs of the layer against hipBLASLt (torch.bmm) on the
+    same products with an exactly equal split (every expert T*k/E rows: token
+    t's slot j goes to expert (k*t + j) mod E), which a batched product can
+    express. Ours run inside the layer step, with their fused epilogues
+    (SwiGLU and its derivative, the gate and up halves written apart);
+    hipBLASLt's are plain products of contiguous operands into preallocated
+    outputs. Both are timed with events over the same number of launches."""
+    import torch
+    from routing_grouped_expert_router_amd.layer import MoELayer
+    T, d, E, k, F = wl.T, wl.d, wl.E, wl.k, wl.F
+    if (T * k) % E:
+        return None
+    m = T * k // E
+    devc = torch.device("cuda:0")
+    ids = (torch.arange(T * k, device=devc, dtype=torch.int64) % E).to(torch.int32).view(T, k)
+    wts = torch.full((T, k), 1.0 / k, dtype=torch.float32, device=devc)
+    layer = MoELayer(T, d, E, k, F, torch.bfloat16, routing="given")
+
+    def step():
+        layer.forward(t["x"], t["w_gate"], t["w_up"], t["w_down"], topk_idx=ids, topk_w=wts)
+        layer.backward(t["dy"])
+
+    _, st, _ = timed(layer, step, steps, warmup)
+    counts = layer.counts.cpu()
+    assert int(counts.min()) == m and int(counts.max()) == m
+    del layer
+    torch.cuda.empty_cache()
+    # (stage, batch operand shapes [E, M, K] x [E, K, N]); flops 2*E*M*K*N
+    ops = [("gg_fwd_gate_up", (m, d), (d, 2 * F)), ("gg_fwd_down", (m, F), (F, d)),
+           ("gg_dgrad_down", (m, d), (d, F)), ("gg_dgrad_gate_up", (m, 2 * F), (2 * F, d)),
+           ("gg_wgrad_down", (F, m), (m, d)), ("gg_wgrad_gate_up", (d, m), (m, 2 * F))]
+    g = torch.Generator(device=devc)
+    g.manual_seed(7)
+    out = {"experts": E, "rows_per_expert": m, "ops": {}}
+    ours_us = blas_us = flops_all = 0.0
+    for name, (M, K), (K2, N) in ops:
+        a = torch.randn(E, M, K, device=devc, generator=g).to(torch.bfloat16)
+        b = torch.randn(E, K2, N, device=devc, generator=g).to(torch.bfloat16)
+        c = torch.empty(E, M, N, device=devc, dtype=torch.bfloat16)
+        for _ in range(warmup):
+            torch.bmm(a, b, out=c)
+        torch.cuda.synchronize()
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(steps):
+            torch.bmm(a, b, out=c)
+        s1.record()
+        torch.cuda.synchronize()
+        b_us = s0.elapsed_time(s1) / steps * 1e3
+        o_us = st[name] * 1e3
+        fl = 2.0 * E * M * K * N
+        out["ops"][name] = {"ours_us": round(o_us, 1), "ours_tflops": round(fl / o_us / 1e6, 1),
+                            "hipblaslt_us": round(b_us, 1), "hipblaslt_tflops": round(fl / b_us / 1e6, 1)}
+        ours_us += o_us
+        blas_us += b_us
+        flops_all += fl
+        del a, b, c
+    torch.cuda.empty_cache()
+    out["ours_tflops"] = round(flops_all / ours_us / 1e6, 1)
+    out["hipblaslt_tflops"] = round(flops_all / blas_us / 1e6, 1)
+    out["ours_time_vs_hipblaslt"] = round(ours_us / blas_us, 3)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -492,6 +558,8 @@ def main():
     ap.add_argument("--no-mxfp8-layer", action="store_true", help="skip the MXFP8 routed-layer leg")
     ap.add_argument("--no-pool", action="store_true", help="skip the 8-expert comparison leg")
     ap.add_argument("--no-skew", action="store_true", help="skip the Zipf dropless/padded leg")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the hipBLASLt comparison of the six expert GEMMs on an equal split")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the reference "
@@ -620,6 +688,9 @@ def main():
         pd = workload_leg("e128_zipf_bf16", 1.25, args.steps, args.warmup)
         out["skewed_routing"] = {"dropless": dl, "padded_cf1.25": pd,
                                  "padded_time_vs_dropless": round(pd["ms_per_step"] / dl["ms_per_step"], 3)}
+    if not args.no_vendor and cap == 0:
+        log("vendor GEMM leg (hipBLASLt on the equal split) ...")
+        out["vendor_gemm"] = vendor_gemm_leg(wl, t, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host for the CPU baseline ...")
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)

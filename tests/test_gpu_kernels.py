@@ -332,6 +332,7 @@ def _gg_case(kind, counts, d, F, seed, capacity=0):
     ("bf16", [300, 0, 1, 129, 513, 64, 0, 257], 256, 512, 0),          # MFMA path, ragged
     ("bf16", [700, 5, 1000, 0], 512, 256, 0),
     ("bf16", [40, 100, 0, 7, 128, 3], 256, 256, 128),                 # padded (uniform groups)
+    ("bf16", [40, 300, 0, 7, 128, 3], 512, 512, 256),                 # padded, wide data-gradient tiles
     ("bf16", [33, 0, 70], 136, 200, 0),                               # plain path, odd shapes
     ("f32", [33, 0, 70, 1], 128, 256, 0),
     ("f32", [20, 9], 72, 40, 24),
