@@ -11,6 +11,13 @@ namespace moe {
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float df32x16_t;
 
+// sigmoid(x) = 1 / (1 + e^-x) with the hardware exponential and reciprocal
+// (v_exp_f32 after the scaling by log2 e, v_rcp_f32): a few binary32 ulp from
+// the correctly rounded value, far below the bf16 rounding of every output it
+// feeds, and it takes the SwiGLU epilogues' VALU time off the GEMMs (an IEEE
+// division is a dozen instructions). Large |x| give exactly 0 or 1.
+MOE_DEV float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
 MOE_DEV uint2 dpack4(const float* v) { return make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])); }
 MOE_DEV void dunpack4(uint2 p, float* v) {
   v[0] = __uint_as_float(p.x << 16);
@@ -194,7 +201,7 @@ MOE_DEV void gg_store_tile(const GGArgs& a, const df32x16_t (&acc)[C::MI][C::NI]
         unpack(gv, gf);
         unpack(uv, uf);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) hf[i] = gf[i] * uf[i] / (1.0f + expf(-gf[i]));
+        for (int i = 0; i < 8; ++i) hf[i] = gf[i] * uf[i] * fast_sigmoid(gf[i]);
         const V16 hv = pack(hf);
         if (keep_h) *reinterpret_cast<V16*>(outh + o) = hv;
         // H replaces G in the staging plane (this thread's chunk only) for
@@ -229,7 +236,7 @@ MOE_DEV void gg_store_tile(const GGArgs& a, const df32x16_t (&acc)[C::MI][C::NI]
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const float dh = acc[mi][ni][4 * g + r];
-                const float sg = 1.0f / (1.0f + expf(-gf[r]));
+                const float sg = fast_sigmoid(gf[r]);
                 dg[r] = dh * uf[r] * sg * (1.0f + gf[r] * (1.0f - sg));
                 du[r] = dh * gf[r] * sg;
               }
