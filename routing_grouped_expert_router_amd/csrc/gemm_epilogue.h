@@ -36,8 +36,9 @@ MOE_DEV void dunpack4(uint2 p, float* v) {
 //    tile of the expert, so blocks restart at the expert's first row), the
 //    rows past rows_valid counting as zeros; codes of output row col0 + c at
 //    token column qcol0 + ..., scale bytes in the grouped layout of K rows.
-// Each thread takes one 32-value block of each orientation per NT blocks;
-// scale bytes are stored one by one.
+// Each thread takes one 32-value block of each orientation per NT blocks,
+// encoded from the staged bf16 words with the packed encoder (the codes the
+// quantiser writes); scale bytes are stored one by one.
 template <class C>
 MOE_DEV void mx_quantize_plane(const uint16_t* stg, const MxQOut& o, size_t grow0, int rows_valid, int col0,
                                int K, int n_rows, int P, int qcol0, int tid) {
@@ -45,16 +46,15 @@ MOE_DEV void mx_quantize_plane(const uint16_t* stg, const MxQOut& o, size_t grow
   constexpr int RB = CW / 32, CB = BM / 32;        // blocks per tile row / per tile column
   for (int it = tid; it < BM * RB; it += NT) {
     const int r = it / RB, b = it % RB;
-    float v[32];
+    uint32_t w[16];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      float f[8];
-      unpack(*reinterpret_cast<const V16*>(stg + r * LDW + 32 * b + 8 * k), f);
+      const V16 t = *reinterpret_cast<const V16*>(stg + r * LDW + 32 * b + 8 * k);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) v[8 * k + m] = f[m];
+      for (int m = 0; m < 4; ++m) w[4 * k + m] = t.w[m];
     }
     V16 out[2];
-    const uint32_t code = quantize_block(v, out);
+    const uint32_t code = quantize_block_bf16(w, out);
     if (r < rows_valid) {
       const size_t grow = grow0 + r;
       V16* qp = reinterpret_cast<V16*>(o.q_rows + grow * K + col0 + 32 * b);
@@ -65,14 +65,16 @@ MOE_DEV void mx_quantize_plane(const uint16_t* stg, const MxQOut& o, size_t grow
   }
   for (int it = tid; it < CW * CB; it += NT) {
     const int c = it % CW, b = it / CW;
-    float v[32];
+    uint32_t w[16];   // rows 2i, 2i+1 of the block in one word (rows past rows_valid: +0)
 #pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      const int row = 32 * b + r;
-      v[r] = row < rows_valid ? bf16_to_f32(stg[row * LDW + c]) : 0.f;
+    for (int i = 0; i < 16; ++i) {
+      const int row = 32 * b + 2 * i;
+      const uint32_t lo = row < rows_valid ? stg[row * LDW + c] : 0u;
+      const uint32_t hi = row + 1 < rows_valid ? stg[(row + 1) * LDW + c] : 0u;
+      w[i] = lo | hi << 16;
     }
     V16 out[2];
-    const uint32_t code = quantize_block(v, out);
+    const uint32_t code = quantize_block_bf16(w, out);
     V16* qp = reinterpret_cast<V16*>(o.q_cols + (size_t)(col0 + c) * P + qcol0 + 32 * b);
     qp[0] = out[0];
     qp[1] = out[1];
