@@ -16,17 +16,19 @@ constexpr int kWave = 64;
 // bf16 values travel as raw 16-bit patterns; arithmetic is binary32.
 MOE_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
-// Round binary32 to the nearest bf16, ties to even (NaN stays NaN).
-MOE_DEV uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
+// binary32 -> bf16 by gfx950's v_cvt_pk_bf16_f32: round to nearest even,
+// subnormals kept, a NaN becomes the quiet NaN (bits >> 16) | 0x40. Checked
+// on the device against that rule written out in integer arithmetic, for
+// every one of the 2^32 binary32 patterns: no difference.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+MOE_DEV uint16_t f32_to_bf16(float f) { return static_cast<uint16_t>(pack_bf16x2(f, 0.0f)); }
 
 // Element access for the two storage types.
 template <typename T> struct Elem;
