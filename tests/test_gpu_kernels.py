@@ -395,6 +395,53 @@ def test_grouped_gemm_parity(kind, counts, d, F, capacity, ws_kind):
 
 
 @pytest.mark.parametrize("counts,d,F", [
+    ([300, 0, 1, 129, 513, 64], 512, 512),
+    ([700, 5, 1000], 256, 1024),
+])
+def test_grouped_gemm_outputs_round_like_the_oracle(counts, d, F):
+    """Op by op, each bf16 output is compared with the oracle's value of the
+    same op computed in float64 from the library's own inputs to that op (its
+    G and U for H and the SwiGLU derivative, its H for the down projection and
+    dW_down, its dG and dU for dX and the gate/up weight gradients) and
+    rounded once to bf16. The library rounds binary32 sums once, with the
+    SwiGLU's sigmoid from the hardware exponential and reciprocal and the
+    rounding by v_cvt_pk_bf16_f32; nearly every element must then be the
+    oracle's bf16 value itself, the rest lying where the binary32 sum straddles
+    a bf16 rounding boundary."""
+    rng, E, n_rows, groups, st, T, grp = _gg_case("bf16", counts, d, F, 17 + d + F)
+    e = lambda *s: torch.full(s, float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = dict(g=e(n_rows, F), u=e(n_rows, F), h=e(n_rows, F), y_perm=e(n_rows, d), dg=e(n_rows, F),
+               du=e(n_rows, F), dx_perm=e(n_rows, d), dw_gate=e(E, d, F), dw_up=e(E, d, F), dw_down=e(E, F, d))
+    x, dyp, wg, wu, wd = T["x_perm"], T["dy_perm"], T["w_gate"], T["w_up"], T["w_down"]
+    ws = torch.zeros(16, dtype=torch.int32, device="cuda")
+
+    def run(op, **kw):
+        L.moe_grouped_gemm(L.make_gg_desc(op, L.MOE_BF16, E, d, F, n_rows, 0, grp, ws=ws, **kw))
+
+    run(L.MOE_GG_FWD_GATE_UP, x_perm=x[0], w_gate=wg[0], w_up=wu[0], g=out["g"], u=out["u"], h=out["h"])
+    run(L.MOE_GG_FWD_DOWN, h=out["h"], w_down=wd[0], y_perm=out["y_perm"])
+    run(L.MOE_GG_DGRAD_DOWN, dy_perm=dyp[0], w_down=wd[0], g=out["g"], u=out["u"], dg=out["dg"], du=out["du"])
+    run(L.MOE_GG_WGRAD_DOWN, h=out["h"], dy_perm=dyp[0], dw_down=out["dw_down"])
+    run(L.MOE_GG_DGRAD_GATE_UP, dg=out["dg"], du=out["du"], w_gate=wg[0], w_up=wu[0], dx_perm=out["dx_perm"])
+    run(L.MOE_GG_WGRAD_GATE_UP, x_perm=x[0], dg=out["dg"], du=out["du"], dw_gate=out["dw_gate"], dw_up=out["dw_up"])
+    got = {n: host(t) for n, t in out.items()}
+    G, U, _ = om.expert_fwd_gate_up(x[1], wg[1], wu[1], groups, st)
+    ref = {"g": G, "u": U, "h": st(om.silu(got["g"]) * got["u"]),
+           "y_perm": om.expert_fwd_down(got["h"], wd[1], groups, st),
+           "dx_perm": om.expert_dgrad_gate_up(got["dg"], got["du"], wg[1], wu[1], groups, st),
+           "dw_down": om.expert_wgrad_down(got["h"], dyp[1], groups, F, d, st)}
+    ref["dg"], ref["du"] = om.expert_dgrad_down(dyp[1], wd[1], got["g"], got["u"], groups, st)
+    ref["dw_gate"], ref["dw_up"] = om.expert_wgrad_gate_up(x[1], got["dg"], got["du"], groups, d, F, st)
+    fr = {}
+    for n, r in ref.items():
+        assert_close(got[n], r, "bf16", n)
+        fr[n] = float(np.mean(got[n] == r))
+    print("bf16 outputs equal to the oracle's:", {n: f"{v:.4f}" for n, v in fr.items()})
+    for n, v in fr.items():   # measured: 99.98-100 % on both shapes
+        assert v >= 0.999, (n, v)
+
+
+@pytest.mark.parametrize("counts,d,F", [
     ([512] * 16, 512, 256),                                   # equal: the equal-count split stays
     ([0, 4000, 1, 0, 17, 2000, 0, 0, 3, 900], 512, 256),     # skewed: balanced by work
     ([(7 * i) % 5 for i in range(600)], 256, 256),            # many small experts
