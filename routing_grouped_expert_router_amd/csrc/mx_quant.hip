@@ -307,14 +307,16 @@ struct BothTile {
   bool skip;   // would write past col_stride (offsets that break the contract)
 };
 
-// Tile j of the column-tile-major order: column tile j / total_rt, row tile
-// j % total_rt (a workgroup's consecutive tiles are row-adjacent, so its
-// transposed writes continue each output row where the last tile stopped).
+// Tile j of the row-tile-major order: row tile j / tiles_c, column tile
+// j % tiles_c, so a workgroup's consecutive tiles read the same 128 source
+// rows a column tile further each time (whole rows close together in time,
+// which suits DRAM better than revisiting each row once per column pass; every
+// transposed piece is a whole aligned 128-byte line either way).
 MOE_DEV BothTile both_tile(const Groups1& gr, const int* tile_start, const int* grp_rows, int total_rt,
-                           int col_stride, long j) {
+                           int col_stride, long j, int tiles_c) {
   BothTile t;
   int g, i;
-  lookup_tile(gr, tile_start, static_cast<int>(j % total_rt), g, i, t.p_g);
+  lookup_tile(gr, tile_start, static_cast<int>(j / tiles_c), g, i, t.p_g);
   if (gr.offsets) {
     t.r0 = grp_rows[2 * g];
     t.n = grp_rows[2 * g + 1];
@@ -322,7 +324,7 @@ MOE_DEV BothTile both_tile(const Groups1& gr, const int* tile_start, const int* 
     group_range(gr, g, t.r0, t.n);
   }
   t.row_in = i * kQRows;
-  t.c0 = static_cast<int>(j / total_rt) * kBCols;
+  t.c0 = static_cast<int>(j % tiles_c) * kBCols;
   t.skip = t.p_g + t.row_in + kQRows > col_stride;
   return t;
 }
@@ -428,9 +430,9 @@ __global__ void __launch_bounds__(256) mx_both_kernel(const uint16_t* __restrict
   const long b_end = b + per < total ? b + per : total;
   V16 pre[kBChunks];
   uint32_t valid = 0;
-  if (b < b_end) fetch_tile<GATHER>(src, cols, both_tile(gr, tile_start, grp_rows, total_rt, col_stride, b), rg, pre, valid);
+  if (b < b_end) fetch_tile<GATHER>(src, cols, both_tile(gr, tile_start, grp_rows, total_rt, col_stride, b, tiles_c), rg, pre, valid);
   for (; b < b_end; ++b) {
-    const BothTile t = both_tile(gr, tile_start, grp_rows, total_rt, col_stride, b);
+    const BothTile t = both_tile(gr, tile_start, grp_rows, total_rt, col_stride, b, tiles_c);
     if (!t.skip) {
       constexpr int CH = kBCols / 8;
 #pragma unroll
@@ -442,7 +444,7 @@ __global__ void __launch_bounds__(256) mx_both_kernel(const uint16_t* __restrict
     __syncthreads();
     const long nb = b + 1;
     if (nb < b_end)
-      fetch_tile<GATHER>(src, cols, both_tile(gr, tile_start, grp_rows, total_rt, col_stride, nb), rg, pre, valid);
+      fetch_tile<GATHER>(src, cols, both_tile(gr, tile_start, grp_rows, total_rt, col_stride, nb, tiles_c), rg, pre, valid);
     if (!t.skip) {
       const int r0 = t.r0, n = t.n, row_in = t.row_in, c0 = t.c0;
       // rows: thread (r, h) quantises blocks 2h, 2h+1 (64 values) of tile row r
