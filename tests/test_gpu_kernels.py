@@ -394,6 +394,13 @@ def test_grouped_gemm_parity(kind, counts, d, F, capacity, ws_kind):
             assert np.all(host(out["dw_down"][e_]) == 0) and np.all(host(out["dw_gate"][e_]) == 0)
 
 
+def test_grouped_gemm_most_experts():
+    """The most experts the ABI takes (1024), each with 0-3 rows: the tile
+    prefix and the weight-gradient split fill their 1025-entry tables, and a
+    quarter of the experts are empty."""
+    test_grouped_gemm_parity("bf16", [(3 * i) % 4 for i in range(1024)], 256, 256, 0, "sized")
+
+
 @pytest.mark.parametrize("counts,d,F", [
     ([300, 0, 1, 129, 513, 64], 512, 512),
     ([700, 5, 1000], 256, 1024),
