@@ -353,6 +353,13 @@ def test_mx_each_gemm_on_oracle_inputs(counts, d, F):
     print("rel err, exact fraction", report)
 
 
+def test_mx_each_gemm_most_experts():
+    """The most experts the ABI takes (1024), each with 0-3 rows: every
+    group table of the quantiser and the MXFP8 GEMM is full, and each expert's
+    padded token segment is one 128-column tile."""
+    test_mx_each_gemm_on_oracle_inputs([(3 * i) % 4 for i in range(1024)], 256, 256)
+
+
 @pytest.mark.parametrize("counts", [[0, 2500, 1, 0, 17, 1200, 3, 600], [256] * 16])
 def test_mx_wgrad_workspace(counts):
     """The MXFP8 weight gradients' workspace, read back: the tile split is the
