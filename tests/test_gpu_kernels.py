@@ -328,7 +328,7 @@ def _gg_case(kind, counts, d, F, seed, capacity=0):
     return rng, E, n_rows, groups, st, T, grp
 
 
-@pytest.mark.parametrize("kind,counts,d,F,capacity", [
+_GG_CASES = [
     ("bf16", [300, 0, 1, 129, 513, 64, 0, 257], 256, 512, 0),          # MFMA path, ragged
     ("bf16", [700, 5, 1000, 0], 512, 256, 0),
     ("bf16", [40, 100, 0, 7, 128, 3], 256, 256, 128),                 # padded (uniform groups)
@@ -341,14 +341,21 @@ def _gg_case(kind, counts, d, F, seed, capacity=0):
     ("bf16", [5, 3000], 256, 256, 0),
     ("bf16", [0, 4000, 1, 0, 17, 2000, 0, 0, 3, 900], 512, 256, 0),  # strongly skewed
     ("bf16", [(7 * i) % 5 for i in range(600)], 256, 256, 0),        # > 512 experts: two per prefix thread
-])
-@pytest.mark.parametrize("ws_kind", ["tile_split", "sized"])
+]
+
+
+# "sized" workspaces only where K can be split: bf16 weight gradients over
+# device-resident groups
+_GG_PARAMS = [pytest.param(*c, ws, id=f"{ws}-{c[0]}-{len(c[1])}e-{c[2]}-{c[3]}-{c[4]}")
+              for c in _GG_CASES for ws in ("tile_split", "sized")
+              if ws == "tile_split" or (c[0] == "bf16" and not c[4])]
+
+
+@pytest.mark.parametrize("kind,counts,d,F,capacity,ws_kind", _GG_PARAMS)
 def test_grouped_gemm_parity(kind, counts, d, F, capacity, ws_kind):
     """ws_kind "tile_split": a 64-byte workspace (weight gradients unsplit in
     K); "sized": the workspace the library asks for, so launches of few tiles
     split K into chunks and reduce their partial sums."""
-    if ws_kind == "sized" and (kind != "bf16" or capacity):
-        pytest.skip("K is split only for bf16 weight gradients over device-resident groups")
     rng, E, n_rows, groups, st, T, grp = _gg_case(kind, counts, d, F, hash((tuple(counts), d, F)) % 1000, capacity)
     dt = torch.bfloat16 if kind == "bf16" else torch.float32
     code = L.MOE_BF16 if kind == "bf16" else L.MOE_F32
