@@ -147,22 +147,27 @@ __global__ void __launch_bounds__(256) router_gemm_lds_kernel(const uint16_t* __
 }
 
 // The bf16 product on the matrix cores (E <= 16, E % 8 == 0, d % 256 == 0,
-// d * E * 2 bytes of w_r fit in 64 KB). One wave per block of 16 tokens:
-// v_mfma_f32_16x16x32_bf16 with the tokens as rows (A: lane (r, g) holds
-// x[t0 + r][k(s, g) .. + 7]) and the experts as columns (B: lane (r, g)
-// holds w_r[k(s, g) .. + 7][r]). K step s takes the k order
-// k(s, g) = 64 (s / 2) + 16 g + 8 (s % 2) (any order of the sum is the same
-// product): each load instruction then touches whole 128-byte lines of its 16
-// rows (the four lanes of a row 32 bytes apart, the next step filling the
-// gaps), which streams at about 5.4 TB/s where the plain order's 64-byte
-// halves of 16 rows stay near 4.2. The wave streams its 16 rows over the
-// whole of d in chunks of kRmCh K steps, the next chunk's loads issued
-// before the current chunk's MFMAs, and stores its 16 x E logits itself (no
-// cross-wave reduction, no barrier after staging). w_r is staged once per
-// workgroup in LDS in fragment order (the 64 lanes of one K step read one
-// contiguous 1 KB). Columns r >= E read column E-1 and rows past T read row
-// T-1: an A row or B column feeds only its own output, which is not stored.
-constexpr int kRmCh = 8;   // K steps (of 32) per chunk (even): 8 KB of x per wave in flight per chunk
+// d * E * 2 bytes of w_r fit in 64 KB): v_mfma_f32_16x16x32_bf16 with the
+// tokens as rows (A: lane (r, g) holds x[t0 + r][k(s, g) .. + 7]) and the
+// experts as columns (B: lane (r, g) holds w_r[k(s, g) .. + 7][r]). K step s
+// takes the k order k(s, g) = 64 (s / 2) + 16 g + 8 (s % 2) (any order of the
+// sum is the same product): each load instruction then touches whole
+// 128-byte lines of its 16 rows (the four lanes of a row 32 bytes apart, the
+// next step filling the gaps), which streams at about 5.4 TB/s where the
+// plain order's 64-byte halves of 16 rows stay near 4.2.
+//
+// The product only streams x, so its rate is the number of x bytes in flight
+// per CU. A workgroup of 16 waves takes 16 / SPLIT blocks of 16 tokens; the
+// SPLIT waves of one block split d into chunks of kRmCh K steps dealt round
+// robin (wave q takes chunks q, q + SPLIT, ...), issue the loads of all their
+// chunks (NQ <= 2 of them: SPLIT is 4 up to d = 2048 and 8 above) before w_r
+// is staged, and add their partial sums through LDS in the fixed order
+// q = 0, 1, ..., SPLIT - 1 (the result does not depend on timing). w_r is staged once per workgroup in LDS in fragment
+// order (the 64 lanes of one K step read one contiguous 1 KB). Columns r >= E
+// read column E-1, rows past T read row T-1 and chunk indices past d re-read
+// the last chunk: such an A row, B column or chunk feeds only an output that
+// is not stored or a sum that skips it.
+constexpr int kRmCh = 8;     // K steps (of 32) per chunk (even): 8 KB of x per wave per chunk
 constexpr int kRmMaxLds = 64 * 1024;
 
 static bool router_mfma_shape(int d, int E) {
@@ -172,38 +177,47 @@ static bool router_mfma_shape(int d, int E) {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 rbf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float rf32x4_t;
 
-__global__ void __launch_bounds__(256) router_gemm_mfma_kernel(const uint16_t* __restrict__ x,
-                                                               const uint16_t* __restrict__ w_r, int T_,
-                                                               int d, int E, float* __restrict__ logits) {
+// NQ: chunks per wave, ceil(d / (32 kRmCh) / SPLIT)
+template <int NQ, int SPLIT>
+__global__ void __launch_bounds__(1024) router_gemm_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ w_r, int T_,
+                                                                int d, int E, float* __restrict__ logits) {
   extern __shared__ __attribute__((aligned(16))) uint16_t wfrag[];   // [d/32][4][E][8]
+  constexpr int BPW = 16 / SPLIT;                                     // blocks per workgroup
+  __shared__ rf32x4_t part[16 * 64];                                  // [d part][block slot][lane]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
+  const int b = wave % BPW, q = wave / BPW;       // block slot, d part
   const int nblk = (T_ + 15) / 16;
   const int nch = d / (32 * kRmCh);
-  int blk = blockIdx.x * 4 + wave;
-  // k(s, g) = 64 (s / 2) + 16 g + 8 (s % 2); kRmCh is even, so step c kRmCh + s
-  // of chunk c starts at column 32 c kRmCh + k(s, g)
-  const uint16_t* xr = x + (size_t)min(blk * 16 + r, T_ - 1) * d + g * 16;
-  rbf16x8_t a0[kRmCh], a1[kRmCh], a2[kRmCh];
-  auto load = [&](int c, rbf16x8_t (&dst)[kRmCh]) {
+  rbf16x8_t a[NQ][kRmCh];
+  auto load = [&](int blk) {
+    const uint16_t* xr = x + (size_t)min(blk * 16 + r, T_ - 1) * d + g * 16;
 #pragma unroll
-    for (int s = 0; s < kRmCh; ++s)
-      dst[s] = *reinterpret_cast<const rbf16x8_t*>(xr + c * kRmCh * 32 + (s >> 1) * 64 + (s & 1) * 8);
+    for (int j = 0; j < NQ; ++j) {
+      const int c = min(q + SPLIT * j, nch - 1);
+#pragma unroll
+      for (int s = 0; s < kRmCh; ++s)
+        a[j][s] = *reinterpret_cast<const rbf16x8_t*>(xr + c * kRmCh * 32 + (s >> 1) * 64 + (s & 1) * 8);
+    }
   };
-  // the first two chunks are in flight while w_r is staged (a clamped chunk
-  // index re-reads the last chunk, from cache, when d has fewer chunks)
-  load(0, a0);
-  load(min(1, nch - 1), a1);
+  int base = blockIdx.x * BPW;
+  load(base + b);
   // stage w_r: 16-byte pieces (8 experts of one row k) to fragment order,
-  // eight loads per thread in flight before their LDS writes
+  // two loads per thread in flight before their LDS writes (one round when
+  // d * E <= 16384). A thread past the last piece re-reads a distinct real
+  // piece (index mod pieces) rather than all of them one line.
   const int pieces = d * E / 8;
-  for (int p0 = 0; p0 < pieces; p0 += 256 * 8) {
-    V16 v[8];
+  for (int p0 = 0; p0 < pieces; p0 += 2048) {
+    V16 v[2];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = reinterpret_cast<const V16*>(w_r)[min(p0 + j * 256 + (int)threadIdx.x, pieces - 1)];
+    for (int j = 0; j < 2; ++j) {
+      const int p = p0 + j * 1024 + threadIdx.x;
+      v[j] = reinterpret_cast<const V16*>(w_r)[p < pieces ? p : p % pieces];
+    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int p = p0 + j * 256 + threadIdx.x;
+    for (int j = 0; j < 2; ++j) {
+      const int p = p0 + j * 1024 + threadIdx.x;
       if (p >= pieces) break;
       // row k of w_r belongs to step s = 2 (k / 64) + (k / 8) % 2, lane group
       // g = (k % 64) / 16, element k % 8 of the fragment
@@ -219,45 +233,44 @@ __global__ void __launch_bounds__(256) router_gemm_mfma_kernel(const uint16_t* _
   }
   __syncthreads();
   const uint16_t* wl = wfrag + (g * E + min(r, E - 1)) * 8;
-  for (; blk < nblk; blk += gridDim.x * 4) {
+  // the loop condition is the same for every wave of the workgroup (barriers)
+  for (; base < nblk; base += gridDim.x * BPW) {
     rf32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    auto mfmas = [&](int c, const rbf16x8_t (&src)[kRmCh]) {
 #pragma unroll
-      for (int s = 0; s < kRmCh; ++s) {
-        const rbf16x8_t b = *reinterpret_cast<const rbf16x8_t*>(wl + (c * kRmCh + s) * 32 * E);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(src[s], b, acc, 0, 0, 0);
-      }
-    };
-    // three chunk buffers in rotation: while chunk c is multiplied, chunks
-    // c + 1 and c + 2 are in flight. Every load is unconditional (clamped to
-    // the last chunk) and fenced from the MFMAs so that it is issued early.
-    for (int c = 0; c < nch; c += 3) {
-      load(min(c + 2, nch - 1), a2);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(c, a0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (c + 1 >= nch) break;
-      load(min(c + 3, nch - 1), a0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(c + 1, a1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (c + 2 >= nch) break;
-      load(min(c + 4, nch - 1), a1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(c + 2, a2);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // lane (r, g) holds tokens 4g .. 4g+3 of the block, expert r
-    if (r < E) {
+    for (int j = 0; j < NQ; ++j) {
+      const int c = q + SPLIT * j;
+      if (c < nch) {   // wave-uniform; no load sits under it
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = blk * 16 + 4 * g + i;
-        if (t < T_) logits[(size_t)t * E + r] = acc[i];
+        for (int s = 0; s < kRmCh; ++s) {
+          const rbf16x8_t bw = *reinterpret_cast<const rbf16x8_t*>(wl + (c * kRmCh + s) * 32 * E);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j][s], bw, acc, 0, 0, 0);
+        }
       }
     }
-    xr = x + (size_t)min((blk + (int)gridDim.x * 4) * 16 + r, T_ - 1) * d + g * 16;
-    load(0, a0);
-    load(min(1, nch - 1), a1);
+    part[(q * BPW + b) * 64 + lane] = acc;
+    // the next blocks' loads fly while the partials are added (only when this
+    // workgroup has a next iteration: the condition is the same for all its
+    // waves)
+    if (base + (int)gridDim.x * BPW < nblk) load(base + (int)gridDim.x * BPW + b);
+    __syncthreads();
+    if (q == 0) {
+      rf32x4_t sum = part[b * 64 + lane];
+#pragma unroll
+      for (int p = 1; p < SPLIT; ++p) {
+        const rf32x4_t v = part[(p * BPW + b) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[i] += v[i];
+      }
+      // lane (r, g) holds tokens 4g .. 4g+3 of the block, expert r
+      if (r < E) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = (base + b) * 16 + 4 * g + i;
+          if (t < T_) logits[(size_t)t * E + r] = sum[i];
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -905,11 +918,20 @@ extern "C" int moe_router_gemm(int dtype, const void* x, const void* w_r, int T,
   MOE_CHECK_ARG(x && w_r && logits && aligned16(x));
   const bool wide = E % kRouterEC == 0 && aligned16(w_r);
   if (dtype == MOE_BF16 && wide && router_mfma_shape(d, E)) {
-    // one wave per 16 tokens, at most 256 workgroups of four waves (one per CU)
+    // 16 / split blocks of 16 tokens per workgroup of 16 waves, at most 256
+    // workgroups (one per CU); dynamic LDS holds w_r
     const long nblk = (T + 15) / 16;
-    const int blocks = static_cast<int>(std::min<long>(256, (nblk + 3) / 4));
-    router_gemm_mfma_kernel<<<blocks, 256, (size_t)d * E * 2, stream>>>(
-        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_r), T, d, E, logits);
+    const int nch = d / (32 * kRmCh);                 // 1..16 under the 64 KB w_r limit
+    const int split = nch <= 8 ? 4 : 8;
+    const int nq = (nch + split - 1) / split;         // 1 or 2
+    const int bpw = 16 / split;
+    const int blocks = static_cast<int>(std::min<long>(256, (nblk + bpw - 1) / bpw));
+    const size_t lds = (size_t)d * E * 2;
+    const auto* xp = static_cast<const uint16_t*>(x);
+    const auto* wp = static_cast<const uint16_t*>(w_r);
+    if (split == 4 && nq == 1) router_gemm_mfma_kernel<1, 4><<<blocks, 1024, lds, stream>>>(xp, wp, T, d, E, logits);
+    else if (split == 4) router_gemm_mfma_kernel<2, 4><<<blocks, 1024, lds, stream>>>(xp, wp, T, d, E, logits);
+    else router_gemm_mfma_kernel<2, 8><<<blocks, 1024, lds, stream>>>(xp, wp, T, d, E, logits);
     return launch_status();
   }
   const int waves = (T + kRouterTok - 1) / kRouterTok;

@@ -228,7 +228,8 @@ def test_combine_adjoint_with_bad_ids(C):
         assert np.array_equal(got["rows"][1], got["tokens"][1])
 
 
-@pytest.mark.parametrize("T,d,E", [(333, 1024, 16), (2000, 512, 8)])
+@pytest.mark.parametrize("T,d,E", [(333, 1024, 16), (2000, 512, 8),
+                                   (300, 2304, 8), (1500, 4096, 8), (5000, 256, 16)])
 def test_router_gemm_matrix_core_and_cache_paths(T, d, E):
     """The bf16 router GEMM on the matrix cores (w_r 16-byte aligned) and the
     FMA kernel that reads w_r through the cache (w_r at a 2-byte offset) both
