@@ -229,7 +229,8 @@ def test_combine_adjoint_with_bad_ids(C):
 
 
 @pytest.mark.parametrize("T,d,E", [(333, 1024, 16), (2000, 512, 8),
-                                   (300, 2304, 8), (1500, 4096, 8), (5000, 256, 16)])
+                                   (300, 2304, 8), (1500, 4096, 8), (5000, 256, 16),
+                                   (1, 2048, 8), (15, 2048, 16), (17, 4096, 8), (16400, 2048, 8)])
 def test_router_gemm_matrix_core_and_cache_paths(T, d, E):
     """The bf16 router GEMM on the matrix cores (w_r 16-byte aligned) and the
     FMA kernel that reads w_r through the cache (w_r at a 2-byte offset) both
