@@ -181,6 +181,8 @@ def test_row_movement_parity(kind, T, d, E, k, C):
     L.moe_permute_bwd(dxpt, row_of, k, dx, dev(dl.astype(np.float32), "f32"), wrt, dx_add=yat)
     assert_close(host(dx), om.permute_bwd(dxp, meta["row_of"], T, k, st, dl @ wr.T + ya), kind,
                  "dx+router+shared")
+    L.moe_permute_bwd(dxpt, row_of, k, dx, dx_add=yat)
+    assert_close(host(dx), om.permute_bwd(dxp, meta["row_of"], T, k, st, ya), kind, "dx+shared")
 
 
 @pytest.mark.parametrize("C", [0, 40])
