@@ -209,7 +209,7 @@ def mfma(args):
     if args.command:
         out += ["Command (from the repository root):", "", "```", args.command, "```", ""]
     out += ["Source: rocprofv3 `--pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16`, means over the run's "
-            "launches. `MfmaUtil` is the fraction of SIMD cycles with the matrix core busy while the GPU "
+            f"launches after each kernel's first {args.skip} (the bench's warm-up steps). `MfmaUtil` is the fraction of SIMD cycles with the matrix core busy while the GPU "
             "is active (so it is measured against the clock the GPU actually ran at); executed GFLOP "
             "counts every MFMA issued, including the zero rows of partial tiles.", "",
             "| stage | launches | MfmaUtil % | executed GFLOP | algorithmic GFLOP | executed / algorithmic |",
@@ -218,8 +218,8 @@ def mfma(args):
         v = vals.get(st)
         if not v:
             continue
-        util = v.get("MfmaUtil", [])
-        mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [])
+        util = v.get("MfmaUtil", [])[args.skip:]
+        mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [])[args.skip:]
         ex = sum(mops) / len(mops) * 512 / 1e9 if mops else float("nan")
         _, work = stage_work(st, wl, R, R)
         out.append(f"| {st} | {len(util)} | {sum(util) / max(len(util), 1):.1f} | {ex:.1f} | "
@@ -328,6 +328,7 @@ def main():
     m.add_argument("csv")
     m.add_argument("--workload", default="e128_uniform_bf16")
     m.add_argument("--command")
+    m.add_argument("--skip", type=int, default=0, help="warm-up launches per kernel to leave out")
     a = ap.parse_args()
     if a.mode == "mfma":
         return mfma(a)
