@@ -199,6 +199,7 @@ def mfma(args):
     from moe_inputs import workload
     wl = workload(args.workload)
     R = wl.T * wl.k
+    skip = getattr(args, "skip", 0)
     vals = {}
     for r in csv.DictReader(open(args.csv)):
         st = stage_of(r["Kernel_Name"])
@@ -208,8 +209,10 @@ def mfma(args):
     out = ["# Matrix-core utilisation of the grouped GEMMs: " + wl.name, ""]
     if args.command:
         out += ["Command (from the repository root):", "", "```", args.command, "```", ""]
+    span = (f"launches after each kernel's first {skip} (the bench's warm-up steps)" if skip
+            else "launches")
     out += ["Source: rocprofv3 `--pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16`, means over the run's "
-            f"launches after each kernel's first {args.skip} (the bench's warm-up steps). `MfmaUtil` is the fraction of SIMD cycles with the matrix core busy while the GPU "
+            f"{span}. `MfmaUtil` is the fraction of SIMD cycles with the matrix core busy while the GPU "
             "is active (so it is measured against the clock the GPU actually ran at); executed GFLOP "
             "counts every MFMA issued, including the zero rows of partial tiles.", "",
             "| stage | launches | MfmaUtil % | executed GFLOP | algorithmic GFLOP | executed / algorithmic |",
@@ -218,8 +221,8 @@ def mfma(args):
         v = vals.get(st)
         if not v:
             continue
-        util = v.get("MfmaUtil", [])[args.skip:]
-        mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [])[args.skip:]
+        util = v.get("MfmaUtil", [])[skip:]
+        mops = v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [])[skip:]
         ex = sum(mops) / len(mops) * 512 / 1e9 if mops else float("nan")
         _, work = stage_work(st, wl, R, R)
         out.append(f"| {st} | {len(util)} | {sum(util) / max(len(util), 1):.1f} | {ex:.1f} | "

@@ -132,4 +132,9 @@ def test_mfma_summary(tmp_path):
     line = [l for l in out.read_text().splitlines() if l.startswith("| gg_fwd_down")][0]
     assert line == "| gg_fwd_down | 2 | 40.0 | 412.3 | 274.9 | 1.500 |"
     assert "gg_wgrad_down" not in out.read_text()
+    # warm-up launches left out: only the second launch counts
+    mfma(argparse.Namespace(out=str(out), csv=str(tmp_path / "m.csv"), workload="e128_uniform_bf16",
+                            command=None, skip=1))
+    line = [l for l in out.read_text().splitlines() if l.startswith("| gg_fwd_down")][0]
+    assert line == "| gg_fwd_down | 1 | 50.0 | 412.3 | 274.9 | 1.500 |"
 
